@@ -1,0 +1,174 @@
+"""Pins of the oracle's ModUp, ModDown and whole key switch (CPU only).
+
+ModUp and ModDown are checked coefficient by coefficient against exact CRT
+reconstruction with big integers (sympy): fast base conversion must return
+x + u*Q_d with 0 <= u < alpha_d (exactly x when alpha_d = 1), and ModDown's
+output times P must equal acc - C with C = [acc]_P + v*P, 0 <= v < K. The
+whole key switch is checked by decrypting under the real secrets: the error
+must be the same small integer polynomial on every limb and stay within the
+analytic bound. Planted mistakes in a copy of the oracle must fail the check.
+"""
+
+import math
+
+import numpy as np
+import pytest
+from sympy.ntheory.modular import crt
+
+import ks_inputs as ki
+from oracle import keyswitch as ks
+from oracle import rns
+
+
+def small_params(log2n=6, L=6, dnum=3, K=2, rounds=12):
+    return ks.Params(log2n, L, dnum, K, chacha_rounds=rounds)
+
+
+def _coef(limbs, moduli):
+    return [rns.intt(limbs[j], m) for j, m in enumerate(moduli)]
+
+
+@pytest.mark.parametrize("L,dnum,level", [(6, 3, 6), (6, 2, 6), (5, 2, 5), (6, 3, 4), (3, 3, 3)])
+def test_modup_is_fast_base_conversion(L, dnum, level):
+    prm = small_params(L=L, dnum=dnum)
+    N = prm.N
+    c1 = ki.uniform_limbs(np.random.default_rng(L * 10 + level), prm.q[:level], N)
+    ext = ks.modup(prm, c1, level)
+    basis = prm.basis(level)
+    c1_coef = _coef(c1, prm.q[:level])
+    for d, D in enumerate(prm.digits(level)):
+        Qd = math.prod(prm.q[i] for i in D)
+        ext_coef = _coef(ext[d], basis)
+        for i in D:  # the digit's own limbs are passed through
+            assert np.array_equal(ext[d, i], c1[i])
+        others = [j for j in range(len(basis)) if j not in D]
+        for n in range(N):
+            x = int(crt([prm.q[i] for i in D], [int(c1_coef[i][n]) for i in D])[0])
+            us = set()
+            for j in others:
+                t = basis[j]
+                z = int(ext_coef[j][n])
+                # find u with z = x + u*Qd (mod t), 0 <= u < alpha
+                cand = [u for u in range(len(D)) if (x + u * Qd - z) % t == 0]
+                assert len(cand) == 1, (d, j, n)
+                us.add(cand[0])
+            assert len(us) == 1  # the same u on every target
+            if len(D) == 1:
+                assert us == {0}
+
+
+@pytest.mark.parametrize("K,level", [(1, 3), (2, 6), (3, 5)])
+def test_moddown_floor_invariant(K, level):
+    prm = small_params(L=6, dnum=3, K=K)
+    N = prm.N
+    basis = prm.basis(level)
+    acc = ki.uniform_limbs(np.random.default_rng(K), basis, N)
+    out = ks.moddown(prm, acc, level)
+    acc_coef = _coef(acc, basis)
+    out_coef = _coef(out, prm.q[:level])
+    P = prm.P
+    Q = math.prod(prm.q[:level])
+    for n in range(N):
+        A = int(crt(basis, [int(acc_coef[j][n]) for j in range(len(basis))])[0])
+        O = int(crt(list(prm.q[:level]), [int(out_coef[i][n]) for i in range(level)])[0])
+        D = (A - P * O) % (P * Q)
+        assert D % P == A % P and D < K * P
+
+
+def _keys_and_secret(prm, widx, level, galois_list, h):
+    s = ki.ternary_secret(widx, prm.N, h)
+    keys, emax = [], 0
+    for kidx, g in enumerate(galois_list):
+        errs = ki.gaussian_errors(widx, kidx, len(prm.digits(level)), prm.N)
+        emax = max(emax, int(np.abs(errs).max()))
+        keys.append(ks.keygen(prm, s, errs, ki.key_seed(widx, kidx), level, g))
+    return s, keys, emax
+
+
+def _check_decrypts(prm, ct, out, s, galois, level, emax, h):
+    e = ks.decryption_error(prm, ct, out, s, galois, level)
+    assert e is not None, "error residues differ between limbs"
+    B = ks.error_bound(prm, level, emax, h)
+    assert np.abs(e).max() <= B
+    return e
+
+
+def test_tiny_rotation_decrypts():
+    w = ki.WORKLOADS["tiny"]
+    prm = ks.Params(w.log2n, w.L, w.dnum, w.K)
+    s, (key,), emax = _keys_and_secret(prm, w.index, w.L, (5,), w.h)
+    assert key.seed == bytes(32)
+    ct = ki.ciphertexts(w.index, prm.q, prm.N, 1)[0]
+    out = ks.keyswitch(prm, ct, key, w.L)
+    e = _check_decrypts(prm, ct, out, s, 5, w.L, emax, w.h)
+    assert np.abs(e).max() > 0  # a real, noisy key switch
+
+
+@pytest.mark.parametrize("galois,level", [(1, 6), (5, 6), (127, 4), (25, 5), (1, 1)])
+def test_small_keyswitch_decrypts(galois, level):
+    prm = small_params(log2n=6, L=6, dnum=3, K=2)
+    s, (key,), emax = _keys_and_secret(prm, 9, level, (galois,), 8)
+    ct = ki.ciphertexts(9, prm.q[:level], prm.N, 1)[0]
+    out = ks.keyswitch(prm, ct, key, level)
+    _check_decrypts(prm, ct, out, s, galois, level, emax, 8)
+
+
+def test_hoisted_equals_singles_and_stored_equals_regenerated():
+    prm = small_params(log2n=7, L=4, dnum=2, K=2)
+    level = 4
+    s, keys, _ = _keys_and_secret(prm, 5, level, (5, 25, 255), 10)
+    ct = ki.ciphertexts(5, prm.q, prm.N, 1)[0]
+    hoisted = ks.keyswitch_hoisted(prm, ct, keys, level)
+    for r, key in enumerate(keys):
+        assert np.array_equal(hoisted[r], ks.keyswitch(prm, ct, key, level))
+        stored = ks.Key(b=key.b, seed=None, level=level, galois=key.galois, a=ks.key_a(prm, key))
+        assert np.array_equal(ks.keyswitch(prm, ct, stored, level), hoisted[r])
+
+
+def test_planted_mistakes_fail_the_decryption_check(monkeypatch):
+    """Mistakes planted in the oracle (on the CPU) must break the decryption check."""
+    prm = small_params(log2n=6, L=4, dnum=2, K=2)
+    level = 4
+    s, (key,), emax = _keys_and_secret(prm, 11, level, (5,), 8)
+    ct = ki.ciphertexts(11, prm.q, prm.N, 1)[0]
+    good = ks.keyswitch(prm, ct, key, level)
+    _check_decrypts(prm, ct, good, s, 5, level, emax, 8)
+    B = ks.error_bound(prm, level, emax, 8)
+
+    def fails(out):
+        e = ks.decryption_error(prm, ct, out, s, 5, level)
+        return e is None or np.abs(e).max() > B
+
+    # dropped c0 term
+    bad = good.copy()
+    bad[0] = ks.moddown(prm, ks.inner_product(prm, ks.modup(prm, ct[1], level), key, level)[0], level)
+    assert fails(bad)
+    # one limb of the output off by one
+    bad = good.copy()
+    bad[1, 2, 7] = (int(bad[1, 2, 7]) + 1) % prm.q[2]
+    assert fails(bad)
+    # a digit dropped from the inner product
+    ext = ks.modup(prm, ct[1], level)
+    ext[1] = 0
+    assert fails(ks.keyswitch_from_ext(prm, ct, ext, key, level))
+    # a transposed automorphism (inverse map instead of the forward one)
+    real = ks.automorphism_index
+    monkeypatch.setattr(ks, "automorphism_index", lambda N, k: np.argsort(real(N, k)))
+    bad = ks.keyswitch(prm, ct, key, level)
+    monkeypatch.setattr(ks, "automorphism_index", real)
+    assert fails(bad)
+    # the wrong special-prime scale in ModDown
+    with monkeypatch.context() as m:
+        m.setattr(ks.Params, "P", property(lambda self: math.prod(self.p) + 2))
+        bad = ks.keyswitch(prm, ct, key, level)
+    assert fails(bad)
+
+
+@pytest.mark.slow
+def test_full_size_relinearisation_decrypts():
+    w = ki.WORKLOADS["n16"]
+    prm = ks.Params(w.log2n, w.L, w.dnum, w.K)
+    s, (key,), emax = _keys_and_secret(prm, w.index, w.L, (1,), w.h)
+    ct = ki.ciphertexts(w.index, prm.q, prm.N, 1)[0]
+    out = ks.keyswitch(prm, ct, key, w.L)
+    _check_decrypts(prm, ct, out, s, 1, w.L, emax, w.h)
