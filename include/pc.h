@@ -1,0 +1,162 @@
+/*
+ * pc.h -- C ABI of the MI355X (gfx950) CKKS hybrid key-switching library.
+ *
+ * What it computes. The Perseus README ('What's inside') describes a CKKS
+ * runtime whose key switching regenerates half of every key-switching key on
+ * the GPU from a ChaCha12 seed instead of storing it, and ('Layout') whose
+ * device runtime provides NTT and key-switching kernels over a 32-bit prime
+ * chain (opening paragraph: 32-bit kernels). The arXiv summary page of the
+ * Perseus paper (methodology, item (i)) calls the regeneration a ChaCha12
+ * counter-mode expander. The pages do not write the algorithm out; this
+ * library implements textbook RNS-CKKS hybrid key switching:
+ *
+ *   ModUp (iNTT, fast base conversion per digit, NTT) -> automorphism ->
+ *   inner product with the key (b half read, a half regenerated) ->
+ *   ModDown (iNTT of the special limbs, base conversion, NTT, scale by P^-1)
+ *   -> add the automorphism of c0.
+ *
+ * Conventions (readings of what the pages leave open):
+ *   - primes: q_0..q_{L-1} then p_0..p_{K-1}, by default every prime r < 2^31
+ *     with r = 1 (mod 2N), descending; user chains must be primes in
+ *     (2^30, 2^31), r = 1 (mod 2N), pairwise distinct;
+ *   - psi_r is the smallest primitive 2N-th root of unity mod r;
+ *   - a "limb" is N uint32 canonical residues (< r); polynomials are stored
+ *     limb-major, contiguous; evaluation form is natural order,
+ *     a_hat[j] = a(psi^(2j+1)) mod r;
+ *   - level l = number of active q primes; at level l the digits have
+ *     alpha(l) = ceil(l / dnum) primes, D_d = [d alpha, min((d+1) alpha, l)),
+ *     beta(l) = ceil(l / alpha) digits; a key used at level l was generated at
+ *     level l and has limbs q_0..q_{l-1}, p_0..p_{K-1} (the "key basis");
+ *   - ciphertext ct = [2][l][N] (c0 then c1), decrypting as c0 + c1 s;
+ *   - key b half: [beta][l+K][N] evaluation form (digit, key-basis limb,
+ *     position); the a half of digit d, limb j, position i is
+ *     (w[2i] + 2^32 w[2i+1]) mod r_j with w the ChaCha stream (12 rounds;
+ *     state: "expand 32-byte k", the 32-byte seed as 8 little-endian words,
+ *     block counter from 0 in word 12, nonce words (0, d, j)), read in
+ *     evaluation form;
+ *   - automorphism_idx = Galois element k (odd, < 2N; 1 = none): in evaluation
+ *     form out[i] = in[(i k + (k-1)/2) mod N]. It is applied to the ModUp
+ *     output (after ModUp, before the inner product) and to c0;
+ *   - ModDown uses the floor form (acc - Conv_{P->Q}([acc]_P)) * P^-1.
+ *
+ * Memory and streams. Every device pointer is a plain device address
+ * (hipMalloc or PyTorch memory), 16-byte aligned, on the device the params
+ * were created for; host pointers are marked "host". Calls enqueue work on
+ * `stream` (a hipStream_t; NULL = the null stream) and return without waiting;
+ * results are valid once the stream has reached that point. Inputs and outputs
+ * must not overlap. The library owns a workspace arena inside pc_params, sized
+ * at creation for max_batch ciphertexts and max_hoist keys; calls that use it
+ * must not run concurrently on different streams for the same pc_params.
+ *
+ * Errors. Every entry point validates its arguments on the host before any
+ * launch and returns PC_EINVAL (null pointer, level outside [1, L], even or
+ * out-of-range Galois element, batch above max_batch, ...), PC_EUNSUPPORTED
+ * (a shape the kernels do not cover), PC_ENOMEM (allocation at creation) or
+ * PC_EDEVICE (a HIP error, including no usable device). No call aborts the
+ * process; pc_strerror gives a static message.
+ */
+#ifndef PC_H
+#define PC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pc_params pc_params; /* opaque, library-owned, immutable after creation */
+
+enum {
+  PC_OK = 0,
+  PC_EINVAL = -1,
+  PC_ENOMEM = -2,
+  PC_EDEVICE = -3,
+  PC_EUNSUPPORTED = -4
+};
+
+typedef struct {
+  uint32_t log2n;         /* ring degree N = 2^log2n; 12, 16 or 17 */
+  uint32_t L;             /* q primes at the top level, >= 1 */
+  uint32_t dnum;          /* digits at the top level, 1..6, <= L */
+  uint32_t K;             /* special primes, >= 1 */
+  uint32_t max_batch;     /* most ciphertexts per key-switch call (0 means 1) */
+  uint32_t max_hoist;     /* most keys per hoisted call (0 means 1), <= 32 */
+  uint32_t chacha_rounds; /* 12 (0 means 12); 20 is accepted for testing against ChaCha20 */
+  const uint32_t *primes; /* host; NULL = the descending rule, else L + K primes (q's then p's) */
+} pc_params_desc;
+
+/* Build the prime chain, psi and every constant table on the host; with
+ * device >= 0, also upload them and allocate the workspace arena on that
+ * device. device = -1 builds the host tables only (pc_params_get works; every
+ * compute call returns PC_EDEVICE). The caller owns *out and frees it with
+ * pc_params_destroy. */
+int pc_params_create(const pc_params_desc *desc, int device, pc_params **out);
+void pc_params_destroy(pc_params *p);
+
+enum {
+  PC_GET_N = 1,               /* uint32: N */
+  PC_GET_PRIMES = 2,          /* uint32[L+K] */
+  PC_GET_PSI = 3,             /* uint32[L+K] */
+  PC_GET_ALPHA = 4,           /* uint32: alpha at level `arg` */
+  PC_GET_BETA = 5,            /* uint32: beta at level `arg` */
+  PC_GET_WORKSPACE_BYTES = 6, /* uint64: workspace of pc_keyswitch_ex at level `arg` for max_batch x max_hoist */
+  PC_GET_DEVICE_TABLE = 7     /* uint32[N]: forward twiddles psi^bitrev(k) of prime index `arg` (host copy) */
+};
+/* Copy a property into host memory dst (bytes must match exactly). */
+int pc_params_get(const pc_params *p, int what, uint32_t arg, void *dst, size_t bytes);
+
+/* Negacyclic NTT in place: coefficients -> natural-order evaluations, for
+ * nlimbs limbs of `data` ([nlimbs][N], device); limb z uses the prime with
+ * chain index prime_idx[z] (host array, values < L + K). Uses the arena. */
+int pc_ntt(const pc_params *p, uint32_t *data, const uint32_t *prime_idx, uint32_t nlimbs, void *stream);
+/* Inverse of pc_ntt (includes the N^-1 scale). */
+int pc_intt(const pc_params *p, uint32_t *data, const uint32_t *prime_idx, uint32_t nlimbs, void *stream);
+
+/* ModUp of c1 ([level][N], evaluation form, device) into
+ * ext ([beta][level+K][N], evaluation form, device): for digit d, limbs of D_d
+ * are copied from c1, the others are the fast base conversion of the digit
+ * ((sum_i [c1_i (Q_d/q_i)^-1]_{q_i} (Q_d/q_i)) mod r_j), taken to evaluation form. */
+int pc_modup(const pc_params *p, const uint32_t *c1, uint32_t level, uint32_t *ext, void *stream);
+
+/* One key switch: out ([2][level][N], device) from ct ([2][level][N], device)
+ * with the key whose b half is evk_b ([beta][level+K][N], device) and whose
+ * a half is regenerated from evk_seed (32 bytes, host). automorphism_idx is
+ * the key's Galois element (1 for relinearisation). */
+int pc_keyswitch(const pc_params *p, const uint32_t *ct, const uint32_t *evk_b, const uint8_t *evk_seed,
+                 uint32_t level, uint32_t automorphism_idx, uint32_t *out, void *stream);
+
+/* ModDown of one accumulator acc ([level+K][N], evaluation form, device) into
+ * out ([level][N], device): (acc - Conv_{P->Q}([acc]_P)) * P^-1 on the q limbs. */
+int pc_moddown(const pc_params *p, const uint32_t *acc, uint32_t level, uint32_t *out, void *stream);
+
+/* Batched / hoisted / stored-key key switching. Every ciphertext of the batch
+ * is key-switched by every key; ModUp runs once per ciphertext and is shared
+ * by all keys (hoisting). */
+typedef struct {
+  const uint32_t *ct;             /* device [batch][2][level][N] */
+  uint32_t batch;                 /* 1..max_batch */
+  uint32_t nkeys;                 /* 1..max_hoist */
+  const uint32_t *const *evk_b;   /* host array of nkeys device pointers, each [beta][level+K][N] */
+  const uint32_t *const *evk_a;   /* NULL (regenerate a from seeds) or host array of nkeys device pointers */
+  const uint8_t *seeds;           /* host [nkeys][32]; ignored when evk_a is given */
+  const uint32_t *galois;         /* host [nkeys] Galois elements */
+  uint32_t level;
+  uint32_t *out;                  /* device [nkeys][batch][2][level][N] */
+  void *workspace;                /* NULL: the params arena; else device memory of workspace_bytes */
+  size_t workspace_bytes;         /* >= PC_GET_WORKSPACE_BYTES for this level (when workspace is given) */
+} pc_ks_args;
+int pc_keyswitch_ex(const pc_params *p, const pc_ks_args *args, void *stream);
+
+/* Debug / parity: limb j (key-basis index at `level`) of digit d of the a half
+ * regenerated from seed (32 bytes, host): dst ([N], device) canonical mod r_j. */
+int pc_chacha_expand(const pc_params *p, const uint8_t *seed, uint32_t d, uint32_t j, uint32_t level, uint32_t *dst,
+                     void *stream);
+
+const char *pc_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PC_H */

@@ -1,0 +1,301 @@
+"""Python binding of libpc.so, the gfx950 CKKS hybrid key-switching library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/pc.h. Device buffers are
+PyTorch tensors (torch.int32 storage holding uint32 residues) and calls are
+enqueued on the current PyTorch stream. The module raises if the shared
+library has not been built (``python -m key_switching_amd.build``); there is
+no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpc.so")
+
+PC_OK, PC_EINVAL, PC_ENOMEM, PC_EDEVICE, PC_EUNSUPPORTED = 0, -1, -2, -3, -4
+PC_GET_N, PC_GET_PRIMES, PC_GET_PSI, PC_GET_ALPHA, PC_GET_BETA, PC_GET_WORKSPACE_BYTES, PC_GET_DEVICE_TABLE = range(1, 8)
+
+EXPORTED = ("pc_params_create", "pc_params_destroy", "pc_params_get", "pc_ntt", "pc_intt", "pc_modup",
+            "pc_keyswitch", "pc_moddown", "pc_keyswitch_ex", "pc_chacha_expand", "pc_strerror")
+
+
+class PcError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {_lib().pc_strerror(code).decode()} ({code})")
+        self.code = code
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("log2n", ctypes.c_uint32), ("L", ctypes.c_uint32), ("dnum", ctypes.c_uint32),
+                ("K", ctypes.c_uint32), ("max_batch", ctypes.c_uint32), ("max_hoist", ctypes.c_uint32),
+                ("chacha_rounds", ctypes.c_uint32), ("primes", ctypes.POINTER(ctypes.c_uint32))]
+
+
+class _KsArgs(ctypes.Structure):
+    _fields_ = [("ct", ctypes.c_void_p), ("batch", ctypes.c_uint32), ("nkeys", ctypes.c_uint32),
+                ("evk_b", ctypes.POINTER(ctypes.c_void_p)), ("evk_a", ctypes.POINTER(ctypes.c_void_p)),
+                ("seeds", ctypes.c_char_p), ("galois", ctypes.POINTER(ctypes.c_uint32)),
+                ("level", ctypes.c_uint32), ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m key_switching_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, u32, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int
+        lib.pc_params_create.argtypes = [ctypes.POINTER(_Desc), i32, ctypes.POINTER(vp)]
+        lib.pc_params_destroy.argtypes = [vp]
+        lib.pc_params_destroy.restype = None
+        lib.pc_params_get.argtypes = [vp, i32, u32, vp, ctypes.c_size_t]
+        lib.pc_ntt.argtypes = [vp, vp, ctypes.POINTER(u32), u32, vp]
+        lib.pc_intt.argtypes = [vp, vp, ctypes.POINTER(u32), u32, vp]
+        lib.pc_modup.argtypes = [vp, vp, u32, vp, vp]
+        lib.pc_keyswitch.argtypes = [vp, vp, vp, ctypes.c_char_p, u32, u32, vp, vp]
+        lib.pc_moddown.argtypes = [vp, vp, u32, vp, vp]
+        lib.pc_keyswitch_ex.argtypes = [vp, ctypes.POINTER(_KsArgs), vp]
+        lib.pc_chacha_expand.argtypes = [vp, ctypes.c_char_p, u32, u32, u32, vp, vp]
+        lib.pc_strerror.argtypes = [i32]
+        lib.pc_strerror.restype = ctypes.c_char_p
+        for name in ("pc_params_create", "pc_params_get", "pc_ntt", "pc_intt", "pc_modup", "pc_keyswitch",
+                     "pc_moddown", "pc_keyswitch_ex", "pc_chacha_expand"):
+            getattr(lib, name).restype = i32
+        _LIB = lib
+    return _LIB
+
+
+def _check(code: int, what: str):
+    if code != PC_OK:
+        raise PcError(code, what)
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev_ptr(t, name: str, shape=None, device=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if t.dtype not in (torch.int32, torch.uint32):
+        raise ValueError(f"{name} must hold 32-bit words (torch.int32 or torch.uint32)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if device is not None and t.device.index != device:
+        raise ValueError(f"{name} is on cuda:{t.device.index}, the params on cuda:{device}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Params:
+    """Parameter set, constant tables and workspace arena (pc_params_create)."""
+
+    def __init__(self, log2n: int, L: int, dnum: int, K: int, max_batch: int = 1, max_hoist: int = 1,
+                 chacha_rounds: int = 12, primes: Optional[Sequence[int]] = None, device: Optional[int] = 0):
+        lib = _lib()
+        desc = _Desc(log2n, L, dnum, K, max_batch, max_hoist, chacha_rounds, None)
+        self._primes_buf = None
+        if primes is not None:
+            self._primes_buf = (ctypes.c_uint32 * len(primes))(*[int(p) for p in primes])
+            desc.primes = ctypes.cast(self._primes_buf, ctypes.POINTER(ctypes.c_uint32))
+        self.device = -1 if device is None else int(device)
+        h = ctypes.c_void_p()
+        _check(lib.pc_params_create(ctypes.byref(desc), self.device, ctypes.byref(h)), "pc_params_create")
+        self._h = h
+        self.log2n, self.L, self.dnum, self.K = log2n, L, dnum, K
+        self.max_batch, self.max_hoist = max_batch, max_hoist
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("params closed")
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            _lib().pc_params_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    @property
+    def N(self) -> int:
+        return 1 << self.log2n
+
+    def _get_u32(self, what: int, arg: int = 0, count: int = 1):
+        buf = (ctypes.c_uint32 * count)()
+        _check(_lib().pc_params_get(self.handle, what, arg, buf, 4 * count), "pc_params_get")
+        return list(buf)
+
+    @property
+    def primes(self):
+        return self._get_u32(PC_GET_PRIMES, 0, self.L + self.K)
+
+    @property
+    def psi(self):
+        return self._get_u32(PC_GET_PSI, 0, self.L + self.K)
+
+    def alpha(self, level: int) -> int:
+        return self._get_u32(PC_GET_ALPHA, level)[0]
+
+    def beta(self, level: int) -> int:
+        return self._get_u32(PC_GET_BETA, level)[0]
+
+    def workspace_bytes(self, level: int) -> int:
+        buf = ctypes.c_uint64()
+        _check(_lib().pc_params_get(self.handle, PC_GET_WORKSPACE_BYTES, level, ctypes.byref(buf), 8),
+               "pc_params_get")
+        return int(buf.value)
+
+    def twiddles(self, prime_index: int):
+        return self._get_u32(PC_GET_DEVICE_TABLE, prime_index, self.N)
+
+    def basis(self, level: int):
+        """Moduli of the extended basis at this level: q_0..q_{level-1}, p_0..p_{K-1}."""
+        pr = self.primes
+        return pr[:level] + pr[self.L:]
+
+
+def _new(shape, like_device: int):
+    import torch
+    return torch.empty(shape, dtype=torch.int32, device=f"cuda:{like_device}")
+
+
+def ntt(prm: Params, data, prime_idx: Sequence[int]):
+    """In-place negacyclic NTT of data [len(prime_idx)][N] (pc_ntt)."""
+    idx = (ctypes.c_uint32 * len(prime_idx))(*[int(i) for i in prime_idx])
+    ptr = _dev_ptr(data, "data", (len(prime_idx), prm.N), prm.device)
+    _check(_lib().pc_ntt(prm.handle, ptr, idx, len(prime_idx), _stream()), "pc_ntt")
+    return data
+
+
+def intt(prm: Params, data, prime_idx: Sequence[int]):
+    """In-place inverse NTT (pc_intt)."""
+    idx = (ctypes.c_uint32 * len(prime_idx))(*[int(i) for i in prime_idx])
+    ptr = _dev_ptr(data, "data", (len(prime_idx), prm.N), prm.device)
+    _check(_lib().pc_intt(prm.handle, ptr, idx, len(prime_idx), _stream()), "pc_intt")
+    return data
+
+
+def modup(prm: Params, c1, level: int, ext=None):
+    """ModUp of c1 [level][N] into ext [beta][level+K][N] (pc_modup)."""
+    shape = (prm.beta(level), level + prm.K, prm.N)
+    if ext is None:
+        ext = _new(shape, prm.device)
+    _check(_lib().pc_modup(prm.handle, _dev_ptr(c1, "c1", (level, prm.N), prm.device), level,
+                           _dev_ptr(ext, "ext", shape, prm.device), _stream()), "pc_modup")
+    return ext
+
+
+def moddown(prm: Params, acc, level: int, out=None):
+    """ModDown of acc [level+K][N] into out [level][N] (pc_moddown)."""
+    if out is None:
+        out = _new((level, prm.N), prm.device)
+    _check(_lib().pc_moddown(prm.handle, _dev_ptr(acc, "acc", (level + prm.K, prm.N), prm.device), level,
+                             _dev_ptr(out, "out", (level, prm.N), prm.device), _stream()), "pc_moddown")
+    return out
+
+
+def _seed_bytes(seed) -> bytes:
+    seed = bytes(seed)
+    if len(seed) != 32:
+        raise ValueError("a seed is 32 bytes")
+    return seed
+
+
+def keyswitch(prm: Params, ct, evk_b, seed: bytes, level: int, galois: int, out=None):
+    """One key switch of ct [2][level][N] (pc_keyswitch)."""
+    if out is None:
+        out = _new((2, level, prm.N), prm.device)
+    kshape = (prm.beta(level), level + prm.K, prm.N)
+    _check(_lib().pc_keyswitch(prm.handle, _dev_ptr(ct, "ct", (2, level, prm.N), prm.device),
+                               _dev_ptr(evk_b, "evk_b", kshape, prm.device), _seed_bytes(seed), level, galois,
+                               _dev_ptr(out, "out", (2, level, prm.N), prm.device), _stream()), "pc_keyswitch")
+    return out
+
+
+def keyswitch_ex(prm: Params, ct, evk_b: Sequence, galois: Sequence[int], level: int, seeds=None, evk_a=None,
+                 out=None, workspace=None):
+    """Every ciphertext of ct [batch][2][level][N] under every key (pc_keyswitch_ex).
+
+    Returns out [nkeys][batch][2][level][N]. ``seeds`` lists one 32-byte seed
+    per key (regenerated a half); ``evk_a`` lists stored a halves instead.
+    """
+    batch = int(ct.shape[0])
+    nkeys = len(evk_b)
+    if len(galois) != nkeys:
+        raise ValueError("one Galois element per key")
+    kshape = (prm.beta(level), level + prm.K, prm.N)
+    if out is None:
+        out = _new((nkeys, batch, 2, level, prm.N), prm.device)
+    args = _KsArgs()
+    args.ct = _dev_ptr(ct, "ct", (batch, 2, level, prm.N), prm.device)
+    args.batch = batch
+    args.nkeys = nkeys
+    b_ptrs = (ctypes.c_void_p * nkeys)(*[_dev_ptr(b, "evk_b", kshape, prm.device).value for b in evk_b])
+    args.evk_b = b_ptrs
+    a_ptrs = None
+    if evk_a is not None:
+        if len(evk_a) != nkeys:
+            raise ValueError("one stored a half per key")
+        a_ptrs = (ctypes.c_void_p * nkeys)(*[_dev_ptr(a, "evk_a", kshape, prm.device).value for a in evk_a])
+        args.evk_a = a_ptrs
+    seed_blob = None
+    if seeds is not None:
+        if len(seeds) != nkeys:
+            raise ValueError("one seed per key")
+        seed_blob = b"".join(_seed_bytes(s) for s in seeds)
+        args.seeds = seed_blob
+    gal = (ctypes.c_uint32 * nkeys)(*[int(g) for g in galois])
+    args.galois = gal
+    args.level = level
+    args.out = _dev_ptr(out, "out", (nkeys, batch, 2, level, prm.N), prm.device)
+    if workspace is not None:
+        args.workspace = _dev_ptr(workspace, "workspace", None, prm.device)
+        args.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib().pc_keyswitch_ex(prm.handle, ctypes.byref(args), _stream()), "pc_keyswitch_ex")
+    return out
+
+
+def chacha_expand(prm: Params, seed: bytes, d: int, j: int, level: int, out=None):
+    """Limb j (key basis at level) of digit d of the regenerated a half (pc_chacha_expand)."""
+    if out is None:
+        out = _new((prm.N,), prm.device)
+    _check(_lib().pc_chacha_expand(prm.handle, _seed_bytes(seed), d, j, level,
+                                   _dev_ptr(out, "out", (prm.N,), prm.device), _stream()), "pc_chacha_expand")
+    return out
+
+
+# host <-> device helpers (uint32 residues held in int32 tensors)
+def to_device(arr, device: int = 0):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(np.asarray(arr).astype(np.uint32)).view(np.int32)
+    return torch.from_numpy(a).to(f"cuda:{device}")
+
+
+def to_host(t):
+    import numpy as np
+    return t.detach().cpu().numpy().view(np.uint32)

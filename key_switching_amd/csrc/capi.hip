@@ -1,0 +1,594 @@
+// C-ABI entry points and host-side construction of the constant tables.
+//
+// The tables follow the readings stated in include/pc.h: the descending
+// prime rule for the 32-bit chain (Perseus README, opening paragraph: 32-bit
+// kernels), psi = the smallest primitive 2N-th root, natural-order evaluation,
+// digits of alpha(l) = ceil(l/dnum) primes, ModDown in floor form.
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "internal.h"
+
+namespace pc {
+namespace {
+
+uint32_t mulmod(uint32_t a, uint32_t b, uint32_t r) { return (uint32_t)((uint64_t)a * b % r); }
+
+uint32_t powmod(uint32_t a, uint64_t e, uint32_t r) {
+  uint64_t x = 1, b = a % r;
+  while (e) {
+    if (e & 1) x = x * b % r;
+    b = b * b % r;
+    e >>= 1;
+  }
+  return (uint32_t)x;
+}
+
+uint32_t invmod(uint32_t a, uint32_t r) { return powmod(a, r - 2, r); }  // r prime
+
+uint32_t shoup(uint32_t w, uint32_t r) { return (uint32_t)(((uint64_t)w << 32) / r); }
+
+// Deterministic Miller-Rabin for n < 2^32 (bases 2, 7, 61).
+bool is_prime32(uint32_t n) {
+  if (n < 2) return false;
+  for (uint32_t p : {2u, 3u, 5u, 7u, 11u, 13u, 61u})
+    if (n % p == 0) return n == p;
+  uint32_t d = n - 1;
+  int s = 0;
+  while ((d & 1) == 0) {
+    d >>= 1;
+    ++s;
+  }
+  for (uint32_t a : {2u, 7u, 61u}) {
+    uint32_t x = powmod(a, d, n);
+    if (x == 1 || x == n - 1) continue;
+    bool composite = true;
+    for (int i = 1; i < s; ++i) {
+      x = mulmod(x, x, n);
+      if (x == n - 1) {
+        composite = false;
+        break;
+      }
+    }
+    if (composite) return false;
+  }
+  return true;
+}
+
+// Smallest primitive 2N-th root of unity mod r: find one root r0, then take the
+// minimum over its odd powers (exactly the primitive 2N-th roots).
+uint32_t smallest_psi(uint32_t r, uint32_t N) {
+  uint32_t r0 = 0;
+  for (uint32_t g = 2; g < r; ++g) {
+    r0 = powmod(g, (r - 1) / (2 * (uint64_t)N), r);
+    if (powmod(r0, N, r) == r - 1) break;
+  }
+  const uint32_t r0sq = mulmod(r0, r0, r);
+  uint32_t best = r0, x = r0;
+  for (uint32_t t = 1; t < N; ++t) {
+    x = mulmod(x, r0sq, r);
+    best = std::min(best, x);
+  }
+  return best;
+}
+
+uint32_t neg_inv32(uint32_t r) {
+  uint32_t x = 1;
+  for (int i = 0; i < 5; ++i) x *= 2u - r * x;  // Newton: x = r^-1 mod 2^32
+  return 0u - x;
+}
+
+uint32_t bitrev_host(uint32_t x, int bits) {
+  uint32_t y = 0;
+  for (int b = 0; b < bits; ++b) y |= ((x >> b) & 1u) << (bits - 1 - b);
+  return y;
+}
+
+int alpha_of(const pc_params* p, uint32_t level) { return (int)((level + p->dnum - 1) / p->dnum); }
+int beta_of(const pc_params* p, uint32_t level) {
+  const int a = alpha_of(p, level);
+  return (int)((level + a - 1) / a);
+}
+
+// product of primes q_i, i in [i0, i1) \ {skip}, modulo r
+uint32_t prod_mod(const pc_params* p, int i0, int i1, int skip, uint32_t r) {
+  uint32_t x = 1 % r;
+  for (int i = i0; i < i1; ++i)
+    if (i != skip) x = mulmod(x, p->primes[i] % r, r);
+  return x;
+}
+
+uint32_t pow2_32(uint32_t r) { return (uint32_t)((uint64_t(1) << 32) % r); }
+
+int build_tables(pc_params* p) {
+  const uint32_t N = p->N, L = p->L, K = p->K, P = L + K;
+  const int n = (int)p->log2n;
+  p->psi.resize(P);
+  p->h_rinv.resize(P);
+  p->h_ninv.resize(P);
+  p->h_ninvp.resize(P);
+  p->h_r2.resize(P);
+  p->h_tw_fwd.resize((size_t)P * N);
+  p->h_twp_fwd.resize((size_t)P * N);
+  p->h_tw_inv.resize((size_t)P * N);
+  p->h_twp_inv.resize((size_t)P * N);
+  for (uint32_t k = 0; k < P; ++k) {
+    const uint32_t r = p->primes[k];
+    const uint32_t psi = smallest_psi(r, N);
+    const uint32_t psi_inv = invmod(psi, r);
+    p->psi[k] = psi;
+    p->h_rinv[k] = neg_inv32(r);
+    p->h_ninv[k] = invmod(N % r, r);
+    p->h_ninvp[k] = shoup(p->h_ninv[k], r);
+    p->h_r2[k] = mulmod(pow2_32(r), pow2_32(r), r);
+    // psi^e for e = 0..N-1, then scatter by bit reversal
+    std::vector<uint32_t> pw(N), pwi(N);
+    pw[0] = pwi[0] = 1;
+    for (uint32_t e = 1; e < N; ++e) {
+      pw[e] = mulmod(pw[e - 1], psi, r);
+      pwi[e] = mulmod(pwi[e - 1], psi_inv, r);
+    }
+    uint32_t* tf = &p->h_tw_fwd[(size_t)k * N];
+    uint32_t* tfp = &p->h_twp_fwd[(size_t)k * N];
+    uint32_t* ti = &p->h_tw_inv[(size_t)k * N];
+    uint32_t* tip = &p->h_twp_inv[(size_t)k * N];
+    for (uint32_t i = 0; i < N; ++i) {
+      const uint32_t e = bitrev_host(i, n);
+      tf[i] = pw[e];
+      tfp[i] = shoup(pw[e], r);
+      ti[i] = pwi[e];
+      tip[i] = shoup(pwi[e], r);
+    }
+  }
+  // ModUp tables per level
+  p->mu_scale_off.assign(L + 1, 0);
+  p->mu_bconv_off.assign(L + 1, 0);
+  size_t so = 0, bo = 0;
+  for (uint32_t l = 1; l <= L; ++l) {
+    p->mu_scale_off[l] = so;
+    p->mu_bconv_off[l] = bo;
+    so += l;
+    bo += (size_t)l * (l + K);
+  }
+  p->h_mu_scale.assign(so, 0);
+  p->h_mu_scalep.assign(so, 0);
+  p->h_mu_bconv.assign(bo, 0);
+  for (uint32_t l = 1; l <= L; ++l) {
+    const int a = alpha_of(p, l);
+    const uint32_t lk = l + K;
+    for (uint32_t i = 0; i < l; ++i) {
+      const int d = (int)i / a;
+      const int i0 = d * a, i1 = std::min<int>(i0 + a, (int)l);
+      const uint32_t qi = p->primes[i];
+      const uint32_t qhat_inv = invmod(prod_mod(p, i0, i1, (int)i, qi), qi);
+      const uint32_t sc = mulmod(p->h_ninv[i], qhat_inv, qi);
+      p->h_mu_scale[p->mu_scale_off[l] + i] = sc;
+      p->h_mu_scalep[p->mu_scale_off[l] + i] = shoup(sc, qi);
+      for (uint32_t j = 0; j < lk; ++j) {
+        if ((int)j >= i0 && (int)j < i1) continue;
+        const uint32_t rj = j < l ? p->primes[j] : p->primes[L + (j - l)];
+        const uint32_t qhat = prod_mod(p, i0, i1, (int)i, rj);
+        p->h_mu_bconv[p->mu_bconv_off[l] + (size_t)i * lk + j] = mulmod(qhat, pow2_32(rj), rj);
+      }
+    }
+  }
+  // ModDown tables: variant 0 (plain input), variant 1 (input carrying 2^-64)
+  p->h_md_scale.assign(2 * K, 0);
+  p->h_md_scalep.assign(2 * K, 0);
+  p->h_md_bconv.assign((size_t)2 * K * L, 0);
+  p->h_md_pinv.assign(2 * L, 0);
+  p->h_md_pinvp.assign(2 * L, 0);
+  for (int v = 0; v < 2; ++v) {
+    for (uint32_t t = 0; t < K; ++t) {
+      const uint32_t pt = p->primes[L + t];
+      uint32_t phat = 1;
+      for (uint32_t u = 0; u < K; ++u)
+        if (u != t) phat = mulmod(phat, p->primes[L + u] % pt, pt);
+      uint32_t sc = mulmod(p->h_ninv[L + t], invmod(phat, pt), pt);
+      if (v == 1) sc = mulmod(sc, p->h_r2[L + t], pt);  // times 2^64
+      p->h_md_scale[v * K + t] = sc;
+      p->h_md_scalep[v * K + t] = shoup(sc, pt);
+      for (uint32_t i = 0; i < L; ++i) {
+        const uint32_t qi = p->primes[i];
+        uint32_t ph = 1;
+        for (uint32_t u = 0; u < K; ++u)
+          if (u != t) ph = mulmod(ph, p->primes[L + u] % qi, qi);
+        // (P/p_t) 2^32 S^-1 with S = 1 or 2^64, i.e. times 2^32 or 2^-32
+        const uint32_t f = v == 0 ? pow2_32(qi) : invmod(pow2_32(qi), qi);
+        p->h_md_bconv[((size_t)v * K + t) * L + i] = mulmod(ph, f, qi);
+      }
+    }
+    for (uint32_t i = 0; i < L; ++i) {
+      const uint32_t qi = p->primes[i];
+      uint32_t Pm = 1;
+      for (uint32_t u = 0; u < K; ++u) Pm = mulmod(Pm, p->primes[L + u] % qi, qi);
+      uint32_t pinv = invmod(Pm, qi);
+      if (v == 1) pinv = mulmod(pinv, p->h_r2[i], qi);
+      p->h_md_pinv[v * L + i] = pinv;
+      p->h_md_pinvp[v * L + i] = shoup(pinv, qi);
+    }
+  }
+  return PC_OK;
+}
+
+template <class T>
+size_t append(std::vector<uint8_t>& blob, const std::vector<T>& v) {
+  size_t off = (blob.size() + 255) & ~size_t(255);
+  blob.resize(off + v.size() * sizeof(T));
+  if (!v.empty()) memcpy(blob.data() + off, v.data(), v.size() * sizeof(T));
+  return off;
+}
+
+int upload_tables(pc_params* p) {
+  std::vector<uint32_t> r32(p->primes.begin(), p->primes.end());
+  std::vector<uint8_t> blob;
+  const size_t o_r = append(blob, r32), o_rinv = append(blob, p->h_rinv), o_ninv = append(blob, p->h_ninv),
+               o_ninvp = append(blob, p->h_ninvp), o_r2 = append(blob, p->h_r2);
+  const size_t o_tf = append(blob, p->h_tw_fwd), o_tfp = append(blob, p->h_twp_fwd), o_ti = append(blob, p->h_tw_inv),
+               o_tip = append(blob, p->h_twp_inv);
+  const size_t o_ms = append(blob, p->h_mu_scale), o_msp = append(blob, p->h_mu_scalep),
+               o_mb = append(blob, p->h_mu_bconv);
+  const size_t o_ds = append(blob, p->h_md_scale), o_dsp = append(blob, p->h_md_scalep),
+               o_db = append(blob, p->h_md_bconv), o_dp = append(blob, p->h_md_pinv),
+               o_dpp = append(blob, p->h_md_pinvp);
+  void* d = nullptr;
+  if (hipMalloc(&d, blob.size()) != hipSuccess) return PC_ENOMEM;
+  if (hipMemcpy(d, blob.data(), blob.size(), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(d);
+    return PC_EDEVICE;
+  }
+  p->d_tables = d;
+  auto at = [d](size_t off) { return reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(d) + off); };
+  p->tabs = DevTables{at(o_r), at(o_rinv), at(o_ninv), at(o_ninvp), at(o_r2), at(o_tf), at(o_tfp), at(o_ti), at(o_tip)};
+  p->ltabs = DevLevelTables{at(o_ms), at(o_msp), at(o_mb), at(o_ds), at(o_dsp), at(o_db), at(o_dp), at(o_dpp)};
+  return PC_OK;
+}
+
+struct DeviceGuard {
+  int old = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&old) != hipSuccess) {
+      ok = false;
+      return;
+    }
+    if (old != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (old >= 0 && hipGetDevice(&cur) == hipSuccess && cur != old) (void)hipSetDevice(old);
+  }
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+size_t ks_workspace_bytes(const pc_params* p, uint32_t level, uint32_t batch, uint32_t items) {
+  const size_t N = p->N, l = level, K = p->K, lk = l + K, beta = (size_t)beta_of(p, level);
+  size_t b = 0;
+  b += align256(batch * l * N * 4);
+  b += 2 * align256(batch * beta * lk * N * 4);
+  b += align256(items * 2 * lk * N * 4);
+  b += align256(items * 2 * K * N * 4);
+  b += align256(items * 2 * l * N * 4);
+  return b;
+}
+
+KsWorkspace ks_workspace_carve(const pc_params* p, void* base, uint32_t level, uint32_t batch, uint32_t items) {
+  const size_t N = p->N, l = level, K = p->K, lk = l + K, beta = (size_t)beta_of(p, level);
+  uint8_t* c = static_cast<uint8_t*>(base);
+  KsWorkspace w;
+  auto take = [&c](size_t bytes) {
+    uint32_t* r = reinterpret_cast<uint32_t*>(c);
+    c += align256(bytes);
+    return r;
+  };
+  w.y = take(batch * l * N * 4);
+  w.tmp = take(batch * beta * lk * N * 4);
+  w.ext = take(batch * beta * lk * N * 4);
+  w.acc = take(items * 2 * lk * N * 4);
+  w.y2 = take(items * 2 * K * N * 4);
+  w.tmp2 = take(items * 2 * l * N * 4);
+  return w;
+}
+
+}  // namespace pc
+
+using namespace pc;
+
+extern "C" {
+
+const char* pc_strerror(int code) {
+  switch (code) {
+    case PC_OK: return "ok";
+    case PC_EINVAL: return "invalid argument";
+    case PC_ENOMEM: return "out of memory";
+    case PC_EDEVICE: return "device error (HIP call failed or no device)";
+    case PC_EUNSUPPORTED: return "unsupported shape";
+    default: return "unknown error";
+  }
+}
+
+int pc_params_create(const pc_params_desc* desc, int device, pc_params** out) {
+  if (desc == nullptr || out == nullptr) return PC_EINVAL;
+  *out = nullptr;
+  const uint32_t n = desc->log2n;
+  if (n != 12 && n != 16 && n != 17) return PC_EUNSUPPORTED;
+  if (desc->L < 1 || desc->K < 1 || desc->dnum < 1 || desc->dnum > desc->L) return PC_EINVAL;
+  if (desc->dnum > (uint32_t)kMaxDigits) return PC_EUNSUPPORTED;
+  if (desc->L + desc->K > (uint32_t)kMaxLimbsPerLaunch - 1) return PC_EUNSUPPORTED;
+  const uint32_t rounds = desc->chacha_rounds ? desc->chacha_rounds : 12;
+  if (rounds != 12 && rounds != 20) return PC_EUNSUPPORTED;
+  const uint32_t max_hoist = desc->max_hoist ? desc->max_hoist : 1;
+  if (max_hoist > (uint32_t)kMaxKeysPerLaunch) return PC_EUNSUPPORTED;
+  pc_params* p = new (std::nothrow) pc_params();
+  if (p == nullptr) return PC_ENOMEM;
+  p->log2n = n;
+  p->N = 1u << n;
+  p->L = desc->L;
+  p->K = desc->K;
+  p->dnum = desc->dnum;
+  p->max_batch = desc->max_batch ? desc->max_batch : 1;
+  p->max_hoist = max_hoist;
+  p->chacha_rounds = rounds;
+  const uint32_t count = p->L + p->K;
+  const uint64_t m = 2ull * p->N;
+  if (desc->primes != nullptr) {
+    for (uint32_t k = 0; k < count; ++k) {
+      const uint32_t r = desc->primes[k];
+      if (r <= (1u << 30) || r >= (1u << 31) || r % m != 1 || !is_prime32(r)) {
+        delete p;
+        return PC_EINVAL;
+      }
+      for (uint32_t u = 0; u < k; ++u)
+        if (desc->primes[u] == r) {
+          delete p;
+          return PC_EINVAL;
+        }
+      p->primes.push_back(r);
+    }
+  } else {
+    uint64_t c = ((1ull << 31) - 2) / m * m + 1;
+    while (p->primes.size() < count && c > (1u << 30)) {
+      if (is_prime32((uint32_t)c)) p->primes.push_back((uint32_t)c);
+      c -= m;
+    }
+    if (p->primes.size() < count) {
+      delete p;
+      return PC_EUNSUPPORTED;
+    }
+  }
+  build_tables(p);
+  if (device >= 0) {
+    DeviceGuard g(device);
+    if (!g.ok) {
+      delete p;
+      return PC_EDEVICE;
+    }
+    p->device = device;
+    int rc = upload_tables(p);
+    if (rc != PC_OK) {
+      delete p;
+      return rc;
+    }
+    const size_t ks = ks_workspace_bytes(p, p->L, p->max_batch, p->max_batch * p->max_hoist);
+    p->arena_bytes = std::max<size_t>(ks, (size_t)2 * count * p->N * 4);
+    if (hipMalloc(&p->arena, p->arena_bytes) != hipSuccess) {
+      (void)hipFree(p->d_tables);
+      delete p;
+      return PC_ENOMEM;
+    }
+  }
+  *out = p;
+  return PC_OK;
+}
+
+void pc_params_destroy(pc_params* p) {
+  if (p == nullptr) return;
+  if (p->device >= 0) {
+    DeviceGuard g(p->device);
+    if (p->arena) (void)hipFree(p->arena);
+    if (p->d_tables) (void)hipFree(p->d_tables);
+  }
+  delete p;
+}
+
+int pc_params_get(const pc_params* p, int what, uint32_t arg, void* dst, size_t bytes) {
+  if (p == nullptr || dst == nullptr) return PC_EINVAL;
+  const uint32_t count = p->L + p->K;
+  switch (what) {
+    case PC_GET_N:
+      if (bytes != 4) return PC_EINVAL;
+      memcpy(dst, &p->N, 4);
+      return PC_OK;
+    case PC_GET_PRIMES:
+      if (bytes != count * 4) return PC_EINVAL;
+      memcpy(dst, p->primes.data(), bytes);
+      return PC_OK;
+    case PC_GET_PSI:
+      if (bytes != count * 4) return PC_EINVAL;
+      memcpy(dst, p->psi.data(), bytes);
+      return PC_OK;
+    case PC_GET_ALPHA:
+    case PC_GET_BETA: {
+      if (bytes != 4 || arg < 1 || arg > p->L) return PC_EINVAL;
+      const uint32_t v = (uint32_t)(what == PC_GET_ALPHA ? alpha_of(p, arg) : beta_of(p, arg));
+      memcpy(dst, &v, 4);
+      return PC_OK;
+    }
+    case PC_GET_WORKSPACE_BYTES: {
+      if (bytes != 8 || arg < 1 || arg > p->L) return PC_EINVAL;
+      const uint64_t v = ks_workspace_bytes(p, arg, p->max_batch, p->max_batch * p->max_hoist);
+      memcpy(dst, &v, 8);
+      return PC_OK;
+    }
+    case PC_GET_DEVICE_TABLE:
+      if (arg >= count || bytes != (size_t)p->N * 4) return PC_EINVAL;
+      memcpy(dst, &p->h_tw_fwd[(size_t)arg * p->N], bytes);
+      return PC_OK;
+    default:
+      return PC_EINVAL;
+  }
+}
+
+static int ntt_common(const pc_params* p, uint32_t* data, const uint32_t* prime_idx, uint32_t nlimbs, void* stream,
+                      bool inverse) {
+  if (p == nullptr || data == nullptr || prime_idx == nullptr) return PC_EINVAL;
+  for (uint32_t z = 0; z < nlimbs; ++z)
+    if (prime_idx[z] >= p->L + p->K) return PC_EINVAL;
+  if (p->device < 0) return PC_EDEVICE;
+  if (nlimbs == 0) return PC_OK;
+  DeviceGuard g(p->device);
+  if (!g.ok) return PC_EDEVICE;
+  const uint32_t chunk = (uint32_t)std::min<size_t>(nlimbs, p->arena_bytes / ((size_t)p->N * 4));
+  for (uint32_t base = 0; base < nlimbs; base += chunk) {
+    const uint32_t cnt = std::min(chunk, nlimbs - base);
+    if (launch_ntt(p, data + (size_t)base * p->N, static_cast<uint32_t*>(p->arena), prime_idx + base, cnt, inverse,
+                   (hipStream_t)stream) != hipSuccess)
+      return PC_EDEVICE;
+  }
+  return PC_OK;
+}
+
+int pc_ntt(const pc_params* p, uint32_t* data, const uint32_t* prime_idx, uint32_t nlimbs, void* stream) {
+  return ntt_common(p, data, prime_idx, nlimbs, stream, false);
+}
+
+int pc_intt(const pc_params* p, uint32_t* data, const uint32_t* prime_idx, uint32_t nlimbs, void* stream) {
+  return ntt_common(p, data, prime_idx, nlimbs, stream, true);
+}
+
+int pc_modup(const pc_params* p, const uint32_t* c1, uint32_t level, uint32_t* ext, void* stream) {
+  if (p == nullptr || c1 == nullptr || ext == nullptr) return PC_EINVAL;
+  if (level < 1 || level > p->L) return PC_EINVAL;
+  if (p->device < 0) return PC_EDEVICE;
+  DeviceGuard g(p->device);
+  if (!g.ok) return PC_EDEVICE;
+  KsWorkspace ws = ks_workspace_carve(p, p->arena, level, 1, 1);
+  ws.ext = ext;
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_modup(p, c1, 0, 0, 1, level, ws, s) != hipSuccess) return PC_EDEVICE;
+  const int a = alpha_of(p, level), beta = beta_of(p, level);
+  const size_t lk = level + p->K, N = p->N;
+  for (int d = 0; d < beta; ++d) {
+    const int i0 = d * a, i1 = std::min<int>(i0 + a, (int)level);
+    if (hipMemcpyAsync(ext + ((size_t)d * lk + i0) * N, c1 + (size_t)i0 * N, (size_t)(i1 - i0) * N * 4,
+                       hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return PC_EDEVICE;
+  }
+  return PC_OK;
+}
+
+int pc_moddown(const pc_params* p, const uint32_t* acc, uint32_t level, uint32_t* out, void* stream) {
+  if (p == nullptr || acc == nullptr || out == nullptr) return PC_EINVAL;
+  if (level < 1 || level > p->L) return PC_EINVAL;
+  if (p->device < 0) return PC_EDEVICE;
+  DeviceGuard g(p->device);
+  if (!g.ok) return PC_EDEVICE;
+  KsWorkspace ws = ks_workspace_carve(p, p->arena, level, 1, 1);
+  if (launch_moddown(p, acc, 1, 1, level, 0, out, ws, nullptr, 0, 1, nullptr, (hipStream_t)stream) != hipSuccess)
+    return PC_EDEVICE;
+  return PC_OK;
+}
+
+int pc_keyswitch_ex(const pc_params* p, const pc_ks_args* a, void* stream) {
+  if (p == nullptr || a == nullptr || a->ct == nullptr || a->out == nullptr || a->evk_b == nullptr ||
+      a->galois == nullptr)
+    return PC_EINVAL;
+  if (a->level < 1 || a->level > p->L) return PC_EINVAL;
+  if (a->batch < 1 || a->batch > p->max_batch) return PC_EINVAL;
+  if (a->nkeys < 1 || a->nkeys > p->max_hoist) return PC_EINVAL;
+  if (a->evk_a == nullptr && a->seeds == nullptr) return PC_EINVAL;
+  std::vector<KeyRef> keys(a->nkeys);
+  for (uint32_t k = 0; k < a->nkeys; ++k) {
+    const uint32_t gk = a->galois[k];
+    if ((gk & 1u) == 0 || gk >= 2 * p->N) return PC_EINVAL;
+    if (a->evk_b[k] == nullptr) return PC_EINVAL;
+    keys[k].b = a->evk_b[k];
+    keys[k].a = nullptr;
+    if (a->evk_a != nullptr) {
+      if (a->evk_a[k] == nullptr) return PC_EINVAL;
+      keys[k].a = a->evk_a[k];
+    }
+    if (a->seeds != nullptr) {
+      for (int w = 0; w < 8; ++w) {
+        const uint8_t* s = a->seeds + 32 * k + 4 * w;
+        keys[k].seed[w] = (uint32_t)s[0] | ((uint32_t)s[1] << 8) | ((uint32_t)s[2] << 16) | ((uint32_t)s[3] << 24);
+      }
+    } else {
+      memset(keys[k].seed, 0, sizeof(keys[k].seed));
+    }
+    keys[k].galois = gk;
+  }
+  if (p->device < 0) return PC_EDEVICE;
+  const uint32_t items = a->nkeys * a->batch;
+  const size_t need = ks_workspace_bytes(p, a->level, a->batch, items);
+  void* base = p->arena;
+  if (a->workspace != nullptr) {
+    if (a->workspace_bytes < need) return PC_EINVAL;
+    base = a->workspace;
+  } else if (need > p->arena_bytes) {
+    return PC_EINVAL;
+  }
+  DeviceGuard g(p->device);
+  if (!g.ok) return PC_EDEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  const KsWorkspace ws = ks_workspace_carve(p, base, a->level, a->batch, items);
+  const uint64_t ct_stride = 2ull * a->level * p->N;
+  const uint32_t c1_off = a->level * p->N;
+  if (launch_modup(p, a->ct, ct_stride, c1_off, a->batch, a->level, ws, s) != hipSuccess) return PC_EDEVICE;
+  if (launch_inner_product(p, a->ct, ct_stride, c1_off, a->batch, a->level, ws, keys.data(), a->nkeys, s) !=
+      hipSuccess)
+    return PC_EDEVICE;
+  const size_t lk = a->level + p->K;
+  for (uint32_t k0 = 0; k0 < a->nkeys; k0 += kMaxKeysPerLaunch) {
+    const uint32_t nk = std::min<uint32_t>(kMaxKeysPerLaunch, a->nkeys - k0);
+    const size_t item0 = (size_t)k0 * a->batch;
+    if (launch_moddown(p, ws.acc + item0 * 2 * lk * p->N, nk * a->batch, 2, a->level, 1,
+                       a->out + item0 * 2 * a->level * p->N, ws, a->ct, ct_stride, a->batch, a->galois + k0,
+                       s) != hipSuccess)
+      return PC_EDEVICE;
+  }
+  return PC_OK;
+}
+
+int pc_keyswitch(const pc_params* p, const uint32_t* ct, const uint32_t* evk_b, const uint8_t* evk_seed,
+                 uint32_t level, uint32_t automorphism_idx, uint32_t* out, void* stream) {
+  if (evk_seed == nullptr || evk_b == nullptr) return PC_EINVAL;
+  const uint32_t* bl[1] = {evk_b};
+  const uint32_t gl[1] = {automorphism_idx};
+  pc_ks_args a;
+  memset(&a, 0, sizeof(a));
+  a.ct = ct;
+  a.batch = 1;
+  a.nkeys = 1;
+  a.evk_b = bl;
+  a.evk_a = nullptr;
+  a.seeds = evk_seed;
+  a.galois = gl;
+  a.level = level;
+  a.out = out;
+  return pc_keyswitch_ex(p, &a, stream);
+}
+
+int pc_chacha_expand(const pc_params* p, const uint8_t* seed, uint32_t d, uint32_t j, uint32_t level, uint32_t* dst,
+                     void* stream) {
+  if (p == nullptr || seed == nullptr || dst == nullptr) return PC_EINVAL;
+  if (level < 1 || level > p->L) return PC_EINVAL;
+  if (d >= (uint32_t)beta_of(p, level) || j >= level + p->K) return PC_EINVAL;
+  if (p->device < 0) return PC_EDEVICE;
+  uint32_t key[8];
+  for (int w = 0; w < 8; ++w)
+    key[w] = (uint32_t)seed[4 * w] | ((uint32_t)seed[4 * w + 1] << 8) | ((uint32_t)seed[4 * w + 2] << 16) |
+             ((uint32_t)seed[4 * w + 3] << 24);
+  const uint32_t pi = j < level ? j : p->L + (j - level);
+  DeviceGuard g(p->device);
+  if (!g.ok) return PC_EDEVICE;
+  if (launch_chacha_expand(p, key, d, j, pi, dst, (hipStream_t)stream) != hipSuccess) return PC_EDEVICE;
+  return PC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Internal types shared by the C-ABI layer (capi.hip) and the kernels (kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/pc.h"
+
+namespace pc {
+
+constexpr int kMaxLimbsPerLaunch = 256;  // prime indices travel in kernel arguments
+constexpr int kMaxKeysPerLaunch = 32;    // keys (seeds, pointers, Galois elements) per inner-product launch
+constexpr int kMaxDigits = 6;            // digits supported by the inner-product kernel
+
+// Device pointers to the per-prime tables (prime index = position in the chain:
+// q_0..q_{L-1} then p_0..p_{K-1}).
+struct DevTables {
+  const uint32_t* r;        // [P] primes
+  const uint32_t* rinv;     // [P] -r^-1 mod 2^32
+  const uint32_t* ninv;     // [P] N^-1 mod r
+  const uint32_t* ninvp;    // [P] Shoup companions
+  const uint32_t* r2;       // [P] 2^64 mod r (leaves Montgomery form through one REDC)
+  const uint32_t* tw_fwd;   // [P][N] psi^bitrev(k)
+  const uint32_t* twp_fwd;
+  const uint32_t* tw_inv;   // [P][N] psi^-bitrev(k)
+  const uint32_t* twp_inv;
+};
+
+// Per-level constants for ModUp and ModDown (level l = number of active q primes).
+struct DevLevelTables {
+  const uint32_t* mu_scale;   // [sum_l l] N^-1 (Q_d/q_i)^-1 mod q_i, by level then limb
+  const uint32_t* mu_scalep;
+  const uint32_t* mu_bconv;   // [sum_l l (l+K)] (Q_d/q_i) 2^32 mod r_j, by level, source limb i, target j
+  // ModDown, two variants v: 0 = plain input, 1 = input carrying a factor 2^-64
+  const uint32_t* md_scale;   // [2][K] N^-1 (P/p_t)^-1 S mod p_t
+  const uint32_t* md_scalep;
+  const uint32_t* md_bconv;   // [2][K][L] (P/p_t) 2^32 S^-1 mod q_i
+  const uint32_t* md_pinv;    // [2][L] S P^-1 mod q_i
+  const uint32_t* md_pinvp;
+};
+
+}  // namespace pc
+
+struct pc_params {
+  int device = -1;
+  uint32_t log2n = 0, N = 0, L = 0, dnum = 0, K = 0;
+  uint32_t max_batch = 1, max_hoist = 1, chacha_rounds = 12;
+  std::vector<uint32_t> primes;  // L q-primes then K p-primes
+  std::vector<uint32_t> psi;
+  // host copies of the tables (always built; uploaded when device >= 0)
+  std::vector<uint32_t> h_rinv, h_ninv, h_ninvp, h_r2;
+  std::vector<uint32_t> h_tw_fwd, h_twp_fwd, h_tw_inv, h_twp_inv;
+  std::vector<uint32_t> h_mu_scale, h_mu_scalep, h_mu_bconv;
+  std::vector<size_t> mu_scale_off, mu_bconv_off;  // by level (index l, 1..L)
+  std::vector<uint32_t> h_md_scale, h_md_scalep, h_md_bconv, h_md_pinv, h_md_pinvp;
+  // device state
+  void* d_tables = nullptr;  // one allocation holding every table
+  pc::DevTables tabs{};
+  pc::DevLevelTables ltabs{};
+  void* arena = nullptr;  // workspace arena sized at create
+  size_t arena_bytes = 0;
+};
+
+namespace pc {
+
+// Workspace carve-up for a key switch of `items` (ciphertext, key) pairs over a
+// batch of `batch` ciphertexts at level l.
+struct KsWorkspace {
+  uint32_t* y;     // [batch][l][N]          ModUp coefficients (scaled)
+  uint32_t* tmp;   // [batch][beta][l+K][N]  ModUp after the column pass
+  uint32_t* ext;   // [batch][beta][l+K][N]  ModUp output (evaluation form)
+  uint32_t* acc;   // [items][2][l+K][N]     inner product
+  uint32_t* y2;    // [items][2][K][N]       ModDown coefficients of the P limbs
+  uint32_t* tmp2;  // [items][2][l][N]       ModDown after the column pass
+};
+size_t ks_workspace_bytes(const pc_params* p, uint32_t level, uint32_t batch, uint32_t items);
+KsWorkspace ks_workspace_carve(const pc_params* p, void* base, uint32_t level, uint32_t batch, uint32_t items);
+
+struct KeyRef {
+  const uint32_t* b;  // [beta][l+K][N]
+  const uint32_t* a;  // stored a half (same shape) or nullptr to regenerate from seed
+  uint32_t seed[8];
+  uint32_t galois;
+};
+
+// Launchers (return hipError_t of the last launch).
+hipError_t launch_ntt(const pc_params* p, uint32_t* data, uint32_t* tmp, const uint32_t* prime_idx, uint32_t nlimbs,
+                      bool inverse, hipStream_t s);
+hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_offset, uint32_t batch,
+                        uint32_t level, const KsWorkspace& ws, hipStream_t s);
+hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_offset,
+                                uint32_t batch, uint32_t level, const KsWorkspace& ws, const KeyRef* keys,
+                                uint32_t nkeys, hipStream_t s);
+// ModDown of items*2 accumulators; out[item][u][l][N]. variant: 0 plain acc, 1 acc carrying 2^-64.
+// When c0 is non-null, c0 of ciphertext (item % batch) under the item's Galois element is added to u = 0.
+hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t items, uint32_t polys, uint32_t level,
+                          int variant, uint32_t* out, const KsWorkspace& ws, const uint32_t* c0, uint64_t ct_stride,
+                          uint32_t batch, const uint32_t* galois_per_key, hipStream_t s);
+hipError_t launch_chacha_expand(const pc_params* p, const uint32_t seed[8], uint32_t d, uint32_t j,
+                                uint32_t prime_index, uint32_t* dst, hipStream_t s);
+
+}  // namespace pc

@@ -1,0 +1,253 @@
+// Two-pass negacyclic NTT for gfx950, natural order in and out.
+//
+// The pages name NTT kernels over the 32-bit chain (Perseus README, 'Layout')
+// and leave the transform's layout open; the evaluation layout here is natural
+// order, a_hat[j] = a(psi^(2j+1)).
+//
+// Forward (Cooley-Tukey, twiddles psi^bitrev(k)): the n = LOGRC + LOGRB stages
+// split into
+//   * a column pass: the first LOGRC stages only pair indices that agree mod
+//     2^LOGRB, so each "column" col (elements col + 2^LOGRB * x) is an
+//     independent 2^LOGRC-point problem; its twiddles are entries [1, 2^LOGRC)
+//     of the table and are shared by every column;
+//   * a block pass: the last LOGRB stages act inside contiguous blocks of 2^LOGRB
+//     elements; block B uses entries 2^(LOGRC+s) + B 2^s + ... of the table.
+// The in-place result is bit-reversed: element x of block B belongs at natural
+// position bitrev(x) 2^LOGRC + bitrev(B). A workgroup therefore takes the C
+// blocks B = bitrev(c0 + k), k < C, so that every output row bitrev(x) is a
+// contiguous run of C words; the transpose goes through LDS.
+// Inverse (Gentleman-Sande, twiddles psi^-bitrev(k)): the mirror image -- a
+// block pass with the transposed load first, then a column pass.
+//
+// Inside a pass a workgroup holds C columns (or blocks) of R = 2^LOGR elements;
+// each thread keeps E = 2^LOGE of them in registers and runs LOGE radix-2
+// stages per round; rounds exchange data through LDS.  Element index held by
+// thread t in round i, slot m (forward rounds walk the bits from the top,
+// inverse rounds from the bottom):
+//   x = (t_high << (lo + LOGE)) | (m << lo) | t_low,  t_low = t mod 2^lo.
+#pragma once
+
+#include "device_common.h"
+
+namespace pc {
+
+template <int LOGR, int LOGE, bool GS>
+__device__ __forceinline__ int pass_lo(int round) {
+  return GS ? round * LOGE : LOGR - (round + 1) * LOGE;
+}
+
+template <int LOGR, int LOGE, bool GS>
+__device__ __forceinline__ int elem_index(int round, int t, int m) {
+  const int lo = pass_lo<LOGR, LOGE, GS>(round);
+  const int tlow = t & ((1 << lo) - 1);
+  const int thigh = t >> lo;
+  return (thigh << (lo + LOGE)) | (m << lo) | tlow;
+}
+
+// Row stride (words) of the LDS tile; the pad spreads columns over banks.
+template <int LOGR>
+struct LdsTile {
+  static constexpr int R = 1 << LOGR;
+  static constexpr int STRIDE = R + 4;
+};
+
+// Forward CT round: stages s = round*LOGE + sl for sl < LOGE.
+// TwBase(s) returns the table offset of group 0 of stage s for this thread's
+// row/block (the part that does not depend on the slot m); the twiddle index is
+// TwBase(s) + (t_high << sl) + (m >> (LOGE - sl)).
+template <int LOGR, int LOGE, class TwBase>
+__device__ __forceinline__ void ct_round(uint32_t (&v)[1 << LOGE], int round, int t, uint32_t r,
+                                         const uint32_t* __restrict__ tw, const uint32_t* __restrict__ twp,
+                                         TwBase twbase) {
+  constexpr int E = 1 << LOGE;
+  const int lo = pass_lo<LOGR, LOGE, false>(round);
+  const int thigh = t >> lo;
+#pragma unroll
+  for (int sl = 0; sl < LOGE; ++sl) {
+    const int s = round * LOGE + sl;
+    const int base = twbase(s) + (thigh << sl);
+    constexpr int dummy = 0;
+    (void)dummy;
+    const int half = E >> (sl + 1);
+#pragma unroll
+    for (int g = 0; g < (1 << sl); ++g) {
+      const uint32_t w = tw[base + g];
+      const uint32_t wp = twp[base + g];
+#pragma unroll
+      for (int j = 0; j < half; ++j) {
+        const int m0 = g * 2 * half + j;
+        const uint32_t u = v[m0];
+        const uint32_t x = mul_shoup(v[m0 + half], w, wp, r);
+        v[m0] = add_mod(u, x, r);
+        v[m0 + half] = sub_mod(u, x, r);
+      }
+    }
+  }
+}
+
+// Inverse GS round: stages u = round*LOGE + ul, pairs (m, m + 2^ul).
+// TwBase(u) returns the table offset for group 0; the twiddle index is
+// TwBase(u) + (t_high << (LOGE - ul - 1)) + (m >> (ul + 1)).
+template <int LOGR, int LOGE, class TwBase>
+__device__ __forceinline__ void gs_round(uint32_t (&v)[1 << LOGE], int round, int t, uint32_t r,
+                                         const uint32_t* __restrict__ tw, const uint32_t* __restrict__ twp,
+                                         TwBase twbase) {
+  constexpr int E = 1 << LOGE;
+  const int lo = pass_lo<LOGR, LOGE, true>(round);
+  const int thigh = t >> lo;
+#pragma unroll
+  for (int ul = 0; ul < LOGE; ++ul) {
+    const int u = round * LOGE + ul;
+    const int half = 1 << ul;
+    const int base = twbase(u) + (thigh << (LOGE - ul - 1));
+#pragma unroll
+    for (int g = 0; g < (E >> (ul + 1)); ++g) {
+      const uint32_t w = tw[base + g];
+      const uint32_t wp = twp[base + g];
+#pragma unroll
+      for (int j = 0; j < half; ++j) {
+        const int m0 = g * 2 * half + j;
+        const uint32_t a = v[m0];
+        const uint32_t b = v[m0 + half];
+        v[m0] = add_mod(a, b, r);
+        v[m0 + half] = mul_shoup(sub_mod(a, b, r), w, wp, r);
+      }
+    }
+  }
+}
+
+// Exchange the register tile between two round layouts through LDS.
+template <int LOGR, int LOGE, bool GS>
+__device__ __forceinline__ void exchange(uint32_t (&v)[1 << LOGE], uint32_t* lds_row, int from_round, int t) {
+  constexpr int E = 1 << LOGE;
+#pragma unroll
+  for (int m = 0; m < E; ++m) lds_row[elem_index<LOGR, LOGE, GS>(from_round, t, m)] = v[m];
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < E; ++m) v[m] = lds_row[elem_index<LOGR, LOGE, GS>(from_round + 1, t, m)];
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Pass bodies. A Limb policy supplies, for the limb of this workgroup:
+//   r, tw, twp                   prime and its twiddle tables (forward or inverse)
+//   uint32_t load(int pos)       element at limb position pos (pass input)
+//   void store(int pos, uint32_t v)  element at position pos (pass output)
+// Positions are limb offsets in [0, N).
+// ---------------------------------------------------------------------------
+
+// Forward column pass: stages 0..LOGRC-1, columns [col0, col0 + C).
+template <int LOGRC, int LOGE, int LOGRB, int C, class Limb>
+__device__ __forceinline__ void fwd_col_pass(Limb& L, int col0) {
+  constexpr int R = 1 << LOGRC, E = 1 << LOGE, ROUNDS = LOGRC / LOGE;
+  static_assert(LOGRC % LOGE == 0, "rounds must tile the pass");
+  __shared__ uint32_t lds[C * LdsTile<LOGRC>::STRIDE];
+  const int tid = threadIdx.x;
+  const int col = tid % C, t = tid / C;
+  uint32_t v[E];
+#pragma unroll
+  for (int m = 0; m < E; ++m) v[m] = L.load(col0 + col + (elem_index<LOGRC, LOGE, false>(0, t, m) << LOGRB));
+  auto twb = [](int s) { return 1 << s; };
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    if (rd > 0) exchange<LOGRC, LOGE, false>(v, lds + col * LdsTile<LOGRC>::STRIDE, rd - 1, t);
+    ct_round<LOGRC, LOGE>(v, rd, t, L.r, L.tw, L.twp, twb);
+  }
+#pragma unroll
+  for (int m = 0; m < E; ++m)
+    L.store(col0 + col + (elem_index<LOGRC, LOGE, false>(ROUNDS - 1, t, m) << LOGRB), v[m]);
+  (void)R;
+}
+
+// Forward block pass: stages LOGRC..n-1 on blocks B = bitrev(c0 + k), k < C.
+// Output element x of block B goes to natural position bitrev(x) 2^LOGRC + c0 + k.
+template <int LOGRC, int LOGRB, int LOGE, int C, class Limb>
+__device__ __forceinline__ void fwd_blk_pass(Limb& L, int c0) {
+  constexpr int R = 1 << LOGRB, E = 1 << LOGE, ROUNDS = LOGRB / LOGE, TPB = R / E;
+  static_assert(LOGRB % LOGE == 0, "rounds must tile the pass");
+  constexpr int STRIDE = LdsTile<LOGRB>::STRIDE;
+  __shared__ uint32_t lds[C * STRIDE];
+  const int tid = threadIdx.x;
+  const int t = tid % TPB, k = tid / TPB;
+  const int B = (int)bitrev((uint32_t)(c0 + k), LOGRC);
+  uint32_t v[E];
+#pragma unroll
+  for (int m = 0; m < E; ++m) v[m] = L.load((B << LOGRB) + elem_index<LOGRB, LOGE, false>(0, t, m));
+  auto twb = [B](int s) { return (1 << (LOGRC + s)) + (B << s); };
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    if (rd > 0) exchange<LOGRB, LOGE, false>(v, lds + k * STRIDE, rd - 1, t);
+    ct_round<LOGRB, LOGE>(v, rd, t, L.r, L.tw, L.twp, twb);
+  }
+  // transpose through LDS so that consecutive lanes write consecutive words
+#pragma unroll
+  for (int m = 0; m < E; ++m) lds[k * STRIDE + elem_index<LOGRB, LOGE, false>(ROUNDS - 1, t, m)] = v[m];
+  __syncthreads();
+  const int kk = tid % C, rest = tid / C;
+#pragma unroll
+  for (int m = 0; m < E; ++m) {
+    const int x = rest + TPB * m;
+    L.store(((int)bitrev((uint32_t)x, LOGRB) << LOGRC) + c0 + kk, lds[kk * STRIDE + x]);
+  }
+}
+
+// Inverse block pass: GS stages 0..LOGRB-1 on blocks B = bitrev(c0 + k); element
+// x of block B is read from natural position bitrev(x) 2^LOGRC + c0 + k and
+// written to B 2^LOGRB + x.
+template <int LOGRC, int LOGRB, int LOGE, int C, class Limb>
+__device__ __forceinline__ void inv_blk_pass(Limb& L, int c0) {
+  constexpr int R = 1 << LOGRB, E = 1 << LOGE, ROUNDS = LOGRB / LOGE, TPB = R / E;
+  static_assert(LOGRB % LOGE == 0, "rounds must tile the pass");
+  constexpr int STRIDE = LdsTile<LOGRB>::STRIDE;
+  constexpr int n = LOGRC + LOGRB;
+  __shared__ uint32_t lds[C * STRIDE];
+  const int tid = threadIdx.x;
+  {
+    const int kk = tid % C, rest = tid / C;
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      const int x = rest + TPB * m;
+      lds[kk * STRIDE + x] = L.load(((int)bitrev((uint32_t)x, LOGRB) << LOGRC) + c0 + kk);
+    }
+  }
+  __syncthreads();
+  const int t = tid % TPB, k = tid / TPB;
+  const int B = (int)bitrev((uint32_t)(c0 + k), LOGRC);
+  uint32_t v[E];
+#pragma unroll
+  for (int m = 0; m < E; ++m) v[m] = lds[k * STRIDE + elem_index<LOGRB, LOGE, true>(0, t, m)];
+  __syncthreads();
+  auto twb = [B](int u) { return (1 << (n - u - 1)) + (B << (LOGRB - u - 1)); };
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    if (rd > 0) exchange<LOGRB, LOGE, true>(v, lds + k * STRIDE, rd - 1, t);
+    gs_round<LOGRB, LOGE>(v, rd, t, L.r, L.tw, L.twp, twb);
+  }
+#pragma unroll
+  for (int m = 0; m < E; ++m) L.store((B << LOGRB) + elem_index<LOGRB, LOGE, true>(ROUNDS - 1, t, m), v[m]);
+}
+
+// Inverse column pass: GS stages LOGRB..n-1 on columns [col0, col0 + C); the
+// output is in natural coefficient order (the caller's store applies N^-1).
+template <int LOGRC, int LOGE, int LOGRB, int C, class Limb>
+__device__ __forceinline__ void inv_col_pass(Limb& L, int col0) {
+  constexpr int E = 1 << LOGE, ROUNDS = LOGRC / LOGE;
+  static_assert(LOGRC % LOGE == 0, "rounds must tile the pass");
+  __shared__ uint32_t lds[C * LdsTile<LOGRC>::STRIDE];
+  const int tid = threadIdx.x;
+  const int col = tid % C, t = tid / C;
+  uint32_t v[E];
+#pragma unroll
+  for (int m = 0; m < E; ++m) v[m] = L.load(col0 + col + (elem_index<LOGRC, LOGE, true>(0, t, m) << LOGRB));
+  auto twb = [](int u) { return 1 << (LOGRC - u - 1); };
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    if (rd > 0) exchange<LOGRC, LOGE, true>(v, lds + col * LdsTile<LOGRC>::STRIDE, rd - 1, t);
+    gs_round<LOGRC, LOGE>(v, rd, t, L.r, L.tw, L.twp, twb);
+  }
+#pragma unroll
+  for (int m = 0; m < E; ++m)
+    L.store(col0 + col + (elem_index<LOGRC, LOGE, true>(ROUNDS - 1, t, m) << LOGRB), v[m]);
+}
+
+}  // namespace pc

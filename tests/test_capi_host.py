@@ -1,0 +1,137 @@
+"""The C-ABI library on the CPU: loading, exported symbols, host tables, validation.
+
+No compute call reaches a GPU here: parameters are created host-only
+(device = -1) and every compute entry point must reject its arguments, or
+report PC_EDEVICE, before touching HIP.
+"""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import key_switching_amd as ksa
+from oracle import keyswitch as ks
+from oracle import rns
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ksa.LIB_PATH), reason="libpc.so not built")
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pc.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(pc_\w+)\s*\(", text))
+
+
+def test_exports_every_declared_symbol():
+    declared = declared_functions()
+    assert declared == set(ksa.EXPORTED)
+    lib = ctypes.CDLL(ksa.LIB_PATH)
+    for name in declared:
+        assert getattr(lib, name) is not None
+
+
+@pytest.mark.parametrize("log2n,L,dnum,K", [(12, 3, 3, 1), (16, 24, 4, 6), (17, 40, 5, 8)])
+def test_host_tables_match_golden(log2n, L, dnum, K):
+    with ksa.Params(log2n, L, dnum, K, device=None) as prm:
+        g = json.load(open(os.path.join(GOLDEN, f"chain_n{log2n}.json")))
+        assert prm.primes == g["primes"][: L + K]
+        assert prm.psi == g["psi"][: L + K]
+        N = 1 << log2n
+        for pi in (0, L + K - 1):
+            tw = prm.twiddles(pi)
+            q, psi = g["primes"][pi], g["psi"][pi]
+            for k in (0, 1, 2, 3, N // 2, N - 1):
+                e = int(format(k, f"0{log2n}b")[::-1], 2)
+                assert tw[k] == pow(psi, e, q)
+
+
+@pytest.mark.parametrize("L,dnum", [(24, 4), (40, 5), (3, 3), (7, 3), (6, 6)])
+def test_digit_partition_matches_oracle(L, dnum):
+    with ksa.Params(12, L, dnum, 2, device=None) as prm:
+        oprm = ks.Params(12, L, dnum, 2, primes=tuple(prm.primes))
+        for level in range(1, L + 1):
+            D = oprm.digits(level)
+            assert prm.beta(level) == len(D)
+            assert prm.alpha(level) == len(D[0])
+
+
+def test_user_primes_accepted_and_checked():
+    N = 1 << 12
+    chain = rns.ntt_primes(N, 6)[2:]
+    with ksa.Params(12, 3, 1, 1, primes=chain, device=None) as prm:
+        assert prm.primes == chain
+    bad = [chain[0], chain[1], chain[2], chain[3] + 2 * N]  # not prime or not 1 mod 2N
+    for b in (bad, [chain[0]] * 4, [97, 193, 257, 449]):
+        with pytest.raises(ksa.PcError) as e:
+            ksa.Params(12, 3, 1, 1, primes=b, device=None)
+        assert e.value.code == ksa.PC_EINVAL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(log2n=13, L=3, dnum=3, K=1), ksa.PC_EUNSUPPORTED),
+    (dict(log2n=12, L=3, dnum=4, K=1), ksa.PC_EINVAL),
+    (dict(log2n=12, L=0, dnum=1, K=1), ksa.PC_EINVAL),
+    (dict(log2n=12, L=3, dnum=3, K=0), ksa.PC_EINVAL),
+    (dict(log2n=12, L=8, dnum=7, K=1), ksa.PC_EUNSUPPORTED),
+    (dict(log2n=12, L=3, dnum=3, K=1, chacha_rounds=8), ksa.PC_EUNSUPPORTED),
+    (dict(log2n=12, L=3, dnum=3, K=1, max_hoist=33), ksa.PC_EUNSUPPORTED),
+])
+def test_create_rejects(kw, code):
+    with pytest.raises(ksa.PcError) as e:
+        ksa.Params(device=None, **kw)
+    assert e.value.code == code
+
+
+def test_compute_calls_validate_before_touching_a_device():
+    lib = ksa._lib()
+    with ksa.Params(12, 3, 3, 1, device=None) as prm:
+        h = prm.handle
+        dummy = ctypes.c_void_p(0x1000)  # never dereferenced: validation or the device check fails first
+        idx = (ctypes.c_uint32 * 1)(0)
+        bad_idx = (ctypes.c_uint32 * 1)(4)
+        assert lib.pc_ntt(h, None, idx, 1, None) == ksa.PC_EINVAL
+        assert lib.pc_ntt(h, dummy, bad_idx, 1, None) == ksa.PC_EINVAL
+        assert lib.pc_ntt(h, dummy, idx, 1, None) == ksa.PC_EDEVICE
+        assert lib.pc_intt(h, dummy, idx, 1, None) == ksa.PC_EDEVICE
+        assert lib.pc_modup(h, dummy, 0, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_modup(h, dummy, 4, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_modup(h, dummy, 3, dummy, None) == ksa.PC_EDEVICE
+        assert lib.pc_moddown(h, dummy, 3, None, None) == ksa.PC_EINVAL
+        seed = bytes(32)
+        assert lib.pc_keyswitch(h, dummy, dummy, seed, 3, 4, dummy, None) == ksa.PC_EINVAL  # even Galois element
+        assert lib.pc_keyswitch(h, dummy, dummy, seed, 3, 1 << 13, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_keyswitch(h, dummy, dummy, None, 3, 5, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_keyswitch(h, dummy, dummy, seed, 9, 5, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_keyswitch(h, dummy, dummy, seed, 3, 5, dummy, None) == ksa.PC_EDEVICE
+        assert lib.pc_chacha_expand(h, seed, 3, 0, 3, dummy, None) == ksa.PC_EINVAL  # beta = 3 digits
+        assert lib.pc_chacha_expand(h, seed, 0, 4, 3, dummy, None) == ksa.PC_EINVAL  # 3 + K limbs
+        assert lib.pc_chacha_expand(h, seed, 2, 3, 3, dummy, None) == ksa.PC_EDEVICE
+        # batch above max_batch
+        args = ksa._KsArgs()
+        args.ct, args.batch, args.nkeys, args.level, args.out = dummy, 2, 1, 3, dummy
+        bp = (ctypes.c_void_p * 1)(0x1000)
+        gal = (ctypes.c_uint32 * 1)(5)
+        args.evk_b, args.galois, args.seeds = bp, gal, seed
+        assert lib.pc_keyswitch_ex(h, ctypes.byref(args), None) == ksa.PC_EINVAL
+        args.batch = 1
+        assert lib.pc_keyswitch_ex(h, ctypes.byref(args), None) == ksa.PC_EDEVICE
+        args.seeds = None
+        assert lib.pc_keyswitch_ex(h, ctypes.byref(args), None) == ksa.PC_EINVAL
+        # params_get argument checks
+        buf = (ctypes.c_uint32 * 4)()
+        assert lib.pc_params_get(h, ksa.PC_GET_PRIMES, 0, buf, 12) == ksa.PC_EINVAL
+        assert lib.pc_params_get(h, ksa.PC_GET_ALPHA, 0, buf, 4) == ksa.PC_EINVAL
+        assert lib.pc_params_get(h, 99, 0, buf, 4) == ksa.PC_EINVAL
+    assert lib.pc_strerror(ksa.PC_EDEVICE).startswith(b"device")
+
+
+def test_workspace_grows_with_level():
+    with ksa.Params(16, 24, 4, 6, max_batch=8, device=None) as prm:
+        sizes = [prm.workspace_bytes(l) for l in (4, 8, 12, 16, 20, 24)]
+        assert sizes == sorted(sizes) and sizes[0] > 0

@@ -1,0 +1,336 @@
+"""Bit-exact parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Everything here is integer arithmetic, so the bar is equality of every word.
+Inputs are seeded synthetic draws from ks_inputs; keys come from the oracle's
+key generation (small rings) or are uniform b halves with a ChaCha seed (large
+rings: bit-exactness does not depend on b being a real key, and the full-size
+decryption bound is checked on the CPU by the oracle's own tests and here on
+the headline workload). The oracle computes its own primes, which must equal
+the library's.
+"""
+
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import ks_inputs as ki
+from oracle import chacha
+from oracle import keyswitch as ks
+from oracle import rns
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+ksa = pytest.importorskip("key_switching_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "these tests need the GPU"
+    torch.cuda.set_device(0)
+    yield 0
+    torch.cuda.synchronize()
+
+
+def dev(a):
+    return ksa.to_device(a, 0)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return ksa.to_host(t)
+
+
+def assert_equal(gpu_words, oracle_words, what):
+    g = np.asarray(gpu_words, dtype=np.uint64)
+    o = np.asarray(oracle_words, dtype=np.uint64)
+    assert g.shape == o.shape, (what, g.shape, o.shape)
+    bad = np.flatnonzero(g.reshape(-1) != o.reshape(-1))
+    assert bad.size == 0, f"{what}: {bad.size} of {g.size} words differ, first at flat index {bad[0]}"
+
+
+def params_pair(log2n, L, dnum, K, **kw):
+    prm = ksa.Params(log2n, L, dnum, K, device=0, **kw)
+    oprm = ks.Params(log2n, L, dnum, K, chacha_rounds=kw.get("chacha_rounds", 12))
+    assert tuple(prm.primes) == oprm.primes
+    assert tuple(prm.psi) == tuple(rns.find_psi(p, oprm.N) for p in oprm.primes)
+    return prm, oprm
+
+
+# ---------------------------------------------------------------------------
+# NTT
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("log2n,L,K", [(12, 3, 1), (16, 24, 6), (17, 40, 8)])
+def test_ntt_and_intt_match_oracle(log2n, L, K):
+    prm, oprm = params_pair(log2n, L, 1, K)
+    N = oprm.N
+    primes = oprm.primes
+    idx = list(range(len(primes)))[::-1]  # a non-trivial prime order
+    x = ki.uniform_limbs(np.random.default_rng(log2n), [primes[i] for i in idx], N)
+    t = dev(x)
+    ksa.ntt(prm, t, idx)
+    fw = host(t)
+    for z in range(0, len(idx), max(1, len(idx) // 8)):
+        assert_equal(fw[z], rns.ntt(x[z], primes[idx[z]]), f"ntt limb {z}")
+    ksa.intt(prm, t, idx)
+    assert_equal(host(t), x, "intt(ntt(x))")
+    t2 = dev(x)
+    ksa.intt(prm, t2, idx)
+    back = host(t2)
+    for z in range(0, len(idx), max(1, len(idx) // 8)):
+        assert_equal(back[z], rns.intt(x[z], primes[idx[z]]), f"intt limb {z}")
+    prm.close()
+
+
+def test_ntt_edge_values():
+    prm, oprm = params_pair(16, 2, 1, 1)
+    N, q = oprm.N, oprm.primes[0]
+    cases = np.stack([np.zeros(N), np.full(N, q - 1), np.eye(1, N, 0)[0], np.eye(1, N, N - 1)[0]]).astype(np.uint64)
+    t = dev(cases)
+    ksa.ntt(prm, t, [0] * 4)
+    out = host(t)
+    for z in range(4):
+        assert_equal(out[z], rns.ntt(cases[z], q), f"edge case {z}")
+    prm.close()
+
+
+# ---------------------------------------------------------------------------
+# ChaCha expander
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("log2n,L,dnum,K", [(12, 3, 3, 1), (16, 24, 4, 6)])
+def test_chacha_expand_matches_oracle(log2n, L, dnum, K):
+    prm, oprm = params_pair(log2n, L, dnum, K)
+    seed = bytes(range(7, 39))
+    for level in (L, max(1, L // 2)):
+        basis = oprm.basis(level)
+        for d in range(len(oprm.digits(level))):
+            for j in (0, level - 1, level, len(basis) - 1):
+                g = host(ksa.chacha_expand(prm, seed, d, j, level))
+                assert_equal(g, chacha.expand_uniform(seed, d, j, oprm.N, basis[j], 12), f"a[{d}][{j}] l={level}")
+    prm.close()
+
+
+@pytest.mark.skipif(shutil.which("openssl") is None, reason="openssl command line not available")
+def test_chacha20_expand_matches_openssl():
+    prm, oprm = params_pair(12, 3, 3, 1, chacha_rounds=20)
+    seed = bytes(range(100, 132))
+    N = oprm.N
+    for d, j in ((0, 0), (2, 3)):
+        r = oprm.basis(3)[j]
+        iv = bytes(4) + (0).to_bytes(4, "little") + d.to_bytes(4, "little") + j.to_bytes(4, "little")
+        res = subprocess.run(["openssl", "enc", "-chacha20", "-K", seed.hex(), "-iv", iv.hex()],
+                             input=bytes(8 * N), stdout=subprocess.PIPE, check=True)
+        ref = [int.from_bytes(res.stdout[8 * i: 8 * i + 8], "little") % r for i in range(N)]
+        assert_equal(host(ksa.chacha_expand(prm, seed, d, j, 3)), ref, f"chacha20 a[{d}][{j}]")
+    prm.close()
+
+
+# ---------------------------------------------------------------------------
+# ModUp and ModDown
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("log2n,L,dnum,K,levels", [
+    (12, 3, 3, 1, (3, 2, 1)),
+    (12, 7, 3, 2, (7, 5, 4, 1)),   # short last digit, one-prime digits
+    (16, 24, 4, 6, (24, 13)),
+])
+def test_modup_matches_oracle(log2n, L, dnum, K, levels):
+    prm, oprm = params_pair(log2n, L, dnum, K)
+    for level in levels:
+        c1 = ki.uniform_limbs(np.random.default_rng(level), oprm.q[:level], oprm.N)
+        ext = host(ksa.modup(prm, dev(c1), level))
+        assert_equal(ext, ks.modup(oprm, c1, level), f"modup level {level}")
+    prm.close()
+
+
+@pytest.mark.parametrize("log2n,L,dnum,K,levels", [
+    (12, 3, 3, 1, (3, 1)),
+    (12, 7, 3, 3, (7, 2)),
+    (16, 24, 4, 6, (24, 9)),
+])
+def test_moddown_matches_oracle(log2n, L, dnum, K, levels):
+    prm, oprm = params_pair(log2n, L, dnum, K)
+    for level in levels:
+        acc = ki.uniform_limbs(np.random.default_rng(100 + level), oprm.basis(level), oprm.N)
+        out = host(ksa.moddown(prm, dev(acc), level))
+        assert_equal(out, ks.moddown(oprm, acc, level), f"moddown level {level}")
+    prm.close()
+
+
+# ---------------------------------------------------------------------------
+# whole key switch
+# ---------------------------------------------------------------------------
+
+def _real_keys(oprm, widx, level, galois_list, h):
+    s = ki.ternary_secret(widx, oprm.N, h)
+    keys, emax = [], 0
+    for kidx, g in enumerate(galois_list):
+        errs = ki.gaussian_errors(widx, kidx, len(oprm.digits(level)), oprm.N)
+        emax = max(emax, int(np.abs(errs).max()))
+        keys.append(ks.keygen(oprm, s, errs, ki.key_seed(widx, kidx), level, g))
+    return s, keys, emax
+
+
+def _uniform_keys(oprm, widx, level, galois_list):
+    beta = len(oprm.digits(level))
+    return [ks.Key(b=ki.uniform_key_b(widx, k, beta, oprm.basis(level), oprm.N), seed=ki.key_seed(widx, k),
+                   level=level, galois=g) for k, g in enumerate(galois_list)]
+
+
+def _decrypts(oprm, ct, out, s, galois, level, emax, h):
+    e = ks.decryption_error(oprm, ct, out, s, galois, level)
+    assert e is not None, "error residues differ between limbs"
+    assert np.abs(e).max() <= ks.error_bound(oprm, level, emax, h)
+
+
+def test_tiny_rotation_bit_exact_and_decrypts():
+    w = ki.WORKLOADS["tiny"]
+    prm, oprm = params_pair(w.log2n, w.L, w.dnum, w.K)
+    s, (key,), emax = _real_keys(oprm, w.index, w.L, (5,), w.h)
+    ct = ki.ciphertexts(w.index, oprm.q, oprm.N, 1)[0]
+    out = host(ksa.keyswitch(prm, dev(ct), dev(key.b), key.seed, w.L, 5))
+    assert_equal(out, ks.keyswitch(oprm, ct, key, w.L), "tiny key switch")
+    _decrypts(oprm, ct, out, s, 5, w.L, emax, w.h)
+    prm.close()
+
+
+@pytest.mark.parametrize("level,galois", [(7, 1), (7, 8191), (5, 25), (4, 5), (1, 5), (1, 1)])
+def test_small_ring_levels_and_partitions(level, galois):
+    # K = 3 special primes: P is about as large as the biggest digit (3 primes),
+    # which the decryption bound needs; digits at level 7 are 3, 3 and 1 primes.
+    prm, oprm = params_pair(12, 7, 3, 3)
+    s, (key,), emax = _real_keys(oprm, 20 + level, level, (galois,), 32)
+    ct = ki.ciphertexts(20 + level, oprm.q[:level], oprm.N, 1)[0]
+    out = host(ksa.keyswitch(prm, dev(ct), dev(key.b), key.seed, level, galois))
+    assert_equal(out, ks.keyswitch(oprm, ct, key, level), f"level {level} galois {galois}")
+    _decrypts(oprm, ct, out, s, galois, level, emax, 32)
+    prm.close()
+
+
+def test_headline_n16_relinearisation_k1_k8():
+    """N=2^16, L=24, dnum=4, K=6, relinearisation key, k=1 and k=8."""
+    w = ki.WORKLOADS["n16"]
+    prm, oprm = params_pair(w.log2n, w.L, w.dnum, w.K, max_batch=8)
+    s, (key,), emax = _real_keys(oprm, w.index, w.L, (1,), w.h)
+    cts = ki.ciphertexts(w.index, oprm.q, oprm.N, 8)
+    kb = dev(key.b)
+    single = host(ksa.keyswitch(prm, dev(cts[0]), kb, key.seed, w.L, 1))
+    ref0 = ks.keyswitch(oprm, cts[0], key, w.L)
+    assert_equal(single, ref0, "k=1")
+    _decrypts(oprm, cts[0], single, s, 1, w.L, emax, w.h)
+    batch = host(ksa.keyswitch_ex(prm, dev(cts), [kb], [1], w.L, seeds=[key.seed]))[0]
+    assert_equal(batch[0], ref0, "k=8 item 0")
+    assert_equal(batch[7], ks.keyswitch(oprm, cts[7], key, w.L), "k=8 item 7")
+    _decrypts(oprm, cts[5], batch[5], s, 1, w.L, emax, w.h)
+    for b in (1, 3, 6):
+        assert_equal(batch[b], host(ksa.keyswitch(prm, dev(cts[b]), kb, key.seed, w.L, 1)), f"batch item {b} vs single")
+    # stored a half gives the same bits as the regenerated one
+    a = dev(ks.key_a(oprm, key))
+    stored = host(ksa.keyswitch_ex(prm, dev(cts), [kb], [1], w.L, evk_a=[a]))[0]
+    assert_equal(stored, batch, "stored vs regenerated")
+    # repeat: deterministic
+    again = host(ksa.keyswitch_ex(prm, dev(cts), [kb], [1], w.L, seeds=[key.seed]))[0]
+    assert_equal(again, batch, "repeat")
+    prm.close()
+
+
+def test_hoisted16_sixteen_rotations():
+    """One ciphertext, ModUp once, 16 rotation keys X -> X^(5^r)."""
+    w = ki.WORKLOADS["hoist16"]
+    prm, oprm = params_pair(w.log2n, w.L, w.dnum, w.K, max_hoist=16)
+    keys = _uniform_keys(oprm, w.index, w.L, w.galois)
+    ct = ki.ciphertexts(w.index, oprm.q, oprm.N, 1)
+    kbs = [dev(k.b) for k in keys]
+    out = host(ksa.keyswitch_ex(prm, dev(ct), kbs, list(w.galois), w.L, seeds=[k.seed for k in keys]))
+    picks = [0, 7, 15]
+    ref = ks.keyswitch_hoisted(oprm, ct[0], [keys[r] for r in picks], w.L)
+    for n, r in enumerate(picks):
+        assert_equal(out[r, 0], ref[n], f"hoisted key r={r + 1}")
+    for r in range(16):
+        single = host(ksa.keyswitch(prm, dev(ct[0]), kbs[r], keys[r].seed, w.L, w.galois[r]))
+        assert_equal(out[r, 0], single, f"hoisted vs single r={r + 1}")
+    prm.close()
+
+
+def test_levels16_sweep():
+    """Levels 24..4 with alpha = ceil(l/4), k=8, keys X -> X^5 and X -> X^-1 made at each level."""
+    w = ki.WORKLOADS["levels16"]
+    prm, oprm = params_pair(w.log2n, w.L, w.dnum, w.K, max_batch=8, max_hoist=2)
+    for level in w.levels:
+        keys = _uniform_keys(oprm, w.index * 100 + level, level, w.galois)
+        cts = ki.ciphertexts(w.index * 100 + level, oprm.q[:level], oprm.N, 8)
+        out = host(ksa.keyswitch_ex(prm, dev(cts), [dev(k.b) for k in keys], list(w.galois), level,
+                                    seeds=[k.seed for k in keys]))
+        b = level % 8
+        ref = ks.keyswitch_hoisted(oprm, cts[b], keys, level)
+        for r in range(2):
+            assert_equal(out[r, b], ref[r], f"level {level} key {r} item {b}")
+    prm.close()
+
+
+@pytest.fixture(scope="module")
+def n17_case():
+    """N=2^17, L=40, dnum=5, K=8, k=8 with a relinearisation key and an X -> X^5 key.
+
+    The oracle's relinearisation of one sampled ciphertext (about 45 s on one
+    core) is computed once and shared by the two tests below.
+    """
+    w = ki.WORKLOADS["n17"]
+    prm, oprm = params_pair(w.log2n, w.L, w.dnum, w.K, max_batch=8)
+    relin, rot = _uniform_keys(oprm, w.index, w.L, w.galois)
+    cts = ki.ciphertexts(w.index, oprm.q, oprm.N, 8)
+    b = 3
+    ref1 = ks.keyswitch(oprm, cts[b], relin, w.L)
+    yield dict(w=w, prm=prm, oprm=oprm, relin=relin, rot=rot, cts=cts, b=b, ref1=ref1)
+    prm.close()
+
+
+def test_n17_relinearise(n17_case):
+    c = n17_case
+    prm, w, relin = c["prm"], c["w"], c["relin"]
+    out = host(ksa.keyswitch_ex(prm, dev(c["cts"]), [dev(relin.b)], [1], w.L, seeds=[relin.seed]))[0]
+    assert_equal(out[c["b"]], c["ref1"], "n17 relinearisation")
+
+
+def test_n17_rotate_after_relinearise(n17_case):
+    """Relinearise the batch, then rotate the result by X -> X^5 (two chained key switches)."""
+    c = n17_case
+    prm, w, relin, rot = c["prm"], c["w"], c["relin"], c["rot"]
+    step1 = ksa.keyswitch_ex(prm, dev(c["cts"]), [dev(relin.b)], [1], w.L, seeds=[relin.seed])
+    step2 = host(ksa.keyswitch_ex(prm, step1[0].contiguous(), [dev(rot.b)], [5], w.L, seeds=[rot.seed]))[0]
+    ref2 = ks.keyswitch(c["oprm"], c["ref1"], rot, w.L)
+    assert_equal(step2[c["b"]], ref2, "n17 chain")
+
+
+def test_caller_workspace_matches_arena():
+    prm, oprm = params_pair(12, 7, 3, 2, max_batch=3, max_hoist=2)
+    keys = _uniform_keys(oprm, 77, 7, (5, 1))
+    cts = ki.ciphertexts(77, oprm.q, oprm.N, 3)
+    kbs = [dev(k.b) for k in keys]
+    seeds = [k.seed for k in keys]
+    a = host(ksa.keyswitch_ex(prm, dev(cts), kbs, [5, 1], 7, seeds=seeds))
+    ws = torch.empty(prm.workspace_bytes(7) // 4, dtype=torch.int32, device="cuda:0")
+    b = host(ksa.keyswitch_ex(prm, dev(cts), kbs, [5, 1], 7, seeds=seeds, workspace=ws))
+    assert_equal(a, b, "caller workspace")
+    ref = ks.keyswitch_hoisted(oprm, cts[2], keys, 7)
+    assert_equal(a[:, 2], ref, "3-item batch, 2 keys")
+    small = torch.empty(16, dtype=torch.int32, device="cuda:0")
+    with pytest.raises(ksa.PcError):
+        ksa.keyswitch_ex(prm, dev(cts), kbs, [5, 1], 7, seeds=seeds, workspace=small)
+    prm.close()
+
+
+def test_rejected_arguments_on_gpu():
+    prm, oprm = params_pair(12, 3, 3, 1)
+    ct = dev(np.zeros((2, 3, oprm.N), dtype=np.uint32))
+    b = dev(np.zeros((3, 4, oprm.N), dtype=np.uint32))
+    with pytest.raises(ksa.PcError) as e:
+        ksa.keyswitch(prm, ct, b, bytes(32), 3, 4)
+    assert e.value.code == ksa.PC_EINVAL
+    with pytest.raises(ValueError):
+        ksa.keyswitch(prm, ct[:, :2].contiguous(), b, bytes(32), 3, 5)
+    prm.close()
