@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Throughput of CKKS hybrid key switching on one MI355X.
+
+A step is one call of the whole hot path (ModUp, automorphism + inner product
+with the ChaCha12-regenerated key half, ModDown) on one batch of synthetic
+ciphertexts at N=2^16, L=24, dnum=4, K=6 with one relinearisation key: the
+workload the headline metric (key switches/s at N=2^16, L=24, k=1 and 8) is
+quoted on. `value` is key switches per second at batch k=8; the k=1 rate and
+the stored-key variants are reported beside it.
+
+Inputs are resident in HBM before timing starts. Ciphertext inputs and outputs
+rotate through more than 1 GiB of buffers so that the 256 MB Infinity Cache
+cannot hold them between steps; the key is reused, as in real
+relinearisation. The key's b half is a uniform draw (a real b half is
+indistinguishable from uniform) so that timing never depends on key
+generation.
+
+Prints one JSON line. `python bench.py --gpus N` with N > 1 exits: this build
+measures one GPU.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import ks_inputs as ki  # noqa: E402
+
+METRIC = "key switches/sec at N=2^16, L=24 (k=1,8); % of HBM/INT32 roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+CUS, CLOCK_GHZ = 256, 2.4       # MI355X compute units and peak engine clock
+VALU_LANES_PER_CU = 128         # 32-bit lanes per CU per clock (fp32 vector 157.3 TFLOP/s = 256*128*2.4e9*2)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--buffers-gib", type=float, default=1.1, help="ciphertext buffer rotation size")
+    return ap.parse_args()
+
+
+def alg_bytes_per_launch(kernel, w, batch, beta, alpha):
+    """Algorithmic bytes one launch must move: each input limb read once, each output limb written once.
+
+    Limb = N words of 4 bytes. l = level, K special primes, T_d = l - alpha + K
+    targets per digit (the last digit may be shorter; handled exactly below).
+    """
+    N, l, K = w.N, w.L, w.K
+    limb = 4 * N
+    digits = [min(alpha, l - d * alpha) for d in range(beta)]
+    targets = sum(l + K - a for a in digits)
+    table = {
+        # ModUp: c1 in, y out; y in place; y in, targets out; targets in, ext out
+        "modup_inv_blk": batch * (l + l),
+        "modup_inv_col": batch * (l + l),
+        "modup_bconv_col": batch * (l + targets),
+        "modup_fwd_blk": batch * (targets + targets),
+        # IP: ext (targets) + own c1 limbs read, b read once per batch, acc written
+        "inner_product": batch * (targets + l) + beta * (l + K) + batch * 2 * (l + K),
+        # ModDown on 2 polys per item
+        "moddown_inv_blk": batch * 2 * (K + K),
+        "moddown_inv_col": batch * 2 * (K + K),
+        "moddown_bconv_col": batch * 2 * (K + l),
+        "moddown_fwd_blk": batch * 2 * (l + l + l) + batch * l,  # tmp2 + acc in, out; c0 in
+    }
+    return table[kernel] * limb
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(key switching shards by ciphertext batch; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import key_switching_amd as ksa
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    torch.cuda.set_device(0)
+    w = ki.WORKLOADS["n16"]
+    K8 = 8
+    prm = ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=K8, device=0)
+    primes = prm.primes
+    q = primes[: w.L]
+    basis = prm.basis(w.L)
+    beta, alpha = prm.beta(w.L), prm.alpha(w.L)
+
+    # resident inputs: rotating ciphertext / output buffers, one key
+    ct_bytes = K8 * 2 * w.L * w.N * 4
+    nbuf = max(2, int(np.ceil(args.buffers_gib * (1 << 30) / (2 * ct_bytes))))
+    base = ki.ciphertexts(w.index, q, w.N, K8)
+    cts, outs = [], []
+    for i in range(nbuf):
+        t = ksa.to_device(base, 0)
+        if i:
+            t = torch.roll(t, shifts=i, dims=-1).contiguous()  # distinct contents, same distribution
+        cts.append(t)
+        outs.append(torch.empty((1, K8, 2, w.L, w.N), dtype=torch.int32, device="cuda:0"))
+    evk_b = ksa.to_device(ki.uniform_key_b(w.index, 0, beta, basis, w.N), 0)
+    evk_a = ksa.to_device(ki.uniform_key_b(w.index, 1, beta, basis, w.N), 0)  # stands in for a stored a half
+    seed = ki.key_seed(w.index, 0)
+    torch.cuda.synchronize()
+
+    def step(i, batch, stored=False):
+        ct = cts[i % nbuf][:batch]
+        out = outs[i % nbuf][:, :batch]
+        if stored:
+            ksa.keyswitch_ex(prm, ct, [evk_b], [1], w.L, evk_a=[evk_a], out=out)
+        else:
+            ksa.keyswitch_ex(prm, ct, [evk_b], [1], w.L, seeds=[seed], out=out)
+
+    def timed(batch, stored=False, steps=args.steps):
+        for i in range(args.warmup):
+            step(i, batch, stored)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            step(i, batch, stored)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = e0.elapsed_time(e1)
+        return ms / steps, wall
+
+    ms8, wall8 = timed(K8)
+    ms1, _ = timed(1)
+    ms8s, _ = timed(K8, stored=True)
+    ms1s, _ = timed(1, stored=True)
+    print(f"[bench] k=8 {ms8:.3f} ms/step, k=1 {ms1:.3f} ms/step, stored k=8 {ms8s:.3f}, stored k=1 {ms1s:.3f}",
+          file=sys.stderr, flush=True)
+
+    # per-kernel HIP-event timings over a timed region of the same k=8 steps
+    ksa.profile_begin(prm)
+    ms8p, _ = timed(K8)
+    kstats = ksa.profile_end(prm)
+    kernels = {k: {"launches": n, "avg_us": 1000.0 * t / n, "share": t / (ms8p * args.steps)}
+               for k, (n, t) in sorted(kstats.items(), key=lambda kv: -kv[1][1])}
+    dom = next(iter(kernels))
+    dom_avg_s = kernels[dom]["avg_us"] * 1e-6
+    dom_bytes = alg_bytes_per_launch(dom, w, K8, beta, alpha)
+    achieved = dom_bytes / dom_avg_s / 1e9
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "alg_bytes_per_launch": dom_bytes}
+
+    result = {
+        "metric": METRIC,
+        "value": round(K8 * 1000.0 / ms8, 1),
+        "unit": "key switches/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms8, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": "n16: N=2^16, L=24 q-primes (31-bit), dnum=4 (alpha=6), K=6, relinearisation key, "
+                               "a half regenerated in-kernel (ChaCha12), batch k=8",
+                   "N": w.N, "L": w.L, "dnum": w.dnum, "K": w.K, "batch": K8, "buffers": nbuf},
+        "variants": {
+            "k8_chacha": {"ks_per_s": round(K8 * 1000.0 / ms8, 1), "ms_per_call": round(ms8, 4)},
+            "k1_chacha": {"ks_per_s": round(1000.0 / ms1, 1), "ms_per_call": round(ms1, 4)},
+            "k8_stored": {"ks_per_s": round(K8 * 1000.0 / ms8s, 1), "ms_per_call": round(ms8s, 4)},
+            "k1_stored": {"ks_per_s": round(1000.0 / ms1s, 1), "ms_per_call": round(ms1s, 4)},
+            "k8_chacha_profiled": {"ms_per_call": round(ms8p, 4)},
+        },
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "roofline": roofline,
+        "wall_s_k8": round(wall8, 3),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    prm.close()
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle as it stands, one thread, on a bounded sample: whole key switches of single
+    N=2^16, L=24 ciphertexts (k=1) with the same key shape, repeated until the budget is used."""
+    from oracle import keyswitch as ks
+    oprm = ks.Params(w.log2n, w.L, w.dnum, w.K)
+    beta = len(oprm.digits(w.L))
+    key = ks.Key(b=ki.uniform_key_b(w.index, 0, beta, oprm.basis(w.L), w.N), seed=ki.key_seed(w.index, 0),
+                 level=w.L, galois=1)
+    cts = ki.ciphertexts(w.index, oprm.q, w.N, 4)
+    ks.keyswitch(oprm, cts[0], key, w.L)  # warm the oracle's table caches
+    n, t0 = 0, time.perf_counter()
+    while True:
+        ks.keyswitch(oprm, cts[n % 4], key, w.L)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 50:
+            break
+    return {"value": round(n / el, 4), "unit": "key switches/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} single-ciphertext key switches (N=2^16, L=24, dnum=4, K=6, ChaCha12 a half) "
+                      f"in {el:.1f} s on one host core (numpy, single-threaded)"}
+
+
+if __name__ == "__main__":
+    main()

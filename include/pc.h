@@ -153,6 +153,21 @@ int pc_keyswitch_ex(const pc_params *p, const pc_ks_args *args, void *stream);
 int pc_chacha_expand(const pc_params *p, const uint8_t *seed, uint32_t d, uint32_t j, uint32_t level, uint32_t *dst,
                      void *stream);
 
+/* Measurement support. Between pc_profile_begin and pc_profile_end every
+ * kernel the library launches for p is bracketed by two hipEvents recorded on
+ * the stream it runs on. pc_profile_end waits for those events and writes, per
+ * kernel family (stats[k].name is a static string), the number of launches and
+ * their summed event-to-event milliseconds; *count receives the number of
+ * families written (at most max_stats). Not thread-safe; one profiling window
+ * per params at a time. */
+typedef struct {
+  const char *name;
+  uint32_t launches;
+  double total_ms;
+} pc_kernel_stat;
+int pc_profile_begin(const pc_params *p);
+int pc_profile_end(const pc_params *p, pc_kernel_stat *stats, uint32_t max_stats, uint32_t *count);
+
 const char *pc_strerror(int code);
 
 #ifdef __cplusplus

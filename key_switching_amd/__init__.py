@@ -21,7 +21,8 @@ PC_OK, PC_EINVAL, PC_ENOMEM, PC_EDEVICE, PC_EUNSUPPORTED = 0, -1, -2, -3, -4
 PC_GET_N, PC_GET_PRIMES, PC_GET_PSI, PC_GET_ALPHA, PC_GET_BETA, PC_GET_WORKSPACE_BYTES, PC_GET_DEVICE_TABLE = range(1, 8)
 
 EXPORTED = ("pc_params_create", "pc_params_destroy", "pc_params_get", "pc_ntt", "pc_intt", "pc_modup",
-            "pc_keyswitch", "pc_moddown", "pc_keyswitch_ex", "pc_chacha_expand", "pc_strerror")
+            "pc_keyswitch", "pc_moddown", "pc_keyswitch_ex", "pc_chacha_expand", "pc_profile_begin",
+            "pc_profile_end", "pc_strerror")
 
 
 class PcError(RuntimeError):
@@ -42,6 +43,10 @@ class _KsArgs(ctypes.Structure):
                 ("seeds", ctypes.c_char_p), ("galois", ctypes.POINTER(ctypes.c_uint32)),
                 ("level", ctypes.c_uint32), ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t)]
+
+
+class _KStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_uint32), ("total_ms", ctypes.c_double)]
 
 
 _LIB = None
@@ -65,10 +70,12 @@ def _lib():
         lib.pc_moddown.argtypes = [vp, vp, u32, vp, vp]
         lib.pc_keyswitch_ex.argtypes = [vp, ctypes.POINTER(_KsArgs), vp]
         lib.pc_chacha_expand.argtypes = [vp, ctypes.c_char_p, u32, u32, u32, vp, vp]
+        lib.pc_profile_begin.argtypes = [vp]
+        lib.pc_profile_end.argtypes = [vp, ctypes.POINTER(_KStat), u32, ctypes.POINTER(u32)]
         lib.pc_strerror.argtypes = [i32]
         lib.pc_strerror.restype = ctypes.c_char_p
         for name in ("pc_params_create", "pc_params_get", "pc_ntt", "pc_intt", "pc_modup", "pc_keyswitch",
-                     "pc_moddown", "pc_keyswitch_ex", "pc_chacha_expand"):
+                     "pc_moddown", "pc_keyswitch_ex", "pc_chacha_expand", "pc_profile_begin", "pc_profile_end"):
             getattr(lib, name).restype = i32
         _LIB = lib
     return _LIB
@@ -286,6 +293,19 @@ def chacha_expand(prm: Params, seed: bytes, d: int, j: int, level: int, out=None
     _check(_lib().pc_chacha_expand(prm.handle, _seed_bytes(seed), d, j, level,
                                    _dev_ptr(out, "out", (prm.N,), prm.device), _stream()), "pc_chacha_expand")
     return out
+
+
+def profile_begin(prm: Params):
+    """Start bracketing every kernel launch of ``prm`` with HIP events (pc_profile_begin)."""
+    _check(_lib().pc_profile_begin(prm.handle), "pc_profile_begin")
+
+
+def profile_end(prm: Params) -> dict:
+    """Stop and return {kernel family: (launches, summed milliseconds)} (pc_profile_end)."""
+    stats = (_KStat * 32)()
+    n = ctypes.c_uint32()
+    _check(_lib().pc_profile_end(prm.handle, stats, 32, ctypes.byref(n)), "pc_profile_end")
+    return {stats[i].name.decode(): (int(stats[i].launches), float(stats[i].total_ms)) for i in range(n.value)}
 
 
 # host <-> device helpers (uint32 residues held in int32 tensors)

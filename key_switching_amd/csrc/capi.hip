@@ -295,6 +295,34 @@ KsWorkspace ks_workspace_carve(const pc_params* p, void* base, uint32_t level, u
   return w;
 }
 
+const char* const kKernelNames[KID_COUNT] = {
+    "ntt_fwd_col",  "ntt_fwd_blk",     "ntt_inv_blk",   "ntt_inv_col",     "modup_inv_blk",
+    "modup_inv_col", "modup_bconv_col", "modup_fwd_blk", "inner_product",   "moddown_inv_blk",
+    "moddown_inv_col", "moddown_bconv_col", "moddown_fwd_blk", "chacha_expand"};
+
+static hipEvent_t prof_event(const pc_params* p) {
+  if (p->prof_used == p->prof_pool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    p->prof_pool.push_back(e);
+  }
+  return p->prof_pool[p->prof_used++];
+}
+
+LaunchTimer::LaunchTimer(const pc_params* params, int kid, hipStream_t stream) : p(params), kernel(kid), s(stream) {
+  if (p->prof_on) {
+    start = prof_event(p);
+    if (start) (void)hipEventRecord(start, s);
+  }
+}
+
+LaunchTimer::~LaunchTimer() {
+  if (p->prof_on && start) {
+    hipEvent_t stop = prof_event(p);
+    if (stop && hipEventRecord(stop, s) == hipSuccess) p->prof_recs.push_back({kernel, start, stop});
+  }
+}
+
 }  // namespace pc
 
 using namespace pc;
@@ -390,10 +418,50 @@ void pc_params_destroy(pc_params* p) {
   if (p == nullptr) return;
   if (p->device >= 0) {
     DeviceGuard g(p->device);
+    for (hipEvent_t e : p->prof_pool) (void)hipEventDestroy(e);
     if (p->arena) (void)hipFree(p->arena);
     if (p->d_tables) (void)hipFree(p->d_tables);
   }
   delete p;
+}
+
+int pc_profile_begin(const pc_params* p) {
+  if (p == nullptr) return PC_EINVAL;
+  if (p->device < 0) return PC_EDEVICE;
+  p->prof_recs.clear();
+  p->prof_used = 0;
+  p->prof_on = true;
+  return PC_OK;
+}
+
+int pc_profile_end(const pc_params* p, pc_kernel_stat* stats, uint32_t max_stats, uint32_t* count) {
+  if (p == nullptr || count == nullptr || (stats == nullptr && max_stats > 0)) return PC_EINVAL;
+  if (p->device < 0) return PC_EDEVICE;
+  DeviceGuard g(p->device);
+  if (!g.ok) return PC_EDEVICE;
+  p->prof_on = false;
+  double ms[KID_COUNT] = {0};
+  uint32_t n[KID_COUNT] = {0};
+  int rc = PC_OK;
+  for (const auto& r : p->prof_recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) {
+      rc = PC_EDEVICE;
+      continue;
+    }
+    ms[r.kernel] += t;
+    n[r.kernel] += 1;
+  }
+  p->prof_recs.clear();
+  p->prof_used = 0;
+  uint32_t c = 0;
+  for (int k = 0; k < KID_COUNT; ++k) {
+    if (n[k] == 0) continue;
+    if (c < max_stats) stats[c] = pc_kernel_stat{kKernelNames[k], n[k], ms[k]};
+    ++c;
+  }
+  *count = c < max_stats ? c : max_stats;
+  return rc;
 }
 
 int pc_params_get(const pc_params* p, int what, uint32_t arg, void* dst, size_t bytes) {

@@ -62,6 +62,15 @@ struct pc_params {
   pc::DevLevelTables ltabs{};
   void* arena = nullptr;  // workspace arena sized at create
   size_t arena_bytes = 0;
+  // measurement support (pc_profile_begin / pc_profile_end)
+  mutable bool prof_on = false;
+  mutable std::vector<hipEvent_t> prof_pool;  // events owned by the params
+  mutable size_t prof_used = 0;               // events handed out in this window
+  struct ProfRec {
+    int kernel;
+    hipEvent_t start, stop;
+  };
+  mutable std::vector<ProfRec> prof_recs;
 };
 
 namespace pc {
@@ -84,6 +93,36 @@ struct KeyRef {
   const uint32_t* a;  // stored a half (same shape) or nullptr to regenerate from seed
   uint32_t seed[8];
   uint32_t galois;
+};
+
+// Kernel families for measurement (names in kKernelNames).
+enum KernelId {
+  KID_NTT_FWD_COL,
+  KID_NTT_FWD_BLK,
+  KID_NTT_INV_BLK,
+  KID_NTT_INV_COL,
+  KID_MODUP_INV_BLK,
+  KID_MODUP_INV_COL,
+  KID_MODUP_BCONV_COL,
+  KID_MODUP_FWD_BLK,
+  KID_INNER_PRODUCT,
+  KID_MODDOWN_INV_BLK,
+  KID_MODDOWN_INV_COL,
+  KID_MODDOWN_BCONV_COL,
+  KID_MODDOWN_FWD_BLK,
+  KID_CHACHA_EXPAND,
+  KID_COUNT
+};
+extern const char* const kKernelNames[KID_COUNT];
+
+// Brackets one launch with events when profiling is on (no-op otherwise).
+struct LaunchTimer {
+  const pc_params* p;
+  int kernel;
+  hipStream_t s;
+  hipEvent_t start = nullptr;
+  LaunchTimer(const pc_params* params, int kid, hipStream_t stream);
+  ~LaunchTimer();
 };
 
 // Launchers (return hipError_t of the last launch).

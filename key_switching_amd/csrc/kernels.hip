@@ -470,11 +470,11 @@ hipError_t launch_ntt(const pc_params* p, uint32_t* data, uint32_t* tmp, const u
     for (uint32_t z = 0; z < cnt; ++z) A.pidx[z] = (uint8_t)prime_idx[base + z];
     PC_DISPATCH_LOGN(p->log2n, {
       if (!inverse) {
-        hipLaunchKernelGGL(k_ntt_fwd_col<LN>, dim3(col_tiles<LN>(), cnt), dim3(col_threads<LN>()), 0, s, A);
-        hipLaunchKernelGGL(k_ntt_fwd_blk<LN>, dim3(blk_tiles<LN>(), cnt), dim3(blk_threads<LN>()), 0, s, A);
+        { LaunchTimer tm(p, KID_NTT_FWD_COL, s); hipLaunchKernelGGL(k_ntt_fwd_col<LN>, dim3(col_tiles<LN>(), cnt), dim3(col_threads<LN>()), 0, s, A); }
+        { LaunchTimer tm(p, KID_NTT_FWD_BLK, s); hipLaunchKernelGGL(k_ntt_fwd_blk<LN>, dim3(blk_tiles<LN>(), cnt), dim3(blk_threads<LN>()), 0, s, A); }
       } else {
-        hipLaunchKernelGGL(k_ntt_inv_blk<LN>, dim3(blk_tiles<LN>(), cnt), dim3(blk_threads<LN>()), 0, s, A);
-        hipLaunchKernelGGL(k_ntt_inv_col<LN>, dim3(col_tiles<LN>(), cnt), dim3(col_threads<LN>()), 0, s, A);
+        { LaunchTimer tm(p, KID_NTT_INV_BLK, s); hipLaunchKernelGGL(k_ntt_inv_blk<LN>, dim3(blk_tiles<LN>(), cnt), dim3(blk_threads<LN>()), 0, s, A); }
+        { LaunchTimer tm(p, KID_NTT_INV_COL, s); hipLaunchKernelGGL(k_ntt_inv_col<LN>, dim3(col_tiles<LN>(), cnt), dim3(col_threads<LN>()), 0, s, A); }
       }
     });
   }
@@ -509,10 +509,10 @@ hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stri
   const uint32_t rows_in = batch * level;
   const uint32_t rows_ext = batch * (uint32_t)A.beta * (level + p->K);
   PC_DISPATCH_LOGN(p->log2n, {
-    hipLaunchKernelGGL(k_modup_inv_blk<LN>, dim3(blk_tiles<LN>(), rows_in), dim3(blk_threads<LN>()), 0, s, A);
-    hipLaunchKernelGGL(k_modup_inv_col<LN>, dim3(col_tiles<LN>(), rows_in), dim3(col_threads<LN>()), 0, s, A);
-    hipLaunchKernelGGL(k_modup_bconv_col<LN>, dim3(col_tiles<LN>(), rows_ext), dim3(col_threads<LN>()), 0, s, A);
-    hipLaunchKernelGGL(k_modup_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_ext), dim3(blk_threads<LN>()), 0, s, A);
+    { LaunchTimer tm(p, KID_MODUP_INV_BLK, s); hipLaunchKernelGGL(k_modup_inv_blk<LN>, dim3(blk_tiles<LN>(), rows_in), dim3(blk_threads<LN>()), 0, s, A); }
+    { LaunchTimer tm(p, KID_MODUP_INV_COL, s); hipLaunchKernelGGL(k_modup_inv_col<LN>, dim3(col_tiles<LN>(), rows_in), dim3(col_threads<LN>()), 0, s, A); }
+    { LaunchTimer tm(p, KID_MODUP_BCONV_COL, s); hipLaunchKernelGGL(k_modup_bconv_col<LN>, dim3(col_tiles<LN>(), rows_ext), dim3(col_threads<LN>()), 0, s, A); }
+    { LaunchTimer tm(p, KID_MODUP_FWD_BLK, s); hipLaunchKernelGGL(k_modup_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_ext), dim3(blk_threads<LN>()), 0, s, A); }
   });
   return hipGetLastError();
 }
@@ -520,6 +520,7 @@ hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stri
 template <int BETA>
 static void launch_ip_beta(const pc_params* p, const IPArgs& A, uint32_t nkeys, bool stored, hipStream_t s) {
   const dim3 grid((p->N / 8 + kIpThreads - 1) / kIpThreads, (uint32_t)(A.level + A.K), nkeys);
+  LaunchTimer tm(p, KID_INNER_PRODUCT, s);
   if (stored)
     hipLaunchKernelGGL((k_inner_product<BETA, 12, true>), grid, dim3(kIpThreads), 0, s, A);
   else if (p->chacha_rounds == 20)
@@ -596,10 +597,10 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
   const uint32_t rows_p = items * polys * p->K;
   const uint32_t rows_q = items * polys * level;
   PC_DISPATCH_LOGN(p->log2n, {
-    hipLaunchKernelGGL(k_md_inv_blk<LN>, dim3(blk_tiles<LN>(), rows_p), dim3(blk_threads<LN>()), 0, s, A);
-    hipLaunchKernelGGL(k_md_inv_col<LN>, dim3(col_tiles<LN>(), rows_p), dim3(col_threads<LN>()), 0, s, A);
-    hipLaunchKernelGGL(k_md_bconv_col<LN>, dim3(col_tiles<LN>(), rows_q), dim3(col_threads<LN>()), 0, s, A);
-    hipLaunchKernelGGL(k_md_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_q), dim3(blk_threads<LN>()), 0, s, A);
+    { LaunchTimer tm(p, KID_MODDOWN_INV_BLK, s); hipLaunchKernelGGL(k_md_inv_blk<LN>, dim3(blk_tiles<LN>(), rows_p), dim3(blk_threads<LN>()), 0, s, A); }
+    { LaunchTimer tm(p, KID_MODDOWN_INV_COL, s); hipLaunchKernelGGL(k_md_inv_col<LN>, dim3(col_tiles<LN>(), rows_p), dim3(col_threads<LN>()), 0, s, A); }
+    { LaunchTimer tm(p, KID_MODDOWN_BCONV_COL, s); hipLaunchKernelGGL(k_md_bconv_col<LN>, dim3(col_tiles<LN>(), rows_q), dim3(col_threads<LN>()), 0, s, A); }
+    { LaunchTimer tm(p, KID_MODDOWN_FWD_BLK, s); hipLaunchKernelGGL(k_md_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_q), dim3(blk_threads<LN>()), 0, s, A); }
   });
   return hipGetLastError();
 }
@@ -612,6 +613,7 @@ hipError_t launch_chacha_expand(const pc_params* p, const uint32_t seed[8], uint
   const uint32_t rinv = p->h_rinv[prime_index];
   const uint32_t r2 = p->h_r2[prime_index];
   const dim3 grid((p->N / 8 + 255) / 256);
+  LaunchTimer tm(p, KID_CHACHA_EXPAND, s);
   if (p->chacha_rounds == 20)
     hipLaunchKernelGGL(k_chacha_expand<20>, grid, dim3(256), 0, s, key, d, j, r, rinv, r2, dst, (int)p->N);
   else
