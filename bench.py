@@ -60,17 +60,17 @@ def alg_bytes_per_launch(kernel, w, batch, beta, alpha):
     digits = [min(alpha, l - d * alpha) for d in range(beta)]
     targets = sum(l + K - a for a in digits)
     table = {
-        # ModUp: c1 in, y out; y in place; y in, targets out; targets in, ext out
+        # ModUp: c1 in, y' out; y' in place (scaled y); y in, targets out; targets in, ext out
         "modup_inv_blk": batch * (l + l),
         "modup_inv_col": batch * (l + l),
-        "modup_bconv_col": batch * (l + targets),
+        "modup_bconv": batch * (l + targets),
         "modup_fwd_blk": batch * (targets + targets),
         # IP: ext (targets) + own c1 limbs read, b read once per batch, acc written
         "inner_product": batch * (targets + l) + beta * (l + K) + batch * 2 * (l + K),
         # ModDown on 2 polys per item
         "moddown_inv_blk": batch * 2 * (K + K),
         "moddown_inv_col": batch * 2 * (K + K),
-        "moddown_bconv_col": batch * 2 * (K + l),
+        "moddown_bconv": batch * 2 * (K + l),
         "moddown_fwd_blk": batch * 2 * (l + l + l) + batch * l,  # tmp2 + acc in, out; c0 in
     }
     return table[kernel] * limb

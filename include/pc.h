@@ -78,8 +78,8 @@ enum {
 typedef struct {
   uint32_t log2n;         /* ring degree N = 2^log2n; 12, 16 or 17 */
   uint32_t L;             /* q primes at the top level, >= 1 */
-  uint32_t dnum;          /* digits at the top level, 1..6, <= L */
-  uint32_t K;             /* special primes, >= 1 */
+  uint32_t dnum;          /* digits at the top level, 1..6, <= L, with ceil(L / dnum) <= 8 */
+  uint32_t K;             /* special primes, 1..8 */
   uint32_t max_batch;     /* most ciphertexts per key-switch call (0 means 1) */
   uint32_t max_hoist;     /* most keys per hoisted call (0 means 1), <= 32 */
   uint32_t chacha_rounds; /* 12 (0 means 12); 20 is accepted for testing against ChaCha20 */

@@ -296,9 +296,9 @@ KsWorkspace ks_workspace_carve(const pc_params* p, void* base, uint32_t level, u
 }
 
 const char* const kKernelNames[KID_COUNT] = {
-    "ntt_fwd_col",  "ntt_fwd_blk",     "ntt_inv_blk",   "ntt_inv_col",     "modup_inv_blk",
-    "modup_inv_col", "modup_bconv_col", "modup_fwd_blk", "inner_product",   "moddown_inv_blk",
-    "moddown_inv_col", "moddown_bconv_col", "moddown_fwd_blk", "chacha_expand"};
+    "ntt_fwd_col",     "ntt_fwd_blk",     "ntt_inv_blk",     "ntt_inv_col",   "modup_inv_blk",
+    "modup_inv_col",   "modup_bconv",     "modup_fwd_blk",   "inner_product", "moddown_inv_blk",
+    "moddown_inv_col", "moddown_bconv",   "moddown_fwd_blk", "chacha_expand"};
 
 static hipEvent_t prof_event(const pc_params* p) {
   if (p->prof_used == p->prof_pool.size()) {
@@ -347,6 +347,8 @@ int pc_params_create(const pc_params_desc* desc, int device, pc_params** out) {
   if (n != 12 && n != 16 && n != 17) return PC_EUNSUPPORTED;
   if (desc->L < 1 || desc->K < 1 || desc->dnum < 1 || desc->dnum > desc->L) return PC_EINVAL;
   if (desc->dnum > (uint32_t)kMaxDigits) return PC_EUNSUPPORTED;
+  if (desc->K > (uint32_t)kMaxSpecial) return PC_EUNSUPPORTED;
+  if ((desc->L + desc->dnum - 1) / desc->dnum > (uint32_t)kMaxAlpha) return PC_EUNSUPPORTED;
   if (desc->L + desc->K > (uint32_t)kMaxLimbsPerLaunch - 1) return PC_EUNSUPPORTED;
   const uint32_t rounds = desc->chacha_rounds ? desc->chacha_rounds : 12;
   if (rounds != 12 && rounds != 20) return PC_EUNSUPPORTED;

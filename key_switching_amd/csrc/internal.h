@@ -14,6 +14,8 @@ namespace pc {
 constexpr int kMaxLimbsPerLaunch = 256;  // prime indices travel in kernel arguments
 constexpr int kMaxKeysPerLaunch = 32;    // keys (seeds, pointers, Galois elements) per inner-product launch
 constexpr int kMaxDigits = 6;            // digits supported by the inner-product kernel
+constexpr int kMaxSpecial = 8;           // special primes (ModDown)
+constexpr int kMaxAlpha = 8;             // primes per digit (ModUp)
 
 // Device pointers to the per-prime tables (prime index = position in the chain:
 // q_0..q_{L-1} then p_0..p_{K-1}).
@@ -103,12 +105,12 @@ enum KernelId {
   KID_NTT_INV_COL,
   KID_MODUP_INV_BLK,
   KID_MODUP_INV_COL,
-  KID_MODUP_BCONV_COL,
+  KID_MODUP_BCONV,
   KID_MODUP_FWD_BLK,
   KID_INNER_PRODUCT,
   KID_MODDOWN_INV_BLK,
   KID_MODDOWN_INV_COL,
-  KID_MODDOWN_BCONV_COL,
+  KID_MODDOWN_BCONV,
   KID_MODDOWN_FWD_BLK,
   KID_CHACHA_EXPAND,
   KID_COUNT

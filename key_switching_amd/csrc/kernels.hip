@@ -11,6 +11,8 @@
 //             k_md_fwd_blk                        NTT pass 2 fused with (acc - z) P^-1 (+ phi(c0))
 // Every limb of every launch is one grid row (blockIdx.y); blockIdx.x walks the
 // column/block tiles of that limb.
+#include <algorithm>
+
 #include "internal.h"
 #include "ntt_pass.h"
 
@@ -32,7 +34,7 @@ struct Cfg<16> {
 };
 template <>
 struct Cfg<17> {
-  static constexpr int LRC = 9, LEC = 3, LRB = 8, LEB = 4, CC = 16, CB = 16;
+  static constexpr int LRC = 8, LEC = 4, LRB = 9, LEB = 3, CC = 16, CB = 16;
 };
 
 template <int LOGN>
@@ -196,31 +198,103 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_inv_col(ModUpArgs
   inv_col_pass<C::LRC, C::LEC, C::LRB, C::CC>(L, blockIdx.x * C::CC);
 }
 
-// grid row z = (b * beta + d) * (l+K) + j; rows with j in D_d have nothing to do.
+// Grouped fast base conversion fused with the forward column pass: one
+// workgroup converts G targets at once, streaming each source column tile once
+// (two sources per REDC), then runs the G column passes. Source tiles are
+// therefore read ceil(targets / G) times instead of once per target.
+template <int G, int E>
+struct TargetGroup {
+  int n;          // valid targets in this group (uniform)
+  int j[G];       // target limb index
+  uint32_t r[G], rinv[G];
+  size_t pidx[G];  // prime index of the target
+  uint32_t z[G][E];
+};
+
+template <int G, int E, class SrcFn, class ConstFn>
+__device__ __forceinline__ void grouped_bconv(TargetGroup<G, E>& tg, int cnt, SrcFn src, ConstFn cst) {
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int m = 0; m < E; ++m) tg.z[g][m] = 0;
+  int k = 0;
+  for (; k + 1 < cnt; k += 2) {
+    uint32_t v0[E], v1[E];
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      v0[m] = src(k, m);
+      v1[m] = src(k + 1, m);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (g < tg.n) {
+        const uint32_t c0 = cst(k, g), c1 = cst(k + 1, g);
+#pragma unroll
+        for (int m = 0; m < E; ++m)
+          tg.z[g][m] = add_mod(tg.z[g][m], redc(mul_wide(v0[m], c0) + mul_wide(v1[m], c1), tg.r[g], tg.rinv[g]),
+                               tg.r[g]);
+      }
+    }
+  }
+  if (k < cnt) {
+    uint32_t v0[E];
+#pragma unroll
+    for (int m = 0; m < E; ++m) v0[m] = src(k, m);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (g < tg.n) {
+        const uint32_t c0 = cst(k, g);
+#pragma unroll
+        for (int m = 0; m < E; ++m)
+          tg.z[g][m] = add_mod(tg.z[g][m], redc(mul_wide(v0[m], c0), tg.r[g], tg.rinv[g]), tg.r[g]);
+      }
+    }
+  }
+}
+
+constexpr int kBconvGroup = 4;
+
+// ModUp conversion: row (b, d), column tile blockIdx.x, target group blockIdx.z.
 template <int LOGN>
-__global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_bconv_col(ModUpArgs A) {
+__global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_bconv(ModUpArgs A) {
   using C = Cfg<LOGN>;
+  constexpr int E = 1 << C::LEC, G = kBconvGroup;
+  __shared__ uint32_t lds[C::CC * LdsTile<C::LRC>::STRIDE];
   const int lk = A.level + A.K;
-  const size_t z = blockIdx.y;
-  const int j = (int)(z % lk);
-  const size_t bd = z / lk;
-  const int d = (int)(bd % A.beta);
-  const size_t b = bd / A.beta;
-  const int i0 = d * A.alpha;
-  const int i1 = min(i0 + A.alpha, A.level);
-  if (j >= i0 && j < i1) return;
-  const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
-  BconvLimb L{A.T.r[pj],
-              A.T.rinv[pj],
-              A.T.tw_fwd + pj * A.N,
-              A.T.twp_fwd + pj * A.N,
-              A.y + (b * A.level + i0) * A.N,
-              (size_t)A.N,
-              A.LT.mu_bconv + A.bconv_off + (size_t)i0 * lk + j,
-              lk,
-              i1 - i0,
-              A.tmp + z * A.N};
-  fwd_col_pass<C::LRC, C::LEC, C::LRB, C::CC>(L, blockIdx.x * C::CC);
+  const int d = (int)(blockIdx.y % A.beta);
+  const size_t b = blockIdx.y / A.beta;
+  const int i0 = d * A.alpha, cnt = min(A.alpha, A.level - i0);
+  const int T = lk - cnt;
+  const int tt0 = blockIdx.z * G;
+  if (tt0 >= T) return;
+  const int col0 = blockIdx.x * C::CC;
+  TargetGroup<G, E> tg;
+  tg.n = min(G, T - tt0);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int tt = tt0 + min(g, tg.n - 1);
+    const int j = tt < i0 ? tt : tt + cnt;
+    tg.j[g] = j;
+    tg.pidx[g] = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
+    tg.r[g] = A.T.r[tg.pidx[g]];
+    tg.rinv[g] = A.T.rinv[tg.pidx[g]];
+  }
+  const uint32_t* ybase = A.y + (b * A.level + i0) * A.N;
+  const uint32_t* cbase = A.LT.mu_bconv + A.bconv_off + (size_t)i0 * lk;
+  grouped_bconv<G, E>(
+      tg, cnt,
+      [&](int k, int m) { return ybase[(size_t)k * A.N + col_pos_fwd_in<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)]; },
+      [&](int k, int g) { return cbase[(size_t)k * lk + tg.j[g]]; });
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (g < tg.n) {
+      fwd_col_compute<C::LRC, C::LEC, C::CC>(tg.z[g], lds, tg.r[g], A.T.tw_fwd + tg.pidx[g] * A.N,
+                                             A.T.twp_fwd + tg.pidx[g] * A.N);
+      uint32_t* dst = A.tmp + ((b * A.beta + d) * lk + tg.j[g]) * A.N;
+#pragma unroll
+      for (int m = 0; m < E; ++m) dst[col_pos_fwd_out<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)] = tg.z[g][m];
+    }
+  }
 }
 
 template <int LOGN>
@@ -372,21 +446,43 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_inv_col(ModDownArgs 
   inv_col_pass<C::LRC, C::LEC, C::LRB, C::CC>(L, blockIdx.x * C::CC);
 }
 
+// ModDown conversion P -> q_i: row ip = (item, u), column tile blockIdx.x,
+// group of G target limbs q_i blockIdx.z.
 template <int LOGN>
-__global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv_col(ModDownArgs A) {
+__global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv(ModDownArgs A) {
   using C = Cfg<LOGN>;
-  const size_t z = blockIdx.y, ip = z / A.level, i = z % A.level;
-  BconvLimb L{A.T.r[i],
-              A.T.rinv[i],
-              A.T.tw_fwd + i * A.N,
-              A.T.twp_fwd + i * A.N,
-              A.y2 + ip * A.K * A.N,
-              (size_t)A.N,
-              A.LT.md_bconv + (size_t)A.variant * A.K * A.L + i,
-              A.L,
-              A.K,
-              A.tmp2 + z * A.N};
-  fwd_col_pass<C::LRC, C::LEC, C::LRB, C::CC>(L, blockIdx.x * C::CC);
+  constexpr int E = 1 << C::LEC, G = kBconvGroup;
+  __shared__ uint32_t lds[C::CC * LdsTile<C::LRC>::STRIDE];
+  const size_t ip = blockIdx.y;
+  const int tt0 = blockIdx.z * G;
+  if (tt0 >= A.level) return;
+  const int col0 = blockIdx.x * C::CC;
+  TargetGroup<G, E> tg;
+  tg.n = min(G, A.level - tt0);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int i = tt0 + min(g, tg.n - 1);
+    tg.j[g] = i;
+    tg.pidx[g] = (size_t)i;
+    tg.r[g] = A.T.r[i];
+    tg.rinv[g] = A.T.rinv[i];
+  }
+  const uint32_t* ybase = A.y2 + ip * A.K * A.N;
+  const uint32_t* cbase = A.LT.md_bconv + (size_t)A.variant * A.K * A.L;
+  grouped_bconv<G, E>(
+      tg, A.K,
+      [&](int k, int m) { return ybase[(size_t)k * A.N + col_pos_fwd_in<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)]; },
+      [&](int k, int g) { return cbase[(size_t)k * A.L + tg.j[g]]; });
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (g < tg.n) {
+      fwd_col_compute<C::LRC, C::LEC, C::CC>(tg.z[g], lds, tg.r[g], A.T.tw_fwd + tg.pidx[g] * A.N,
+                                             A.T.twp_fwd + tg.pidx[g] * A.N);
+      uint32_t* dst = A.tmp2 + (ip * A.level + tg.j[g]) * A.N;
+#pragma unroll
+      for (int m = 0; m < E; ++m) dst[col_pos_fwd_out<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)] = tg.z[g][m];
+    }
+  }
 }
 
 template <int LOGN>
@@ -437,25 +533,25 @@ __global__ void __launch_bounds__(256) k_chacha_expand(ChaChaKey key, uint32_t d
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-#define PC_DISPATCH_LOGN(logn, CALL) \
-  switch (logn) {                    \
-    case 12: {                       \
-      constexpr int LN = 12;         \
-      CALL;                          \
-      break;                         \
-    }                                \
-    case 16: {                       \
-      constexpr int LN = 16;         \
-      CALL;                          \
-      break;                         \
-    }                                \
-    case 17: {                       \
-      constexpr int LN = 17;         \
-      CALL;                          \
-      break;                         \
-    }                                \
-    default:                         \
-      return hipErrorInvalidValue;   \
+#define PC_DISPATCH_LOGN(logn, ...) \
+  switch (logn) {                   \
+    case 12: {                      \
+      constexpr int LN = 12;        \
+      __VA_ARGS__;                  \
+      break;                        \
+    }                               \
+    case 16: {                      \
+      constexpr int LN = 16;        \
+      __VA_ARGS__;                  \
+      break;                        \
+    }                               \
+    case 17: {                      \
+      constexpr int LN = 17;        \
+      __VA_ARGS__;                  \
+      break;                        \
+    }                               \
+    default:                        \
+      return hipErrorInvalidValue;  \
   }
 
 hipError_t launch_ntt(const pc_params* p, uint32_t* data, uint32_t* tmp, const uint32_t* prime_idx, uint32_t nlimbs,
@@ -508,10 +604,13 @@ hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stri
   A.bconv_off = p->mu_bconv_off[level];
   const uint32_t rows_in = batch * level;
   const uint32_t rows_ext = batch * (uint32_t)A.beta * (level + p->K);
+  // the last digit is the shortest, so it has the most targets
+  const int targets = (int)(level + p->K) - ((int)level - (A.beta - 1) * A.alpha);
+  const uint32_t groups = (uint32_t)((targets + kBconvGroup - 1) / kBconvGroup);
   PC_DISPATCH_LOGN(p->log2n, {
     { LaunchTimer tm(p, KID_MODUP_INV_BLK, s); hipLaunchKernelGGL(k_modup_inv_blk<LN>, dim3(blk_tiles<LN>(), rows_in), dim3(blk_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_MODUP_INV_COL, s); hipLaunchKernelGGL(k_modup_inv_col<LN>, dim3(col_tiles<LN>(), rows_in), dim3(col_threads<LN>()), 0, s, A); }
-    { LaunchTimer tm(p, KID_MODUP_BCONV_COL, s); hipLaunchKernelGGL(k_modup_bconv_col<LN>, dim3(col_tiles<LN>(), rows_ext), dim3(col_threads<LN>()), 0, s, A); }
+    { LaunchTimer tm(p, KID_MODUP_BCONV, s); hipLaunchKernelGGL(k_modup_bconv<LN>, dim3(col_tiles<LN>(), batch * (uint32_t)A.beta, groups), dim3(col_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_MODUP_FWD_BLK, s); hipLaunchKernelGGL(k_modup_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_ext), dim3(blk_threads<LN>()), 0, s, A); }
   });
   return hipGetLastError();
@@ -596,10 +695,11 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
     A.galois[k] = (galois_per_key != nullptr && k < nkeys) ? galois_per_key[k] : 1u;
   const uint32_t rows_p = items * polys * p->K;
   const uint32_t rows_q = items * polys * level;
+  const uint32_t groups = (level + kBconvGroup - 1) / kBconvGroup;
   PC_DISPATCH_LOGN(p->log2n, {
     { LaunchTimer tm(p, KID_MODDOWN_INV_BLK, s); hipLaunchKernelGGL(k_md_inv_blk<LN>, dim3(blk_tiles<LN>(), rows_p), dim3(blk_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_MODDOWN_INV_COL, s); hipLaunchKernelGGL(k_md_inv_col<LN>, dim3(col_tiles<LN>(), rows_p), dim3(col_threads<LN>()), 0, s, A); }
-    { LaunchTimer tm(p, KID_MODDOWN_BCONV_COL, s); hipLaunchKernelGGL(k_md_bconv_col<LN>, dim3(col_tiles<LN>(), rows_q), dim3(col_threads<LN>()), 0, s, A); }
+    { LaunchTimer tm(p, KID_MODDOWN_BCONV, s); hipLaunchKernelGGL(k_md_bconv<LN>, dim3(col_tiles<LN>(), items * polys, groups), dim3(col_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_MODDOWN_FWD_BLK, s); hipLaunchKernelGGL(k_md_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_q), dim3(blk_threads<LN>()), 0, s, A); }
   });
   return hipGetLastError();

@@ -81,6 +81,8 @@ def test_user_primes_accepted_and_checked():
     (dict(log2n=12, L=8, dnum=7, K=1), ksa.PC_EUNSUPPORTED),
     (dict(log2n=12, L=3, dnum=3, K=1, chacha_rounds=8), ksa.PC_EUNSUPPORTED),
     (dict(log2n=12, L=3, dnum=3, K=1, max_hoist=33), ksa.PC_EUNSUPPORTED),
+    (dict(log2n=12, L=3, dnum=3, K=9), ksa.PC_EUNSUPPORTED),
+    (dict(log2n=16, L=24, dnum=2, K=6), ksa.PC_EUNSUPPORTED),
 ])
 def test_create_rejects(kw, code):
     with pytest.raises(ksa.PcError) as e:

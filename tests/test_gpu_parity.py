@@ -63,9 +63,9 @@ def params_pair(log2n, L, dnum, K, **kw):
 # NTT
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("log2n,L,K", [(12, 3, 1), (16, 24, 6), (17, 40, 8)])
-def test_ntt_and_intt_match_oracle(log2n, L, K):
-    prm, oprm = params_pair(log2n, L, 1, K)
+@pytest.mark.parametrize("log2n,L,dnum,K", [(12, 3, 1, 1), (16, 24, 4, 6), (17, 40, 5, 8)])
+def test_ntt_and_intt_match_oracle(log2n, L, dnum, K):
+    prm, oprm = params_pair(log2n, L, dnum, K)
     N = oprm.N
     primes = oprm.primes
     idx = list(range(len(primes)))[::-1]  # a non-trivial prime order
