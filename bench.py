@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--buffers-gib", type=float, default=1.1, help="ciphertext buffer rotation size")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 256 MiB copy kernel (reference for rocprofv3 byte counters)")
     return ap.parse_args()
 
 
@@ -110,6 +112,12 @@ def main():
     evk_b = ksa.to_device(ki.uniform_key_b(w.index, 0, beta, basis, w.N), 0)
     evk_a = ksa.to_device(ki.uniform_key_b(w.index, 1, beta, basis, w.N), 0)  # stands in for a stored a half
     seed = ki.key_seed(w.index, 0)
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.bitwise_or(src, 0, out=dst)
+        del src, dst
     torch.cuda.synchronize()
 
     def step(i, batch, stored=False):
@@ -152,9 +160,12 @@ def main():
     dom_avg_s = kernels[dom]["avg_us"] * 1e-6
     dom_bytes = alg_bytes_per_launch(dom, w, K8, beta, alpha)
     achieved = dom_bytes / dom_avg_s / 1e9
+    from key_switching_amd import profiling
+    traffic = profiling.read_traffic(os.path.join(ROOT, "profiles", f"{dom}_n16_k8_traffic.md"), dom)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "alg_bytes_per_launch": dom_bytes}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else round(traffic),
+                "alg_bytes_per_launch": dom_bytes, "avg_us": round(kernels[dom]["avg_us"], 3)}
 
     result = {
         "metric": METRIC,

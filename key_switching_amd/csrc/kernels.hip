@@ -176,14 +176,16 @@ struct ModUpArgs {
   uint32_t* y;    // [batch][l][N]
   uint32_t* tmp;  // [batch][beta][l+K][N]
   uint32_t* ext;  // [batch][beta][l+K][N]
-  int N, level, K, L, alpha, beta;
+  int N, level, K, L, alpha, beta, batch, ngroups;
   size_t scale_off, bconv_off;
 };
 
 template <int LOGN>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_modup_inv_blk(ModUpArgs A) {
   using C = Cfg<LOGN>;
-  const size_t z = blockIdx.y, b = z / A.level, i = z % A.level;
+  // rows are prime-major (all batch items of limb i together) so that a prime's
+  // twiddle slice stays in the L2 of the XCD that runs the tile
+  const size_t i = blockIdx.y / A.batch, b = blockIdx.y % A.batch, z = b * A.level + i;
   PlainLimb L{A.T.r[i], A.T.tw_inv + i * A.N, A.T.twp_inv + i * A.N, A.ct + b * A.ct_stride + A.c1_off + i * A.N,
               A.y + z * A.N};
   inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
@@ -196,6 +198,26 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_inv_col(ModUpArgs
   ScaledLimb L{A.T.r[i], A.LT.mu_scale[A.scale_off + i], A.LT.mu_scalep[A.scale_off + i], A.T.tw_inv + i * A.N,
                A.T.twp_inv + i * A.N, A.y + z * A.N, A.y + z * A.N};
   inv_col_pass<C::LRC, C::LEC, C::LRB, C::CC>(L, blockIdx.x * C::CC);
+}
+
+// XCD-aware decode of a 1-D grid of units x groups. Workgroup i runs on XCD
+// i mod 8; all groups of one unit (the workgroups that read the same source
+// tiles) go to the same XCD in consecutive slots, so their shared reads hit that
+// XCD's L2. The grid has ceil(units / 8) * 8 * groups workgroups; padding ones
+// return false.
+__device__ __forceinline__ bool xcd_unit(int tiles, int rows, int groups, int& tile, int& row, int& grp) {
+  const int i = (int)blockIdx.x;
+  const int xcd = i & 7, slot = i >> 3;
+  grp = slot % groups;
+  const int unit = (slot / groups) * 8 + xcd;
+  if (unit >= tiles * rows) return false;
+  tile = unit % tiles;
+  row = unit / tiles;
+  return true;
+}
+
+static inline uint32_t xcd_grid(int tiles, int rows, int groups) {
+  return (uint32_t)(((tiles * rows + 7) / 8) * 8 * groups);
 }
 
 // Grouped fast base conversion fused with the forward column pass: one
@@ -261,13 +283,15 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_bconv(ModUpArgs A
   constexpr int E = 1 << C::LEC, G = kBconvGroup;
   __shared__ uint32_t lds[C::CC * LdsTile<C::LRC>::STRIDE];
   const int lk = A.level + A.K;
-  const int d = (int)(blockIdx.y % A.beta);
-  const size_t b = blockIdx.y / A.beta;
+  int tile, row, grp;
+  if (!xcd_unit(col_tiles<LOGN>(), A.batch * A.beta, A.ngroups, tile, row, grp)) return;
+  const int d = row % A.beta;
+  const size_t b = row / A.beta;
   const int i0 = d * A.alpha, cnt = min(A.alpha, A.level - i0);
   const int T = lk - cnt;
-  const int tt0 = blockIdx.z * G;
+  const int tt0 = grp * G;
   if (tt0 >= T) return;
-  const int col0 = blockIdx.x * C::CC;
+  const int col0 = tile * C::CC;
   TargetGroup<G, E> tg;
   tg.n = min(G, T - tt0);
 #pragma unroll
@@ -301,9 +325,10 @@ template <int LOGN>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_modup_fwd_blk(ModUpArgs A) {
   using C = Cfg<LOGN>;
   const int lk = A.level + A.K;
-  const size_t z = blockIdx.y;
-  const int j = (int)(z % lk);
-  const int d = (int)((z / lk) % A.beta);
+  const size_t nbd = (size_t)A.batch * A.beta;
+  const int j = (int)(blockIdx.y / nbd);  // prime-major rows (see k_modup_inv_blk)
+  const size_t bd = blockIdx.y % nbd, z = bd * lk + j;
+  const int d = (int)(bd % A.beta);
   const int i0 = d * A.alpha;
   if (j >= i0 && j < min(i0 + A.alpha, A.level)) return;
   const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
@@ -422,7 +447,7 @@ struct ModDownArgs {
   uint32_t* out;        // [items][polys][l][N]
   const uint32_t* c0;   // c0 of ciphertext b at c0 + b * ct_stride, or nullptr
   uint64_t ct_stride;
-  int N, level, K, L, polys, variant, batch;
+  int N, level, K, L, polys, variant, batch, rows_ip, ngroups;
   uint32_t galois[kMaxKeysPerLaunch];  // per key = item / batch
 };
 
@@ -430,7 +455,8 @@ template <int LOGN>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_inv_blk(ModDownArgs A) {
   using C = Cfg<LOGN>;
   const int lk = A.level + A.K;
-  const size_t z = blockIdx.y, ip = z / A.K, t = z % A.K, pt = A.L + t;
+  // prime-major rows (see k_modup_inv_blk)
+  const size_t t = blockIdx.y / A.rows_ip, ip = blockIdx.y % A.rows_ip, z = ip * A.K + t, pt = A.L + t;
   PlainLimb L{A.T.r[pt], A.T.tw_inv + pt * A.N, A.T.twp_inv + pt * A.N, A.acc + (ip * lk + A.level + t) * A.N,
               A.y2 + z * A.N};
   inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
@@ -453,10 +479,12 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv(ModDownArgs A)
   using C = Cfg<LOGN>;
   constexpr int E = 1 << C::LEC, G = kBconvGroup;
   __shared__ uint32_t lds[C::CC * LdsTile<C::LRC>::STRIDE];
-  const size_t ip = blockIdx.y;
-  const int tt0 = blockIdx.z * G;
+  int tile, row, grp;
+  if (!xcd_unit(col_tiles<LOGN>(), A.rows_ip, A.ngroups, tile, row, grp)) return;
+  const size_t ip = row;
+  const int tt0 = grp * G;
   if (tt0 >= A.level) return;
-  const int col0 = blockIdx.x * C::CC;
+  const int col0 = tile * C::CC;
   TargetGroup<G, E> tg;
   tg.n = min(G, A.level - tt0);
 #pragma unroll
@@ -489,7 +517,8 @@ template <int LOGN>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_fwd_blk(ModDownArgs A) {
   using C = Cfg<LOGN>;
   const int lk = A.level + A.K;
-  const size_t z = blockIdx.y, ip = z / A.level, i = z % A.level;
+  // prime-major rows (see k_modup_inv_blk)
+  const size_t i = blockIdx.y / A.rows_ip, ip = blockIdx.y % A.rows_ip, z = ip * A.level + i;
   const size_t item = ip / A.polys, u = ip % A.polys;
   const size_t pi = (size_t)A.variant * A.L + i;
   const uint32_t* c0 = nullptr;
@@ -602,15 +631,17 @@ hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stri
   A.beta = beta_at(p, level);
   A.scale_off = p->mu_scale_off[level];
   A.bconv_off = p->mu_bconv_off[level];
+  A.batch = (int)batch;
   const uint32_t rows_in = batch * level;
   const uint32_t rows_ext = batch * (uint32_t)A.beta * (level + p->K);
   // the last digit is the shortest, so it has the most targets
   const int targets = (int)(level + p->K) - ((int)level - (A.beta - 1) * A.alpha);
   const uint32_t groups = (uint32_t)((targets + kBconvGroup - 1) / kBconvGroup);
+  A.ngroups = (int)groups;
   PC_DISPATCH_LOGN(p->log2n, {
     { LaunchTimer tm(p, KID_MODUP_INV_BLK, s); hipLaunchKernelGGL(k_modup_inv_blk<LN>, dim3(blk_tiles<LN>(), rows_in), dim3(blk_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_MODUP_INV_COL, s); hipLaunchKernelGGL(k_modup_inv_col<LN>, dim3(col_tiles<LN>(), rows_in), dim3(col_threads<LN>()), 0, s, A); }
-    { LaunchTimer tm(p, KID_MODUP_BCONV, s); hipLaunchKernelGGL(k_modup_bconv<LN>, dim3(col_tiles<LN>(), batch * (uint32_t)A.beta, groups), dim3(col_threads<LN>()), 0, s, A); }
+    { LaunchTimer tm(p, KID_MODUP_BCONV, s); hipLaunchKernelGGL(k_modup_bconv<LN>, dim3(xcd_grid(col_tiles<LN>(), (int)batch * A.beta, (int)groups)), dim3(col_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_MODUP_FWD_BLK, s); hipLaunchKernelGGL(k_modup_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_ext), dim3(blk_threads<LN>()), 0, s, A); }
   });
   return hipGetLastError();
@@ -696,10 +727,12 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
   const uint32_t rows_p = items * polys * p->K;
   const uint32_t rows_q = items * polys * level;
   const uint32_t groups = (level + kBconvGroup - 1) / kBconvGroup;
+  A.rows_ip = (int)(items * polys);
+  A.ngroups = (int)groups;
   PC_DISPATCH_LOGN(p->log2n, {
     { LaunchTimer tm(p, KID_MODDOWN_INV_BLK, s); hipLaunchKernelGGL(k_md_inv_blk<LN>, dim3(blk_tiles<LN>(), rows_p), dim3(blk_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_MODDOWN_INV_COL, s); hipLaunchKernelGGL(k_md_inv_col<LN>, dim3(col_tiles<LN>(), rows_p), dim3(col_threads<LN>()), 0, s, A); }
-    { LaunchTimer tm(p, KID_MODDOWN_BCONV, s); hipLaunchKernelGGL(k_md_bconv<LN>, dim3(col_tiles<LN>(), items * polys, groups), dim3(col_threads<LN>()), 0, s, A); }
+    { LaunchTimer tm(p, KID_MODDOWN_BCONV, s); hipLaunchKernelGGL(k_md_bconv<LN>, dim3(xcd_grid(col_tiles<LN>(), (int)(items * polys), (int)groups)), dim3(col_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_MODDOWN_FWD_BLK, s); hipLaunchKernelGGL(k_md_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_q), dim3(blk_threads<LN>()), 0, s, A); }
   });
   return hipGetLastError();

@@ -185,6 +185,39 @@ __device__ __forceinline__ int col_pos_inv_in(int col0, int m) {
   return col0 + col + (elem_index<LOGRC, LOGE, true>(0, t, m) << LOGRB);
 }
 
+// Register-level block passes on block B (LOGRB-point, TPB = 2^(LOGRB-LOGE)
+// threads, t = this thread's index in the block, lds_row = the block's LDS row
+// used for the exchanges). The forward pass takes the round-0 layout and leaves
+// the last-round layout; the inverse (GS) pass likewise with its own layouts.
+// Every thread of the workgroup must call these the same number of times (they
+// contain barriers).
+template <int LOGRC, int LOGRB, int LOGE>
+__device__ __forceinline__ void fwd_blk_compute(uint32_t (&v)[1 << LOGE], uint32_t* lds_row, int t, int B,
+                                                uint32_t r, const uint32_t* __restrict__ tw,
+                                                const uint32_t* __restrict__ twp) {
+  constexpr int ROUNDS = LOGRB / LOGE;
+  auto twb = [B](int s) { return (1 << (LOGRC + s)) + (B << s); };
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    if (rd > 0) exchange<LOGRB, LOGE, false>(v, lds_row, rd - 1, t);
+    ct_round<LOGRB, LOGE>(v, rd, t, r, tw, twp, twb);
+  }
+}
+
+template <int LOGRC, int LOGRB, int LOGE>
+__device__ __forceinline__ void inv_blk_compute(uint32_t (&v)[1 << LOGE], uint32_t* lds_row, int t, int B,
+                                                uint32_t r, const uint32_t* __restrict__ tw,
+                                                const uint32_t* __restrict__ twp) {
+  constexpr int ROUNDS = LOGRB / LOGE;
+  constexpr int n = LOGRC + LOGRB;
+  auto twb = [B](int u) { return (1 << (n - u - 1)) + (B << (LOGRB - u - 1)); };
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    if (rd > 0) exchange<LOGRB, LOGE, true>(v, lds_row, rd - 1, t);
+    gs_round<LOGRB, LOGE>(v, rd, t, r, tw, twp, twb);
+  }
+}
+
 // Forward column pass: stages 0..LOGRC-1, columns [col0, col0 + C).
 template <int LOGRC, int LOGE, int LOGRB, int C, class Limb>
 __device__ __forceinline__ void fwd_col_pass(Limb& L, int col0) {
@@ -231,6 +264,36 @@ __device__ __forceinline__ void fwd_blk_pass(Limb& L, int c0) {
   // transpose through LDS so that consecutive lanes write consecutive words
 #pragma unroll
   for (int m = 0; m < E; ++m) lds[k * STRIDE + elem_index<LOGRB, LOGE, false>(ROUNDS - 1, t, m)] = v[m];
+  __syncthreads();
+  const int kk = tid % C, rest = tid / C;
+#pragma unroll
+  for (int m = 0; m < E; ++m) {
+    const int x = rest + TPB * m;
+    L.store(((int)bitrev((uint32_t)x, LOGRB) << LOGRC) + c0 + kk, lds[kk * STRIDE + x]);
+  }
+}
+
+// Forward block pass as above, with a hook applied to every element in the
+// block (pre-transpose) layout: pre(B, residue, x, v) -> v' where the element
+// sits at natural position bitrev(x) 2^LOGRC + residue; the result is then
+// transposed and passed to L.store(pos, v').
+template <int LOGRC, int LOGRB, int LOGE, int C, class Limb, class Pre>
+__device__ __forceinline__ void fwd_blk_pass_pre(Limb& L, int c0, Pre pre) {
+  constexpr int R = 1 << LOGRB, E = 1 << LOGE, ROUNDS = LOGRB / LOGE, TPB = R / E;
+  constexpr int STRIDE = LdsTile<LOGRB>::STRIDE;
+  __shared__ uint32_t lds[C * STRIDE];
+  const int tid = threadIdx.x;
+  const int t = tid % TPB, k = tid / TPB;
+  const int B = (int)bitrev((uint32_t)(c0 + k), LOGRC);
+  uint32_t v[E];
+#pragma unroll
+  for (int m = 0; m < E; ++m) v[m] = L.load((B << LOGRB) + elem_index<LOGRB, LOGE, false>(0, t, m));
+  fwd_blk_compute<LOGRC, LOGRB, LOGE>(v, lds + k * STRIDE, t, B, L.r, L.tw, L.twp);
+#pragma unroll
+  for (int m = 0; m < E; ++m) {
+    const int x = elem_index<LOGRB, LOGE, false>(ROUNDS - 1, t, m);
+    lds[k * STRIDE + x] = pre(B, c0 + k, x, v[m]);
+  }
   __syncthreads();
   const int kk = tid % C, rest = tid / C;
 #pragma unroll
