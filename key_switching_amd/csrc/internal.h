@@ -29,7 +29,25 @@ struct DevTables {
   const uint32_t* twp_fwd;
   const uint32_t* tw_inv;   // [P][N] psi^-bitrev(k)
   const uint32_t* twp_inv;
+  // block-major copies for the block passes: block B's twiddles are the run
+  // [B 2^LRB, B 2^LRB + 2^LRB - 1), stage s of the forward pass at offset
+  // 2^s - 1, stage u of the inverse pass at offset 2^(LRB-u-1) - 1
+  const uint32_t* tw_fblk;  // [P][N]
+  const uint32_t* twp_fblk;
+  const uint32_t* tw_iblk;  // [P][N]
+  const uint32_t* twp_iblk;
 };
+
+// Split of the n = log2 N NTT stages into a column pass of 2^lrc points and a
+// block pass of 2^lrb points (must match the kernels' pass shapes).
+constexpr int pass_split_lrc(uint32_t log2n) { return log2n == 12 ? 6 : log2n == 16 ? 8 : log2n == 17 ? 9 : -1; }
+inline bool pass_split(uint32_t log2n, int* lrc, int* lrb) {
+  const int c = pass_split_lrc(log2n);
+  if (c < 0) return false;
+  *lrc = c;
+  *lrb = (int)log2n - c;
+  return true;
+}
 
 // Per-level constants for ModUp and ModDown (level l = number of active q primes).
 struct DevLevelTables {
@@ -55,6 +73,7 @@ struct pc_params {
   // host copies of the tables (always built; uploaded when device >= 0)
   std::vector<uint32_t> h_rinv, h_ninv, h_ninvp, h_r2;
   std::vector<uint32_t> h_tw_fwd, h_twp_fwd, h_tw_inv, h_twp_inv;
+  std::vector<uint32_t> h_tw_fblk, h_twp_fblk, h_tw_iblk, h_twp_iblk;
   std::vector<uint32_t> h_mu_scale, h_mu_scalep, h_mu_bconv;
   std::vector<size_t> mu_scale_off, mu_bconv_off;  // by level (index l, 1..L)
   std::vector<uint32_t> h_md_scale, h_md_scalep, h_md_bconv, h_md_pinv, h_md_pinvp;

@@ -21,6 +21,7 @@ namespace pc {
 // ---------------------------------------------------------------------------
 // pass shapes per ring size: column pass 2^LRC points (E = 2^LEC per thread),
 // block pass 2^LRB points (E = 2^LEB); CC / CB columns / blocks per workgroup.
+// LRC / LRB must match pass_split(), which lays out the block-major twiddles.
 // ---------------------------------------------------------------------------
 template <int LOGN>
 struct Cfg;
@@ -30,12 +31,19 @@ struct Cfg<12> {
 };
 template <>
 struct Cfg<16> {
-  static constexpr int LRC = 8, LEC = 4, LRB = 8, LEB = 4, CC = 16, CB = 16;
+  static constexpr int LRC = 8, LEC = 4, LRB = 8, LEB = 4, CC = 16, CB = 32;
 };
 template <>
 struct Cfg<17> {
-  static constexpr int LRC = 8, LEC = 4, LRB = 9, LEB = 3, CC = 16, CB = 16;
+  static constexpr int LRC = 9, LEC = 3, LRB = 8, LEB = 4, CC = 16, CB = 32;
 };
+
+template <int LOGN>
+constexpr bool split_matches() {
+  return pass_split_lrc(LOGN) == Cfg<LOGN>::LRC && pass_split_lrc(LOGN) + Cfg<LOGN>::LRB == LOGN;
+}
+static_assert(split_matches<12>() && split_matches<16>() && split_matches<17>(),
+              "kernel pass shapes must match the host twiddle layout");
 
 template <int LOGN>
 constexpr int col_threads() {
@@ -143,7 +151,7 @@ template <int LOGN>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_ntt_fwd_blk(NttArgs A) {
   using C = Cfg<LOGN>;
   const size_t z = blockIdx.y, pi = A.pidx[z];
-  PlainLimb L{A.T.r[pi], A.T.tw_fwd + pi * A.N, A.T.twp_fwd + pi * A.N, A.tmp + z * A.N, A.data + z * A.N};
+  PlainLimb L{A.T.r[pi], A.T.tw_fblk + pi * A.N, A.T.twp_fblk + pi * A.N, A.tmp + z * A.N, A.data + z * A.N};
   fwd_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
 }
 
@@ -151,7 +159,7 @@ template <int LOGN>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_ntt_inv_blk(NttArgs A) {
   using C = Cfg<LOGN>;
   const size_t z = blockIdx.y, pi = A.pidx[z];
-  PlainLimb L{A.T.r[pi], A.T.tw_inv + pi * A.N, A.T.twp_inv + pi * A.N, A.data + z * A.N, A.tmp + z * A.N};
+  PlainLimb L{A.T.r[pi], A.T.tw_iblk + pi * A.N, A.T.twp_iblk + pi * A.N, A.data + z * A.N, A.tmp + z * A.N};
   inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
 }
 
@@ -186,7 +194,7 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_modup_inv_blk(ModUpArgs
   // rows are prime-major (all batch items of limb i together) so that a prime's
   // twiddle slice stays in the L2 of the XCD that runs the tile
   const size_t i = blockIdx.y / A.batch, b = blockIdx.y % A.batch, z = b * A.level + i;
-  PlainLimb L{A.T.r[i], A.T.tw_inv + i * A.N, A.T.twp_inv + i * A.N, A.ct + b * A.ct_stride + A.c1_off + i * A.N,
+  PlainLimb L{A.T.r[i], A.T.tw_iblk + i * A.N, A.T.twp_iblk + i * A.N, A.ct + b * A.ct_stride + A.c1_off + i * A.N,
               A.y + z * A.N};
   inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
 }
@@ -332,7 +340,7 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_modup_fwd_blk(ModUpArgs
   const int i0 = d * A.alpha;
   if (j >= i0 && j < min(i0 + A.alpha, A.level)) return;
   const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
-  PlainLimb L{A.T.r[pj], A.T.tw_fwd + pj * A.N, A.T.twp_fwd + pj * A.N, A.tmp + z * A.N, A.ext + z * A.N};
+  PlainLimb L{A.T.r[pj], A.T.tw_fblk + pj * A.N, A.T.twp_fblk + pj * A.N, A.tmp + z * A.N, A.ext + z * A.N};
   fwd_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
 }
 
@@ -361,7 +369,8 @@ struct IPArgs {
 
 constexpr int kIpThreads = 256;
 
-template <int BETA, int ROUNDS, bool STORED>
+// BT: the batch size when it is known at compile time (1 or 8), else 0.
+template <int BETA, int ROUNDS, bool STORED, int BT>
 __global__ void __launch_bounds__(kIpThreads) k_inner_product(IPArgs A) {
   const int j = blockIdx.y, key = blockIdx.z;
   const int lk = A.level + A.K;
@@ -399,7 +408,9 @@ __global__ void __launch_bounds__(kIpThreads) k_inner_product(IPArgs A) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) src_idx[k] = ((uint32_t)(i0 + k) * g + h) & mask;
 
-  for (int b = 0; b < A.batch; ++b) {
+  const int batch = BT ? BT : A.batch;
+#pragma unroll 1
+  for (int b = 0; b < batch; ++b) {
     uint32_t e[BETA][8];
 #pragma unroll
     for (int d = 0; d < BETA; ++d) {
@@ -457,7 +468,7 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_inv_blk(ModDownArgs 
   const int lk = A.level + A.K;
   // prime-major rows (see k_modup_inv_blk)
   const size_t t = blockIdx.y / A.rows_ip, ip = blockIdx.y % A.rows_ip, z = ip * A.K + t, pt = A.L + t;
-  PlainLimb L{A.T.r[pt], A.T.tw_inv + pt * A.N, A.T.twp_inv + pt * A.N, A.acc + (ip * lk + A.level + t) * A.N,
+  PlainLimb L{A.T.r[pt], A.T.tw_iblk + pt * A.N, A.T.twp_iblk + pt * A.N, A.acc + (ip * lk + A.level + t) * A.N,
               A.y2 + z * A.N};
   inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
 }
@@ -530,8 +541,8 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_fwd_blk(ModDownArgs 
   CombineLimb L{A.T.r[i],
                 A.LT.md_pinv[pi],
                 A.LT.md_pinvp[pi],
-                A.T.tw_fwd + i * A.N,
-                A.T.twp_fwd + i * A.N,
+                A.T.tw_fblk + i * A.N,
+                A.T.twp_fblk + i * A.N,
                 A.tmp2 + z * A.N,
                 A.acc + (ip * lk + i) * A.N,
                 c0,
@@ -647,16 +658,26 @@ hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stri
   return hipGetLastError();
 }
 
-template <int BETA>
-static void launch_ip_beta(const pc_params* p, const IPArgs& A, uint32_t nkeys, bool stored, hipStream_t s) {
+template <int BETA, int BT>
+static void launch_ip_bt(const pc_params* p, const IPArgs& A, uint32_t nkeys, bool stored, hipStream_t s) {
   const dim3 grid((p->N / 8 + kIpThreads - 1) / kIpThreads, (uint32_t)(A.level + A.K), nkeys);
   LaunchTimer tm(p, KID_INNER_PRODUCT, s);
   if (stored)
-    hipLaunchKernelGGL((k_inner_product<BETA, 12, true>), grid, dim3(kIpThreads), 0, s, A);
+    hipLaunchKernelGGL((k_inner_product<BETA, 12, true, BT>), grid, dim3(kIpThreads), 0, s, A);
   else if (p->chacha_rounds == 20)
-    hipLaunchKernelGGL((k_inner_product<BETA, 20, false>), grid, dim3(kIpThreads), 0, s, A);
+    hipLaunchKernelGGL((k_inner_product<BETA, 20, false, BT>), grid, dim3(kIpThreads), 0, s, A);
   else
-    hipLaunchKernelGGL((k_inner_product<BETA, 12, false>), grid, dim3(kIpThreads), 0, s, A);
+    hipLaunchKernelGGL((k_inner_product<BETA, 12, false, BT>), grid, dim3(kIpThreads), 0, s, A);
+}
+
+template <int BETA>
+static void launch_ip_beta(const pc_params* p, const IPArgs& A, uint32_t nkeys, bool stored, hipStream_t s) {
+  if (A.batch == 8)
+    launch_ip_bt<BETA, 8>(p, A, nkeys, stored, s);
+  else if (A.batch == 1)
+    launch_ip_bt<BETA, 1>(p, A, nkeys, stored, s);
+  else
+    launch_ip_bt<BETA, 0>(p, A, nkeys, stored, s);
 }
 
 hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_offset,

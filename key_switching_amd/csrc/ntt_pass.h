@@ -11,7 +11,9 @@
 //     independent 2^LOGRC-point problem; its twiddles are entries [1, 2^LOGRC)
 //     of the table and are shared by every column;
 //   * a block pass: the last LOGRB stages act inside contiguous blocks of 2^LOGRB
-//     elements; block B uses entries 2^(LOGRC+s) + B 2^s + ... of the table.
+//     elements; block B uses entries 2^(LOGRC+s) + B 2^s + ... of the table,
+//     read from a block-major copy (block B's 2^LOGRB - 1 twiddles contiguous);
+//     the Limb's tw/twp of a block pass point at that copy.
 // The in-place result is bit-reversed: element x of block B belongs at natural
 // position bitrev(x) 2^LOGRC + bitrev(B). A workgroup therefore takes the C
 // blocks B = bitrev(c0 + k), k < C, so that every output row bitrev(x) is a
@@ -196,7 +198,7 @@ __device__ __forceinline__ void fwd_blk_compute(uint32_t (&v)[1 << LOGE], uint32
                                                 uint32_t r, const uint32_t* __restrict__ tw,
                                                 const uint32_t* __restrict__ twp) {
   constexpr int ROUNDS = LOGRB / LOGE;
-  auto twb = [B](int s) { return (1 << (LOGRC + s)) + (B << s); };
+  auto twb = [B](int s) { return (B << LOGRB) + (1 << s) - 1; };  // block-major table
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRB, LOGE, false>(v, lds_row, rd - 1, t);
@@ -209,8 +211,7 @@ __device__ __forceinline__ void inv_blk_compute(uint32_t (&v)[1 << LOGE], uint32
                                                 uint32_t r, const uint32_t* __restrict__ tw,
                                                 const uint32_t* __restrict__ twp) {
   constexpr int ROUNDS = LOGRB / LOGE;
-  constexpr int n = LOGRC + LOGRB;
-  auto twb = [B](int u) { return (1 << (n - u - 1)) + (B << (LOGRB - u - 1)); };
+  auto twb = [B](int u) { return (B << LOGRB) + (1 << (LOGRB - u - 1)) - 1; };  // block-major table
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRB, LOGE, true>(v, lds_row, rd - 1, t);
@@ -255,7 +256,7 @@ __device__ __forceinline__ void fwd_blk_pass(Limb& L, int c0) {
   uint32_t v[E];
 #pragma unroll
   for (int m = 0; m < E; ++m) v[m] = L.load((B << LOGRB) + elem_index<LOGRB, LOGE, false>(0, t, m));
-  auto twb = [B](int s) { return (1 << (LOGRC + s)) + (B << s); };
+  auto twb = [B](int s) { return (B << LOGRB) + (1 << s) - 1; };  // block-major table
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRB, LOGE, false>(v, lds + k * STRIDE, rd - 1, t);
@@ -311,7 +312,6 @@ __device__ __forceinline__ void inv_blk_pass(Limb& L, int c0) {
   constexpr int R = 1 << LOGRB, E = 1 << LOGE, ROUNDS = LOGRB / LOGE, TPB = R / E;
   static_assert(LOGRB % LOGE == 0, "rounds must tile the pass");
   constexpr int STRIDE = LdsTile<LOGRB>::STRIDE;
-  constexpr int n = LOGRC + LOGRB;
   __shared__ uint32_t lds[C * STRIDE];
   const int tid = threadIdx.x;
   {
@@ -329,7 +329,7 @@ __device__ __forceinline__ void inv_blk_pass(Limb& L, int c0) {
 #pragma unroll
   for (int m = 0; m < E; ++m) v[m] = lds[k * STRIDE + elem_index<LOGRB, LOGE, true>(0, t, m)];
   __syncthreads();
-  auto twb = [B](int u) { return (1 << (n - u - 1)) + (B << (LOGRB - u - 1)); };
+  auto twb = [B](int u) { return (B << LOGRB) + (1 << (LOGRB - u - 1)) - 1; };  // block-major table
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRB, LOGE, true>(v, lds + k * STRIDE, rd - 1, t);

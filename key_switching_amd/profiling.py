@@ -17,8 +17,8 @@ The traffic summary also records a hash of the device sources; bench.py
 reports the traffic figure only while the sources still hash the same.
 
 Usage:
-  python -m key_switching_amd.profiling stats --trace T.csv --stats S.csv --kernel NAME --grid G --cmd "..."
-  python -m key_switching_amd.profiling traffic --fetch F.csv --write W.csv --kernel NAME --grid G --cmd "..."
+  python -m key_switching_amd.profiling stats --trace T.csv --stats S.csv --kernel NAME --family F --grid G --cmd "..."
+  python -m key_switching_amd.profiling traffic --fetch F.csv --write W.csv --kernel NAME --family F --grid G --cmd "..."
 """
 
 from __future__ import annotations
@@ -49,22 +49,21 @@ def _short(name: str) -> str:
 
 
 def _grid(row: dict) -> int:
-    for k in ("Grid_Size", "Grid_Size_X", "grid_size"):
-        if k in row and row[k] != "":
-            return int(row[k])
-    x = int(row.get("Grid_Size_X", 1)) * int(row.get("Grid_Size_Y", 1)) * int(row.get("Grid_Size_Z", 1))
-    return x
+    """Total work-items of a dispatch (counter CSVs give Grid_Size, traces X, Y and Z)."""
+    if row.get("Grid_Size", "") != "":
+        return int(row["Grid_Size"])
+    return int(row.get("Grid_Size_X", 1)) * int(row.get("Grid_Size_Y", 1)) * int(row.get("Grid_Size_Z", 1))
 
 
 def cmd_stats(a) -> str:
     rows = list(csv.DictReader(open(a.trace)))
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
-            if a.kernel in _short(r["Kernel_Name"]) and _grid(r) == a.grid]
+            if a.kernel in r["Kernel_Name"] and _grid(r) == a.grid]
     out = [f"# rocprofv3 kernel statistics: {a.title}", "",
            "Commands:", "", "```", a.cmd, "```", "",
            f"Device sources hash: {device_source_hash()}", ""]
     if durs:
-        out += [f"Kernel `{a.kernel}`, dispatches with grid size {a.grid}: {len(durs)} launches, "
+        out += [f"Kernel family `{a.family}` (dispatches named `{a.kernel}`, grid size {a.grid}): {len(durs)} launches, "
                 f"average {statistics.mean(durs):.2f} us, median {statistics.median(durs):.2f} us, "
                 f"min {min(durs):.2f} us, max {max(durs):.2f} us", ""]
     out += ["kernel_stats.csv (all dispatches of the run, every batch size):", "", "```"]
@@ -82,7 +81,7 @@ def _counter_per_dispatch(path: str, counter: str):
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
             continue
-        key = (r["Dispatch_Id"], _short(r["Kernel_Name"]), _grid(r))
+        key = (r["Dispatch_Id"], r["Kernel_Name"], _grid(r))
         per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
     return per
 
@@ -109,7 +108,8 @@ def cmd_traffic(a) -> str:
     out = [f"# HBM traffic per launch: {a.title}", "",
            "Commands:", "", "```", a.cmd, "```", "",
            f"device_sources_hash: {device_source_hash()}",
-           f"kernel: {a.kernel}",
+           f"kernel: {a.family}",
+           f"dispatch_filter: {a.kernel}",
            f"grid_size: {a.grid}",
            f"copy calibration: plain copy of {COPY_BYTES} bytes read FETCH_SIZE {cf_big:.0f} KiB, "
            f"WRITE_SIZE {cw_big:.0f} KiB -> scale read {rf:.4f}, write {rw:.4f}",
@@ -144,7 +144,8 @@ def main(argv=None):
     s = sub.add_parser("stats")
     s.add_argument("--trace", required=True)
     s.add_argument("--stats", required=True)
-    s.add_argument("--kernel", required=True)
+    s.add_argument("--kernel", required=True, help="substring of the dispatch name")
+    s.add_argument("--family", required=True, help="kernel family name used by bench.py")
     s.add_argument("--grid", type=int, required=True)
     s.add_argument("--top", type=int, default=16)
     s.add_argument("--title", default="")
@@ -152,7 +153,8 @@ def main(argv=None):
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
-    t.add_argument("--kernel", required=True)
+    t.add_argument("--kernel", required=True, help="substring of the dispatch name")
+    t.add_argument("--family", required=True, help="kernel family name used by bench.py")
     t.add_argument("--grid", type=int, required=True)
     t.add_argument("--title", default="")
     t.add_argument("--cmd", default="")
