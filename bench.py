@@ -156,6 +156,10 @@ def main():
     kstats = ksa.profile_end(prm)
     kernels = {k: {"launches": n, "avg_us": 1000.0 * t / n, "share": t / (ms8p * args.steps)}
                for k, (n, t) in sorted(kstats.items(), key=lambda kv: -kv[1][1])}
+    ksa.profile_begin(prm)
+    timed(K8, stored=True)
+    kstats_stored = ksa.profile_end(prm)
+    kernels_stored = {k: round(1000.0 * t / n, 3) for k, (n, t) in sorted(kstats_stored.items(), key=lambda kv: -kv[1][1])}
     dom = next(iter(kernels))
     dom_avg_s = kernels[dom]["avg_us"] * 1e-6
     dom_bytes = alg_bytes_per_launch(dom, w, K8, beta, alpha)
@@ -192,6 +196,7 @@ def main():
         },
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
+        "kernels_k8_stored_avg_us": kernels_stored,
         "roofline": roofline,
         "wall_s_k8": round(wall8, 3),
     }

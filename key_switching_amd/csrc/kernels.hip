@@ -12,6 +12,8 @@
 // Every limb of every launch is one grid row (blockIdx.y); blockIdx.x walks the
 // column/block tiles of that limb.
 #include <algorithm>
+#include <map>
+#include <mutex>
 
 #include "internal.h"
 #include "ntt_pass.h"
@@ -83,31 +85,6 @@ struct ScaledLimb {
   uint32_t* dst;
   __device__ __forceinline__ uint32_t load(int pos) const { return src[pos]; }
   __device__ __forceinline__ void store(int pos, uint32_t v) const { dst[pos] = mul_shoup(v, s, sp, r); }
-};
-
-// Fast base conversion: value at pos = sum_i y_i[pos] c_i mod r, with c_i
-// carrying a factor 2^32 that one REDC per pair of products removes.
-struct BconvLimb {
-  uint32_t r, rinv;
-  const uint32_t* __restrict__ tw;
-  const uint32_t* __restrict__ twp;
-  const uint32_t* __restrict__ src;  // first source limb; source k at src + k*src_stride
-  size_t src_stride;
-  const uint32_t* __restrict__ c;  // constant of source k at c[k * c_stride]
-  int c_stride, count;
-  uint32_t* __restrict__ dst;
-  __device__ __forceinline__ uint32_t load(int pos) const {
-    uint32_t acc = 0;
-    int k = 0;
-    for (; k + 1 < count; k += 2) {
-      const uint64_t x = mul_wide(src[k * src_stride + pos], c[k * c_stride]) +
-                         mul_wide(src[(k + 1) * src_stride + pos], c[(k + 1) * c_stride]);
-      acc = add_mod(acc, redc(x, r, rinv), r);
-    }
-    if (k < count) acc = add_mod(acc, redc(mul_wide(src[k * src_stride + pos], c[k * c_stride]), r, rinv), r);
-    return acc;
-  }
-  __device__ __forceinline__ void store(int pos, uint32_t v) const { dst[pos] = v; }
 };
 
 // ModDown combine: out = (acc - v) P^-1 (+ c0 at the automorphism's source index).
@@ -241,51 +218,76 @@ struct TargetGroup {
   uint32_t z[G][E];
 };
 
-template <int G, int E, class SrcFn, class ConstFn>
+// r 2^32 folded out of a 64-bit sum whose high word is below 2r.
+__device__ __forceinline__ uint64_t fold_hi(uint64_t x, uint32_t r) {
+  uint32_t hi = (uint32_t)(x >> 32);
+  hi = min(hi, hi - r);
+  return ((uint64_t)hi << 32) | (uint32_t)x;
+}
+
+// sum_k v[k] c[k] 2^-32 mod r over CNT products with v[k] < 2^31 and
+// c[k] < r, with one REDC: four products sum below 2r 2^32, and after each
+// fold (high word below r) two more do, so the sum is folded after the fourth
+// product, after every further pair and once more after an odd tail.
+template <int CNT>
+__device__ __forceinline__ uint32_t dot_redc(const uint32_t (&v)[CNT], const uint32_t (&c)[CNT], uint32_t r,
+                                             uint32_t rinv) {
+  uint64_t acc = 0;
+#pragma unroll
+  for (int k = 0; k < CNT; ++k) {
+    acc += mul_wide(v[k], c[k]);
+    if (k == 3 || (k > 3 && (k & 1))) acc = fold_hi(acc, r);
+  }
+  constexpr bool folded_last = CNT == 4 || (CNT > 4 && !(CNT & 1));
+  if constexpr (CNT > 2 && !folded_last) acc = fold_hi(acc, r);
+  return redc(acc, r, rinv);
+}
+
+// Grouped conversion, a few positions at a time: the source values of MC
+// positions are loaded once and dotted with each target's constants, while
+// the loads of the next MC positions are in flight (compiler memory barriers
+// keep it from hoisting every load and spending a register on each).
+// CNT is the source count the kernel is built for; a row with cnt < CNT
+// sources (the last, shorter digit) repeats its last source with constant 0.
+template <int G, int E, int CNT, class SrcFn, class ConstFn>
 __device__ __forceinline__ void grouped_bconv(TargetGroup<G, E>& tg, int cnt, SrcFn src, ConstFn cst) {
+  constexpr int MC = 2, CHUNKS = E / MC;
+  static_assert(E % MC == 0, "positions must tile into chunks");
+  uint32_t c[G][CNT];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int m = 0; m < E; ++m) tg.z[g][m] = 0;
-  int k = 0;
-  for (; k + 1 < cnt; k += 2) {
-    uint32_t v0[E], v1[E];
-#pragma unroll
-    for (int m = 0; m < E; ++m) {
-      v0[m] = src(k, m);
-      v1[m] = src(k + 1, m);
+    for (int k = 0; k < CNT; ++k) {
+      const uint32_t x = cst(min(k, cnt - 1), g);
+      c[g][k] = k < cnt ? x : 0u;
     }
+  uint32_t v[2][MC][CNT];
+  auto load = [&](int chunk, uint32_t (&buf)[MC][CNT]) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (g < tg.n) {
-        const uint32_t c0 = cst(k, g), c1 = cst(k + 1, g);
+    for (int i = 0; i < MC; ++i)
 #pragma unroll
-        for (int m = 0; m < E; ++m)
-          tg.z[g][m] = add_mod(tg.z[g][m], redc(mul_wide(v0[m], c0) + mul_wide(v1[m], c1), tg.r[g], tg.rinv[g]),
-                               tg.r[g]);
+      for (int k = 0; k < CNT; ++k) buf[i][k] = src(min(k, cnt - 1), chunk * MC + i);
+  };
+  load(0, v[0]);
+#pragma unroll
+  for (int ch = 0; ch < CHUNKS; ++ch) {
+    if (ch + 1 < CHUNKS) load(ch + 1, v[(ch + 1) & 1]);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < MC; ++i)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        tg.z[g][ch * MC + i] = dot_redc<CNT>(v[ch & 1][i], c[g], tg.r[g], tg.rinv[g]);
+        asm volatile("" : "+v"(tg.z[g][ch * MC + i]));  // computed here, before the next loads
       }
-    }
-  }
-  if (k < cnt) {
-    uint32_t v0[E];
-#pragma unroll
-    for (int m = 0; m < E; ++m) v0[m] = src(k, m);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (g < tg.n) {
-        const uint32_t c0 = cst(k, g);
-#pragma unroll
-        for (int m = 0; m < E; ++m)
-          tg.z[g][m] = add_mod(tg.z[g][m], redc(mul_wide(v0[m], c0), tg.r[g], tg.rinv[g]), tg.r[g]);
-      }
-    }
+    asm volatile("" ::: "memory");
   }
 }
 
 constexpr int kBconvGroup = 4;
 
 // ModUp conversion: row (b, d), column tile blockIdx.x, target group blockIdx.z.
-template <int LOGN>
+template <int LOGN, int CNT>
 __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_bconv(ModUpArgs A) {
   using C = Cfg<LOGN>;
   constexpr int E = 1 << C::LEC, G = kBconvGroup;
@@ -313,7 +315,7 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_bconv(ModUpArgs A
   }
   const uint32_t* ybase = A.y + (b * A.level + i0) * A.N;
   const uint32_t* cbase = A.LT.mu_bconv + A.bconv_off + (size_t)i0 * lk;
-  grouped_bconv<G, E>(
+  grouped_bconv<G, E, CNT>(
       tg, cnt,
       [&](int k, int m) { return ybase[(size_t)k * A.N + col_pos_fwd_in<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)]; },
       [&](int k, int g) { return cbase[(size_t)k * lk + tg.j[g]]; });
@@ -346,11 +348,15 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_modup_fwd_blk(ModUpArgs
 
 // ---------------------------------------------------------------------------
 // inner product with the key: acc_u[j] = sum_d phi(ext_d[j]) * (b_d[j], a_d[j])
-// Each thread owns 8 consecutive positions (one ChaCha block per digit) of limb
-// j = blockIdx.y for key blockIdx.z, and loops over the batch so that the key
-// values (b read, a regenerated) are loaded once per batch. Products are
-// reduced with REDC in pairs; b and a are first put in Montgomery form, so the
-// accumulators carry a factor 2^-64 that ModDown's constants remove.
+// A thread owns 8 positions of limb j for one key and loops over the batch, so
+// the key values (b read, a read or regenerated) are loaded once per batch.
+// The 8 positions are two runs of 4, at p0 and p1: where a thread also expands
+// its own ChaCha block, p1 = p0 + 4 (the block's 8 consecutive positions);
+// otherwise p1 = p0 + half a tile and consecutive lanes own consecutive
+// 16-byte chunks, so every load and store instruction covers whole cache lines.
+// Products are reduced with REDC in pairs; b and a are first put in
+// Montgomery form, so the accumulators carry a factor 2^-64 that ModDown's
+// constants remove.
 // ---------------------------------------------------------------------------
 struct IPArgs {
   DevTables T;
@@ -359,7 +365,7 @@ struct IPArgs {
   uint32_t c1_off;
   const uint32_t* ext;  // [batch][beta][l+K][N]
   uint32_t* acc;        // [items][2][l+K][N], item = key * batch + b
-  int N, level, K, L, alpha, batch;
+  int N, level, K, L, alpha, batch, nkeys;
   uint32_t key_base;
   const uint32_t* evk_b[kMaxKeysPerLaunch];
   const uint32_t* evk_a[kMaxKeysPerLaunch];
@@ -367,82 +373,219 @@ struct IPArgs {
   uint32_t galois[kMaxKeysPerLaunch];
 };
 
+__device__ __forceinline__ int pos8(int p0, int p1, int k) { return k < 4 ? p0 + k : p1 + k - 4; }
+
+__device__ __forceinline__ void load8(const uint32_t* base, int p0, int p1, uint32_t (&v)[8]) {
+  const uint4 x = *reinterpret_cast<const uint4*>(base + p0);
+  const uint4 y = *reinterpret_cast<const uint4*>(base + p1);
+  v[0] = x.x;
+  v[1] = x.y;
+  v[2] = x.z;
+  v[3] = x.w;
+  v[4] = y.x;
+  v[5] = y.y;
+  v[6] = y.z;
+  v[7] = y.w;
+}
+
+__device__ __forceinline__ void store8(uint32_t* base, int p0, int p1, const uint32_t (&v)[8]) {
+  *reinterpret_cast<uint4*>(base + p0) = make_uint4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<uint4*>(base + p1) = make_uint4(v[4], v[5], v[6], v[7]);
+}
+
+// Key values of digit d, limb j at the thread's 8 positions, in Montgomery form.
+__device__ __forceinline__ void load_key8(const uint32_t* limb, int p0, int p1, uint32_t r, uint32_t rinv,
+                                          uint32_t (&m)[8]) {
+  uint32_t w[8];
+  load8(limb, p0, p1, w);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m[k] = redc(w[k], r, rinv);
+}
+
+// phi(ext_d[j]) of batch item b at the thread's 8 positions: the digit's own
+// limbs come straight from c1, the others from ModUp's output; the automorphism
+// index map is a gather unless the Galois element is 1.
+template <int BETA>
+__device__ __forceinline__ void load_digits(const IPArgs& A, int b, int j, int lk, uint32_t g, int p0, int p1,
+                                            const uint32_t (&src_idx)[8], uint32_t (&e)[BETA][8]) {
+#pragma unroll
+  for (int d = 0; d < BETA; ++d) {
+    const bool own = j < A.level && j >= d * A.alpha && j < (d + 1) * A.alpha;
+    const uint32_t* src = own ? A.ct + b * A.ct_stride + A.c1_off + (size_t)j * A.N
+                              : A.ext + (((size_t)b * BETA + d) * lk + j) * A.N;
+    if (g == 1u) {
+      load8(src, p0, p1, e[d]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) e[d][k] = src[src_idx[k]];
+    }
+  }
+}
+
+// Source index of each of the thread's 8 positions under the automorphism
+// i -> i*g + (g-1)/2 mod N.
+__device__ __forceinline__ void gather_index(int N, uint32_t g, int p0, int p1, uint32_t (&idx)[8]) {
+  const uint32_t h = (g - 1) >> 1, mask = (uint32_t)N - 1;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) idx[k] = ((uint32_t)pos8(p0, p1, k) * g + h) & mask;
+}
+
+// (sum_d e_d b_d, sum_d e_d a_d) at one position; am(d) gives a_d there.
+template <int BETA, class AFn>
+__device__ __forceinline__ void ip_sums(const uint32_t (&e)[BETA][8], const uint32_t (&bm)[BETA][8], int k, AFn am,
+                                        uint32_t r, uint32_t rinv, uint32_t& s0, uint32_t& s1) {
+  s0 = 0;
+  s1 = 0;
+#pragma unroll
+  for (int d = 0; d + 1 < BETA; d += 2) {
+    s0 = add_mod(s0, redc(mul_wide(e[d][k], bm[d][k]) + mul_wide(e[d + 1][k], bm[d + 1][k]), r, rinv), r);
+    s1 = add_mod(s1, redc(mul_wide(e[d][k], am(d)) + mul_wide(e[d + 1][k], am(d + 1)), r, rinv), r);
+  }
+  if constexpr (BETA % 2) {
+    s0 = add_mod(s0, redc(mul_wide(e[BETA - 1][k], bm[BETA - 1][k]), r, rinv), r);
+    s1 = add_mod(s1, redc(mul_wide(e[BETA - 1][k], am(BETA - 1)), r, rinv), r);
+  }
+}
+
 constexpr int kIpThreads = 256;
 
-// BT: the batch size when it is known at compile time (1 or 8), else 0.
+// One workgroup per (tile of 8*kIpThreads positions, limb blockIdx.y, key
+// blockIdx.z). STORED: the a half is read; otherwise each thread expands its
+// ChaCha block per digit. BT: the batch size when known at compile time (1 or
+// 8), else 0.
 template <int BETA, int ROUNDS, bool STORED, int BT>
 __global__ void __launch_bounds__(kIpThreads) k_inner_product(IPArgs A) {
+  constexpr int TILE = 8 * kIpThreads;
   const int j = blockIdx.y, key = blockIdx.z;
   const int lk = A.level + A.K;
-  const int i0 = (blockIdx.x * kIpThreads + threadIdx.x) * 8;
-  if (i0 >= A.N) return;
+  const int p0 = STORED ? (int)blockIdx.x * TILE + 4 * (int)threadIdx.x : ((int)blockIdx.x * kIpThreads + threadIdx.x) * 8;
+  const int p1 = STORED ? p0 + TILE / 2 : p0 + 4;
   const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
   const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj];
-  const uint32_t g = A.galois[key], h = (g - 1) >> 1, mask = (uint32_t)A.N - 1;
+  const uint32_t g = A.galois[key];
+  uint32_t src_idx[8];
+  gather_index(A.N, g, p0, p1, src_idx);
 
   uint32_t bm[BETA][8], am[BETA][8];
 #pragma unroll
   for (int d = 0; d < BETA; ++d) {
-    const uint32_t* bp = A.evk_b[key] + ((size_t)d * lk + j) * A.N + i0;
-    const uint4 b0 = *reinterpret_cast<const uint4*>(bp);
-    const uint4 b1 = *reinterpret_cast<const uint4*>(bp + 4);
-    const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) bm[d][k] = redc(bw[k], r, rinv);
+    load_key8(A.evk_b[key] + ((size_t)d * lk + j) * A.N, p0, p1, r, rinv, bm[d]);
     if constexpr (STORED) {
-      const uint32_t* ap = A.evk_a[key] + ((size_t)d * lk + j) * A.N + i0;
-      const uint4 a0 = *reinterpret_cast<const uint4*>(ap);
-      const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 4);
-      const uint32_t aw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) am[d][k] = redc(aw[k], r, rinv);
+      load_key8(A.evk_a[key] + ((size_t)d * lk + j) * A.N, p0, p1, r, rinv, am[d]);
     } else {
       uint32_t w[16];
-      chacha_block<ROUNDS>(A.seed[key], (uint32_t)(i0 >> 3), 0u, (uint32_t)d, (uint32_t)j, w);
+      chacha_block<ROUNDS>(A.seed[key], (uint32_t)(p0 >> 3), 0u, (uint32_t)d, (uint32_t)j, w);
 #pragma unroll
       for (int k = 0; k < 8; ++k) am[d][k] = word_pair_to_mont(w[2 * k], w[2 * k + 1], r, rinv);
     }
   }
 
-  uint32_t src_idx[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) src_idx[k] = ((uint32_t)(i0 + k) * g + h) & mask;
-
   const int batch = BT ? BT : A.batch;
 #pragma unroll 1
   for (int b = 0; b < batch; ++b) {
     uint32_t e[BETA][8];
-#pragma unroll
-    for (int d = 0; d < BETA; ++d) {
-      const bool own = j < A.level && j >= d * A.alpha && j < (d + 1) * A.alpha;
-      const uint32_t* src = own ? A.ct + b * A.ct_stride + A.c1_off + (size_t)j * A.N
-                                : A.ext + (((size_t)b * BETA + d) * lk + j) * A.N;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) e[d][k] = src[src_idx[k]];
-    }
+    load_digits<BETA>(A, b, j, lk, g, p0, p1, src_idx, e);
     uint32_t o0[8], o1[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uint32_t s0 = 0, s1 = 0;
-#pragma unroll
-      for (int d = 0; d + 1 < BETA; d += 2) {
-        s0 = add_mod(s0, redc(mul_wide(e[d][k], bm[d][k]) + mul_wide(e[d + 1][k], bm[d + 1][k]), r, rinv), r);
-        s1 = add_mod(s1, redc(mul_wide(e[d][k], am[d][k]) + mul_wide(e[d + 1][k], am[d + 1][k]), r, rinv), r);
-      }
-      if constexpr (BETA % 2) {
-        s0 = add_mod(s0, redc(mul_wide(e[BETA - 1][k], bm[BETA - 1][k]), r, rinv), r);
-        s1 = add_mod(s1, redc(mul_wide(e[BETA - 1][k], am[BETA - 1][k]), r, rinv), r);
-      }
-      o0[k] = s0;
-      o1[k] = s1;
-    }
+    for (int k = 0; k < 8; ++k) ip_sums<BETA>(e, bm, k, [&](int d) { return am[d][k]; }, r, rinv, o0[k], o1[k]);
     const size_t item = (size_t)(A.key_base + key) * A.batch + b;
-    uint32_t* a0p = A.acc + ((item * 2 + 0) * lk + j) * A.N + i0;
-    uint32_t* a1p = A.acc + ((item * 2 + 1) * lk + j) * A.N + i0;
-    *reinterpret_cast<uint4*>(a0p) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-    *reinterpret_cast<uint4*>(a0p + 4) = make_uint4(o0[4], o0[5], o0[6], o0[7]);
-    *reinterpret_cast<uint4*>(a1p) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
-    *reinterpret_cast<uint4*>(a1p + 4) = make_uint4(o1[4], o1[5], o1[6], o1[7]);
+    store8(A.acc + ((item * 2 + 0) * lk + j) * A.N, p0, p1, o0);
+    store8(A.acc + ((item * 2 + 1) * lk + j) * A.N, p0, p1, o1);
+  }
+}
+
+// Inner product with the a half regenerated from ChaCha, for batches of two or
+// more ciphertexts. Each workgroup splits into producer waves, which expand the
+// a half of the next unit (key, limb j, tile of 8*kIpHalf positions) into LDS,
+// and consumer waves, which stream the current unit's digits and accumulators
+// for the whole batch; the ChaCha arithmetic thus runs under the HBM traffic,
+// and the consumers' layout (two runs of 4 at p0 and p0 + 4*kIpHalf) is free
+// of the ChaCha block layout. Workgroups walk the units with a stride of the
+// grid size; both halves expand the first unit together.
+constexpr int kIpHalf = 128;  // consumer threads = producer threads per workgroup
+
+template <int BETA, int ROUNDS, int BT>
+__global__ void __launch_bounds__(2 * kIpHalf) k_ip_regen(IPArgs A) {
+  constexpr int TILE = 8 * kIpHalf;
+  __shared__ uint32_t am_lds[2][BETA][8][kIpHalf];  // [slot][digit][k][consumer thread]
+  const int lk = A.level + A.K;
+  const int tiles = A.N / TILE;
+  const int units = A.nkeys * lk * tiles;
+  const bool producer = threadIdx.x >= kIpHalf;
+  const int t = threadIdx.x % kIpHalf;
+  int u = blockIdx.x;
+  if (u >= units) return;  // uniform over the workgroup
+
+  auto decode = [&](int unit, int& key, int& j, int& tile) {
+    tile = unit % tiles;
+    j = (unit / tiles) % lk;
+    key = unit / (tiles * lk);
+  };
+  // a half of digits [d0, d1) of `unit`: this thread expands ChaCha block
+  // tile*kIpHalf + t (tile positions 8t..8t+7) and files each value under the
+  // consumer thread and slot that own its position
+  auto produce = [&](int unit, int slot, int d0, int d1) {
+    int key, j, tile;
+    decode(unit, key, j, tile);
+    const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
+    const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj];
+    const int hi = (8 * t) >= TILE / 2;
+    const int ct0 = (8 * t - hi * (TILE / 2)) >> 2;  // consumer thread of positions 8t..8t+3
+#pragma unroll
+    for (int d = 0; d < BETA; ++d) {
+      if (d < d0 || d >= d1) continue;
+      uint32_t w[16];
+      chacha_block<ROUNDS>(A.seed[key], (uint32_t)(tile * kIpHalf + t), 0u, (uint32_t)d, (uint32_t)j, w);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        am_lds[slot][d][4 * hi + (k & 3)][ct0 + (k >> 2)] = word_pair_to_mont(w[2 * k], w[2 * k + 1], r, rinv);
+    }
+  };
+  auto consume = [&](int unit, int slot) {
+    int key, j, tile;
+    decode(unit, key, j, tile);
+    const int p0 = tile * TILE + 4 * t, p1 = p0 + TILE / 2;
+    const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
+    const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj];
+    const uint32_t g = A.galois[key];
+    uint32_t src_idx[8];
+    gather_index(A.N, g, p0, p1, src_idx);
+    uint32_t bm[BETA][8];
+#pragma unroll
+    for (int d = 0; d < BETA; ++d) load_key8(A.evk_b[key] + ((size_t)d * lk + j) * A.N, p0, p1, r, rinv, bm[d]);
+    const int batch = BT ? BT : A.batch;
+#pragma unroll 1
+    for (int b = 0; b < batch; ++b) {
+      // the a values are re-read from LDS for every item (an opaque slot index
+      // keeps the compiler from hoisting 8*BETA registers out of the loop)
+      int sl = slot;
+      asm volatile("" : "+s"(sl));
+      uint32_t e[BETA][8];
+      load_digits<BETA>(A, b, j, lk, g, p0, p1, src_idx, e);
+      uint32_t o0[8], o1[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        ip_sums<BETA>(e, bm, k, [&](int d) { return am_lds[sl][d][k][t]; }, r, rinv, o0[k], o1[k]);
+      const size_t item = (size_t)(A.key_base + key) * A.batch + b;
+      store8(A.acc + ((item * 2 + 0) * lk + j) * A.N, p0, p1, o0);
+      store8(A.acc + ((item * 2 + 1) * lk + j) * A.N, p0, p1, o1);
+    }
+  };
+
+  if (producer)
+    produce(u, 0, BETA / 2, BETA);
+  else
+    produce(u, 0, 0, BETA / 2);
+  __syncthreads();
+  int slot = 0;
+#pragma unroll 1
+  for (; u < units; u += gridDim.x, slot ^= 1) {
+    if (producer) {
+      if (u + (int)gridDim.x < units) produce(u + gridDim.x, slot ^ 1, 0, BETA);
+    } else {
+      consume(u, slot);
+    }
+    __syncthreads();
   }
 }
 
@@ -485,7 +628,7 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_inv_col(ModDownArgs 
 
 // ModDown conversion P -> q_i: row ip = (item, u), column tile blockIdx.x,
 // group of G target limbs q_i blockIdx.z.
-template <int LOGN>
+template <int LOGN, int CNT>
 __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv(ModDownArgs A) {
   using C = Cfg<LOGN>;
   constexpr int E = 1 << C::LEC, G = kBconvGroup;
@@ -508,7 +651,7 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv(ModDownArgs A)
   }
   const uint32_t* ybase = A.y2 + ip * A.K * A.N;
   const uint32_t* cbase = A.LT.md_bconv + (size_t)A.variant * A.K * A.L;
-  grouped_bconv<G, E>(
+  grouped_bconv<G, E, CNT>(
       tg, A.K,
       [&](int k, int m) { return ybase[(size_t)k * A.N + col_pos_fwd_in<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)]; },
       [&](int k, int g) { return cbase[(size_t)k * A.L + tg.j[g]]; });
@@ -594,6 +737,21 @@ __global__ void __launch_bounds__(256) k_chacha_expand(ChaChaKey key, uint32_t d
       return hipErrorInvalidValue;  \
   }
 
+// CNT = x for x in 1..kMaxAlpha (= kMaxSpecial)
+#define PC_DISPATCH_CNT(x, ...)                         \
+  switch (x) {                                          \
+    case 1: { constexpr int CNT = 1; __VA_ARGS__; break; } \
+    case 2: { constexpr int CNT = 2; __VA_ARGS__; break; } \
+    case 3: { constexpr int CNT = 3; __VA_ARGS__; break; } \
+    case 4: { constexpr int CNT = 4; __VA_ARGS__; break; } \
+    case 5: { constexpr int CNT = 5; __VA_ARGS__; break; } \
+    case 6: { constexpr int CNT = 6; __VA_ARGS__; break; } \
+    case 7: { constexpr int CNT = 7; __VA_ARGS__; break; } \
+    case 8: { constexpr int CNT = 8; __VA_ARGS__; break; } \
+    default: return hipErrorInvalidValue;               \
+  }
+static_assert(kMaxAlpha == 8 && kMaxSpecial == 8, "PC_DISPATCH_CNT covers 1..8");
+
 hipError_t launch_ntt(const pc_params* p, uint32_t* data, uint32_t* tmp, const uint32_t* prime_idx, uint32_t nlimbs,
                       bool inverse, hipStream_t s) {
   for (uint32_t base = 0; base < nlimbs; base += kMaxLimbsPerLaunch) {
@@ -652,14 +810,56 @@ hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stri
   PC_DISPATCH_LOGN(p->log2n, {
     { LaunchTimer tm(p, KID_MODUP_INV_BLK, s); hipLaunchKernelGGL(k_modup_inv_blk<LN>, dim3(blk_tiles<LN>(), rows_in), dim3(blk_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_MODUP_INV_COL, s); hipLaunchKernelGGL(k_modup_inv_col<LN>, dim3(col_tiles<LN>(), rows_in), dim3(col_threads<LN>()), 0, s, A); }
-    { LaunchTimer tm(p, KID_MODUP_BCONV, s); hipLaunchKernelGGL(k_modup_bconv<LN>, dim3(xcd_grid(col_tiles<LN>(), (int)batch * A.beta, (int)groups)), dim3(col_threads<LN>()), 0, s, A); }
+    PC_DISPATCH_CNT(A.alpha, {
+      LaunchTimer tm(p, KID_MODUP_BCONV, s);
+      hipLaunchKernelGGL((k_modup_bconv<LN, CNT>), dim3(xcd_grid(col_tiles<LN>(), (int)batch * A.beta, (int)groups)), dim3(col_threads<LN>()), 0, s, A);
+    });
     { LaunchTimer tm(p, KID_MODUP_FWD_BLK, s); hipLaunchKernelGGL(k_modup_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_ext), dim3(blk_threads<LN>()), 0, s, A); }
   });
   return hipGetLastError();
 }
 
+// Workgroups of `kernel` resident on the current device at once, cached per
+// (kernel, device).
+template <class F>
+static uint32_t resident_workgroups(F kernel, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, uint32_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const auto key = std::make_pair(reinterpret_cast<const void*>(kernel), dev);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+  const uint32_t n = (uint32_t)(per_cu * cus);
+  cache[key] = n;
+  return n;
+}
+
+template <int BETA, int ROUNDS, int BT>
+static void launch_ip_regen(const pc_params* p, const IPArgs& A, hipStream_t s) {
+  auto kern = k_ip_regen<BETA, ROUNDS, BT>;
+  const uint32_t units = (uint32_t)A.nkeys * (uint32_t)(A.level + A.K) * (p->N / (8 * kIpHalf));
+  const uint32_t grid = std::min(units, resident_workgroups(kern, 2 * kIpHalf));
+  LaunchTimer tm(p, KID_INNER_PRODUCT, s);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(2 * kIpHalf), 0, s, A);
+}
+
 template <int BETA, int BT>
 static void launch_ip_bt(const pc_params* p, const IPArgs& A, uint32_t nkeys, bool stored, hipStream_t s) {
+  if constexpr (BT != 1) {
+    if (!stored && A.batch >= 2) {  // regenerated a half and a batch to overlap it with
+      if (p->chacha_rounds == 20)
+        launch_ip_regen<BETA, 20, BT>(p, A, s);
+      else
+        launch_ip_regen<BETA, 12, BT>(p, A, s);
+      return;
+    }
+  }
   const dim3 grid((p->N / 8 + kIpThreads - 1) / kIpThreads, (uint32_t)(A.level + A.K), nkeys);
   LaunchTimer tm(p, KID_INNER_PRODUCT, s);
   if (stored)
@@ -699,6 +899,7 @@ hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t
     A.L = (int)p->L;
     A.alpha = alpha_at(p, level);
     A.batch = (int)batch;
+    A.nkeys = (int)cnt;
     A.key_base = base;
     bool stored = false;
     for (uint32_t k = 0; k < cnt; ++k) {
@@ -753,7 +954,10 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
   PC_DISPATCH_LOGN(p->log2n, {
     { LaunchTimer tm(p, KID_MODDOWN_INV_BLK, s); hipLaunchKernelGGL(k_md_inv_blk<LN>, dim3(blk_tiles<LN>(), rows_p), dim3(blk_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_MODDOWN_INV_COL, s); hipLaunchKernelGGL(k_md_inv_col<LN>, dim3(col_tiles<LN>(), rows_p), dim3(col_threads<LN>()), 0, s, A); }
-    { LaunchTimer tm(p, KID_MODDOWN_BCONV, s); hipLaunchKernelGGL(k_md_bconv<LN>, dim3(xcd_grid(col_tiles<LN>(), (int)(items * polys), (int)groups)), dim3(col_threads<LN>()), 0, s, A); }
+    PC_DISPATCH_CNT(A.K, {
+      LaunchTimer tm(p, KID_MODDOWN_BCONV, s);
+      hipLaunchKernelGGL((k_md_bconv<LN, CNT>), dim3(xcd_grid(col_tiles<LN>(), (int)(items * polys), (int)groups)), dim3(col_threads<LN>()), 0, s, A);
+    });
     { LaunchTimer tm(p, KID_MODDOWN_FWD_BLK, s); hipLaunchKernelGGL(k_md_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_q), dim3(blk_threads<LN>()), 0, s, A); }
   });
   return hipGetLastError();
