@@ -111,13 +111,11 @@ int build_tables(pc_params* p) {
   p->h_ninvp.resize(P);
   p->h_r2.resize(P);
   p->h_tw_fwd.resize((size_t)P * N);
-  p->h_twp_fwd.resize((size_t)P * N);
   p->h_tw_inv.resize((size_t)P * N);
-  p->h_twp_inv.resize((size_t)P * N);
-  p->h_tw_fblk.assign((size_t)P * N, 0);
-  p->h_twp_fblk.assign((size_t)P * N, 0);
-  p->h_tw_iblk.assign((size_t)P * N, 0);
-  p->h_twp_iblk.assign((size_t)P * N, 0);
+  p->h_twm_fwd.resize((size_t)P * N);
+  p->h_twm_inv.resize((size_t)P * N);
+  p->h_twm_fblk.assign((size_t)P * N, 0);
+  p->h_twm_iblk.assign((size_t)P * N, 0);
   for (uint32_t k = 0; k < P; ++k) {
     const uint32_t r = p->primes[k];
     const uint32_t psi = smallest_psi(r, N);
@@ -135,38 +133,31 @@ int build_tables(pc_params* p) {
       pwi[e] = mulmod(pwi[e - 1], psi_inv, r);
     }
     uint32_t* tf = &p->h_tw_fwd[(size_t)k * N];
-    uint32_t* tfp = &p->h_twp_fwd[(size_t)k * N];
     uint32_t* ti = &p->h_tw_inv[(size_t)k * N];
-    uint32_t* tip = &p->h_twp_inv[(size_t)k * N];
+    uint32_t* tfm = &p->h_twm_fwd[(size_t)k * N];
+    uint32_t* tim = &p->h_twm_inv[(size_t)k * N];
+    const uint32_t mont = pow2_32(r);
     for (uint32_t i = 0; i < N; ++i) {
       const uint32_t e = bitrev_host(i, n);
       tf[i] = pw[e];
-      tfp[i] = shoup(pw[e], r);
       ti[i] = pwi[e];
-      tip[i] = shoup(pwi[e], r);
+      tfm[i] = mulmod(pw[e], mont, r);
+      tim[i] = mulmod(pwi[e], mont, r);
     }
     // block-major copies: forward stage s, group g of block B -> entry
     // 2^(lrc+s) + B 2^s + g; inverse stage u, group g -> 2^(n-u-1) + B 2^(lrb-u-1) + g
     int lrc = 0, lrb = 0;
     pass_split(p->log2n, &lrc, &lrb);
-    uint32_t* bf = &p->h_tw_fblk[(size_t)k * N];
-    uint32_t* bfp = &p->h_twp_fblk[(size_t)k * N];
-    uint32_t* bi = &p->h_tw_iblk[(size_t)k * N];
-    uint32_t* bip = &p->h_twp_iblk[(size_t)k * N];
+    uint32_t* bf = &p->h_twm_fblk[(size_t)k * N];
+    uint32_t* bi = &p->h_twm_iblk[(size_t)k * N];
     for (uint32_t B = 0; B < (1u << lrc); ++B) {
       const size_t base = (size_t)B << lrb;
       for (int st = 0; st < lrb; ++st) {
-        for (uint32_t g = 0; g < (1u << st); ++g) {
-          const size_t src = ((size_t)1 << (lrc + st)) + ((size_t)B << st) + g;
-          bf[base + (1u << st) - 1 + g] = tf[src];
-          bfp[base + (1u << st) - 1 + g] = tfp[src];
-        }
+        for (uint32_t g = 0; g < (1u << st); ++g)
+          bf[base + (1u << st) + g] = tfm[((size_t)1 << (lrc + st)) + ((size_t)B << st) + g];
         const int w = lrb - st - 1;  // inverse stage u = st has 2^(lrb-u-1) groups
-        for (uint32_t g = 0; g < (1u << w); ++g) {
-          const size_t src = ((size_t)1 << (n - st - 1)) + ((size_t)B << w) + g;
-          bi[base + (1u << w) - 1 + g] = ti[src];
-          bip[base + (1u << w) - 1 + g] = tip[src];
-        }
+        for (uint32_t g = 0; g < (1u << w); ++g)
+          bi[base + (1u << w) + g] = tim[((size_t)1 << (n - st - 1)) + ((size_t)B << w) + g];
       }
     }
   }
@@ -254,10 +245,8 @@ int upload_tables(pc_params* p) {
   std::vector<uint8_t> blob;
   const size_t o_r = append(blob, r32), o_rinv = append(blob, p->h_rinv), o_ninv = append(blob, p->h_ninv),
                o_ninvp = append(blob, p->h_ninvp), o_r2 = append(blob, p->h_r2);
-  const size_t o_tf = append(blob, p->h_tw_fwd), o_tfp = append(blob, p->h_twp_fwd), o_ti = append(blob, p->h_tw_inv),
-               o_tip = append(blob, p->h_twp_inv);
-  const size_t o_bf = append(blob, p->h_tw_fblk), o_bfp = append(blob, p->h_twp_fblk),
-               o_bi = append(blob, p->h_tw_iblk), o_bip = append(blob, p->h_twp_iblk);
+  const size_t o_tf = append(blob, p->h_twm_fwd), o_ti = append(blob, p->h_twm_inv);
+  const size_t o_bf = append(blob, p->h_twm_fblk), o_bi = append(blob, p->h_twm_iblk);
   const size_t o_ms = append(blob, p->h_mu_scale), o_msp = append(blob, p->h_mu_scalep),
                o_mb = append(blob, p->h_mu_bconv);
   const size_t o_ds = append(blob, p->h_md_scale), o_dsp = append(blob, p->h_md_scalep),
@@ -271,8 +260,8 @@ int upload_tables(pc_params* p) {
   }
   p->d_tables = d;
   auto at = [d](size_t off) { return reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(d) + off); };
-  p->tabs = DevTables{at(o_r),  at(o_rinv), at(o_ninv), at(o_ninvp), at(o_r2),  at(o_tf),  at(o_tfp),
-                      at(o_ti), at(o_tip),  at(o_bf),   at(o_bfp),   at(o_bi), at(o_bip)};
+  p->tabs = DevTables{at(o_r), at(o_rinv), at(o_ninv), at(o_ninvp), at(o_r2),
+                      at(o_tf), at(o_ti),   at(o_bf),   at(o_bi)};
   p->ltabs = DevLevelTables{at(o_ms), at(o_msp), at(o_mb), at(o_ds), at(o_dsp), at(o_db), at(o_dp), at(o_dpp)};
   return PC_OK;
 }

@@ -53,6 +53,12 @@ __device__ __forceinline__ uint32_t redc(uint64_t x, uint32_t r, uint32_t rinv_n
 
 __device__ __forceinline__ uint64_t mul_wide(uint32_t a, uint32_t b) { return (uint64_t)a * b; }
 
+// x w 2^-32 mod r for any 32-bit x and w < r, canonical: with w a twiddle in
+// Montgomery form (w0 2^32 mod r) this is x w0 mod r.
+__device__ __forceinline__ uint32_t mul_mont(uint32_t x, uint32_t w, uint32_t r, uint32_t rinv_neg) {
+  return redc(mul_wide(x, w), r, rinv_neg);
+}
+
 __device__ __forceinline__ uint32_t bitrev(uint32_t x, int bits) {
   return bits ? (__builtin_bitreverse32(x) >> (32 - bits)) : 0u;
 }

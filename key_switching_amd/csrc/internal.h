@@ -25,17 +25,15 @@ struct DevTables {
   const uint32_t* ninv;     // [P] N^-1 mod r
   const uint32_t* ninvp;    // [P] Shoup companions
   const uint32_t* r2;       // [P] 2^64 mod r (leaves Montgomery form through one REDC)
+  // twiddles in Montgomery form (w 2^32 mod r), so that one REDC of x*w gives x*w mod r
   const uint32_t* tw_fwd;   // [P][N] psi^bitrev(k)
-  const uint32_t* twp_fwd;
   const uint32_t* tw_inv;   // [P][N] psi^-bitrev(k)
-  const uint32_t* twp_inv;
   // block-major copies for the block passes: block B's twiddles are the run
-  // [B 2^LRB, B 2^LRB + 2^LRB - 1), stage s of the forward pass at offset
-  // 2^s - 1, stage u of the inverse pass at offset 2^(LRB-u-1) - 1
+  // [B 2^LRB + 1, B 2^LRB + 2^LRB), stage s of the forward pass at offset 2^s,
+  // stage u of the inverse pass at offset 2^(LRB-u-1) (each stage's run is
+  // aligned to its length)
   const uint32_t* tw_fblk;  // [P][N]
-  const uint32_t* twp_fblk;
   const uint32_t* tw_iblk;  // [P][N]
-  const uint32_t* twp_iblk;
 };
 
 // Split of the n = log2 N NTT stages into a column pass of 2^lrc points and a
@@ -72,8 +70,8 @@ struct pc_params {
   std::vector<uint32_t> psi;
   // host copies of the tables (always built; uploaded when device >= 0)
   std::vector<uint32_t> h_rinv, h_ninv, h_ninvp, h_r2;
-  std::vector<uint32_t> h_tw_fwd, h_twp_fwd, h_tw_inv, h_twp_inv;
-  std::vector<uint32_t> h_tw_fblk, h_twp_fblk, h_tw_iblk, h_twp_iblk;
+  std::vector<uint32_t> h_tw_fwd, h_tw_inv;                       // psi^+-bitrev(k), plain
+  std::vector<uint32_t> h_twm_fwd, h_twm_inv, h_twm_fblk, h_twm_iblk;  // Montgomery form, uploaded
   std::vector<uint32_t> h_mu_scale, h_mu_scalep, h_mu_bconv;
   std::vector<size_t> mu_scale_off, mu_bconv_off;  // by level (index l, 1..L)
   std::vector<uint32_t> h_md_scale, h_md_scalep, h_md_bconv, h_md_pinv, h_md_pinvp;

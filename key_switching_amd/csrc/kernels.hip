@@ -68,9 +68,8 @@ constexpr int blk_tiles() {
 // limb policies
 // ---------------------------------------------------------------------------
 struct PlainLimb {
-  uint32_t r;
+  uint32_t r, rinv;
   const uint32_t* __restrict__ tw;
-  const uint32_t* __restrict__ twp;
   const uint32_t* __restrict__ src;
   uint32_t* __restrict__ dst;
   __device__ __forceinline__ uint32_t load(int pos) const { return src[pos]; }
@@ -78,29 +77,35 @@ struct PlainLimb {
 };
 
 struct ScaledLimb {
-  uint32_t r, s, sp;
+  uint32_t r, rinv, s, sp;
   const uint32_t* __restrict__ tw;
-  const uint32_t* __restrict__ twp;
   const uint32_t* src;
   uint32_t* dst;
   __device__ __forceinline__ uint32_t load(int pos) const { return src[pos]; }
   __device__ __forceinline__ void store(int pos, uint32_t v) const { dst[pos] = mul_shoup(v, s, sp, r); }
 };
 
-// ModDown combine: out = (acc - v) P^-1 (+ c0 at the automorphism's source index).
+// ModDown combine: out = (acc - v) P^-1 (+ c0 at the automorphism's source
+// index). acc and c0 at the E output positions of this thread are fetched
+// before the transform (fwd_blk_pass_fetch).
+template <int E>
 struct CombineLimb {
-  uint32_t r, pinv, pinvp;
+  uint32_t r, rinv, pinv, pinvp;
   const uint32_t* __restrict__ tw;
-  const uint32_t* __restrict__ twp;
   const uint32_t* __restrict__ src;
   const uint32_t* __restrict__ acc;
   const uint32_t* __restrict__ c0;  // nullptr: nothing to add
   uint32_t g, h, mask;
   uint32_t* __restrict__ dst;
+  uint32_t av[E], cv[E];
   __device__ __forceinline__ uint32_t load(int pos) const { return src[pos]; }
-  __device__ __forceinline__ void store(int pos, uint32_t v) const {
-    uint32_t o = mul_shoup(sub_mod(acc[pos], v, r), pinv, pinvp, r);
-    if (c0) o = add_mod(o, c0[((uint32_t)pos * g + h) & mask], r);
+  __device__ __forceinline__ void fetch(int m, int pos) {
+    av[m] = acc[pos];
+    cv[m] = c0 ? c0[((uint32_t)pos * g + h) & mask] : 0u;
+  }
+  __device__ __forceinline__ void finish(int m, int pos, uint32_t v) const {
+    uint32_t o = mul_shoup(sub_mod(av[m], v, r), pinv, pinvp, r);
+    if (c0) o = add_mod(o, cv[m], r);
     dst[pos] = o;
   }
 };
@@ -120,7 +125,7 @@ template <int LOGN>
 __global__ void __launch_bounds__(col_threads<LOGN>()) k_ntt_fwd_col(NttArgs A) {
   using C = Cfg<LOGN>;
   const size_t z = blockIdx.y, pi = A.pidx[z];
-  PlainLimb L{A.T.r[pi], A.T.tw_fwd + pi * A.N, A.T.twp_fwd + pi * A.N, A.data + z * A.N, A.tmp + z * A.N};
+  PlainLimb L{A.T.r[pi], A.T.rinv[pi], A.T.tw_fwd + pi * A.N, A.data + z * A.N, A.tmp + z * A.N};
   fwd_col_pass<C::LRC, C::LEC, C::LRB, C::CC>(L, blockIdx.x * C::CC);
 }
 
@@ -128,7 +133,7 @@ template <int LOGN>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_ntt_fwd_blk(NttArgs A) {
   using C = Cfg<LOGN>;
   const size_t z = blockIdx.y, pi = A.pidx[z];
-  PlainLimb L{A.T.r[pi], A.T.tw_fblk + pi * A.N, A.T.twp_fblk + pi * A.N, A.tmp + z * A.N, A.data + z * A.N};
+  PlainLimb L{A.T.r[pi], A.T.rinv[pi], A.T.tw_fblk + pi * A.N, A.tmp + z * A.N, A.data + z * A.N};
   fwd_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
 }
 
@@ -136,7 +141,7 @@ template <int LOGN>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_ntt_inv_blk(NttArgs A) {
   using C = Cfg<LOGN>;
   const size_t z = blockIdx.y, pi = A.pidx[z];
-  PlainLimb L{A.T.r[pi], A.T.tw_iblk + pi * A.N, A.T.twp_iblk + pi * A.N, A.data + z * A.N, A.tmp + z * A.N};
+  PlainLimb L{A.T.r[pi], A.T.rinv[pi], A.T.tw_iblk + pi * A.N, A.data + z * A.N, A.tmp + z * A.N};
   inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
 }
 
@@ -144,7 +149,7 @@ template <int LOGN>
 __global__ void __launch_bounds__(col_threads<LOGN>()) k_ntt_inv_col(NttArgs A) {
   using C = Cfg<LOGN>;
   const size_t z = blockIdx.y, pi = A.pidx[z];
-  ScaledLimb L{A.T.r[pi], A.T.ninv[pi], A.T.ninvp[pi], A.T.tw_inv + pi * A.N, A.T.twp_inv + pi * A.N,
+  ScaledLimb L{A.T.r[pi], A.T.rinv[pi], A.T.ninv[pi], A.T.ninvp[pi], A.T.tw_inv + pi * A.N,
                A.tmp + z * A.N, A.data + z * A.N};
   inv_col_pass<C::LRC, C::LEC, C::LRB, C::CC>(L, blockIdx.x * C::CC);
 }
@@ -171,7 +176,7 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_modup_inv_blk(ModUpArgs
   // rows are prime-major (all batch items of limb i together) so that a prime's
   // twiddle slice stays in the L2 of the XCD that runs the tile
   const size_t i = blockIdx.y / A.batch, b = blockIdx.y % A.batch, z = b * A.level + i;
-  PlainLimb L{A.T.r[i], A.T.tw_iblk + i * A.N, A.T.twp_iblk + i * A.N, A.ct + b * A.ct_stride + A.c1_off + i * A.N,
+  PlainLimb L{A.T.r[i], A.T.rinv[i], A.T.tw_iblk + i * A.N, A.ct + b * A.ct_stride + A.c1_off + i * A.N,
               A.y + z * A.N};
   inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
 }
@@ -180,8 +185,8 @@ template <int LOGN>
 __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_inv_col(ModUpArgs A) {
   using C = Cfg<LOGN>;
   const size_t z = blockIdx.y, i = z % A.level;
-  ScaledLimb L{A.T.r[i], A.LT.mu_scale[A.scale_off + i], A.LT.mu_scalep[A.scale_off + i], A.T.tw_inv + i * A.N,
-               A.T.twp_inv + i * A.N, A.y + z * A.N, A.y + z * A.N};
+  ScaledLimb L{A.T.r[i],          A.T.rinv[i], A.LT.mu_scale[A.scale_off + i], A.LT.mu_scalep[A.scale_off + i],
+               A.T.tw_inv + i * A.N, A.y + z * A.N, A.y + z * A.N};
   inv_col_pass<C::LRC, C::LEC, C::LRB, C::CC>(L, blockIdx.x * C::CC);
 }
 
@@ -322,8 +327,7 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_bconv(ModUpArgs A
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (g < tg.n) {
-      fwd_col_compute<C::LRC, C::LEC, C::CC>(tg.z[g], lds, tg.r[g], A.T.tw_fwd + tg.pidx[g] * A.N,
-                                             A.T.twp_fwd + tg.pidx[g] * A.N);
+      fwd_col_compute<C::LRC, C::LEC, C::CC>(tg.z[g], lds, tg.r[g], tg.rinv[g], A.T.tw_fwd + tg.pidx[g] * A.N);
       uint32_t* dst = A.tmp + ((b * A.beta + d) * lk + tg.j[g]) * A.N;
 #pragma unroll
       for (int m = 0; m < E; ++m) dst[col_pos_fwd_out<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)] = tg.z[g][m];
@@ -342,7 +346,7 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_modup_fwd_blk(ModUpArgs
   const int i0 = d * A.alpha;
   if (j >= i0 && j < min(i0 + A.alpha, A.level)) return;
   const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
-  PlainLimb L{A.T.r[pj], A.T.tw_fblk + pj * A.N, A.T.twp_fblk + pj * A.N, A.tmp + z * A.N, A.ext + z * A.N};
+  PlainLimb L{A.T.r[pj], A.T.rinv[pj], A.T.tw_fblk + pj * A.N, A.tmp + z * A.N, A.ext + z * A.N};
   fwd_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
 }
 
@@ -611,7 +615,7 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_inv_blk(ModDownArgs 
   const int lk = A.level + A.K;
   // prime-major rows (see k_modup_inv_blk)
   const size_t t = blockIdx.y / A.rows_ip, ip = blockIdx.y % A.rows_ip, z = ip * A.K + t, pt = A.L + t;
-  PlainLimb L{A.T.r[pt], A.T.tw_iblk + pt * A.N, A.T.twp_iblk + pt * A.N, A.acc + (ip * lk + A.level + t) * A.N,
+  PlainLimb L{A.T.r[pt], A.T.rinv[pt], A.T.tw_iblk + pt * A.N, A.acc + (ip * lk + A.level + t) * A.N,
               A.y2 + z * A.N};
   inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
 }
@@ -621,7 +625,7 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_inv_col(ModDownArgs 
   using C = Cfg<LOGN>;
   const size_t z = blockIdx.y, t = z % A.K, pt = A.L + t;
   const size_t si = (size_t)A.variant * A.K + t;
-  ScaledLimb L{A.T.r[pt], A.LT.md_scale[si], A.LT.md_scalep[si], A.T.tw_inv + pt * A.N, A.T.twp_inv + pt * A.N,
+  ScaledLimb L{A.T.r[pt], A.T.rinv[pt], A.LT.md_scale[si], A.LT.md_scalep[si], A.T.tw_inv + pt * A.N,
                A.y2 + z * A.N, A.y2 + z * A.N};
   inv_col_pass<C::LRC, C::LEC, C::LRB, C::CC>(L, blockIdx.x * C::CC);
 }
@@ -658,8 +662,7 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv(ModDownArgs A)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (g < tg.n) {
-      fwd_col_compute<C::LRC, C::LEC, C::CC>(tg.z[g], lds, tg.r[g], A.T.tw_fwd + tg.pidx[g] * A.N,
-                                             A.T.twp_fwd + tg.pidx[g] * A.N);
+      fwd_col_compute<C::LRC, C::LEC, C::CC>(tg.z[g], lds, tg.r[g], tg.rinv[g], A.T.tw_fwd + tg.pidx[g] * A.N);
       uint32_t* dst = A.tmp2 + (ip * A.level + tg.j[g]) * A.N;
 #pragma unroll
       for (int m = 0; m < E; ++m) dst[col_pos_fwd_out<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)] = tg.z[g][m];
@@ -681,19 +684,21 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_fwd_blk(ModDownArgs 
     c0 = A.c0 + (item % A.batch) * A.ct_stride + i * A.N;
     g = A.galois[item / A.batch];
   }
-  CombineLimb L{A.T.r[i],
+  CombineLimb<(1 << C::LEB)> L{A.T.r[i],
+                A.T.rinv[i],
                 A.LT.md_pinv[pi],
                 A.LT.md_pinvp[pi],
                 A.T.tw_fblk + i * A.N,
-                A.T.twp_fblk + i * A.N,
                 A.tmp2 + z * A.N,
                 A.acc + (ip * lk + i) * A.N,
                 c0,
                 g,
                 (g - 1) >> 1,
                 (uint32_t)A.N - 1,
-                A.out + z * A.N};
-  fwd_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
+                A.out + z * A.N,
+                {},
+                {}};
+  fwd_blk_pass_fetch<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
 }
 
 // ---------------------------------------------------------------------------

@@ -12,8 +12,8 @@
 //     of the table and are shared by every column;
 //   * a block pass: the last LOGRB stages act inside contiguous blocks of 2^LOGRB
 //     elements; block B uses entries 2^(LOGRC+s) + B 2^s + ... of the table,
-//     read from a block-major copy (block B's 2^LOGRB - 1 twiddles contiguous);
-//     the Limb's tw/twp of a block pass point at that copy.
+//     read from a block-major copy (block B's 2^LOGRB - 1 twiddles contiguous,
+//     stage s at offset 2^s); the Limb's tw of a block pass points at that copy.
 // The in-place result is bit-reversed: element x of block B belongs at natural
 // position bitrev(x) 2^LOGRC + bitrev(B). A workgroup therefore takes the C
 // blocks B = bitrev(c0 + k), k < C, so that every output row bitrev(x) is a
@@ -53,33 +53,51 @@ struct LdsTile {
   static constexpr int STRIDE = R + 4;
 };
 
-// Forward CT round: stages s = round*LOGE + sl for sl < LOGE.
-// TwBase(s) returns the table offset of group 0 of stage s for this thread's
-// row/block (the part that does not depend on the slot m); the twiddle index is
-// TwBase(s) + (t_high << sl) + (m >> (LOGE - sl)).
+// n consecutive twiddles from p (n a power of two; p aligned to min(n, 4)
+// words, which every table layout here guarantees): one vector load per four.
+__device__ __forceinline__ void load_run(const uint32_t* __restrict__ p, int n, uint32_t* w) {
+  if (n >= 4) {
+#pragma unroll
+    for (int i = 0; i < n; i += 4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p + i);
+      w[i] = x.x;
+      w[i + 1] = x.y;
+      w[i + 2] = x.z;
+      w[i + 3] = x.w;
+    }
+  } else if (n == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    w[0] = x.x;
+    w[1] = x.y;
+  } else {
+    w[0] = p[0];
+  }
+}
+
+// Forward CT round: stages s = round*LOGE + sl for sl < LOGE. Twiddles are in
+// Montgomery form (one REDC per product). TwBase(s) returns the table offset of
+// group 0 of stage s for this thread's row/block (the part that does not depend
+// on the slot m); the 2^sl twiddles of stage sl are the run starting at
+// TwBase(s) + (t_high << sl), indexed by m >> (LOGE - sl).
 template <int LOGR, int LOGE, class TwBase>
-__device__ __forceinline__ void ct_round(uint32_t (&v)[1 << LOGE], int round, int t, uint32_t r,
-                                         const uint32_t* __restrict__ tw, const uint32_t* __restrict__ twp,
-                                         TwBase twbase) {
+__device__ __forceinline__ void ct_round(uint32_t (&v)[1 << LOGE], int round, int t, uint32_t r, uint32_t rinv,
+                                         const uint32_t* __restrict__ tw, TwBase twbase) {
   constexpr int E = 1 << LOGE;
   const int lo = pass_lo<LOGR, LOGE, false>(round);
   const int thigh = t >> lo;
 #pragma unroll
   for (int sl = 0; sl < LOGE; ++sl) {
     const int s = round * LOGE + sl;
-    const int base = twbase(s) + (thigh << sl);
-    constexpr int dummy = 0;
-    (void)dummy;
     const int half = E >> (sl + 1);
+    uint32_t w[E / 2];
+    load_run(tw + twbase(s) + (thigh << sl), 1 << sl, w);
 #pragma unroll
     for (int g = 0; g < (1 << sl); ++g) {
-      const uint32_t w = tw[base + g];
-      const uint32_t wp = twp[base + g];
 #pragma unroll
       for (int j = 0; j < half; ++j) {
         const int m0 = g * 2 * half + j;
         const uint32_t u = v[m0];
-        const uint32_t x = mul_shoup(v[m0 + half], w, wp, r);
+        const uint32_t x = mul_mont(v[m0 + half], w[g], r, rinv);
         v[m0] = add_mod(u, x, r);
         v[m0 + half] = sub_mod(u, x, r);
       }
@@ -87,13 +105,12 @@ __device__ __forceinline__ void ct_round(uint32_t (&v)[1 << LOGE], int round, in
   }
 }
 
-// Inverse GS round: stages u = round*LOGE + ul, pairs (m, m + 2^ul).
-// TwBase(u) returns the table offset for group 0; the twiddle index is
-// TwBase(u) + (t_high << (LOGE - ul - 1)) + (m >> (ul + 1)).
+// Inverse GS round: stages u = round*LOGE + ul, pairs (m, m + 2^ul). The
+// 2^(LOGE-ul-1) twiddles of stage ul are the run starting at
+// TwBase(u) + (t_high << (LOGE - ul - 1)), indexed by m >> (ul + 1).
 template <int LOGR, int LOGE, class TwBase>
-__device__ __forceinline__ void gs_round(uint32_t (&v)[1 << LOGE], int round, int t, uint32_t r,
-                                         const uint32_t* __restrict__ tw, const uint32_t* __restrict__ twp,
-                                         TwBase twbase) {
+__device__ __forceinline__ void gs_round(uint32_t (&v)[1 << LOGE], int round, int t, uint32_t r, uint32_t rinv,
+                                         const uint32_t* __restrict__ tw, TwBase twbase) {
   constexpr int E = 1 << LOGE;
   const int lo = pass_lo<LOGR, LOGE, true>(round);
   const int thigh = t >> lo;
@@ -101,18 +118,18 @@ __device__ __forceinline__ void gs_round(uint32_t (&v)[1 << LOGE], int round, in
   for (int ul = 0; ul < LOGE; ++ul) {
     const int u = round * LOGE + ul;
     const int half = 1 << ul;
-    const int base = twbase(u) + (thigh << (LOGE - ul - 1));
+    const int groups = E >> (ul + 1);
+    uint32_t w[E / 2];
+    load_run(tw + twbase(u) + (thigh << (LOGE - ul - 1)), groups, w);
 #pragma unroll
-    for (int g = 0; g < (E >> (ul + 1)); ++g) {
-      const uint32_t w = tw[base + g];
-      const uint32_t wp = twp[base + g];
+    for (int g = 0; g < groups; ++g) {
 #pragma unroll
       for (int j = 0; j < half; ++j) {
         const int m0 = g * 2 * half + j;
         const uint32_t a = v[m0];
         const uint32_t b = v[m0 + half];
         v[m0] = add_mod(a, b, r);
-        v[m0 + half] = mul_shoup(sub_mod(a, b, r), w, wp, r);
+        v[m0 + half] = mul_mont(sub_mod(a, b, r), w[g], r, rinv);
       }
     }
   }
@@ -132,7 +149,8 @@ __device__ __forceinline__ void exchange(uint32_t (&v)[1 << LOGE], uint32_t* lds
 
 // ---------------------------------------------------------------------------
 // Pass bodies. A Limb policy supplies, for the limb of this workgroup:
-//   r, tw, twp                   prime and its twiddle tables (forward or inverse)
+//   r, rinv, tw                  prime, -r^-1 mod 2^32 and its twiddle table
+//                                (forward or inverse, Montgomery form)
 //   uint32_t load(int pos)       element at limb position pos (pass input)
 //   void store(int pos, uint32_t v)  element at position pos (pass output)
 // Positions are limb offsets in [0, N).
@@ -144,28 +162,28 @@ __device__ __forceinline__ void exchange(uint32_t (&v)[1 << LOGE], uint32_t* lds
 // layout (both put slot m at x = (m << (LOGRC - LOGE)) | t), so an inverse
 // column pass can feed a forward column pass without an exchange.
 template <int LOGRC, int LOGE, int C>
-__device__ __forceinline__ void fwd_col_compute(uint32_t (&v)[1 << LOGE], uint32_t* lds, uint32_t r,
-                                                const uint32_t* __restrict__ tw, const uint32_t* __restrict__ twp) {
+__device__ __forceinline__ void fwd_col_compute(uint32_t (&v)[1 << LOGE], uint32_t* lds, uint32_t r, uint32_t rinv,
+                                                const uint32_t* __restrict__ tw) {
   constexpr int ROUNDS = LOGRC / LOGE;
   const int col = threadIdx.x % C, t = threadIdx.x / C;
   auto twb = [](int s) { return 1 << s; };
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRC, LOGE, false>(v, lds + col * LdsTile<LOGRC>::STRIDE, rd - 1, t);
-    ct_round<LOGRC, LOGE>(v, rd, t, r, tw, twp, twb);
+    ct_round<LOGRC, LOGE>(v, rd, t, r, rinv, tw, twb);
   }
 }
 
 template <int LOGRC, int LOGE, int C>
-__device__ __forceinline__ void inv_col_compute(uint32_t (&v)[1 << LOGE], uint32_t* lds, uint32_t r,
-                                                const uint32_t* __restrict__ tw, const uint32_t* __restrict__ twp) {
+__device__ __forceinline__ void inv_col_compute(uint32_t (&v)[1 << LOGE], uint32_t* lds, uint32_t r, uint32_t rinv,
+                                                const uint32_t* __restrict__ tw) {
   constexpr int ROUNDS = LOGRC / LOGE;
   const int col = threadIdx.x % C, t = threadIdx.x / C;
   auto twb = [](int u) { return 1 << (LOGRC - u - 1); };
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRC, LOGE, true>(v, lds + col * LdsTile<LOGRC>::STRIDE, rd - 1, t);
-    gs_round<LOGRC, LOGE>(v, rd, t, r, tw, twp, twb);
+    gs_round<LOGRC, LOGE>(v, rd, t, r, rinv, tw, twb);
   }
 }
 
@@ -195,27 +213,25 @@ __device__ __forceinline__ int col_pos_inv_in(int col0, int m) {
 // contain barriers).
 template <int LOGRC, int LOGRB, int LOGE>
 __device__ __forceinline__ void fwd_blk_compute(uint32_t (&v)[1 << LOGE], uint32_t* lds_row, int t, int B,
-                                                uint32_t r, const uint32_t* __restrict__ tw,
-                                                const uint32_t* __restrict__ twp) {
+                                                uint32_t r, uint32_t rinv, const uint32_t* __restrict__ tw) {
   constexpr int ROUNDS = LOGRB / LOGE;
-  auto twb = [B](int s) { return (B << LOGRB) + (1 << s) - 1; };  // block-major table
+  auto twb = [B](int s) { return (B << LOGRB) + (1 << s); };  // block-major table
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRB, LOGE, false>(v, lds_row, rd - 1, t);
-    ct_round<LOGRB, LOGE>(v, rd, t, r, tw, twp, twb);
+    ct_round<LOGRB, LOGE>(v, rd, t, r, rinv, tw, twb);
   }
 }
 
 template <int LOGRC, int LOGRB, int LOGE>
 __device__ __forceinline__ void inv_blk_compute(uint32_t (&v)[1 << LOGE], uint32_t* lds_row, int t, int B,
-                                                uint32_t r, const uint32_t* __restrict__ tw,
-                                                const uint32_t* __restrict__ twp) {
+                                                uint32_t r, uint32_t rinv, const uint32_t* __restrict__ tw) {
   constexpr int ROUNDS = LOGRB / LOGE;
-  auto twb = [B](int u) { return (B << LOGRB) + (1 << (LOGRB - u - 1)) - 1; };  // block-major table
+  auto twb = [B](int u) { return (B << LOGRB) + (1 << (LOGRB - u - 1)); };  // block-major table
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRB, LOGE, true>(v, lds_row, rd - 1, t);
-    gs_round<LOGRB, LOGE>(v, rd, t, r, tw, twp, twb);
+    gs_round<LOGRB, LOGE>(v, rd, t, r, rinv, tw, twb);
   }
 }
 
@@ -234,7 +250,7 @@ __device__ __forceinline__ void fwd_col_pass(Limb& L, int col0) {
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRC, LOGE, false>(v, lds + col * LdsTile<LOGRC>::STRIDE, rd - 1, t);
-    ct_round<LOGRC, LOGE>(v, rd, t, L.r, L.tw, L.twp, twb);
+    ct_round<LOGRC, LOGE>(v, rd, t, L.r, L.rinv, L.tw, twb);
   }
 #pragma unroll
   for (int m = 0; m < E; ++m)
@@ -256,11 +272,11 @@ __device__ __forceinline__ void fwd_blk_pass(Limb& L, int c0) {
   uint32_t v[E];
 #pragma unroll
   for (int m = 0; m < E; ++m) v[m] = L.load((B << LOGRB) + elem_index<LOGRB, LOGE, false>(0, t, m));
-  auto twb = [B](int s) { return (B << LOGRB) + (1 << s) - 1; };  // block-major table
+  auto twb = [B](int s) { return (B << LOGRB) + (1 << s); };  // block-major table
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRB, LOGE, false>(v, lds + k * STRIDE, rd - 1, t);
-    ct_round<LOGRB, LOGE>(v, rd, t, L.r, L.tw, L.twp, twb);
+    ct_round<LOGRB, LOGE>(v, rd, t, L.r, L.rinv, L.tw, twb);
   }
   // transpose through LDS so that consecutive lanes write consecutive words
 #pragma unroll
@@ -274,34 +290,32 @@ __device__ __forceinline__ void fwd_blk_pass(Limb& L, int c0) {
   }
 }
 
-// Forward block pass as above, with a hook applied to every element in the
-// block (pre-transpose) layout: pre(B, residue, x, v) -> v' where the element
-// sits at natural position bitrev(x) 2^LOGRC + residue; the result is then
-// transposed and passed to L.store(pos, v').
-template <int LOGRC, int LOGRB, int LOGE, int C, class Limb, class Pre>
-__device__ __forceinline__ void fwd_blk_pass_pre(Limb& L, int c0, Pre pre) {
+// Forward block pass whose output stage also reads side inputs at the output
+// positions: L.fetch(m, pos) runs for every output slot m before the
+// transform, so those loads are in flight while it computes, and
+// L.finish(m, pos, v) stores slot m afterwards.
+template <int LOGRC, int LOGRB, int LOGE, int C, class Limb>
+__device__ __forceinline__ void fwd_blk_pass_fetch(Limb& L, int c0) {
   constexpr int R = 1 << LOGRB, E = 1 << LOGE, ROUNDS = LOGRB / LOGE, TPB = R / E;
+  static_assert(LOGRB % LOGE == 0, "rounds must tile the pass");
   constexpr int STRIDE = LdsTile<LOGRB>::STRIDE;
   __shared__ uint32_t lds[C * STRIDE];
   const int tid = threadIdx.x;
+  const int kk = tid % C, rest = tid / C;
+  auto out_pos = [&](int m) { return ((int)bitrev((uint32_t)(rest + TPB * m), LOGRB) << LOGRC) + c0 + kk; };
+#pragma unroll
+  for (int m = 0; m < E; ++m) L.fetch(m, out_pos(m));
   const int t = tid % TPB, k = tid / TPB;
   const int B = (int)bitrev((uint32_t)(c0 + k), LOGRC);
   uint32_t v[E];
 #pragma unroll
   for (int m = 0; m < E; ++m) v[m] = L.load((B << LOGRB) + elem_index<LOGRB, LOGE, false>(0, t, m));
-  fwd_blk_compute<LOGRC, LOGRB, LOGE>(v, lds + k * STRIDE, t, B, L.r, L.tw, L.twp);
+  fwd_blk_compute<LOGRC, LOGRB, LOGE>(v, lds + k * STRIDE, t, B, L.r, L.rinv, L.tw);
 #pragma unroll
-  for (int m = 0; m < E; ++m) {
-    const int x = elem_index<LOGRB, LOGE, false>(ROUNDS - 1, t, m);
-    lds[k * STRIDE + x] = pre(B, c0 + k, x, v[m]);
-  }
+  for (int m = 0; m < E; ++m) lds[k * STRIDE + elem_index<LOGRB, LOGE, false>(ROUNDS - 1, t, m)] = v[m];
   __syncthreads();
-  const int kk = tid % C, rest = tid / C;
 #pragma unroll
-  for (int m = 0; m < E; ++m) {
-    const int x = rest + TPB * m;
-    L.store(((int)bitrev((uint32_t)x, LOGRB) << LOGRC) + c0 + kk, lds[kk * STRIDE + x]);
-  }
+  for (int m = 0; m < E; ++m) L.finish(m, out_pos(m), lds[kk * STRIDE + rest + TPB * m]);
 }
 
 // Inverse block pass: GS stages 0..LOGRB-1 on blocks B = bitrev(c0 + k); element
@@ -329,11 +343,11 @@ __device__ __forceinline__ void inv_blk_pass(Limb& L, int c0) {
 #pragma unroll
   for (int m = 0; m < E; ++m) v[m] = lds[k * STRIDE + elem_index<LOGRB, LOGE, true>(0, t, m)];
   __syncthreads();
-  auto twb = [B](int u) { return (B << LOGRB) + (1 << (LOGRB - u - 1)) - 1; };  // block-major table
+  auto twb = [B](int u) { return (B << LOGRB) + (1 << (LOGRB - u - 1)); };  // block-major table
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRB, LOGE, true>(v, lds + k * STRIDE, rd - 1, t);
-    gs_round<LOGRB, LOGE>(v, rd, t, L.r, L.tw, L.twp, twb);
+    gs_round<LOGRB, LOGE>(v, rd, t, L.r, L.rinv, L.tw, twb);
   }
 #pragma unroll
   for (int m = 0; m < E; ++m) L.store((B << LOGRB) + elem_index<LOGRB, LOGE, true>(ROUNDS - 1, t, m), v[m]);
@@ -355,7 +369,7 @@ __device__ __forceinline__ void inv_col_pass(Limb& L, int col0) {
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRC, LOGE, true>(v, lds + col * LdsTile<LOGRC>::STRIDE, rd - 1, t);
-    gs_round<LOGRC, LOGE>(v, rd, t, L.r, L.tw, L.twp, twb);
+    gs_round<LOGRC, LOGE>(v, rd, t, L.r, L.rinv, L.tw, twb);
   }
 #pragma unroll
   for (int m = 0; m < E; ++m)
