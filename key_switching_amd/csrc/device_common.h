@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pc {
 
 __device__ __forceinline__ uint32_t add_mod(uint32_t a, uint32_t b, uint32_t r) {
@@ -52,6 +54,15 @@ __device__ __forceinline__ uint32_t redc(uint64_t x, uint32_t r, uint32_t rinv_n
 }
 
 __device__ __forceinline__ uint64_t mul_wide(uint32_t a, uint32_t b) { return (uint64_t)a * b; }
+
+// base[idx] addressed through a 32-bit byte offset (idx < 2^30): the compiler
+// can then use a uniform 64-bit base plus a 32-bit per-lane offset instead of
+// a full 64-bit address per lane.
+template <class T>
+__device__ __forceinline__ T& at32(T* base, uint32_t idx) {
+  using B = typename std::conditional<std::is_const<T>::value, const char, char>::type;
+  return *reinterpret_cast<T*>(reinterpret_cast<B*>(base) + (idx << 2));
+}
 
 // x w 2^-32 mod r for any 32-bit x and w < r, canonical: with w a twiddle in
 // Montgomery form (w0 2^32 mod r) this is x w0 mod r.

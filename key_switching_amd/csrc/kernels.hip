@@ -72,8 +72,8 @@ struct PlainLimb {
   const uint32_t* __restrict__ tw;
   const uint32_t* __restrict__ src;
   uint32_t* __restrict__ dst;
-  __device__ __forceinline__ uint32_t load(int pos) const { return src[pos]; }
-  __device__ __forceinline__ void store(int pos, uint32_t v) const { dst[pos] = v; }
+  __device__ __forceinline__ uint32_t load(int pos) const { return at32(src, pos); }
+  __device__ __forceinline__ void store(int pos, uint32_t v) const { at32(dst, pos) = v; }
 };
 
 struct ScaledLimb {
@@ -81,8 +81,8 @@ struct ScaledLimb {
   const uint32_t* __restrict__ tw;
   const uint32_t* src;
   uint32_t* dst;
-  __device__ __forceinline__ uint32_t load(int pos) const { return src[pos]; }
-  __device__ __forceinline__ void store(int pos, uint32_t v) const { dst[pos] = mul_shoup(v, s, sp, r); }
+  __device__ __forceinline__ uint32_t load(int pos) const { return at32(src, pos); }
+  __device__ __forceinline__ void store(int pos, uint32_t v) const { at32(dst, pos) = mul_shoup(v, s, sp, r); }
 };
 
 // ModDown combine: out = (acc - v) P^-1 (+ c0 at the automorphism's source
@@ -98,15 +98,15 @@ struct CombineLimb {
   uint32_t g, h, mask;
   uint32_t* __restrict__ dst;
   uint32_t av[E], cv[E];
-  __device__ __forceinline__ uint32_t load(int pos) const { return src[pos]; }
+  __device__ __forceinline__ uint32_t load(int pos) const { return at32(src, pos); }
   __device__ __forceinline__ void fetch(int m, int pos) {
-    av[m] = acc[pos];
-    cv[m] = c0 ? c0[((uint32_t)pos * g + h) & mask] : 0u;
+    av[m] = at32(acc, pos);
+    cv[m] = c0 ? at32(c0, ((uint32_t)pos * g + h) & mask) : 0u;
   }
   __device__ __forceinline__ void finish(int m, int pos, uint32_t v) const {
     uint32_t o = mul_shoup(sub_mod(av[m], v, r), pinv, pinvp, r);
     if (c0) o = add_mod(o, cv[m], r);
-    dst[pos] = o;
+    at32(dst, pos) = o;
   }
 };
 
@@ -322,7 +322,10 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_bconv(ModUpArgs A
   const uint32_t* cbase = A.LT.mu_bconv + A.bconv_off + (size_t)i0 * lk;
   grouped_bconv<G, E, CNT>(
       tg, cnt,
-      [&](int k, int m) { return ybase[(size_t)k * A.N + col_pos_fwd_in<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)]; },
+      [&](int k, int m) {
+        const uint32_t* yk = ybase + (size_t)k * A.N;  // uniform limb base, 32-bit offset
+        return at32(yk, col_pos_fwd_in<C::LRC, C::LEC, C::LRB, C::CC>(col0, m));
+      },
       [&](int k, int g) { return cbase[(size_t)k * lk + tg.j[g]]; });
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -330,7 +333,7 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_bconv(ModUpArgs A
       fwd_col_compute<C::LRC, C::LEC, C::CC>(tg.z[g], lds, tg.r[g], tg.rinv[g], A.T.tw_fwd + tg.pidx[g] * A.N);
       uint32_t* dst = A.tmp + ((b * A.beta + d) * lk + tg.j[g]) * A.N;
 #pragma unroll
-      for (int m = 0; m < E; ++m) dst[col_pos_fwd_out<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)] = tg.z[g][m];
+      for (int m = 0; m < E; ++m) at32(dst, col_pos_fwd_out<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)) = tg.z[g][m];
     }
   }
 }
@@ -380,8 +383,8 @@ struct IPArgs {
 __device__ __forceinline__ int pos8(int p0, int p1, int k) { return k < 4 ? p0 + k : p1 + k - 4; }
 
 __device__ __forceinline__ void load8(const uint32_t* base, int p0, int p1, uint32_t (&v)[8]) {
-  const uint4 x = *reinterpret_cast<const uint4*>(base + p0);
-  const uint4 y = *reinterpret_cast<const uint4*>(base + p1);
+  const uint4 x = *reinterpret_cast<const uint4*>(&at32(base, p0));
+  const uint4 y = *reinterpret_cast<const uint4*>(&at32(base, p1));
   v[0] = x.x;
   v[1] = x.y;
   v[2] = x.z;
@@ -393,8 +396,8 @@ __device__ __forceinline__ void load8(const uint32_t* base, int p0, int p1, uint
 }
 
 __device__ __forceinline__ void store8(uint32_t* base, int p0, int p1, const uint32_t (&v)[8]) {
-  *reinterpret_cast<uint4*>(base + p0) = make_uint4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<uint4*>(base + p1) = make_uint4(v[4], v[5], v[6], v[7]);
+  *reinterpret_cast<uint4*>(&at32(base, p0)) = make_uint4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<uint4*>(&at32(base, p1)) = make_uint4(v[4], v[5], v[6], v[7]);
 }
 
 // Key values of digit d, limb j at the thread's 8 positions, in Montgomery form.
@@ -421,7 +424,7 @@ __device__ __forceinline__ void load_digits(const IPArgs& A, int b, int j, int l
       load8(src, p0, p1, e[d]);
     } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) e[d][k] = src[src_idx[k]];
+      for (int k = 0; k < 8; ++k) e[d][k] = at32(src, src_idx[k]);
     }
   }
 }
@@ -657,7 +660,10 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv(ModDownArgs A)
   const uint32_t* cbase = A.LT.md_bconv + (size_t)A.variant * A.K * A.L;
   grouped_bconv<G, E, CNT>(
       tg, A.K,
-      [&](int k, int m) { return ybase[(size_t)k * A.N + col_pos_fwd_in<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)]; },
+      [&](int k, int m) {
+        const uint32_t* yk = ybase + (size_t)k * A.N;  // uniform limb base, 32-bit offset
+        return at32(yk, col_pos_fwd_in<C::LRC, C::LEC, C::LRB, C::CC>(col0, m));
+      },
       [&](int k, int g) { return cbase[(size_t)k * A.L + tg.j[g]]; });
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -665,7 +671,7 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv(ModDownArgs A)
       fwd_col_compute<C::LRC, C::LEC, C::CC>(tg.z[g], lds, tg.r[g], tg.rinv[g], A.T.tw_fwd + tg.pidx[g] * A.N);
       uint32_t* dst = A.tmp2 + (ip * A.level + tg.j[g]) * A.N;
 #pragma unroll
-      for (int m = 0; m < E; ++m) dst[col_pos_fwd_out<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)] = tg.z[g][m];
+      for (int m = 0; m < E; ++m) at32(dst, col_pos_fwd_out<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)) = tg.z[g][m];
     }
   }
 }

@@ -53,6 +53,26 @@ struct LdsTile {
   static constexpr int STRIDE = R + 4;
 };
 
+// LDS layout of a block pass's tile of C blocks of R = 2^LOGRB elements:
+// element x of block k at row(k) + col(x). The pass touches the tile in four
+// patterns, each taken by 32 lanes at a time (32 banks of 4 bytes): two blocks
+// x 16 threads writing x = 16m + t, two blocks x 16 threads reading or writing
+// x = 16t + m, and 32 blocks reading or writing one x (the transpose). For
+// 256-point blocks with 16 elements per thread, row(k) = 272k + k/2 and
+// col(x) = x + x/16 put every one of them on 32 distinct banks (the pad makes
+// 16t + m distinct over t, the stride of 16 mod 32 separates the two blocks, and
+// the k/2 skew separates all 32 blocks of the transpose). Other shapes keep a
+// plain padded stride.
+template <int LOGRB, int LOGE>
+struct BlkLds {
+  static constexpr int R = 1 << LOGRB;
+  static constexpr bool SWZ = LOGRB == 8 && LOGE == 4;
+  static constexpr int S = SWZ ? R + R / 16 : R + 4;
+  __device__ __forceinline__ static int row(int k) { return SWZ ? k * S + (k >> 1) : k * S; }
+  __device__ __forceinline__ static int col(int x) { return SWZ ? x + (x >> 4) : x; }
+  static constexpr int words(int c) { return SWZ ? c * S + c / 2 : c * S; }
+};
+
 // n consecutive twiddles from p (n a power of two; p aligned to min(n, 4)
 // words, which every table layout here guarantees): one vector load per four.
 __device__ __forceinline__ void load_run(const uint32_t* __restrict__ p, int n, uint32_t* w) {
@@ -135,15 +155,20 @@ __device__ __forceinline__ void gs_round(uint32_t (&v)[1 << LOGE], int round, in
   }
 }
 
-// Exchange the register tile between two round layouts through LDS.
-template <int LOGR, int LOGE, bool GS>
+// Exchange the register tile between two round layouts through LDS; Col maps
+// an element index to its word in the row.
+struct IdentityCol {
+  __device__ __forceinline__ static int col(int x) { return x; }
+};
+
+template <int LOGR, int LOGE, bool GS, class Col = IdentityCol>
 __device__ __forceinline__ void exchange(uint32_t (&v)[1 << LOGE], uint32_t* lds_row, int from_round, int t) {
   constexpr int E = 1 << LOGE;
 #pragma unroll
-  for (int m = 0; m < E; ++m) lds_row[elem_index<LOGR, LOGE, GS>(from_round, t, m)] = v[m];
+  for (int m = 0; m < E; ++m) lds_row[Col::col(elem_index<LOGR, LOGE, GS>(from_round, t, m))] = v[m];
   __syncthreads();
 #pragma unroll
-  for (int m = 0; m < E; ++m) v[m] = lds_row[elem_index<LOGR, LOGE, GS>(from_round + 1, t, m)];
+  for (int m = 0; m < E; ++m) v[m] = lds_row[Col::col(elem_index<LOGR, LOGE, GS>(from_round + 1, t, m))];
   __syncthreads();
 }
 
@@ -218,7 +243,7 @@ __device__ __forceinline__ void fwd_blk_compute(uint32_t (&v)[1 << LOGE], uint32
   auto twb = [B](int s) { return (B << LOGRB) + (1 << s); };  // block-major table
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
-    if (rd > 0) exchange<LOGRB, LOGE, false>(v, lds_row, rd - 1, t);
+    if (rd > 0) exchange<LOGRB, LOGE, false, BlkLds<LOGRB, LOGE>>(v, lds_row, rd - 1, t);
     ct_round<LOGRB, LOGE>(v, rd, t, r, rinv, tw, twb);
   }
 }
@@ -230,7 +255,7 @@ __device__ __forceinline__ void inv_blk_compute(uint32_t (&v)[1 << LOGE], uint32
   auto twb = [B](int u) { return (B << LOGRB) + (1 << (LOGRB - u - 1)); };  // block-major table
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
-    if (rd > 0) exchange<LOGRB, LOGE, true>(v, lds_row, rd - 1, t);
+    if (rd > 0) exchange<LOGRB, LOGE, true, BlkLds<LOGRB, LOGE>>(v, lds_row, rd - 1, t);
     gs_round<LOGRB, LOGE>(v, rd, t, r, rinv, tw, twb);
   }
 }
@@ -264,29 +289,24 @@ template <int LOGRC, int LOGRB, int LOGE, int C, class Limb>
 __device__ __forceinline__ void fwd_blk_pass(Limb& L, int c0) {
   constexpr int R = 1 << LOGRB, E = 1 << LOGE, ROUNDS = LOGRB / LOGE, TPB = R / E;
   static_assert(LOGRB % LOGE == 0, "rounds must tile the pass");
-  constexpr int STRIDE = LdsTile<LOGRB>::STRIDE;
-  __shared__ uint32_t lds[C * STRIDE];
+  using Lay = BlkLds<LOGRB, LOGE>;
+  __shared__ uint32_t lds[Lay::words(C)];
   const int tid = threadIdx.x;
   const int t = tid % TPB, k = tid / TPB;
   const int B = (int)bitrev((uint32_t)(c0 + k), LOGRC);
   uint32_t v[E];
 #pragma unroll
   for (int m = 0; m < E; ++m) v[m] = L.load((B << LOGRB) + elem_index<LOGRB, LOGE, false>(0, t, m));
-  auto twb = [B](int s) { return (B << LOGRB) + (1 << s); };  // block-major table
-#pragma unroll
-  for (int rd = 0; rd < ROUNDS; ++rd) {
-    if (rd > 0) exchange<LOGRB, LOGE, false>(v, lds + k * STRIDE, rd - 1, t);
-    ct_round<LOGRB, LOGE>(v, rd, t, L.r, L.rinv, L.tw, twb);
-  }
+  fwd_blk_compute<LOGRC, LOGRB, LOGE>(v, lds + Lay::row(k), t, B, L.r, L.rinv, L.tw);
   // transpose through LDS so that consecutive lanes write consecutive words
 #pragma unroll
-  for (int m = 0; m < E; ++m) lds[k * STRIDE + elem_index<LOGRB, LOGE, false>(ROUNDS - 1, t, m)] = v[m];
+  for (int m = 0; m < E; ++m) lds[Lay::row(k) + Lay::col(elem_index<LOGRB, LOGE, false>(ROUNDS - 1, t, m))] = v[m];
   __syncthreads();
   const int kk = tid % C, rest = tid / C;
 #pragma unroll
   for (int m = 0; m < E; ++m) {
     const int x = rest + TPB * m;
-    L.store(((int)bitrev((uint32_t)x, LOGRB) << LOGRC) + c0 + kk, lds[kk * STRIDE + x]);
+    L.store(((int)bitrev((uint32_t)x, LOGRB) << LOGRC) + c0 + kk, lds[Lay::row(kk) + Lay::col(x)]);
   }
 }
 
@@ -298,8 +318,8 @@ template <int LOGRC, int LOGRB, int LOGE, int C, class Limb>
 __device__ __forceinline__ void fwd_blk_pass_fetch(Limb& L, int c0) {
   constexpr int R = 1 << LOGRB, E = 1 << LOGE, ROUNDS = LOGRB / LOGE, TPB = R / E;
   static_assert(LOGRB % LOGE == 0, "rounds must tile the pass");
-  constexpr int STRIDE = LdsTile<LOGRB>::STRIDE;
-  __shared__ uint32_t lds[C * STRIDE];
+  using Lay = BlkLds<LOGRB, LOGE>;
+  __shared__ uint32_t lds[Lay::words(C)];
   const int tid = threadIdx.x;
   const int kk = tid % C, rest = tid / C;
   auto out_pos = [&](int m) { return ((int)bitrev((uint32_t)(rest + TPB * m), LOGRB) << LOGRC) + c0 + kk; };
@@ -310,12 +330,12 @@ __device__ __forceinline__ void fwd_blk_pass_fetch(Limb& L, int c0) {
   uint32_t v[E];
 #pragma unroll
   for (int m = 0; m < E; ++m) v[m] = L.load((B << LOGRB) + elem_index<LOGRB, LOGE, false>(0, t, m));
-  fwd_blk_compute<LOGRC, LOGRB, LOGE>(v, lds + k * STRIDE, t, B, L.r, L.rinv, L.tw);
+  fwd_blk_compute<LOGRC, LOGRB, LOGE>(v, lds + Lay::row(k), t, B, L.r, L.rinv, L.tw);
 #pragma unroll
-  for (int m = 0; m < E; ++m) lds[k * STRIDE + elem_index<LOGRB, LOGE, false>(ROUNDS - 1, t, m)] = v[m];
+  for (int m = 0; m < E; ++m) lds[Lay::row(k) + Lay::col(elem_index<LOGRB, LOGE, false>(ROUNDS - 1, t, m))] = v[m];
   __syncthreads();
 #pragma unroll
-  for (int m = 0; m < E; ++m) L.finish(m, out_pos(m), lds[kk * STRIDE + rest + TPB * m]);
+  for (int m = 0; m < E; ++m) L.finish(m, out_pos(m), lds[Lay::row(kk) + Lay::col(rest + TPB * m)]);
 }
 
 // Inverse block pass: GS stages 0..LOGRB-1 on blocks B = bitrev(c0 + k); element
@@ -325,15 +345,15 @@ template <int LOGRC, int LOGRB, int LOGE, int C, class Limb>
 __device__ __forceinline__ void inv_blk_pass(Limb& L, int c0) {
   constexpr int R = 1 << LOGRB, E = 1 << LOGE, ROUNDS = LOGRB / LOGE, TPB = R / E;
   static_assert(LOGRB % LOGE == 0, "rounds must tile the pass");
-  constexpr int STRIDE = LdsTile<LOGRB>::STRIDE;
-  __shared__ uint32_t lds[C * STRIDE];
+  using Lay = BlkLds<LOGRB, LOGE>;
+  __shared__ uint32_t lds[Lay::words(C)];
   const int tid = threadIdx.x;
   {
     const int kk = tid % C, rest = tid / C;
 #pragma unroll
     for (int m = 0; m < E; ++m) {
       const int x = rest + TPB * m;
-      lds[kk * STRIDE + x] = L.load(((int)bitrev((uint32_t)x, LOGRB) << LOGRC) + c0 + kk);
+      lds[Lay::row(kk) + Lay::col(x)] = L.load(((int)bitrev((uint32_t)x, LOGRB) << LOGRC) + c0 + kk);
     }
   }
   __syncthreads();
@@ -341,14 +361,9 @@ __device__ __forceinline__ void inv_blk_pass(Limb& L, int c0) {
   const int B = (int)bitrev((uint32_t)(c0 + k), LOGRC);
   uint32_t v[E];
 #pragma unroll
-  for (int m = 0; m < E; ++m) v[m] = lds[k * STRIDE + elem_index<LOGRB, LOGE, true>(0, t, m)];
+  for (int m = 0; m < E; ++m) v[m] = lds[Lay::row(k) + Lay::col(elem_index<LOGRB, LOGE, true>(0, t, m))];
   __syncthreads();
-  auto twb = [B](int u) { return (B << LOGRB) + (1 << (LOGRB - u - 1)); };  // block-major table
-#pragma unroll
-  for (int rd = 0; rd < ROUNDS; ++rd) {
-    if (rd > 0) exchange<LOGRB, LOGE, true>(v, lds + k * STRIDE, rd - 1, t);
-    gs_round<LOGRB, LOGE>(v, rd, t, L.r, L.rinv, L.tw, twb);
-  }
+  inv_blk_compute<LOGRC, LOGRB, LOGE>(v, lds + Lay::row(k), t, B, L.r, L.rinv, L.tw);
 #pragma unroll
   for (int m = 0; m < E; ++m) L.store((B << LOGRB) + elem_index<LOGRB, LOGE, true>(ROUNDS - 1, t, m), v[m]);
 }
