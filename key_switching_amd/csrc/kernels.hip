@@ -33,7 +33,7 @@ struct Cfg<12> {
 };
 template <>
 struct Cfg<16> {
-  static constexpr int LRC = 8, LEC = 4, LRB = 8, LEB = 4, CC = 16, CB = 32;
+  static constexpr int LRC = 8, LEC = 4, LRB = 8, LEB = 4, CC = 32, CB = 32;
 };
 template <>
 struct Cfg<17> {
@@ -289,14 +289,14 @@ __device__ __forceinline__ void grouped_bconv(TargetGroup<G, E>& tg, int cnt, Sr
   }
 }
 
-constexpr int kBconvGroup = 4;
+constexpr int kBconvGroup = 3;
 
 // ModUp conversion: row (b, d), column tile blockIdx.x, target group blockIdx.z.
 template <int LOGN, int CNT>
 __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_bconv(ModUpArgs A) {
   using C = Cfg<LOGN>;
   constexpr int E = 1 << C::LEC, G = kBconvGroup;
-  __shared__ uint32_t lds[C::CC * LdsTile<C::LRC>::STRIDE];
+  __shared__ uint32_t lds[C::CC * LdsTile<C::LRC, C::LEC>::STRIDE];
   const int lk = A.level + A.K;
   int tile, row, grp;
   if (!xcd_unit(col_tiles<LOGN>(), A.batch * A.beta, A.ngroups, tile, row, grp)) return;
@@ -639,7 +639,7 @@ template <int LOGN, int CNT>
 __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv(ModDownArgs A) {
   using C = Cfg<LOGN>;
   constexpr int E = 1 << C::LEC, G = kBconvGroup;
-  __shared__ uint32_t lds[C::CC * LdsTile<C::LRC>::STRIDE];
+  __shared__ uint32_t lds[C::CC * LdsTile<C::LRC, C::LEC>::STRIDE];
   int tile, row, grp;
   if (!xcd_unit(col_tiles<LOGN>(), A.rows_ip, A.ngroups, tile, row, grp)) return;
   const size_t ip = row;

@@ -46,11 +46,15 @@ __device__ __forceinline__ int elem_index(int round, int t, int m) {
   return (thigh << (lo + LOGE)) | (m << lo) | tlow;
 }
 
-// Row stride (words) of the LDS tile; the pad spreads columns over banks.
-template <int LOGR>
+// Row stride (words) of a column pass's LDS tile (one row per column). The
+// exchanges are taken by 32 lanes of consecutive columns at a time (2 threads
+// of 16 columns, or 1 of 32), writing x = 16m + t and reading x = 16t + m; for
+// 256-point columns with 16 elements per thread a stride of 17 mod 32 (273)
+// puts both on 32 distinct banks. Other shapes keep a pad of 4.
+template <int LOGR, int LOGE = 4>
 struct LdsTile {
   static constexpr int R = 1 << LOGR;
-  static constexpr int STRIDE = R + 4;
+  static constexpr int STRIDE = (LOGR == 8 && LOGE == 4) ? R + 17 : R + 4;
 };
 
 // LDS layout of a block pass's tile of C blocks of R = 2^LOGRB elements:
@@ -194,7 +198,7 @@ __device__ __forceinline__ void fwd_col_compute(uint32_t (&v)[1 << LOGE], uint32
   auto twb = [](int s) { return 1 << s; };
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
-    if (rd > 0) exchange<LOGRC, LOGE, false>(v, lds + col * LdsTile<LOGRC>::STRIDE, rd - 1, t);
+    if (rd > 0) exchange<LOGRC, LOGE, false>(v, lds + col * LdsTile<LOGRC, LOGE>::STRIDE, rd - 1, t);
     ct_round<LOGRC, LOGE>(v, rd, t, r, rinv, tw, twb);
   }
 }
@@ -207,7 +211,7 @@ __device__ __forceinline__ void inv_col_compute(uint32_t (&v)[1 << LOGE], uint32
   auto twb = [](int u) { return 1 << (LOGRC - u - 1); };
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
-    if (rd > 0) exchange<LOGRC, LOGE, true>(v, lds + col * LdsTile<LOGRC>::STRIDE, rd - 1, t);
+    if (rd > 0) exchange<LOGRC, LOGE, true>(v, lds + col * LdsTile<LOGRC, LOGE>::STRIDE, rd - 1, t);
     gs_round<LOGRC, LOGE>(v, rd, t, r, rinv, tw, twb);
   }
 }
@@ -265,7 +269,7 @@ template <int LOGRC, int LOGE, int LOGRB, int C, class Limb>
 __device__ __forceinline__ void fwd_col_pass(Limb& L, int col0) {
   constexpr int R = 1 << LOGRC, E = 1 << LOGE, ROUNDS = LOGRC / LOGE;
   static_assert(LOGRC % LOGE == 0, "rounds must tile the pass");
-  __shared__ uint32_t lds[C * LdsTile<LOGRC>::STRIDE];
+  __shared__ uint32_t lds[C * LdsTile<LOGRC, LOGE>::STRIDE];
   const int tid = threadIdx.x;
   const int col = tid % C, t = tid / C;
   uint32_t v[E];
@@ -274,7 +278,7 @@ __device__ __forceinline__ void fwd_col_pass(Limb& L, int col0) {
   auto twb = [](int s) { return 1 << s; };
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
-    if (rd > 0) exchange<LOGRC, LOGE, false>(v, lds + col * LdsTile<LOGRC>::STRIDE, rd - 1, t);
+    if (rd > 0) exchange<LOGRC, LOGE, false>(v, lds + col * LdsTile<LOGRC, LOGE>::STRIDE, rd - 1, t);
     ct_round<LOGRC, LOGE>(v, rd, t, L.r, L.rinv, L.tw, twb);
   }
 #pragma unroll
@@ -374,7 +378,7 @@ template <int LOGRC, int LOGE, int LOGRB, int C, class Limb>
 __device__ __forceinline__ void inv_col_pass(Limb& L, int col0) {
   constexpr int E = 1 << LOGE, ROUNDS = LOGRC / LOGE;
   static_assert(LOGRC % LOGE == 0, "rounds must tile the pass");
-  __shared__ uint32_t lds[C * LdsTile<LOGRC>::STRIDE];
+  __shared__ uint32_t lds[C * LdsTile<LOGRC, LOGE>::STRIDE];
   const int tid = threadIdx.x;
   const int col = tid % C, t = tid / C;
   uint32_t v[E];
@@ -383,7 +387,7 @@ __device__ __forceinline__ void inv_col_pass(Limb& L, int col0) {
   auto twb = [](int u) { return 1 << (LOGRC - u - 1); };
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
-    if (rd > 0) exchange<LOGRC, LOGE, true>(v, lds + col * LdsTile<LOGRC>::STRIDE, rd - 1, t);
+    if (rd > 0) exchange<LOGRC, LOGE, true>(v, lds + col * LdsTile<LOGRC, LOGE>::STRIDE, rd - 1, t);
     gs_round<LOGRC, LOGE>(v, rd, t, L.r, L.rinv, L.tw, twb);
   }
 #pragma unroll
