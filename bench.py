@@ -35,9 +35,25 @@ import ks_inputs as ki  # noqa: E402
 METRIC = "key switches/sec at N=2^16, L=24 (k=1,8); % of HBM/INT32 roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 CUS, CLOCK_GHZ = 256, 2.4       # MI355X compute units and peak engine clock
-VALU_LANES_PER_CU = 128         # 32-bit lanes per CU per clock (fp32 vector 157.3 TFLOP/s = 256*128*2.4e9*2)
+INT32_LANES_PER_CU = 64         # 4 SIMDs x 16 lanes; every 32-bit integer VALU op issues at this rate
+INT32_PEAK_TOPS = CUS * INT32_LANES_PER_CU * CLOCK_GHZ / 1000.0  # 39.3 T int32 lane-ops/s
+
+# 32-bit integer operations of the arithmetic primitives (the minimum instruction
+# count of each with canonical residues below r < 2^31):
+OPS_MONT = 5        # x*w 2^-32 mod r: 64-bit product, m = lo*(-r^-1), + m*r, high word, one correction
+OPS_ADDMOD = 3      # add, subtract r, unsigned min
+OPS_BUTTERFLY = OPS_MONT + 2 * OPS_ADDMOD   # one twiddle product, one modular add, one modular subtract
+OPS_SHOUP = 5       # multiply by a constant with its Shoup companion
+OPS_REDC = 4        # low word times -r^-1, multiply-add, subtract r, min
+OPS_CHACHA12_BLOCK = 6 * 8 * 12 + 16        # 6 double rounds x 8 quarter rounds x 12 ops, + feed-forward
+OPS_WORDPAIR = 6 + OPS_REDC                 # two words -> a residue in Montgomery form
 
 
+def dot_ops(alpha):
+    """Base-conversion dot product of alpha sources: one multiply-add each, a fold of
+    the 64-bit sum after the fourth product and every further pair (two ops each), REDC."""
+    folds = 0 if alpha <= 2 else 1 + (alpha - 3) // 2
+    return alpha + 2 * folds + OPS_REDC
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -76,6 +92,47 @@ def alg_bytes_per_launch(kernel, w, batch, beta, alpha):
         "moddown_fwd_blk": batch * 2 * (l + l + l) + batch * l,  # tmp2 + acc in, out; c0 in
     }
     return table[kernel] * limb
+
+
+def alg_ops_per_launch(kernel, w, batch, beta, alpha):
+    """Algorithmic 32-bit integer operations of one launch (op counts of the primitives above).
+
+    An NTT pass over a limb does N/2 butterflies per stage; the column and block
+    passes of a 2^16-point transform cover 8 stages each.
+    """
+    N, l, K = w.N, w.L, w.K
+    digits = [min(alpha, l - d * alpha) for d in range(beta)]
+    half_pass = N // 2 * 8 * OPS_BUTTERFLY          # one 8-stage pass over one limb
+    conv_targets = sum((l + K - a) * N * dot_ops(a) for a in digits)
+    targets = sum(l + K - a for a in digits)
+    lk = l + K
+    key_ops = lk * N * beta * (OPS_REDC + OPS_CHACHA12_BLOCK / 8 + OPS_WORDPAIR)  # b to Montgomery form, a regenerated
+    pairs = beta // 2 + beta % 2
+    ip_item = lk * N * 2 * (pairs * (2 + OPS_REDC + OPS_ADDMOD))                   # both sums, products paired per REDC
+    table = {
+        "modup_inv_blk": batch * l * half_pass,
+        "modup_inv_col": batch * l * (half_pass + N * OPS_SHOUP),
+        "modup_bconv": batch * (conv_targets + targets * half_pass),
+        "modup_fwd_blk": batch * targets * half_pass,
+        "inner_product": key_ops + batch * ip_item,
+        "moddown_inv_blk": batch * 2 * K * half_pass,
+        "moddown_inv_col": batch * 2 * K * (half_pass + N * OPS_SHOUP),
+        "moddown_bconv": batch * 2 * l * (N * dot_ops(K) + half_pass),
+        "moddown_fwd_blk": batch * 2 * l * (half_pass + N * (2 * OPS_ADDMOD + OPS_SHOUP)),
+    }
+    return table[kernel]
+
+
+def kernel_roofline(kernel, avg_us, w, batch, beta, alpha):
+    """HBM and int32-ALU fractions of one launch; the binding one is the larger."""
+    t = avg_us * 1e-6
+    nbytes = alg_bytes_per_launch(kernel, w, batch, beta, alpha)
+    nops = alg_ops_per_launch(kernel, w, batch, beta, alpha)
+    hbm = nbytes / t / 1e9
+    alu = nops / t / 1e12
+    return {"hbm_gbs": round(hbm, 1), "hbm_frac": round(hbm / HBM_PEAK_GBS, 4),
+            "alu_tops": round(alu, 2), "alu_frac": round(alu / INT32_PEAK_TOPS, 4),
+            "alg_bytes": nbytes, "alg_ops": int(nops), "avg_us": round(avg_us, 3)}
 
 
 def main():
@@ -161,15 +218,26 @@ def main():
     kstats_stored = ksa.profile_end(prm)
     kernels_stored = {k: round(1000.0 * t / n, 3) for k, (n, t) in sorted(kstats_stored.items(), key=lambda kv: -kv[1][1])}
     dom = next(iter(kernels))
-    dom_avg_s = kernels[dom]["avg_us"] * 1e-6
-    dom_bytes = alg_bytes_per_launch(dom, w, K8, beta, alpha)
-    achieved = dom_bytes / dom_avg_s / 1e9
+    roofs = {k: kernel_roofline(k, v["avg_us"], w, K8, beta, alpha) for k, v in kernels.items()}
     from key_switching_amd import profiling
-    traffic = profiling.read_traffic(os.path.join(ROOT, "profiles", f"{dom}_n16_k8_traffic.md"), dom)
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None if traffic is None else round(traffic),
-                "alg_bytes_per_launch": dom_bytes, "avg_us": round(kernels[dom]["avg_us"], 3)}
+    traffic_md = os.path.join(ROOT, "profiles", "keyswitch_n16_k8_traffic.md")
+    rd = roofs[dom]
+    if rd["alu_frac"] >= rd["hbm_frac"]:
+        roofline = {"bound": "alu", "achieved": rd["alu_tops"], "peak": round(INT32_PEAK_TOPS, 2), "unit": "TOP/s",
+                    "frac": rd["alu_frac"]}
+    else:
+        roofline = {"bound": "hbm", "achieved": rd["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": rd["hbm_frac"]}
+    traffic = profiling.read_traffic(traffic_md, dom)
+    roofline.update({"traffic": None if traffic is None else round(traffic), "kernel": dom,
+                     "alg_bytes_per_launch": rd["alg_bytes"], "alg_ops_per_launch": rd["alg_ops"],
+                     "hbm_frac": rd["hbm_frac"], "alu_frac": rd["alu_frac"], "avg_us": rd["avg_us"]})
+    step_s = ms8p * 1e-3
+    path_bytes = sum(r["alg_bytes"] for r in roofs.values())
+    path_ops = sum(r["alg_ops"] for r in roofs.values())
+    path = {"alg_bytes_per_step": path_bytes, "alg_ops_per_step": path_ops,
+            "hbm_frac": round(path_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+            "alu_frac": round(path_ops / step_s / 1e12 / INT32_PEAK_TOPS, 4)}
 
     result = {
         "metric": METRIC,
@@ -194,8 +262,10 @@ def main():
             "k1_stored": {"ks_per_s": round(1000.0 / ms1s, 1), "ms_per_call": round(ms1s, 4)},
             "k8_chacha_profiled": {"ms_per_call": round(ms8p, 4)},
         },
-        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+        "kernels": {k: {**{kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()},
+                        "hbm_frac": roofs[k]["hbm_frac"], "alu_frac": roofs[k]["alu_frac"]}
                     for k, v in kernels.items()},
+        "path_roofline": path,
         "kernels_k8_stored_avg_us": kernels_stored,
         "roofline": roofline,
         "wall_s_k8": round(wall8, 3),
