@@ -83,6 +83,10 @@ typedef struct {
   uint32_t max_batch;     /* most ciphertexts per key-switch call (0 means 1) */
   uint32_t max_hoist;     /* most keys per hoisted call (0 means 1), <= 32 */
   uint32_t chacha_rounds; /* 12 (0 means 12); 20 is accepted for testing against ChaCha20 */
+  uint32_t partition;     /* digits below the top level: 0 = alpha(l) = ceil(l / dnum) and keys
+                             generated at the ciphertext's level l; 1 = alpha = ceil(L / dnum) at
+                             every level (the top-level digits cut at l) and keys generated at
+                             level L, whose limbs q_l..q_{L-1} are skipped */
   const uint32_t *primes; /* host; NULL = the descending rule, else L + K primes (q's then p's) */
 } pc_params_desc;
 
@@ -137,7 +141,8 @@ typedef struct {
   const uint32_t *ct;             /* device [batch][2][level][N] */
   uint32_t batch;                 /* 1..max_batch */
   uint32_t nkeys;                 /* 1..max_hoist */
-  const uint32_t *const *evk_b;   /* host array of nkeys device pointers, each [beta][level+K][N] */
+  const uint32_t *const *evk_b;   /* host array of nkeys device pointers, each [beta(kl)][kl+K][N] with
+                                     kl = the key level (level, or L with partition 1) */
   const uint32_t *const *evk_a;   /* NULL (regenerate a from seeds) or host array of nkeys device pointers */
   const uint8_t *seeds;           /* host [nkeys][32]; ignored when evk_a is given */
   const uint32_t *galois;         /* host [nkeys] Galois elements */

@@ -34,7 +34,8 @@ class PcError(RuntimeError):
 class _Desc(ctypes.Structure):
     _fields_ = [("log2n", ctypes.c_uint32), ("L", ctypes.c_uint32), ("dnum", ctypes.c_uint32),
                 ("K", ctypes.c_uint32), ("max_batch", ctypes.c_uint32), ("max_hoist", ctypes.c_uint32),
-                ("chacha_rounds", ctypes.c_uint32), ("primes", ctypes.POINTER(ctypes.c_uint32))]
+                ("chacha_rounds", ctypes.c_uint32), ("partition", ctypes.c_uint32),
+                ("primes", ctypes.POINTER(ctypes.c_uint32))]
 
 
 class _KsArgs(ctypes.Structure):
@@ -110,9 +111,10 @@ class Params:
     """Parameter set, constant tables and workspace arena (pc_params_create)."""
 
     def __init__(self, log2n: int, L: int, dnum: int, K: int, max_batch: int = 1, max_hoist: int = 1,
-                 chacha_rounds: int = 12, primes: Optional[Sequence[int]] = None, device: Optional[int] = 0):
+                 chacha_rounds: int = 12, primes: Optional[Sequence[int]] = None, device: Optional[int] = 0,
+                 partition: int = 0):
         lib = _lib()
-        desc = _Desc(log2n, L, dnum, K, max_batch, max_hoist, chacha_rounds, None)
+        desc = _Desc(log2n, L, dnum, K, max_batch, max_hoist, chacha_rounds, partition, None)
         self._primes_buf = None
         if primes is not None:
             self._primes_buf = (ctypes.c_uint32 * len(primes))(*[int(p) for p in primes])
@@ -123,6 +125,7 @@ class Params:
         self._h = h
         self.log2n, self.L, self.dnum, self.K = log2n, L, dnum, K
         self.max_batch, self.max_hoist = max_batch, max_hoist
+        self.partition = partition
 
     @property
     def handle(self):
@@ -166,6 +169,15 @@ class Params:
 
     def alpha(self, level: int) -> int:
         return self._get_u32(PC_GET_ALPHA, level)[0]
+
+    def key_level(self, level: int) -> int:
+        """Level of the key that serves ciphertexts at ``level`` (L with partition 1)."""
+        return self.L if self.partition else level
+
+    def key_shape(self, level: int) -> tuple:
+        """Shape of a key half serving ``level``: [beta(kl)][kl + K][N], kl = key_level(level)."""
+        kl = self.key_level(level)
+        return (self.beta(kl), kl + self.K, self.N)
 
     def beta(self, level: int) -> int:
         return self._get_u32(PC_GET_BETA, level)[0]
@@ -236,7 +248,7 @@ def keyswitch(prm: Params, ct, evk_b, seed: bytes, level: int, galois: int, out=
     """One key switch of ct [2][level][N] (pc_keyswitch)."""
     if out is None:
         out = _new((2, level, prm.N), prm.device)
-    kshape = (prm.beta(level), level + prm.K, prm.N)
+    kshape = prm.key_shape(level)
     _check(_lib().pc_keyswitch(prm.handle, _dev_ptr(ct, "ct", (2, level, prm.N), prm.device),
                                _dev_ptr(evk_b, "evk_b", kshape, prm.device), _seed_bytes(seed), level, galois,
                                _dev_ptr(out, "out", (2, level, prm.N), prm.device), _stream()), "pc_keyswitch")
@@ -254,7 +266,7 @@ def keyswitch_ex(prm: Params, ct, evk_b: Sequence, galois: Sequence[int], level:
     nkeys = len(evk_b)
     if len(galois) != nkeys:
         raise ValueError("one Galois element per key")
-    kshape = (prm.beta(level), level + prm.K, prm.N)
+    kshape = prm.key_shape(level)
     if out is None:
         out = _new((nkeys, batch, 2, level, prm.N), prm.device)
     args = _KsArgs()

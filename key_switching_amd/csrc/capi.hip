@@ -86,12 +86,6 @@ uint32_t bitrev_host(uint32_t x, int bits) {
   return y;
 }
 
-int alpha_of(const pc_params* p, uint32_t level) { return (int)((level + p->dnum - 1) / p->dnum); }
-int beta_of(const pc_params* p, uint32_t level) {
-  const int a = alpha_of(p, level);
-  return (int)((level + a - 1) / a);
-}
-
 // product of primes q_i, i in [i0, i1) \ {skip}, modulo r
 uint32_t prod_mod(const pc_params* p, int i0, int i1, int skip, uint32_t r) {
   uint32_t x = 1 % r;
@@ -370,6 +364,7 @@ int pc_params_create(const pc_params_desc* desc, int device, pc_params** out) {
   if (desc->K > (uint32_t)kMaxSpecial) return PC_EUNSUPPORTED;
   if ((desc->L + desc->dnum - 1) / desc->dnum > (uint32_t)kMaxAlpha) return PC_EUNSUPPORTED;
   if (desc->L + desc->K > (uint32_t)kMaxLimbsPerLaunch - 1) return PC_EUNSUPPORTED;
+  if (desc->partition > 1) return PC_EINVAL;
   const uint32_t rounds = desc->chacha_rounds ? desc->chacha_rounds : 12;
   if (rounds != 12 && rounds != 20) return PC_EUNSUPPORTED;
   const uint32_t max_hoist = desc->max_hoist ? desc->max_hoist : 1;
@@ -384,6 +379,7 @@ int pc_params_create(const pc_params_desc* desc, int device, pc_params** out) {
   p->max_batch = desc->max_batch ? desc->max_batch : 1;
   p->max_hoist = max_hoist;
   p->chacha_rounds = rounds;
+  p->partition = desc->partition;
   const uint32_t count = p->L + p->K;
   const uint64_t m = 2ull * p->N;
   if (desc->primes != nullptr) {

@@ -65,7 +65,7 @@ struct DevLevelTables {
 struct pc_params {
   int device = -1;
   uint32_t log2n = 0, N = 0, L = 0, dnum = 0, K = 0;
-  uint32_t max_batch = 1, max_hoist = 1, chacha_rounds = 12;
+  uint32_t max_batch = 1, max_hoist = 1, chacha_rounds = 12, partition = 0;
   std::vector<uint32_t> primes;  // L q-primes then K p-primes
   std::vector<uint32_t> psi;
   // host copies of the tables (always built; uploaded when device >= 0)
@@ -93,6 +93,18 @@ struct pc_params {
 };
 
 namespace pc {
+
+// Digit size and count at a level, and the level of the key that serves it
+// (partition 0: ceil(l/dnum) and l; partition 1: ceil(L/dnum) and L).
+inline int alpha_of(const pc_params* p, uint32_t level) {
+  const uint32_t l = p->partition ? p->L : level;
+  return (int)((l + p->dnum - 1) / p->dnum);
+}
+inline int beta_of(const pc_params* p, uint32_t level) {
+  const int a = alpha_of(p, level);
+  return (int)((level + a - 1) / a);
+}
+inline uint32_t key_level_of(const pc_params* p, uint32_t level) { return p->partition ? p->L : level; }
 
 // Workspace carve-up for a key switch of `items` (ciphertext, key) pairs over a
 // batch of `batch` ciphertexts at level l.

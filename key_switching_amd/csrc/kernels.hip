@@ -373,6 +373,7 @@ struct IPArgs {
   const uint32_t* ext;  // [batch][beta][l+K][N]
   uint32_t* acc;        // [items][2][l+K][N], item = key * batch + b
   int N, level, K, L, alpha, batch, nkeys;
+  int key_level;  // level of the keys (their limbs are [q_0..q_{key_level-1}, p_0..p_{K-1}])
   uint32_t key_base;
   const uint32_t* evk_b[kMaxKeysPerLaunch];
   const uint32_t* evk_a[kMaxKeysPerLaunch];
@@ -381,6 +382,10 @@ struct IPArgs {
 };
 
 __device__ __forceinline__ int pos8(int p0, int p1, int k) { return k < 4 ? p0 + k : p1 + k - 4; }
+
+// Key-basis index of limb j of the extended basis at the ciphertext's level
+// (the q limbs keep their index; the special primes follow the key's own q limbs).
+__device__ __forceinline__ int key_limb(const IPArgs& A, int j) { return j < A.level ? j : A.key_level + (j - A.level); }
 
 __device__ __forceinline__ void load8(const uint32_t* base, int p0, int p1, uint32_t (&v)[8]) {
   const uint4 x = *reinterpret_cast<const uint4*>(&at32(base, p0));
@@ -470,18 +475,20 @@ __global__ void __launch_bounds__(kIpThreads) k_inner_product(IPArgs A) {
   const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
   const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj];
   const uint32_t g = A.galois[key];
+  const int kj = key_limb(A, j);
   uint32_t src_idx[8];
   gather_index(A.N, g, p0, p1, src_idx);
 
   uint32_t bm[BETA][8], am[BETA][8];
 #pragma unroll
   for (int d = 0; d < BETA; ++d) {
-    load_key8(A.evk_b[key] + ((size_t)d * lk + j) * A.N, p0, p1, r, rinv, bm[d]);
+    const size_t kofs = ((size_t)d * (A.key_level + A.K) + kj) * A.N;
+    load_key8(A.evk_b[key] + kofs, p0, p1, r, rinv, bm[d]);
     if constexpr (STORED) {
-      load_key8(A.evk_a[key] + ((size_t)d * lk + j) * A.N, p0, p1, r, rinv, am[d]);
+      load_key8(A.evk_a[key] + kofs, p0, p1, r, rinv, am[d]);
     } else {
       uint32_t w[16];
-      chacha_block<ROUNDS>(A.seed[key], (uint32_t)(p0 >> 3), 0u, (uint32_t)d, (uint32_t)j, w);
+      chacha_block<ROUNDS>(A.seed[key], (uint32_t)(p0 >> 3), 0u, (uint32_t)d, (uint32_t)kj, w);
 #pragma unroll
       for (int k = 0; k < 8; ++k) am[d][k] = word_pair_to_mont(w[2 * k], w[2 * k + 1], r, rinv);
     }
@@ -542,7 +549,7 @@ __global__ void __launch_bounds__(2 * kIpHalf) k_ip_regen(IPArgs A) {
     for (int d = 0; d < BETA; ++d) {
       if (d < d0 || d >= d1) continue;
       uint32_t w[16];
-      chacha_block<ROUNDS>(A.seed[key], (uint32_t)(tile * kIpHalf + t), 0u, (uint32_t)d, (uint32_t)j, w);
+      chacha_block<ROUNDS>(A.seed[key], (uint32_t)(tile * kIpHalf + t), 0u, (uint32_t)d, (uint32_t)key_limb(A, j), w);
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         am_lds[slot][d][4 * hi + (k & 3)][ct0 + (k >> 2)] = word_pair_to_mont(w[2 * k], w[2 * k + 1], r, rinv);
@@ -559,7 +566,8 @@ __global__ void __launch_bounds__(2 * kIpHalf) k_ip_regen(IPArgs A) {
     gather_index(A.N, g, p0, p1, src_idx);
     uint32_t bm[BETA][8];
 #pragma unroll
-    for (int d = 0; d < BETA; ++d) load_key8(A.evk_b[key] + ((size_t)d * lk + j) * A.N, p0, p1, r, rinv, bm[d]);
+    for (int d = 0; d < BETA; ++d)
+      load_key8(A.evk_b[key] + ((size_t)d * (A.key_level + A.K) + key_limb(A, j)) * A.N, p0, p1, r, rinv, bm[d]);
     const int batch = BT ? BT : A.batch;
 #pragma unroll 1
     for (int b = 0; b < batch; ++b) {
@@ -786,12 +794,6 @@ hipError_t launch_ntt(const pc_params* p, uint32_t* data, uint32_t* tmp, const u
   return hipGetLastError();
 }
 
-static int alpha_at(const pc_params* p, uint32_t level) { return (int)((level + p->dnum - 1) / p->dnum); }
-static int beta_at(const pc_params* p, uint32_t level) {
-  const int a = alpha_at(p, level);
-  return (int)((level + a - 1) / a);
-}
-
 hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_offset, uint32_t batch,
                         uint32_t level, const KsWorkspace& ws, hipStream_t s) {
   ModUpArgs A;
@@ -807,8 +809,8 @@ hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stri
   A.level = (int)level;
   A.K = (int)p->K;
   A.L = (int)p->L;
-  A.alpha = alpha_at(p, level);
-  A.beta = beta_at(p, level);
+  A.alpha = alpha_of(p, level);
+  A.beta = beta_of(p, level);
   A.scale_off = p->mu_scale_off[level];
   A.bconv_off = p->mu_bconv_off[level];
   A.batch = (int)batch;
@@ -894,7 +896,7 @@ static void launch_ip_beta(const pc_params* p, const IPArgs& A, uint32_t nkeys, 
 hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_offset,
                                 uint32_t batch, uint32_t level, const KsWorkspace& ws, const KeyRef* keys,
                                 uint32_t nkeys, hipStream_t s) {
-  const int beta = beta_at(p, level);
+  const int beta = beta_of(p, level);
   for (uint32_t base = 0; base < nkeys; base += kMaxKeysPerLaunch) {
     const uint32_t cnt = (nkeys - base) < (uint32_t)kMaxKeysPerLaunch ? (nkeys - base) : kMaxKeysPerLaunch;
     IPArgs A;
@@ -908,9 +910,10 @@ hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t
     A.level = (int)level;
     A.K = (int)p->K;
     A.L = (int)p->L;
-    A.alpha = alpha_at(p, level);
+    A.alpha = alpha_of(p, level);
     A.batch = (int)batch;
     A.nkeys = (int)cnt;
+    A.key_level = (int)key_level_of(p, level);
     A.key_base = base;
     bool stored = false;
     for (uint32_t k = 0; k < cnt; ++k) {

@@ -24,11 +24,15 @@ at level l (l active ciphertext primes) and a key with Galois element k
 6. out0 += the automorphism of c0.
 
 Readings where the pages are silent (all listed in the design notes):
-digits at level l have alpha(l) = ceil(l/dnum) primes each, D_d = [d*alpha,
-min((d+1)*alpha, l)), and the key is generated at level l; a key's limb j is
-indexed in the key basis (q limbs first, then p limbs); the key equation is
-b_d = -a_d s + e_d + g_d s' with g_d = [P]_{q_j} on the q-limbs of D_d and 0
-elsewhere; decryption is c0 + c1 s.
+by default (partition 0) digits at level l have alpha(l) = ceil(l/dnum)
+primes each, D_d = [d*alpha, min((d+1)*alpha, l)), and the key is generated at
+level l; with partition 1 alpha = ceil(L/dnum) at every level, the digits are
+those of the top level cut at l, and one key generated at level L serves every
+level (its limbs q_l..q_{L-1} are not used); a key's limb is indexed in the key
+basis (q limbs first, then p limbs), so at level l limb j of the extended basis
+is key limb j for j < l and key_level + (j - l) for the special primes; the key
+equation is b_d = -a_d s + e_d + g_d s' with g_d = [P]_{q_j} on the q-limbs of
+D_d and 0 elsewhere; decryption is c0 + c1 s.
 """
 
 from __future__ import annotations
@@ -53,6 +57,7 @@ class Params:
     K: int
     primes: tuple = None  # L q-primes then K p-primes; default: the descending rule
     chacha_rounds: int = 12
+    partition: int = 0    # 0: alpha(l) = ceil(l/dnum), key at level l; 1: alpha = ceil(L/dnum), key at level L
 
     def __post_init__(self):
         if self.primes is None:
@@ -79,7 +84,15 @@ class Params:
         return math.prod(self.p)
 
     def alpha(self, level: int) -> int:
-        return -(-level // self.dnum)
+        return -(-(self.L if self.partition else level) // self.dnum)
+
+    def key_level(self, level: int) -> int:
+        """Level of the key that serves ciphertexts at ``level``."""
+        return self.L if self.partition else level
+
+    def key_limb(self, level: int, j: int) -> int:
+        """Key-basis index of limb j of the extended basis at ``level``."""
+        return j if j < level else self.key_level(level) + (j - level)
 
     def digits(self, level: int) -> list:
         """Index lists D_0..D_{beta-1} of the q-limbs at this level."""
@@ -173,8 +186,8 @@ def key_a(prm: Params, key: Key) -> np.ndarray:
 
 def inner_product(prm: Params, ext: np.ndarray, key: Key, level: int) -> np.ndarray:
     """acc [2][l+K][N]: sum over digits of automorphism(ext_d) times (b_d, a_d)."""
-    if key.level != level:
-        raise ValueError("key level must equal the ciphertext level")
+    if key.level != prm.key_level(level):
+        raise ValueError(f"this partition needs a key at level {prm.key_level(level)}")
     basis = prm.basis(level)
     a = key_a(prm, key)
     b = np.asarray(key.b, dtype=U64)
@@ -182,8 +195,9 @@ def inner_product(prm: Params, ext: np.ndarray, key: Key, level: int) -> np.ndar
     for d in range(ext.shape[0]):
         e = automorphism(ext[d], key.galois)
         for j, r in enumerate(basis):
-            acc[0, j] = (acc[0, j] + e[j] * b[d, j] % U64(r)) % U64(r)
-            acc[1, j] = (acc[1, j] + e[j] * a[d, j] % U64(r)) % U64(r)
+            kj = prm.key_limb(level, j)
+            acc[0, j] = (acc[0, j] + e[j] * b[d, kj] % U64(r)) % U64(r)
+            acc[1, j] = (acc[1, j] + e[j] * a[d, kj] % U64(r)) % U64(r)
     return acc
 
 

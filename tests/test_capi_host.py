@@ -51,14 +51,19 @@ def test_host_tables_match_golden(log2n, L, dnum, K):
                 assert tw[k] == pow(psi, e, q)
 
 
+@pytest.mark.parametrize("partition", [0, 1])
 @pytest.mark.parametrize("L,dnum", [(24, 4), (40, 5), (3, 3), (7, 3), (6, 6)])
-def test_digit_partition_matches_oracle(L, dnum):
-    with ksa.Params(12, L, dnum, 2, device=None) as prm:
-        oprm = ks.Params(12, L, dnum, 2, primes=tuple(prm.primes))
+def test_digit_partition_matches_oracle(L, dnum, partition):
+    with ksa.Params(12, L, dnum, 2, device=None, partition=partition) as prm:
+        oprm = ks.Params(12, L, dnum, 2, primes=tuple(prm.primes), partition=partition)
         for level in range(1, L + 1):
             D = oprm.digits(level)
             assert prm.beta(level) == len(D)
-            assert prm.alpha(level) == len(D[0])
+            assert prm.alpha(level) == oprm.alpha(level)
+            assert len(D[0]) == min(oprm.alpha(level), level)
+            assert prm.key_level(level) == oprm.key_level(level)
+            assert prm.key_shape(level) == (len(oprm.digits(oprm.key_level(level))), oprm.key_level(level) + 2,
+                                            oprm.N)
 
 
 def test_user_primes_accepted_and_checked():
@@ -83,6 +88,7 @@ def test_user_primes_accepted_and_checked():
     (dict(log2n=12, L=3, dnum=3, K=1, max_hoist=33), ksa.PC_EUNSUPPORTED),
     (dict(log2n=12, L=3, dnum=3, K=9), ksa.PC_EUNSUPPORTED),
     (dict(log2n=16, L=24, dnum=2, K=6), ksa.PC_EUNSUPPORTED),
+    (dict(log2n=12, L=3, dnum=3, K=1, partition=2), ksa.PC_EINVAL),
 ])
 def test_create_rejects(kw, code):
     with pytest.raises(ksa.PcError) as e:

@@ -53,7 +53,7 @@ def assert_equal(gpu_words, oracle_words, what):
 
 def params_pair(log2n, L, dnum, K, **kw):
     prm = ksa.Params(log2n, L, dnum, K, device=0, **kw)
-    oprm = ks.Params(log2n, L, dnum, K, chacha_rounds=kw.get("chacha_rounds", 12))
+    oprm = ks.Params(log2n, L, dnum, K, chacha_rounds=kw.get("chacha_rounds", 12), partition=kw.get("partition", 0))
     assert tuple(prm.primes) == oprm.primes
     assert tuple(prm.psi) == tuple(rns.find_psi(p, oprm.N) for p in oprm.primes)
     return prm, oprm
@@ -208,6 +208,29 @@ def test_small_ring_levels_and_partitions(level, galois):
     out = host(ksa.keyswitch(prm, dev(ct), dev(key.b), key.seed, level, galois))
     assert_equal(out, ks.keyswitch(oprm, ct, key, level), f"level {level} galois {galois}")
     _decrypts(oprm, ct, out, s, galois, level, emax, 32)
+    prm.close()
+
+
+@pytest.mark.parametrize("level", [7, 5, 4, 2, 1])
+def test_small_ring_top_level_partition(level):
+    """Partition 1: one key generated at L = 7 serves every level (alpha = 3 fixed);
+    batch of 2 under a rotation and the relinearisation key, regenerated and stored a."""
+    prm, oprm = params_pair(12, 7, 3, 3, partition=1, max_batch=2, max_hoist=2)
+    assert prm.key_shape(level) == (3, 10, 4096)
+    s, keys, emax = _real_keys(oprm, 40, 7, (5, 1), 32)
+    cts = ki.ciphertexts(40 + level, oprm.q[:level], oprm.N, 2)
+    kb = [dev(k.b) for k in keys]
+    out = host(ksa.keyswitch_ex(prm, dev(cts), kb, [k.galois for k in keys], level, seeds=[k.seed for k in keys]))
+    for r, key in enumerate(keys):
+        for b in range(2):
+            ref = ks.keyswitch(oprm, cts[b], key, level)
+            assert_equal(out[r, b], ref, f"level {level} key {r} item {b}")
+        _decrypts(oprm, cts[1], out[r, 1], s, key.galois, level, emax, 32)
+    stored = host(ksa.keyswitch_ex(prm, dev(cts), kb, [k.galois for k in keys], level,
+                                   evk_a=[dev(ks.key_a(oprm, k)) for k in keys]))
+    assert_equal(stored, out, f"level {level} stored vs regenerated")
+    single = host(ksa.keyswitch(prm, dev(cts[0]), kb[0], keys[0].seed, level, 5))
+    assert_equal(single, out[0, 0], f"level {level} pc_keyswitch")
     prm.close()
 
 

@@ -125,6 +125,43 @@ def test_hoisted_equals_singles_and_stored_equals_regenerated():
         assert np.array_equal(ks.keyswitch(prm, ct, stored, level), hoisted[r])
 
 
+def test_top_level_partition_serves_every_level():
+    """Partition 1: alpha = ceil(L/dnum) at every level and one key generated at
+    level L; a ciphertext at any lower level key-switches within the bound."""
+    prm = ks.Params(6, 7, 3, 3, partition=1)
+    assert [prm.alpha(l) for l in (7, 5, 2)] == [3, 3, 3]
+    assert prm.digits(5) == [[0, 1, 2], [3, 4]] and prm.digits(2) == [[0, 1]]
+    h = 8
+    s, keys, emax = _keys_and_secret(prm, 31, 7, (5, 1), h)
+    for level in (7, 6, 4, 3, 1):
+        ct = ki.ciphertexts(31, prm.q[:level], prm.N, 1)[0]
+        for key in keys:
+            out = ks.keyswitch(prm, ct, key, level)
+            _check_decrypts(prm, ct, out, s, key.galois, level, emax, h)
+
+
+def test_partitions_agree_at_the_top_level():
+    """At level L both partitions have the same digits and keys: the same bits."""
+    p0, p1 = ks.Params(6, 6, 3, 2), ks.Params(6, 6, 3, 2, partition=1)
+    s, (key,), _ = _keys_and_secret(p0, 32, 6, (5,), 8)
+    ct = ki.ciphertexts(32, p0.q, p0.N, 1)[0]
+    assert np.array_equal(ks.keyswitch(p0, ct, key, 6), ks.keyswitch(p1, ct, key, 6))
+
+
+def test_top_level_partition_needs_the_key_basis_index(monkeypatch):
+    """Reading the special-prime limbs of a top-level key at the ciphertext's own
+    index (as a level-l key would be read) breaks the key switch below L."""
+    prm = ks.Params(6, 6, 3, 2, partition=1)
+    s, (key,), emax = _keys_and_secret(prm, 33, 6, (5,), 8)
+    level = 4
+    ct = ki.ciphertexts(33, prm.q[:level], prm.N, 1)[0]
+    _check_decrypts(prm, ct, ks.keyswitch(prm, ct, key, level), s, 5, level, emax, 8)
+    monkeypatch.setattr(ks.Params, "key_limb", lambda self, level, j: j)
+    out = ks.keyswitch(prm, ct, key, level)
+    e = ks.decryption_error(prm, ct, out, s, 5, level)
+    assert e is None or np.abs(e).max() > ks.error_bound(prm, level, emax, 8)
+
+
 def test_planted_mistakes_fail_the_decryption_check(monkeypatch):
     """Mistakes planted in the oracle (on the CPU) must break the decryption check."""
     prm = small_params(log2n=6, L=4, dnum=2, K=2)
