@@ -216,6 +216,22 @@ def main():
     ksa.profile_begin(prm)
     timed(K8, stored=True)
     kstats_stored = ksa.profile_end(prm)
+
+    # key generation of the same relinearisation key on the GPU (pc_keygen): synthetic
+    # secret / error residues of the right shape (timing does not depend on their values)
+    s_coef = ksa.to_device(ki.uniform_key_b(w.index, 2, 1, basis, w.N)[0], 0)
+    e_coef = ksa.to_device(ki.uniform_key_b(w.index, 3, beta, basis, w.N), 0)
+    kg_out = torch.empty((beta, w.L + w.K, w.N), dtype=torch.int32, device="cuda:0")
+    for _ in range(3):
+        ksa.keygen(prm, seed, w.L, 1, s_coef, e_coef, out=kg_out)
+    torch.cuda.synchronize()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record()
+    for _ in range(10):
+        ksa.keygen(prm, seed, w.L, 1, s_coef, e_coef, out=kg_out)
+    k1.record()
+    torch.cuda.synchronize()
+    ms_kg = k0.elapsed_time(k1) / 10
     kernels_stored = {k: round(1000.0 * t / n, 3) for k, (n, t) in sorted(kstats_stored.items(), key=lambda kv: -kv[1][1])}
     dom = next(iter(kernels))
     roofs = {k: kernel_roofline(k, v["avg_us"], w, K8, beta, alpha) for k, v in kernels.items()}
@@ -261,6 +277,7 @@ def main():
             "k8_stored": {"ks_per_s": round(K8 * 1000.0 / ms8s, 1), "ms_per_call": round(ms8s, 4)},
             "k1_stored": {"ks_per_s": round(1000.0 / ms1s, 1), "ms_per_call": round(ms1s, 4)},
             "k8_chacha_profiled": {"ms_per_call": round(ms8p, 4)},
+            "keygen_relin_key": {"keys_per_s": round(1000.0 / ms_kg, 1), "ms_per_key": round(ms_kg, 4)},
         },
         "kernels": {k: {**{kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()},
                         "hbm_frac": roofs[k]["hbm_frac"], "alu_frac": roofs[k]["alu_frac"]}

@@ -153,6 +153,25 @@ typedef struct {
 } pc_ks_args;
 int pc_keyswitch_ex(const pc_params *p, const pc_ks_args *args, void *stream);
 
+/* Key generation on the GPU (Perseus README, 'What's inside': keys whose a half
+ * is regenerated from a ChaCha12 seed). Writes the b half of a key at key level
+ * `level` (basis q_0..q_{level-1}, p_0..p_{K-1}, lk = level + K limbs) for
+ * Galois element `galois`:
+ *   b_d[j] = -a_d[j] s[j] + e_d[j] + g_{d,j} s'[j]  (mod r_j), evaluation form,
+ * with a_d the expansion of `seed` (the stream pc_keyswitch regenerates),
+ * s' = s^2 for galois 1 (relinearisation) and the automorphism X -> X^galois of
+ * s otherwise, and g_{d,j} = [P]_{q_j} on the q-limbs of digit d (digits of
+ * `level` under the params' partition), 0 elsewhere.
+ *   seed     host, 32 bytes
+ *   s_coef   device [lk][N]: the secret's coefficients as residues mod each r_j
+ *   e_coef   device [beta][lk][N]: digit d's error coefficients, residues mod r_j
+ *   evk_b    device [beta][lk][N] output (beta = digits at `level`)
+ * Uses the params' workspace arena ((beta + 2) lk N words, PC_EINVAL if it is
+ * smaller). Returns PC_EINVAL for null pointers, level outside [1, L] or an even
+ * Galois element or one >= 2N, PC_EDEVICE on launch failure. */
+int pc_keygen(const pc_params *p, const uint8_t *seed, uint32_t level, uint32_t galois, const uint32_t *s_coef,
+              const uint32_t *e_coef, uint32_t *evk_b, void *stream);
+
 /* Debug / parity: limb j (key-basis index at `level`) of digit d of the a half
  * regenerated from seed (32 bytes, host): dst ([N], device) canonical mod r_j. */
 int pc_chacha_expand(const pc_params *p, const uint8_t *seed, uint32_t d, uint32_t j, uint32_t level, uint32_t *dst,

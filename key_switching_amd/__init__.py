@@ -21,8 +21,8 @@ PC_OK, PC_EINVAL, PC_ENOMEM, PC_EDEVICE, PC_EUNSUPPORTED = 0, -1, -2, -3, -4
 PC_GET_N, PC_GET_PRIMES, PC_GET_PSI, PC_GET_ALPHA, PC_GET_BETA, PC_GET_WORKSPACE_BYTES, PC_GET_DEVICE_TABLE = range(1, 8)
 
 EXPORTED = ("pc_params_create", "pc_params_destroy", "pc_params_get", "pc_ntt", "pc_intt", "pc_modup",
-            "pc_keyswitch", "pc_moddown", "pc_keyswitch_ex", "pc_chacha_expand", "pc_profile_begin",
-            "pc_profile_end", "pc_strerror")
+            "pc_keyswitch", "pc_moddown", "pc_keyswitch_ex", "pc_keygen", "pc_chacha_expand",
+            "pc_profile_begin", "pc_profile_end", "pc_strerror")
 
 
 class PcError(RuntimeError):
@@ -71,6 +71,7 @@ def _lib():
         lib.pc_moddown.argtypes = [vp, vp, u32, vp, vp]
         lib.pc_keyswitch_ex.argtypes = [vp, ctypes.POINTER(_KsArgs), vp]
         lib.pc_chacha_expand.argtypes = [vp, ctypes.c_char_p, u32, u32, u32, vp, vp]
+        lib.pc_keygen.argtypes = [vp, ctypes.c_char_p, u32, u32, vp, vp, vp, vp]
         lib.pc_profile_begin.argtypes = [vp]
         lib.pc_profile_end.argtypes = [vp, ctypes.POINTER(_KStat), u32, ctypes.POINTER(u32)]
         lib.pc_strerror.argtypes = [i32]
@@ -295,6 +296,24 @@ def keyswitch_ex(prm: Params, ct, evk_b: Sequence, galois: Sequence[int], level:
         args.workspace = _dev_ptr(workspace, "workspace", None, prm.device)
         args.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(_lib().pc_keyswitch_ex(prm.handle, ctypes.byref(args), _stream()), "pc_keyswitch_ex")
+    return out
+
+
+def keygen(prm: Params, seed: bytes, level: int, galois: int, s_coef, e_coef, out=None):
+    """b half of a key at key level ``level`` for Galois element ``galois`` (pc_keygen).
+
+    s_coef: [level+K][N] residues of the secret's coefficients mod each prime of
+    the key basis; e_coef: [beta][level+K][N] residues of each digit's errors.
+    Returns b [beta][level+K][N]; the a half is the ChaCha expansion of ``seed``.
+    """
+    lk = level + prm.K
+    beta = prm.beta(level)
+    if out is None:
+        out = _new((beta, lk, prm.N), prm.device)
+    _check(_lib().pc_keygen(prm.handle, _seed_bytes(seed), level, galois,
+                            _dev_ptr(s_coef, "s_coef", (lk, prm.N), prm.device),
+                            _dev_ptr(e_coef, "e_coef", (beta, lk, prm.N), prm.device),
+                            _dev_ptr(out, "evk_b", (beta, lk, prm.N), prm.device), _stream()), "pc_keygen")
     return out
 
 

@@ -312,7 +312,7 @@ KsWorkspace ks_workspace_carve(const pc_params* p, void* base, uint32_t level, u
 const char* const kKernelNames[KID_COUNT] = {
     "ntt_fwd_col",     "ntt_fwd_blk",     "ntt_inv_blk",     "ntt_inv_col",   "modup_inv_blk",
     "modup_inv_col",   "modup_bconv",     "modup_fwd_blk",   "inner_product", "moddown_inv_blk",
-    "moddown_inv_col", "moddown_bconv",   "moddown_fwd_blk", "chacha_expand"};
+    "moddown_inv_col", "moddown_bconv",   "moddown_fwd_blk", "chacha_expand", "keygen"};
 
 static hipEvent_t prof_event(const pc_params* p) {
   if (p->prof_used == p->prof_pool.size()) {
@@ -658,6 +658,45 @@ int pc_keyswitch(const pc_params* p, const uint32_t* ct, const uint32_t* evk_b, 
   a.level = level;
   a.out = out;
   return pc_keyswitch_ex(p, &a, stream);
+}
+
+int pc_keygen(const pc_params* p, const uint8_t* seed, uint32_t level, uint32_t galois, const uint32_t* s_coef,
+              const uint32_t* e_coef, uint32_t* evk_b, void* stream) {
+  if (p == nullptr || seed == nullptr || s_coef == nullptr || e_coef == nullptr || evk_b == nullptr) return PC_EINVAL;
+  if (level < 1 || level > p->L) return PC_EINVAL;
+  if ((galois & 1u) == 0 || galois >= 2 * p->N) return PC_EINVAL;
+  if (p->device < 0) return PC_EDEVICE;
+  const uint32_t lk = level + p->K, beta = (uint32_t)beta_of(p, level);
+  const size_t N = p->N;
+  // workspace: s [lk][N], e [beta][lk][N], NTT scratch [beta][lk][N]
+  if ((size_t)(2 * beta + 1) * lk * N * 4 > p->arena_bytes) return PC_EINVAL;
+  uint32_t* ws_s = static_cast<uint32_t*>(p->arena);
+  uint32_t* ws_e = ws_s + (size_t)lk * N;
+  uint32_t* ws_t = ws_e + (size_t)beta * lk * N;
+  uint32_t key[8];
+  for (int w = 0; w < 8; ++w)
+    key[w] = (uint32_t)seed[4 * w] | ((uint32_t)seed[4 * w + 1] << 8) | ((uint32_t)seed[4 * w + 2] << 16) |
+             ((uint32_t)seed[4 * w + 3] << 24);
+  // prime index of every limb of the key basis, per digit block
+  std::vector<uint32_t> pidx((size_t)beta * lk);
+  for (uint32_t d = 0; d < beta; ++d)
+    for (uint32_t j = 0; j < lk; ++j) pidx[(size_t)d * lk + j] = j < level ? j : p->L + (j - level);
+  // [P]_{q_j} 2^32 mod q_j on the q-limbs (the gadget factor of the digit that owns q_j)
+  std::vector<uint32_t> gm(lk, 0);
+  for (uint32_t j = 0; j < level; ++j) {
+    const uint32_t q = p->primes[j];
+    gm[j] = mulmod(prod_mod(p, (int)p->L, (int)(p->L + p->K), -1, q), pow2_32(q), q);
+  }
+  DeviceGuard g(p->device);
+  if (!g.ok) return PC_EDEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(ws_s, s_coef, (size_t)lk * N * 4, hipMemcpyDeviceToDevice, s) != hipSuccess) return PC_EDEVICE;
+  if (hipMemcpyAsync(ws_e, e_coef, (size_t)beta * lk * N * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return PC_EDEVICE;
+  if (launch_ntt(p, ws_s, ws_t, pidx.data(), lk, false, s) != hipSuccess) return PC_EDEVICE;
+  if (launch_ntt(p, ws_e, ws_t, pidx.data(), beta * lk, false, s) != hipSuccess) return PC_EDEVICE;
+  if (launch_keygen(p, key, level, galois, ws_s, ws_e, gm.data(), evk_b, s) != hipSuccess) return PC_EDEVICE;
+  return PC_OK;
 }
 
 int pc_chacha_expand(const pc_params* p, const uint8_t* seed, uint32_t d, uint32_t j, uint32_t level, uint32_t* dst,

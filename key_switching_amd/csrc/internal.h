@@ -142,6 +142,7 @@ enum KernelId {
   KID_MODDOWN_BCONV,
   KID_MODDOWN_FWD_BLK,
   KID_CHACHA_EXPAND,
+  KID_KEYGEN,
   KID_COUNT
 };
 extern const char* const kKernelNames[KID_COUNT];
@@ -169,6 +170,11 @@ hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t
 hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t items, uint32_t polys, uint32_t level,
                           int variant, uint32_t* out, const KsWorkspace& ws, const uint32_t* c0, uint64_t ct_stride,
                           uint32_t batch, const uint32_t* galois_per_key, hipStream_t s);
+// b of a key at `level` from evaluation-form s ([lk][N]) and e ([beta][lk][N]);
+// gm[j] = [P]_{q_j} 2^32 mod q_j (q-limbs).
+hipError_t launch_keygen(const pc_params* p, const uint32_t seed[8], uint32_t level, uint32_t galois,
+                         const uint32_t* s_eval, const uint32_t* e_eval, const uint32_t* gm, uint32_t* evk_b,
+                         hipStream_t s);
 hipError_t launch_chacha_expand(const pc_params* p, const uint32_t seed[8], uint32_t d, uint32_t j,
                                 uint32_t prime_index, uint32_t* dst, hipStream_t s);
 

@@ -733,6 +733,59 @@ __global__ void __launch_bounds__(256) k_chacha_expand(ChaChaKey key, uint32_t d
 }
 
 // ---------------------------------------------------------------------------
+// key generation: b_d[j] = -a_d[j] s[j] + e_d[j] + g_{d,j} s'[j] (mod r_j)
+// One thread per 8 consecutive positions of limb j (one ChaCha block per
+// digit). s'[j] is s^2 (Galois element 1) or s at the automorphism's source
+// index. Products use REDC with Montgomery-form operands: S = s 2^64, so that
+// REDC(a 2^-32 * S) = a s; g 2^32 mod r_j comes precomputed.
+// ---------------------------------------------------------------------------
+struct KeygenArgs {
+  DevTables T;
+  const uint32_t* s;  // [lk][N] evaluation form
+  const uint32_t* e;  // [beta][lk][N] evaluation form
+  uint32_t* b;        // [beta][lk][N]
+  ChaChaKey seed;
+  int N, level, K, L, alpha, beta;
+  uint32_t galois;
+  uint32_t gm[kMaxLimbsPerLaunch];  // [P]_{q_j} 2^32 mod q_j on q-limbs
+};
+
+template <int ROUNDS>
+__global__ void __launch_bounds__(256) k_keygen(KeygenArgs A) {
+  const int j = blockIdx.y, lk = A.level + A.K;
+  const int i0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i0 >= A.N) return;
+  const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
+  const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj], r2 = A.T.r2[pj];
+  const uint32_t* sj = A.s + (size_t)j * A.N;
+  const uint32_t g = A.galois, h = (g - 1) >> 1, mask = (uint32_t)A.N - 1;
+  uint32_t S[8], gs[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t sv = sj[i0 + k];
+    const uint32_t s1 = redc(mul_wide(sv, r2), r, rinv);                   // s 2^32
+    S[k] = redc(mul_wide(s1, r2), r, rinv);                                // s 2^64
+    const uint32_t sp = g == 1u ? redc(mul_wide(sv, s1), r, rinv)          // s^2
+                                : sj[((uint32_t)(i0 + k) * g + h) & mask];  // phi_g(s)
+    gs[k] = redc(mul_wide(sp, A.gm[j]), r, rinv);                          // g s'
+  }
+  for (int d = 0; d < A.beta; ++d) {
+    const bool own = j < A.level && j >= d * A.alpha && j < (d + 1) * A.alpha;
+    uint32_t w[16];
+    chacha_block<ROUNDS>(A.seed, (uint32_t)(i0 >> 3), 0u, (uint32_t)d, (uint32_t)j, w);
+    const uint32_t* ed = A.e + ((size_t)d * lk + j) * A.N + i0;
+    uint32_t* bd = A.b + ((size_t)d * lk + j) * A.N + i0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t am = word_pair_to_mont(w[2 * k], w[2 * k + 1], r, rinv);  // a 2^-32
+      uint32_t t = sub_mod(ed[k], redc(mul_wide(am, S[k]), r, rinv), r);        // e - a s
+      if (own) t = add_mod(t, gs[k], r);
+      bd[k] = t;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 #define PC_DISPATCH_LOGN(logn, ...) \
@@ -974,6 +1027,33 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
     });
     { LaunchTimer tm(p, KID_MODDOWN_FWD_BLK, s); hipLaunchKernelGGL(k_md_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_q), dim3(blk_threads<LN>()), 0, s, A); }
   });
+  return hipGetLastError();
+}
+
+hipError_t launch_keygen(const pc_params* p, const uint32_t seed[8], uint32_t level, uint32_t galois,
+                         const uint32_t* s_eval, const uint32_t* e_eval, const uint32_t* gm, uint32_t* evk_b,
+                         hipStream_t s) {
+  KeygenArgs A;
+  A.T = p->tabs;
+  A.s = s_eval;
+  A.e = e_eval;
+  A.b = evk_b;
+  for (int w = 0; w < 8; ++w) A.seed.k[w] = seed[w];
+  A.N = (int)p->N;
+  A.level = (int)level;
+  A.K = (int)p->K;
+  A.L = (int)p->L;
+  A.alpha = alpha_of(p, level);
+  A.beta = beta_of(p, level);
+  A.galois = galois;
+  const uint32_t lk = level + p->K;
+  for (uint32_t j = 0; j < (uint32_t)kMaxLimbsPerLaunch; ++j) A.gm[j] = j < lk ? gm[j] : 0u;
+  const dim3 grid((p->N / 8 + 255) / 256, lk);
+  LaunchTimer tm(p, KID_KEYGEN, s);
+  if (p->chacha_rounds == 20)
+    hipLaunchKernelGGL(k_keygen<20>, grid, dim3(256), 0, s, A);
+  else
+    hipLaunchKernelGGL(k_keygen<12>, grid, dim3(256), 0, s, A);
   return hipGetLastError();
 }
 

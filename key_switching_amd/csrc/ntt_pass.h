@@ -159,6 +159,70 @@ __device__ __forceinline__ void gs_round(uint32_t (&v)[1 << LOGE], int round, in
   }
 }
 
+// A round's twiddles gathered up front: W holds the run of every stage of the
+// round (forward stage sl at [2^sl - 1, 2^(sl+1) - 1); inverse stage ul, whose
+// run has E/2^(ul+1) entries, after the runs of the stages before it), so a
+// pass can issue the loads of a later round before an earlier one computes.
+template <int LOGR, int LOGE, bool GS, class TwBase>
+__device__ __forceinline__ void load_round_tw(int round, int t, const uint32_t* __restrict__ tw, TwBase twbase,
+                                              uint32_t (&W)[(1 << LOGE) - 1]) {
+  constexpr int E = 1 << LOGE;
+  const int lo = pass_lo<LOGR, LOGE, GS>(round);
+  const int thigh = t >> lo;
+  int off = 0;
+#pragma unroll
+  for (int st = 0; st < LOGE; ++st) {
+    const int n = GS ? E >> (st + 1) : 1 << st;
+    const int base = GS ? twbase(round * LOGE + st) + (thigh << (LOGE - st - 1))
+                        : twbase(round * LOGE + st) + (thigh << st);
+    load_run(tw + base, n, W + off);
+    off += n;
+  }
+}
+
+// The butterflies of ct_round / gs_round with the round's twiddles in W.
+template <int LOGE>
+__device__ __forceinline__ void ct_round_w(uint32_t (&v)[1 << LOGE], const uint32_t (&W)[(1 << LOGE) - 1],
+                                           uint32_t r, uint32_t rinv) {
+  constexpr int E = 1 << LOGE;
+#pragma unroll
+  for (int sl = 0; sl < LOGE; ++sl) {
+    const int half = E >> (sl + 1), off = (1 << sl) - 1;
+#pragma unroll
+    for (int g = 0; g < (1 << sl); ++g)
+#pragma unroll
+      for (int j = 0; j < half; ++j) {
+        const int m0 = g * 2 * half + j;
+        const uint32_t u = v[m0];
+        const uint32_t x = mul_mont(v[m0 + half], W[off + g], r, rinv);
+        v[m0] = add_mod(u, x, r);
+        v[m0 + half] = sub_mod(u, x, r);
+      }
+  }
+}
+
+template <int LOGE>
+__device__ __forceinline__ void gs_round_w(uint32_t (&v)[1 << LOGE], const uint32_t (&W)[(1 << LOGE) - 1],
+                                           uint32_t r, uint32_t rinv) {
+  constexpr int E = 1 << LOGE;
+  int off = 0;
+#pragma unroll
+  for (int ul = 0; ul < LOGE; ++ul) {
+    const int half = 1 << ul, groups = E >> (ul + 1);
+#pragma unroll
+    for (int g = 0; g < groups; ++g)
+#pragma unroll
+      for (int j = 0; j < half; ++j) {
+        const int m0 = g * 2 * half + j;
+        const uint32_t a = v[m0];
+        const uint32_t b = v[m0 + half];
+        v[m0] = add_mod(a, b, r);
+        v[m0 + half] = mul_mont(sub_mod(a, b, r), W[off + g], r, rinv);
+      }
+    off += groups;
+  }
+}
+
 // Exchange the register tile between two round layouts through LDS; Col maps
 // an element index to its word in the row.
 struct IdentityCol {
@@ -245,10 +309,15 @@ __device__ __forceinline__ void fwd_blk_compute(uint32_t (&v)[1 << LOGE], uint32
                                                 uint32_t r, uint32_t rinv, const uint32_t* __restrict__ tw) {
   constexpr int ROUNDS = LOGRB / LOGE;
   auto twb = [B](int s) { return (B << LOGRB) + (1 << s); };  // block-major table
+  // every round's twiddles are requested before the first butterfly, so the
+  // later rounds' loads are not waited for after the exchange
+  uint32_t W[ROUNDS][(1 << LOGE) - 1];
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) load_round_tw<LOGRB, LOGE, false>(rd, t, tw, twb, W[rd]);
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRB, LOGE, false, BlkLds<LOGRB, LOGE>>(v, lds_row, rd - 1, t);
-    ct_round<LOGRB, LOGE>(v, rd, t, r, rinv, tw, twb);
+    ct_round_w<LOGE>(v, W[rd], r, rinv);
   }
 }
 
@@ -257,10 +326,13 @@ __device__ __forceinline__ void inv_blk_compute(uint32_t (&v)[1 << LOGE], uint32
                                                 uint32_t r, uint32_t rinv, const uint32_t* __restrict__ tw) {
   constexpr int ROUNDS = LOGRB / LOGE;
   auto twb = [B](int u) { return (B << LOGRB) + (1 << (LOGRB - u - 1)); };  // block-major table
+  uint32_t W[ROUNDS][(1 << LOGE) - 1];
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) load_round_tw<LOGRB, LOGE, true>(rd, t, tw, twb, W[rd]);
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRB, LOGE, true, BlkLds<LOGRB, LOGE>>(v, lds_row, rd - 1, t);
-    gs_round<LOGRB, LOGE>(v, rd, t, r, rinv, tw, twb);
+    gs_round_w<LOGE>(v, W[rd], r, rinv);
   }
 }
 

@@ -131,6 +131,12 @@ def test_compute_calls_validate_before_touching_a_device():
         assert lib.pc_keyswitch_ex(h, ctypes.byref(args), None) == ksa.PC_EDEVICE
         args.seeds = None
         assert lib.pc_keyswitch_ex(h, ctypes.byref(args), None) == ksa.PC_EINVAL
+        # pc_keygen: arguments first, then the device
+        assert lib.pc_keygen(h, None, 3, 1, dummy, dummy, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_keygen(h, seed, 3, 1, None, dummy, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_keygen(h, seed, 4, 1, dummy, dummy, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_keygen(h, seed, 3, 6, dummy, dummy, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_keygen(h, seed, 3, 5, dummy, dummy, dummy, None) == ksa.PC_EDEVICE
         # params_get argument checks
         buf = (ctypes.c_uint32 * 4)()
         assert lib.pc_params_get(h, ksa.PC_GET_PRIMES, 0, buf, 12) == ksa.PC_EINVAL

@@ -234,6 +234,40 @@ def test_small_ring_top_level_partition(level):
     prm.close()
 
 
+def _keygen_inputs(oprm, widx, level, s):
+    """Residues of the secret and of each digit's errors over the key basis (test-side marshalling)."""
+    basis = oprm.basis(level)
+    errs = ki.gaussian_errors(widx, 0, len(oprm.digits(level)), oprm.N)
+    s_coef = np.stack([rns.to_residues(s, r) for r in basis])
+    e_coef = np.stack([np.stack([rns.to_residues(errs[d], r) for r in basis]) for d in range(len(errs))])
+    return errs, s_coef, e_coef
+
+
+@pytest.mark.parametrize("log2n,L,dnum,K,level,galois,partition,h", [
+    (12, 3, 3, 1, 3, 5, 0, 64),        # the tiny rotation key
+    (12, 7, 3, 3, 5, 25, 0, 32),       # a rotation key below the top level
+    (12, 7, 3, 3, 7, 1, 1, 32),        # the top-level key of partition 1 (relinearisation)
+    (16, 24, 4, 6, 24, 1, 0, 192),     # the full-size relinearisation key
+])
+def test_keygen_matches_oracle(log2n, L, dnum, K, level, galois, partition, h):
+    """pc_keygen against the oracle's key generation, bit for bit; the GPU key then
+    drives a GPU key switch that decrypts within the bound."""
+    prm, oprm = params_pair(log2n, L, dnum, K, partition=partition)
+    widx = 50 + level
+    s = ki.ternary_secret(widx, oprm.N, h)
+    errs, s_coef, e_coef = _keygen_inputs(oprm, widx, level, s)
+    seed = ki.key_seed(widx, 3)
+    key = ks.keygen(oprm, s, errs, seed, level, galois)
+    b = host(ksa.keygen(prm, seed, level, galois, dev(s_coef), dev(e_coef)))
+    assert_equal(b, key.b, f"key b, level {level} galois {galois}")
+    ct_level = level if partition == 0 else max(1, level - 2)
+    ct = ki.ciphertexts(widx, oprm.q[:ct_level], oprm.N, 1)[0]
+    out = host(ksa.keyswitch(prm, dev(ct), dev(b), seed, ct_level, galois))
+    assert_equal(out, ks.keyswitch(oprm, ct, key, ct_level), "key switch with the GPU key")
+    _decrypts(oprm, ct, out, s, galois, ct_level, int(np.abs(errs).max()), h)
+    prm.close()
+
+
 def test_headline_n16_relinearisation_k1_k8():
     """N=2^16, L=24, dnum=4, K=6, relinearisation key, k=1 and k=8."""
     w = ki.WORKLOADS["n16"]
