@@ -172,6 +172,41 @@ int pc_keyswitch_ex(const pc_params *p, const pc_ks_args *args, void *stream);
 int pc_keygen(const pc_params *p, const uint8_t *seed, uint32_t level, uint32_t galois, const uint32_t *s_coef,
               const uint32_t *e_coef, uint32_t *evk_b, void *stream);
 
+/* Homomorphic multiplication around the key switch (Perseus README, 'What's
+ * inside': squaring a ciphertext is one of the session's ops; the pages leave
+ * its steps to the textbook RNS-CKKS product). Ciphertexts are in evaluation
+ * form, 256-byte aligned device buffers owned by the caller; no input may alias
+ * an output. All three run on `stream` (hipStream_t or NULL) and return PC_OK,
+ * PC_EINVAL for null pointers or sizes out of range, PC_EDEVICE on launch
+ * failure or a host-only params.
+ *
+ * pc_tensor: per limb i and position, d0 = a0 b0, d1 = a0 b1 + a1 b0,
+ * d2 = a1 b1 (mod q_i).
+ *   ct_a, ct_b  device [batch][2][level][N]   (1 <= batch <= max_batch)
+ *   d           device [batch][3][level][N]   (d0, d1, d2) */
+int pc_tensor(const pc_params *p, const uint32_t *ct_a, const uint32_t *ct_b, uint32_t batch, uint32_t level,
+              uint32_t *d, void *stream);
+
+/* pc_rescale: divides by the last prime q_{l-1} (l = level >= 2), rounding to
+ * nearest: with x the coefficients of limb l-1 centred into (-q_{l-1}/2,
+ * q_{l-1}/2], limb i < l-1 becomes (c_i - NTT_i(x mod q_i)) q_{l-1}^-1 mod q_i.
+ *   ct   device [batch][2][level][N]
+ *   out  device [batch][2][level-1][N]
+ * Uses the params' workspace arena. */
+int pc_rescale(const pc_params *p, const uint32_t *ct, uint32_t batch, uint32_t level, uint32_t *out, void *stream);
+
+/* pc_hmult: tensor product, relinearisation of d2 with the key of s^2
+ * (Galois element 1; its a half regenerated from evk_seed as in pc_keyswitch),
+ * then pc_rescale: out = rescale(d0 + KS_0(d2), d1 + KS_1(d2)).
+ *   ct_a, ct_b  device [batch][2][level][N], 2 <= level <= L
+ *   evk_b       device b half of the key (shape as in pc_keyswitch_ex)
+ *   evk_seed    host, 32 bytes
+ *   out         device [batch][2][level-1][N]
+ * Uses the params' workspace arena (sized at create for level L and
+ * max_batch). */
+int pc_hmult(const pc_params *p, const uint32_t *ct_a, const uint32_t *ct_b, uint32_t batch, const uint32_t *evk_b,
+             const uint8_t *evk_seed, uint32_t level, uint32_t *out, void *stream);
+
 /* Debug / parity: limb j (key-basis index at `level`) of digit d of the a half
  * regenerated from seed (32 bytes, host): dst ([N], device) canonical mod r_j. */
 int pc_chacha_expand(const pc_params *p, const uint8_t *seed, uint32_t d, uint32_t j, uint32_t level, uint32_t *dst,

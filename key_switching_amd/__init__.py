@@ -21,7 +21,8 @@ PC_OK, PC_EINVAL, PC_ENOMEM, PC_EDEVICE, PC_EUNSUPPORTED = 0, -1, -2, -3, -4
 PC_GET_N, PC_GET_PRIMES, PC_GET_PSI, PC_GET_ALPHA, PC_GET_BETA, PC_GET_WORKSPACE_BYTES, PC_GET_DEVICE_TABLE = range(1, 8)
 
 EXPORTED = ("pc_params_create", "pc_params_destroy", "pc_params_get", "pc_ntt", "pc_intt", "pc_modup",
-            "pc_keyswitch", "pc_moddown", "pc_keyswitch_ex", "pc_keygen", "pc_chacha_expand",
+            "pc_keyswitch", "pc_moddown", "pc_keyswitch_ex", "pc_keygen", "pc_tensor", "pc_rescale",
+            "pc_hmult", "pc_chacha_expand",
             "pc_profile_begin", "pc_profile_end", "pc_strerror")
 
 
@@ -72,6 +73,9 @@ def _lib():
         lib.pc_keyswitch_ex.argtypes = [vp, ctypes.POINTER(_KsArgs), vp]
         lib.pc_chacha_expand.argtypes = [vp, ctypes.c_char_p, u32, u32, u32, vp, vp]
         lib.pc_keygen.argtypes = [vp, ctypes.c_char_p, u32, u32, vp, vp, vp, vp]
+        lib.pc_tensor.argtypes = [vp, vp, vp, u32, u32, vp, vp]
+        lib.pc_rescale.argtypes = [vp, vp, u32, u32, vp, vp]
+        lib.pc_hmult.argtypes = [vp, vp, vp, u32, vp, ctypes.c_char_p, u32, vp, vp]
         lib.pc_profile_begin.argtypes = [vp]
         lib.pc_profile_end.argtypes = [vp, ctypes.POINTER(_KStat), u32, ctypes.POINTER(u32)]
         lib.pc_strerror.argtypes = [i32]
@@ -314,6 +318,54 @@ def keygen(prm: Params, seed: bytes, level: int, galois: int, s_coef, e_coef, ou
                             _dev_ptr(s_coef, "s_coef", (lk, prm.N), prm.device),
                             _dev_ptr(e_coef, "e_coef", (beta, lk, prm.N), prm.device),
                             _dev_ptr(out, "evk_b", (beta, lk, prm.N), prm.device), _stream()), "pc_keygen")
+    return out
+
+
+def _batched(t):
+    """A [2][l][N] ciphertext as a batch of one (a view); [batch][2][l][N] unchanged."""
+    return t.unsqueeze(0) if hasattr(t, "dim") and t.dim() == 3 else t
+
+
+def tensor(prm: Params, ct_a, ct_b, level: int, out=None):
+    """(d0, d1, d2) = (a0 b0, a0 b1 + a1 b0, a1 b1) per limb (pc_tensor).
+
+    ct_a, ct_b: [batch][2][level][N] (or [2][level][N]); returns [batch][3][level][N].
+    """
+    ct_a, ct_b = _batched(ct_a), _batched(ct_b)
+    batch = int(ct_a.shape[0])
+    if out is None:
+        out = _new((batch, 3, level, prm.N), prm.device)
+    _check(_lib().pc_tensor(prm.handle, _dev_ptr(ct_a, "ct_a", (batch, 2, level, prm.N), prm.device),
+                            _dev_ptr(ct_b, "ct_b", (batch, 2, level, prm.N), prm.device), batch, level,
+                            _dev_ptr(out, "d", (batch, 3, level, prm.N), prm.device), _stream()), "pc_tensor")
+    return out
+
+
+def rescale(prm: Params, ct, level: int, out=None):
+    """Divide by the last prime, rounded (pc_rescale): [batch][2][level][N] -> [batch][2][level-1][N]."""
+    ct = _batched(ct)
+    batch = int(ct.shape[0])
+    if out is None:
+        out = _new((batch, 2, level - 1, prm.N), prm.device)
+    _check(_lib().pc_rescale(prm.handle, _dev_ptr(ct, "ct", (batch, 2, level, prm.N), prm.device), batch, level,
+                             _dev_ptr(out, "out", (batch, 2, level - 1, prm.N), prm.device), _stream()),
+           "pc_rescale")
+    return out
+
+
+def hmult(prm: Params, ct_a, ct_b, evk_b, seed: bytes, level: int, out=None):
+    """Tensor, relinearise with the key of s^2 (b half evk_b, a half from seed), rescale (pc_hmult).
+
+    ct_a, ct_b: [batch][2][level][N]; returns [batch][2][level-1][N].
+    """
+    ct_a, ct_b = _batched(ct_a), _batched(ct_b)
+    batch = int(ct_a.shape[0])
+    if out is None:
+        out = _new((batch, 2, level - 1, prm.N), prm.device)
+    _check(_lib().pc_hmult(prm.handle, _dev_ptr(ct_a, "ct_a", (batch, 2, level, prm.N), prm.device),
+                           _dev_ptr(ct_b, "ct_b", (batch, 2, level, prm.N), prm.device), batch,
+                           _dev_ptr(evk_b, "evk_b", prm.key_shape(level), prm.device), _seed_bytes(seed), level,
+                           _dev_ptr(out, "out", (batch, 2, level - 1, prm.N), prm.device), _stream()), "pc_hmult")
     return out
 
 

@@ -223,6 +223,19 @@ int build_tables(pc_params* p) {
       p->h_md_pinvp[v * L + i] = shoup(pinv, qi);
     }
   }
+  // rescale tables: row l' = level - 1 (1 <= l' < L), entry i < l'
+  p->h_rs_qlmod.assign((size_t)L * L, 0);
+  p->h_rs_inv.assign((size_t)L * L, 0);
+  p->h_rs_invp.assign((size_t)L * L, 0);
+  for (uint32_t lp = 1; lp < L; ++lp) {
+    const uint32_t ql = p->primes[lp];
+    for (uint32_t i = 0; i < lp; ++i) {
+      const uint32_t qi = p->primes[i], m = ql % qi, inv = invmod(m, qi);
+      p->h_rs_qlmod[(size_t)lp * L + i] = m;
+      p->h_rs_inv[(size_t)lp * L + i] = inv;
+      p->h_rs_invp[(size_t)lp * L + i] = shoup(inv, qi);
+    }
+  }
   return PC_OK;
 }
 
@@ -309,10 +322,22 @@ KsWorkspace ks_workspace_carve(const pc_params* p, void* base, uint32_t level, u
   return w;
 }
 
+// Workspace of a homomorphic multiplication of `batch` pairs at level l: the
+// tensor [batch][3][l][N] (d0, d2, d1), the relinearised pair
+// [batch][2][l][N], then the key switch's own workspace, whose start the
+// rescale reuses afterwards for x [2 batch][N] and tmp [2 batch][l-1][N].
+size_t hm_workspace_bytes(const pc_params* p, uint32_t level, uint32_t batch) {
+  const size_t N = p->N, l = level;
+  const size_t ks = ks_workspace_bytes(p, level, batch, batch);
+  const size_t rs = align256(2 * batch * N * 4) + align256(2 * batch * (l - 1) * N * 4);
+  return align256(batch * 3 * l * N * 4) + align256(batch * 2 * l * N * 4) + std::max(ks, rs);
+}
+
 const char* const kKernelNames[KID_COUNT] = {
-    "ntt_fwd_col",     "ntt_fwd_blk",     "ntt_inv_blk",     "ntt_inv_col",   "modup_inv_blk",
-    "modup_inv_col",   "modup_bconv",     "modup_fwd_blk",   "inner_product", "moddown_inv_blk",
-    "moddown_inv_col", "moddown_bconv",   "moddown_fwd_blk", "chacha_expand", "keygen"};
+    "ntt_fwd_col",     "ntt_fwd_blk",     "ntt_inv_blk",     "ntt_inv_col",    "modup_inv_blk",
+    "modup_inv_col",   "modup_bconv",     "modup_fwd_blk",   "inner_product",  "moddown_inv_blk",
+    "moddown_inv_col", "moddown_bconv",   "moddown_fwd_blk", "chacha_expand",  "keygen",
+    "tensor",          "rescale_gather",  "rescale_col",     "rescale_blk"};
 
 static hipEvent_t prof_event(const pc_params* p) {
   if (p->prof_used == p->prof_pool.size()) {
@@ -335,6 +360,29 @@ LaunchTimer::~LaunchTimer() {
     hipEvent_t stop = prof_event(p);
     if (stop && hipEventRecord(stop, s) == hipSuccess) p->prof_recs.push_back({kernel, start, stop});
   }
+}
+
+// ModUp, inner product and ModDown of `batch` ciphertexts (c0 of ciphertext z
+// at ct + z ct_stride, c1 at + c1_off) under `nkeys` keys; out is
+// [nkeys][batch][2][l][N] and the workspace at `base` is carved for
+// (level, batch, nkeys * batch).
+hipError_t launch_keyswitch(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_off,
+                            uint32_t batch, uint32_t level, const KeyRef* keys, uint32_t nkeys,
+                            const uint32_t* galois, void* base, uint32_t* out, hipStream_t s) {
+  const KsWorkspace ws = ks_workspace_carve(p, base, level, batch, nkeys * batch);
+  hipError_t e = launch_modup(p, ct, ct_stride, c1_off, batch, level, ws, s);
+  if (e != hipSuccess) return e;
+  e = launch_inner_product(p, ct, ct_stride, c1_off, batch, level, ws, keys, nkeys, s);
+  if (e != hipSuccess) return e;
+  const size_t lk = level + p->K;
+  for (uint32_t k0 = 0; k0 < nkeys; k0 += kMaxKeysPerLaunch) {
+    const uint32_t nk = std::min<uint32_t>(kMaxKeysPerLaunch, nkeys - k0);
+    const size_t item0 = (size_t)k0 * batch;
+    e = launch_moddown(p, ws.acc + item0 * 2 * lk * p->N, nk * batch, 2, level, 1, out + item0 * 2 * level * p->N,
+                       ws, ct, ct_stride, batch, galois + k0, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace pc
@@ -421,7 +469,8 @@ int pc_params_create(const pc_params_desc* desc, int device, pc_params** out) {
       return rc;
     }
     const size_t ks = ks_workspace_bytes(p, p->L, p->max_batch, p->max_batch * p->max_hoist);
-    p->arena_bytes = std::max<size_t>(ks, (size_t)2 * count * p->N * 4);
+    const size_t hm = p->L >= 2 ? hm_workspace_bytes(p, p->L, p->max_batch) : 0;
+    p->arena_bytes = std::max<size_t>(std::max(ks, hm), (size_t)2 * count * p->N * 4);
     if (hipMalloc(&p->arena, p->arena_bytes) != hipSuccess) {
       (void)hipFree(p->d_tables);
       delete p;
@@ -621,23 +670,10 @@ int pc_keyswitch_ex(const pc_params* p, const pc_ks_args* a, void* stream) {
   }
   DeviceGuard g(p->device);
   if (!g.ok) return PC_EDEVICE;
-  hipStream_t s = (hipStream_t)stream;
-  const KsWorkspace ws = ks_workspace_carve(p, base, a->level, a->batch, items);
   const uint64_t ct_stride = 2ull * a->level * p->N;
-  const uint32_t c1_off = a->level * p->N;
-  if (launch_modup(p, a->ct, ct_stride, c1_off, a->batch, a->level, ws, s) != hipSuccess) return PC_EDEVICE;
-  if (launch_inner_product(p, a->ct, ct_stride, c1_off, a->batch, a->level, ws, keys.data(), a->nkeys, s) !=
-      hipSuccess)
+  if (launch_keyswitch(p, a->ct, ct_stride, a->level * p->N, a->batch, a->level, keys.data(), a->nkeys, a->galois,
+                       base, a->out, (hipStream_t)stream) != hipSuccess)
     return PC_EDEVICE;
-  const size_t lk = a->level + p->K;
-  for (uint32_t k0 = 0; k0 < a->nkeys; k0 += kMaxKeysPerLaunch) {
-    const uint32_t nk = std::min<uint32_t>(kMaxKeysPerLaunch, a->nkeys - k0);
-    const size_t item0 = (size_t)k0 * a->batch;
-    if (launch_moddown(p, ws.acc + item0 * 2 * lk * p->N, nk * a->batch, 2, a->level, 1,
-                       a->out + item0 * 2 * a->level * p->N, ws, a->ct, ct_stride, a->batch, a->galois + k0,
-                       s) != hipSuccess)
-      return PC_EDEVICE;
-  }
   return PC_OK;
 }
 
@@ -696,6 +732,74 @@ int pc_keygen(const pc_params* p, const uint8_t* seed, uint32_t level, uint32_t 
   if (launch_ntt(p, ws_s, ws_t, pidx.data(), lk, false, s) != hipSuccess) return PC_EDEVICE;
   if (launch_ntt(p, ws_e, ws_t, pidx.data(), beta * lk, false, s) != hipSuccess) return PC_EDEVICE;
   if (launch_keygen(p, key, level, galois, ws_s, ws_e, gm.data(), evk_b, s) != hipSuccess) return PC_EDEVICE;
+  return PC_OK;
+}
+
+int pc_tensor(const pc_params* p, const uint32_t* ct_a, const uint32_t* ct_b, uint32_t batch, uint32_t level,
+              uint32_t* d, void* stream) {
+  if (p == nullptr || ct_a == nullptr || ct_b == nullptr || d == nullptr) return PC_EINVAL;
+  if (level < 1 || level > p->L || batch < 1 || batch > p->max_batch) return PC_EINVAL;
+  if (p->device < 0) return PC_EDEVICE;
+  DeviceGuard g(p->device);
+  if (!g.ok) return PC_EDEVICE;
+  const uint64_t ln = (uint64_t)level * p->N;
+  const uint64_t off[3] = {0, ln, 2 * ln};
+  if (launch_tensor(p, ct_a, 2 * ln, ct_b, 2 * ln, batch, level, d, 3 * ln, off, (hipStream_t)stream) != hipSuccess)
+    return PC_EDEVICE;
+  return PC_OK;
+}
+
+int pc_rescale(const pc_params* p, const uint32_t* ct, uint32_t batch, uint32_t level, uint32_t* out, void* stream) {
+  if (p == nullptr || ct == nullptr || out == nullptr) return PC_EINVAL;
+  if (level < 2 || level > p->L || batch < 1 || batch > p->max_batch) return PC_EINVAL;
+  if (p->device < 0) return PC_EDEVICE;
+  const size_t N = p->N;
+  uint32_t* x = static_cast<uint32_t*>(p->arena);
+  uint32_t* tmp = x + align256(2 * batch * N * 4) / 4;
+  if (align256(2 * batch * N * 4) + (size_t)2 * batch * (level - 1) * N * 4 > p->arena_bytes) return PC_EINVAL;
+  DeviceGuard g(p->device);
+  if (!g.ok) return PC_EDEVICE;
+  const uint64_t ln = (uint64_t)level * N;
+  if (launch_rescale(p, ct, 2 * ln, (uint32_t)ln, nullptr, 0, batch, level, x, tmp, out, (hipStream_t)stream) !=
+      hipSuccess)
+    return PC_EDEVICE;
+  return PC_OK;
+}
+
+int pc_hmult(const pc_params* p, const uint32_t* ct_a, const uint32_t* ct_b, uint32_t batch, const uint32_t* evk_b,
+             const uint8_t* evk_seed, uint32_t level, uint32_t* out, void* stream) {
+  if (p == nullptr || ct_a == nullptr || ct_b == nullptr || evk_b == nullptr || evk_seed == nullptr || out == nullptr)
+    return PC_EINVAL;
+  if (level < 2 || level > p->L || batch < 1 || batch > p->max_batch) return PC_EINVAL;
+  if (p->device < 0) return PC_EDEVICE;
+  if (hm_workspace_bytes(p, level, batch) > p->arena_bytes) return PC_EINVAL;
+  KeyRef key;
+  key.b = evk_b;
+  key.a = nullptr;
+  for (int w = 0; w < 8; ++w) {
+    const uint8_t* sb = evk_seed + 4 * w;
+    key.seed[w] = (uint32_t)sb[0] | ((uint32_t)sb[1] << 8) | ((uint32_t)sb[2] << 16) | ((uint32_t)sb[3] << 24);
+  }
+  key.galois = 1;
+  const uint32_t one = 1;
+  const size_t N = p->N, l = level;
+  const uint64_t ln = (uint64_t)l * N;
+  uint8_t* c = static_cast<uint8_t*>(p->arena);
+  uint32_t* T = reinterpret_cast<uint32_t*>(c);  // [batch][3][l][N]: d0, d2, d1
+  c += align256(batch * 3 * ln * 4);
+  uint32_t* R = reinterpret_cast<uint32_t*>(c);  // [batch][2][l][N]: relinearised (d0, d2) without d1
+  c += align256(batch * 2 * ln * 4);
+  uint32_t* x = reinterpret_cast<uint32_t*>(c);
+  uint32_t* tmp = x + align256(2 * batch * N * 4) / 4;
+  DeviceGuard g(p->device);
+  if (!g.ok) return PC_EDEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  const uint64_t off[3] = {0, 2 * ln, ln};
+  if (launch_tensor(p, ct_a, 2 * ln, ct_b, 2 * ln, batch, level, T, 3 * ln, off, s) != hipSuccess) return PC_EDEVICE;
+  if (launch_keyswitch(p, T, 3 * ln, (uint32_t)ln, batch, level, &key, 1, &one, c, R, s) != hipSuccess)
+    return PC_EDEVICE;
+  if (launch_rescale(p, R, 2 * ln, (uint32_t)ln, T + 2 * ln, 3 * ln, batch, level, x, tmp, out, s) != hipSuccess)
+    return PC_EDEVICE;
   return PC_OK;
 }
 

@@ -75,6 +75,8 @@ struct pc_params {
   std::vector<uint32_t> h_mu_scale, h_mu_scalep, h_mu_bconv;
   std::vector<size_t> mu_scale_off, mu_bconv_off;  // by level (index l, 1..L)
   std::vector<uint32_t> h_md_scale, h_md_scalep, h_md_bconv, h_md_pinv, h_md_pinvp;
+  // rescale by q_{l'} (row l' = level - 1, entry i < l'): q_{l'} mod q_i, q_{l'}^-1 mod q_i, its Shoup companion
+  std::vector<uint32_t> h_rs_qlmod, h_rs_inv, h_rs_invp;  // [L][L]
   // device state
   void* d_tables = nullptr;  // one allocation holding every table
   pc::DevTables tabs{};
@@ -143,6 +145,10 @@ enum KernelId {
   KID_MODDOWN_FWD_BLK,
   KID_CHACHA_EXPAND,
   KID_KEYGEN,
+  KID_TENSOR,
+  KID_RESCALE_GATHER,
+  KID_RESCALE_COL,
+  KID_RESCALE_BLK,
   KID_COUNT
 };
 extern const char* const kKernelNames[KID_COUNT];
@@ -175,6 +181,20 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
 hipError_t launch_keygen(const pc_params* p, const uint32_t seed[8], uint32_t level, uint32_t galois,
                          const uint32_t* s_eval, const uint32_t* e_eval, const uint32_t* gm, uint32_t* evk_b,
                          hipStream_t s);
+// Tensor product of `batch` ciphertext pairs at `level` (evaluation form):
+// pair z reads a + z a_stride and b + z b_stride ([2][l][N] each) and writes
+// d_k at d + z d_stride + d_off[k] ([l][N]) for d0 = a0 b0, d1 = a0 b1 + a1 b0,
+// d2 = a1 b1.
+hipError_t launch_tensor(const pc_params* p, const uint32_t* a, uint64_t a_stride, const uint32_t* b,
+                         uint64_t b_stride, uint32_t batch, uint32_t level, uint32_t* d, uint64_t d_stride,
+                         const uint64_t d_off[3], hipStream_t s);
+// Rescale of `batch` ciphertexts at `level` by their last prime: polynomial v
+// of ciphertext b at c + b c_stride + v c1_off ([l][N]); when add1 is non-null,
+// add1 + b add_stride ([l][N]) is added to polynomial 1 first. x ([2 batch][N])
+// and tmp ([2 batch][l-1][N]) are workspace; out is [batch][2][l-1][N].
+hipError_t launch_rescale(const pc_params* p, const uint32_t* c, uint64_t c_stride, uint32_t c1_off,
+                          const uint32_t* add1, uint64_t add_stride, uint32_t batch, uint32_t level, uint32_t* x,
+                          uint32_t* tmp, uint32_t* out, hipStream_t s);
 hipError_t launch_chacha_expand(const pc_params* p, const uint32_t seed[8], uint32_t d, uint32_t j,
                                 uint32_t prime_index, uint32_t* dst, hipStream_t s);
 

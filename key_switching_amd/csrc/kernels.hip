@@ -733,6 +733,158 @@ __global__ void __launch_bounds__(256) k_chacha_expand(ChaChaKey key, uint32_t d
 }
 
 // ---------------------------------------------------------------------------
+// homomorphic multiplication around the key switch
+// ---------------------------------------------------------------------------
+// Tensor product of ciphertext pairs: d0 = a0 b0, d1 = a0 b1 + a1 b0,
+// d2 = a1 b1 per limb i = blockIdx.y, pair blockIdx.z. b is put in Montgomery
+// form (b 2^32) so that each product, or the sum of the two cross products,
+// is one REDC. Positions as in the inner product (two runs of 4 per thread).
+struct TensorArgs {
+  DevTables T;
+  const uint32_t* a;  // pair z: a0 at a + z*a_stride, a1 at + l*N
+  const uint32_t* b;
+  uint64_t a_stride, b_stride;
+  uint32_t* d;  // pair z: d_k at d + z*d_stride + d_off[k]
+  uint64_t d_stride;
+  uint64_t d_off[3];
+  int N, level;
+};
+
+constexpr int kTensorThreads = 256;
+
+__global__ void __launch_bounds__(kTensorThreads) k_tensor(TensorArgs A) {
+  constexpr int TILE = 8 * kTensorThreads;
+  const int i = blockIdx.y;
+  const size_t z = blockIdx.z, ln = (size_t)A.level * A.N;
+  const int p0 = (int)blockIdx.x * TILE + 4 * (int)threadIdx.x, p1 = p0 + TILE / 2;
+  const uint32_t r = A.T.r[i], rinv = A.T.rinv[i], r2 = A.T.r2[i];
+  const uint32_t* a0p = A.a + z * A.a_stride + (size_t)i * A.N;
+  const uint32_t* b0p = A.b + z * A.b_stride + (size_t)i * A.N;
+  uint32_t a0[8], a1[8], b0[8], b1[8];
+  load8(a0p, p0, p1, a0);
+  load8(a0p + ln, p0, p1, a1);
+  load8(b0p, p0, p1, b0);
+  load8(b0p + ln, p0, p1, b1);
+  uint32_t d0[8], d1[8], d2[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t b0m = redc(mul_wide(b0[k], r2), r, rinv), b1m = redc(mul_wide(b1[k], r2), r, rinv);
+    d0[k] = redc(mul_wide(a0[k], b0m), r, rinv);
+    d1[k] = redc(mul_wide(a0[k], b1m) + mul_wide(a1[k], b0m), r, rinv);
+    d2[k] = redc(mul_wide(a1[k], b1m), r, rinv);
+  }
+  uint32_t* dz = A.d + z * A.d_stride + (size_t)i * A.N;
+  store8(dz + A.d_off[0], p0, p1, d0);
+  store8(dz + A.d_off[1], p0, p1, d1);
+  store8(dz + A.d_off[2], p0, p1, d2);
+}
+
+// Rescale by the last prime q_l' (l' = level - 1) of 2*batch polynomials:
+// out_i = (c_i - NTT_i([x]_{q_l'} mod q_i)) q_l'^-1 mod q_i for i < l', with x
+// the coefficients of limb l' (already inverse-transformed) and [x] its
+// centred residue. The column pass loads [x] mod q_i, the block pass fetches
+// c_i (plus an optional addend on the second polynomial) at its output
+// positions and stores the division.
+constexpr int kMaxRescaleLimbs = 64;
+
+struct RescaleArgs {
+  DevTables T;
+  const uint32_t* x;  // [polys][N] limb l' of every polynomial, coefficient form
+  const uint32_t* c;  // polynomial u = 2b + v at c + b*c_stride + v*c1_off, limb i at + i*N
+  uint64_t c_stride;
+  uint32_t c1_off;
+  const uint32_t* add1;  // nullptr, or added to polynomial 2b+1: limb i at add1 + b*add_stride + i*N
+  uint64_t add_stride;
+  uint32_t* x_out;  // gather target (= x)
+  uint32_t* tmp;    // [polys][l'][N]
+  uint32_t* out;    // [batch][2][l'][N]
+  int N, lp;        // lp = l' = level - 1
+  uint32_t ql_half;
+  uint32_t ql_mod[kMaxRescaleLimbs], inv[kMaxRescaleLimbs], invp[kMaxRescaleLimbs];
+};
+
+// x[u] = limb l' of polynomial u (plus the addend's limb l' on odd u).
+constexpr int kGatherThreads = 256;
+
+__global__ void __launch_bounds__(kGatherThreads) k_rs_gather(RescaleArgs A) {
+  const size_t u = blockIdx.y, b = u >> 1, v = u & 1;
+  const int pos = 4 * ((int)blockIdx.x * kGatherThreads + (int)threadIdx.x);
+  const uint32_t* src = A.c + b * A.c_stride + v * A.c1_off + (size_t)A.lp * A.N;
+  uint4 w = *reinterpret_cast<const uint4*>(src + pos);
+  if (v == 1 && A.add1 != nullptr) {
+    const uint32_t q = A.T.r[A.lp];
+    const uint4 d = *reinterpret_cast<const uint4*>(A.add1 + b * A.add_stride + (size_t)A.lp * A.N + pos);
+    w.x = add_mod(w.x, d.x, q);
+    w.y = add_mod(w.y, d.y, q);
+    w.z = add_mod(w.z, d.z, q);
+    w.w = add_mod(w.w, d.w, q);
+  }
+  *reinterpret_cast<uint4*>(A.x_out + u * A.N + pos) = w;
+}
+
+struct RescaleSrcLimb {
+  uint32_t r, rinv;
+  const uint32_t* __restrict__ tw;
+  const uint32_t* __restrict__ x;
+  uint32_t ql_half, ql_mod;
+  uint32_t* __restrict__ dst;
+  __device__ __forceinline__ uint32_t load(int pos) const {
+    const uint32_t v = at32(x, pos);
+    const uint32_t m = reduce_2r(v, r);  // v < 2^31 < 2r
+    return v > ql_half ? sub_mod(m, ql_mod, r) : m;
+  }
+  __device__ __forceinline__ void store(int pos, uint32_t v) const { at32(dst, pos) = v; }
+};
+
+template <int E>
+struct RescaleOutLimb {
+  uint32_t r, rinv, inv, invp;
+  const uint32_t* __restrict__ tw;
+  const uint32_t* __restrict__ src;
+  const uint32_t* __restrict__ c;
+  const uint32_t* __restrict__ add;  // nullptr: nothing to add
+  uint32_t* __restrict__ dst;
+  uint32_t cv[E];
+  __device__ __forceinline__ uint32_t load(int pos) const { return at32(src, pos); }
+  __device__ __forceinline__ void fetch(int m, int pos) {
+    cv[m] = at32(c, pos);
+    if (add) cv[m] = add_mod(cv[m], at32(add, pos), r);
+  }
+  __device__ __forceinline__ void finish(int m, int pos, uint32_t v) const {
+    at32(dst, pos) = mul_shoup(sub_mod(cv[m], v, r), inv, invp, r);
+  }
+};
+
+template <int LOGN>
+__global__ void __launch_bounds__(col_threads<LOGN>()) k_rs_col(RescaleArgs A) {
+  using C = Cfg<LOGN>;
+  const int u = blockIdx.y / A.lp, i = blockIdx.y % A.lp;
+  RescaleSrcLimb L{A.T.r[i],      A.T.rinv[i], A.T.tw_fwd + (size_t)i * A.N, A.x + (size_t)u * A.N,
+                   A.ql_half,     A.ql_mod[i], A.tmp + ((size_t)u * A.lp + i) * A.N};
+  fwd_col_pass<C::LRC, C::LEC, C::LRB, C::CC>(L, blockIdx.x * C::CC);
+}
+
+template <int LOGN>
+__global__ void __launch_bounds__(blk_threads<LOGN>()) k_rs_blk(RescaleArgs A) {
+  using C = Cfg<LOGN>;
+  const int u = blockIdx.y / A.lp, i = blockIdx.y % A.lp;
+  const size_t b = u >> 1, v = u & 1;
+  const uint32_t* cu = A.c + b * A.c_stride + v * A.c1_off + (size_t)i * A.N;
+  const uint32_t* add = (v == 1 && A.add1 != nullptr) ? A.add1 + b * A.add_stride + (size_t)i * A.N : nullptr;
+  RescaleOutLimb<(1 << C::LEB)> L{A.T.r[i],
+                                  A.T.rinv[i],
+                                  A.inv[i],
+                                  A.invp[i],
+                                  A.T.tw_fblk + (size_t)i * A.N,
+                                  A.tmp + ((size_t)u * A.lp + i) * A.N,
+                                  cu,
+                                  add,
+                                  A.out + ((size_t)u * A.lp + i) * A.N,
+                                  {}};
+  fwd_blk_pass_fetch<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
+}
+
+// ---------------------------------------------------------------------------
 // key generation: b_d[j] = -a_d[j] s[j] + e_d[j] + g_{d,j} s'[j] (mod r_j)
 // One thread per 8 consecutive positions of limb j (one ChaCha block per
 // digit). s'[j] is s^2 (Galois element 1) or s at the automorphism's source
@@ -1026,6 +1178,68 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
       hipLaunchKernelGGL((k_md_bconv<LN, CNT>), dim3(xcd_grid(col_tiles<LN>(), (int)(items * polys), (int)groups)), dim3(col_threads<LN>()), 0, s, A);
     });
     { LaunchTimer tm(p, KID_MODDOWN_FWD_BLK, s); hipLaunchKernelGGL(k_md_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_q), dim3(blk_threads<LN>()), 0, s, A); }
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_tensor(const pc_params* p, const uint32_t* a, uint64_t a_stride, const uint32_t* b,
+                         uint64_t b_stride, uint32_t batch, uint32_t level, uint32_t* d, uint64_t d_stride,
+                         const uint64_t d_off[3], hipStream_t s) {
+  TensorArgs A;
+  A.T = p->tabs;
+  A.a = a;
+  A.b = b;
+  A.a_stride = a_stride;
+  A.b_stride = b_stride;
+  A.d = d;
+  A.d_stride = d_stride;
+  for (int k = 0; k < 3; ++k) A.d_off[k] = d_off[k];
+  A.N = (int)p->N;
+  A.level = (int)level;
+  const dim3 grid(p->N / (8 * kTensorThreads), level, batch);
+  LaunchTimer tm(p, KID_TENSOR, s);
+  hipLaunchKernelGGL(k_tensor, grid, dim3(kTensorThreads), 0, s, A);
+  return hipGetLastError();
+}
+
+hipError_t launch_rescale(const pc_params* p, const uint32_t* c, uint64_t c_stride, uint32_t c1_off,
+                          const uint32_t* add1, uint64_t add_stride, uint32_t batch, uint32_t level, uint32_t* x,
+                          uint32_t* tmp, uint32_t* out, hipStream_t s) {
+  const uint32_t lp = level - 1, polys = 2 * batch;
+  if (level < 2 || lp > (uint32_t)kMaxRescaleLimbs || polys > (uint32_t)kMaxLimbsPerLaunch) return hipErrorInvalidValue;
+  RescaleArgs A;
+  A.T = p->tabs;
+  A.x = x;
+  A.c = c;
+  A.c_stride = c_stride;
+  A.c1_off = c1_off;
+  A.add1 = add1;
+  A.add_stride = add_stride;
+  A.x_out = x;
+  A.tmp = tmp;
+  A.out = out;
+  A.N = (int)p->N;
+  A.lp = (int)lp;
+  A.ql_half = p->primes[lp] / 2;
+  const size_t off = (size_t)lp * p->L;  // rows of the per-level rescale tables
+  for (uint32_t i = 0; i < (uint32_t)kMaxRescaleLimbs; ++i) {
+    const bool on = i < lp;
+    A.ql_mod[i] = on ? p->h_rs_qlmod[off + i] : 0u;
+    A.inv[i] = on ? p->h_rs_inv[off + i] : 0u;
+    A.invp[i] = on ? p->h_rs_invp[off + i] : 0u;
+  }
+  {
+    LaunchTimer tm(p, KID_RESCALE_GATHER, s);
+    hipLaunchKernelGGL(k_rs_gather, dim3(p->N / (4 * kGatherThreads), polys), dim3(kGatherThreads), 0, s, A);
+  }
+  // limb l' of every polynomial to coefficient form
+  std::vector<uint32_t> pidx(polys, lp);
+  hipError_t e = launch_ntt(p, x, tmp, pidx.data(), polys, true, s);
+  if (e != hipSuccess) return e;
+  const uint32_t rows = polys * lp;
+  PC_DISPATCH_LOGN(p->log2n, {
+    { LaunchTimer tm(p, KID_RESCALE_COL, s); hipLaunchKernelGGL(k_rs_col<LN>, dim3(col_tiles<LN>(), rows), dim3(col_threads<LN>()), 0, s, A); }
+    { LaunchTimer tm(p, KID_RESCALE_BLK, s); hipLaunchKernelGGL(k_rs_blk<LN>, dim3(blk_tiles<LN>(), rows), dim3(blk_threads<LN>()), 0, s, A); }
   });
   return hipGetLastError();
 }

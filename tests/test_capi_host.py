@@ -137,6 +137,21 @@ def test_compute_calls_validate_before_touching_a_device():
         assert lib.pc_keygen(h, seed, 4, 1, dummy, dummy, dummy, None) == ksa.PC_EINVAL
         assert lib.pc_keygen(h, seed, 3, 6, dummy, dummy, dummy, None) == ksa.PC_EINVAL
         assert lib.pc_keygen(h, seed, 3, 5, dummy, dummy, dummy, None) == ksa.PC_EDEVICE
+        # pc_tensor / pc_rescale / pc_hmult (max_batch 1, L 3)
+        assert lib.pc_tensor(h, None, dummy, 1, 3, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_tensor(h, dummy, dummy, 0, 3, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_tensor(h, dummy, dummy, 2, 3, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_tensor(h, dummy, dummy, 1, 4, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_tensor(h, dummy, dummy, 1, 3, dummy, None) == ksa.PC_EDEVICE
+        assert lib.pc_rescale(h, dummy, 1, 1, dummy, None) == ksa.PC_EINVAL  # nothing left to drop to
+        assert lib.pc_rescale(h, dummy, 1, 4, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_rescale(h, dummy, 1, 3, None, None) == ksa.PC_EINVAL
+        assert lib.pc_rescale(h, dummy, 1, 2, dummy, None) == ksa.PC_EDEVICE
+        assert lib.pc_hmult(h, dummy, dummy, 1, dummy, None, 3, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_hmult(h, dummy, dummy, 1, dummy, seed, 1, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_hmult(h, dummy, dummy, 2, dummy, seed, 3, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_hmult(h, dummy, None, 1, dummy, seed, 3, dummy, None) == ksa.PC_EINVAL
+        assert lib.pc_hmult(h, dummy, dummy, 1, dummy, seed, 3, dummy, None) == ksa.PC_EDEVICE
         # params_get argument checks
         buf = (ctypes.c_uint32 * 4)()
         assert lib.pc_params_get(h, ksa.PC_GET_PRIMES, 0, buf, 12) == ksa.PC_EINVAL
