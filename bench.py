@@ -232,6 +232,29 @@ def main():
     k1.record()
     torch.cuda.synchronize()
     ms_kg = k0.elapsed_time(k1) / 10
+    # homomorphic multiplication of 8 ciphertext pairs at the top level around the same
+    # key switch (pc_hmult: tensor, relinearise d2, rescale); per-kernel shares profiled
+    hm_out = torch.empty((K8, 2, w.L - 1, w.N), dtype=torch.int32, device="cuda:0")
+
+    def hm_step(i):
+        ksa.hmult(prm, cts[i % nbuf], cts[(i + 1) % nbuf], evk_b, seed, w.L, out=hm_out)
+
+    for i in range(3):
+        hm_step(i)
+    torch.cuda.synchronize()
+    h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h0.record()
+    for i in range(args.steps):
+        hm_step(i)
+    h1.record()
+    torch.cuda.synchronize()
+    ms_hm = h0.elapsed_time(h1) / args.steps
+    ksa.profile_begin(prm)
+    for i in range(10):
+        hm_step(i)
+    hstats = ksa.profile_end(prm)
+    hm_kernels = {k: round(1000.0 * t / n, 3) for k, (n, t) in hstats.items()
+                  if k in ("tensor", "rescale_gather", "rescale_col", "rescale_blk")}
     kernels_stored = {k: round(1000.0 * t / n, 3) for k, (n, t) in sorted(kstats_stored.items(), key=lambda kv: -kv[1][1])}
     dom = next(iter(kernels))
     roofs = {k: kernel_roofline(k, v["avg_us"], w, K8, beta, alpha) for k, v in kernels.items()}
@@ -278,6 +301,8 @@ def main():
             "k1_stored": {"ks_per_s": round(1000.0 / ms1s, 1), "ms_per_call": round(ms1s, 4)},
             "k8_chacha_profiled": {"ms_per_call": round(ms8p, 4)},
             "keygen_relin_key": {"keys_per_s": round(1000.0 / ms_kg, 1), "ms_per_key": round(ms_kg, 4)},
+            "hmult_k8": {"hmults_per_s": round(K8 * 1000.0 / ms_hm, 1), "ms_per_call": round(ms_hm, 4),
+                         "kernel_avg_us": hm_kernels},
         },
         "kernels": {k: {**{kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()},
                         "hbm_frac": roofs[k]["hbm_frac"], "alu_frac": roofs[k]["alu_frac"]}

@@ -4,9 +4,10 @@ Two subcommands turn rocprofv3 CSV files into the short text summaries kept
 under profiles/ (each summary records the commands that produced it):
 
 * ``stats``   from ``--kernel-trace --stats --output-format csv``: for every
-  kernel family of the N=2^16, L=24, k=8 key switch (regenerated key half),
-  the average duration over the dispatches of that family's k=8 launch, plus
-  the kernel_stats table of the whole run.
+  kernel family of the N=2^16, L=24, k=8 key switch (regenerated key half)
+  and of the homomorphic multiplication of 8 pairs around it, the average
+  duration over the dispatches of that family's batch-8 launch, plus the
+  kernel_stats table of the whole run.
 * ``traffic`` from two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of
   ``bench.py --calibrate-copy``: the counters of every family per dispatch,
   scaled by what the same counters read for a plain copy kernel of known size
@@ -52,6 +53,11 @@ FAMILIES = {
     "moddown_inv_col": "k_md_inv_col<16>",
     "moddown_bconv": "k_md_bconv<16, 6>",
     "moddown_fwd_blk": "k_md_fwd_blk<16>",
+    # homomorphic multiplication of 8 pairs around the same key switch
+    "tensor": "k_tensor",
+    "rescale_gather": "k_rs_gather",
+    "rescale_col": "k_rs_col<16>",
+    "rescale_blk": "k_rs_blk<16>",
 }
 
 
