@@ -173,9 +173,9 @@ struct ModUpArgs {
 template <int LOGN>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_modup_inv_blk(ModUpArgs A) {
   using C = Cfg<LOGN>;
-  // rows are prime-major (all batch items of limb i together) so that a prime's
-  // twiddle slice stays in the L2 of the XCD that runs the tile
-  const size_t i = blockIdx.y / A.batch, b = blockIdx.y % A.batch, z = b * A.level + i;
+  // rows in storage order (limb fastest): the limbs that run at the same time
+  // are neighbours in memory
+  const size_t b = blockIdx.y / A.level, i = blockIdx.y % A.level, z = b * A.level + i;
   PlainLimb L{A.T.r[i], A.T.rinv[i], A.T.tw_iblk + i * A.N, A.ct + b * A.ct_stride + A.c1_off + i * A.N,
               A.y + z * A.N};
   inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
@@ -342,15 +342,19 @@ template <int LOGN>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_modup_fwd_blk(ModUpArgs A) {
   using C = Cfg<LOGN>;
   const int lk = A.level + A.K;
-  const size_t nbd = (size_t)A.batch * A.beta;
-  const int j = (int)(blockIdx.y / nbd);  // prime-major rows (see k_modup_inv_blk)
-  const size_t bd = blockIdx.y % nbd, z = bd * lk + j;
+  // rows in storage order (see k_modup_inv_blk)
+  const int j = (int)(blockIdx.y % lk);
+  const size_t bd = blockIdx.y / lk, z = bd * lk + j;
   const int d = (int)(bd % A.beta);
   const int i0 = d * A.alpha;
   if (j >= i0 && j < min(i0 + A.alpha, A.level)) return;
   const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
   PlainLimb L{A.T.r[pj], A.T.rinv[pj], A.T.tw_fblk + pj * A.N, A.tmp + z * A.N, A.ext + z * A.N};
-  fwd_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
+  // tile order rotated by the prime: neighbouring limbs, which run at the same
+  // time, then touch different offsets, while each XCD still serves one tile
+  // (one slice of the twiddles) per prime
+  const int tile = (int)((blockIdx.x + (uint32_t)j) % (uint32_t)blk_tiles<LOGN>());
+  fwd_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, tile * C::CB);
 }
 
 // ---------------------------------------------------------------------------
@@ -624,8 +628,8 @@ template <int LOGN>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_inv_blk(ModDownArgs A) {
   using C = Cfg<LOGN>;
   const int lk = A.level + A.K;
-  // prime-major rows (see k_modup_inv_blk)
-  const size_t t = blockIdx.y / A.rows_ip, ip = blockIdx.y % A.rows_ip, z = ip * A.K + t, pt = A.L + t;
+  // rows in storage order (see k_modup_inv_blk)
+  const size_t ip = blockIdx.y / A.K, t = blockIdx.y % A.K, z = ip * A.K + t, pt = A.L + t;
   PlainLimb L{A.T.r[pt], A.T.rinv[pt], A.T.tw_iblk + pt * A.N, A.acc + (ip * lk + A.level + t) * A.N,
               A.y2 + z * A.N};
   inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
@@ -688,8 +692,8 @@ template <int LOGN>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_fwd_blk(ModDownArgs A) {
   using C = Cfg<LOGN>;
   const int lk = A.level + A.K;
-  // prime-major rows (see k_modup_inv_blk)
-  const size_t i = blockIdx.y / A.rows_ip, ip = blockIdx.y % A.rows_ip, z = ip * A.level + i;
+  // rows in storage order (see k_modup_inv_blk)
+  const size_t ip = blockIdx.y / A.level, i = blockIdx.y % A.level, z = ip * A.level + i;
   const size_t item = ip / A.polys, u = ip % A.polys;
   const size_t pi = (size_t)A.variant * A.L + i;
   const uint32_t* c0 = nullptr;
