@@ -19,6 +19,10 @@ vectors for key switching):
                rotation keys X->X^5 and X->X^-1 generated at each level.
 * ``n17``      N=2^17, L=40, dnum=5 (alpha=8), K=8, k=8, relinearise then
                rotate by X->X^5.
+* ``bsgs16``   N=2^16, L=24, dnum=4, K=6, one ciphertext through a
+               baby-step/giant-step linear transform of n1 x n2 = 4 x 4
+               diagonals: baby rotations X->X^(5^i), i=1..3, giant rotations
+               X->X^(5^(4j)), j=1..3, diagonals uniform over the extended basis.
 
 Secrets are ternary with Hamming weight h (64 for ``tiny``, 192 otherwise);
 errors are rounded Gaussians with sigma=3.2, tail-cut at |e| <= 19.  This
@@ -41,6 +45,7 @@ STREAM_CT = 1
 STREAM_SECRET = 2
 STREAM_ERROR = 3
 STREAM_KEY_B = 4  # uniform stand-in for a key's b half (benchmark only)
+STREAM_PLAIN = 5  # plaintext diagonals of a linear transform
 
 
 @dataclass(frozen=True)
@@ -85,6 +90,9 @@ WORKLOADS = {
     "levels16": Workload("levels16", 3, 16, 24, 4, 6, 192, batch=(8,), levels=(24, 20, 16, 12, 8, 4),
                          galois=(5, galois_conj(1 << 16))),
     "n17": Workload("n17", 4, 17, 40, 5, 8, 192, batch=(8,), galois=(1, 5), chain=True),
+    "bsgs16": Workload("bsgs16", 5, 16, 24, 4, 6, 192, batch=(1,),
+                       galois=tuple(galois_rot(r, 1 << 16) for r in (1, 2, 3, 4, 8, 12)),
+                       extra={"n1": 4, "n2": 4}),
 }
 
 
@@ -152,4 +160,20 @@ def uniform_key_b(workload_index: int, key_index: int, digits: int, moduli, N: i
     out = np.empty((digits, len(moduli), N), dtype=np.uint32)
     for d in range(digits):
         out[d] = uniform_limbs(g, moduli, N)
+    return out
+
+
+def small_plaintexts(workload_index: int, count: int, N: int, bound: int, idx: int = 0) -> np.ndarray:
+    """[count][N] int64 coefficients uniform in [-bound, bound] (small plaintext polynomials)."""
+    g = rng(workload_index, STREAM_PLAIN, idx)
+    return g.integers(-bound, bound + 1, (count, N), dtype=np.int64)
+
+
+def uniform_diagonals(workload_index: int, n2: int, n1: int, moduli, N: int) -> np.ndarray:
+    """[n2][n1][len(moduli)][N] uint32 uniform words standing in for plaintext diagonals."""
+    g = rng(workload_index, STREAM_PLAIN, 1000)
+    out = np.empty((n2, n1, len(moduli), N), dtype=np.uint32)
+    for j in range(n2):
+        for i in range(n1):
+            out[j, i] = uniform_limbs(g, moduli, N)
     return out
