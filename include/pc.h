@@ -207,6 +207,38 @@ int pc_rescale(const pc_params *p, const uint32_t *ct, uint32_t batch, uint32_t 
 int pc_hmult(const pc_params *p, const uint32_t *ct_a, const uint32_t *ct_b, uint32_t batch, const uint32_t *evk_b,
              const uint8_t *evk_seed, uint32_t level, uint32_t *out, void *stream);
 
+/* Double-hoisted baby-step/giant-step linear transform of one ciphertext, the
+ * key-switch-heavy stage of a bootstrap (the Perseus README, 'Runtime', times
+ * bootstraps with the runtime's primitives). The pages do not write it down;
+ * this is the textbook evaluation:
+ *   R_0 = (P c0, P c1), R_i = (P phi_{g_i}(c0), 0) + IP(phi_{g_i}(ModUp(c1)), key g_i)
+ *       over q_0..q_{l-1}, p_0..p_{K-1} with one shared ModUp (no ModDown);
+ *   inner_j = sum_i diag[j][i] R_i;
+ *   acc = inner_0 + sum_{j>=1} (phi_{G_j}(inner_j,0), 0)
+ *         + IP(phi_{G_j}(ModUp(ModDown(inner_j,1))), key G_j);
+ *   out = ModDown(acc).
+ * Up to key-switching noise out decrypts to
+ * sum_j phi_{G_j}(sum_i diag[j][i] phi_{g_i}(m)). Keys as in pc_keyswitch_ex
+ * (b half in device memory, a half regenerated from its seed). All buffers are
+ * the caller's; out must not alias ct or diag. Uses the params' workspace arena
+ * (PC_EINVAL if it is too small for level, n1, n2). Returns PC_EINVAL for null
+ * pointers, sizes out of range, an even Galois element or one >= 2N,
+ * PC_EDEVICE on launch failure or a host-only params. */
+typedef struct {
+  const uint32_t *ct;             /* device [2][level][N], evaluation form */
+  uint32_t level;                 /* 1..L, with level + K <= 64 */
+  uint32_t n1, n2;                /* baby steps 1..8, giant steps 1..32 (identity included) */
+  const uint32_t *diag;           /* device [n2][n1][level+K][N]: diagonal (j, i) over the extended basis */
+  const uint32_t *const *baby_b;  /* host [n1-1] device pointers: keys of g_1..g_{n1-1} */
+  const uint8_t *baby_seeds;      /* host [n1-1][32] */
+  const uint32_t *baby_galois;    /* host [n1-1] */
+  const uint32_t *const *giant_b; /* host [n2-1] device pointers: keys of G_1..G_{n2-1} */
+  const uint8_t *giant_seeds;     /* host [n2-1][32] */
+  const uint32_t *giant_galois;   /* host [n2-1] */
+  uint32_t *out;                  /* device [2][level][N] */
+} pc_lt_args;
+int pc_linear_transform(const pc_params *p, const pc_lt_args *args, void *stream);
+
 /* Debug / parity: limb j (key-basis index at `level`) of digit d of the a half
  * regenerated from seed (32 bytes, host): dst ([N], device) canonical mod r_j. */
 int pc_chacha_expand(const pc_params *p, const uint8_t *seed, uint32_t d, uint32_t j, uint32_t level, uint32_t *dst,

@@ -22,7 +22,7 @@ PC_GET_N, PC_GET_PRIMES, PC_GET_PSI, PC_GET_ALPHA, PC_GET_BETA, PC_GET_WORKSPACE
 
 EXPORTED = ("pc_params_create", "pc_params_destroy", "pc_params_get", "pc_ntt", "pc_intt", "pc_modup",
             "pc_keyswitch", "pc_moddown", "pc_keyswitch_ex", "pc_keygen", "pc_tensor", "pc_rescale",
-            "pc_hmult", "pc_chacha_expand",
+            "pc_hmult", "pc_linear_transform", "pc_chacha_expand",
             "pc_profile_begin", "pc_profile_end", "pc_strerror")
 
 
@@ -45,6 +45,15 @@ class _KsArgs(ctypes.Structure):
                 ("seeds", ctypes.c_char_p), ("galois", ctypes.POINTER(ctypes.c_uint32)),
                 ("level", ctypes.c_uint32), ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t)]
+
+
+class _LtArgs(ctypes.Structure):
+    _fields_ = [("ct", ctypes.c_void_p), ("level", ctypes.c_uint32), ("n1", ctypes.c_uint32),
+                ("n2", ctypes.c_uint32), ("diag", ctypes.c_void_p),
+                ("baby_b", ctypes.POINTER(ctypes.c_void_p)), ("baby_seeds", ctypes.c_char_p),
+                ("baby_galois", ctypes.POINTER(ctypes.c_uint32)),
+                ("giant_b", ctypes.POINTER(ctypes.c_void_p)), ("giant_seeds", ctypes.c_char_p),
+                ("giant_galois", ctypes.POINTER(ctypes.c_uint32)), ("out", ctypes.c_void_p)]
 
 
 class _KStat(ctypes.Structure):
@@ -76,6 +85,7 @@ def _lib():
         lib.pc_tensor.argtypes = [vp, vp, vp, u32, u32, vp, vp]
         lib.pc_rescale.argtypes = [vp, vp, u32, u32, vp, vp]
         lib.pc_hmult.argtypes = [vp, vp, vp, u32, vp, ctypes.c_char_p, u32, vp, vp]
+        lib.pc_linear_transform.argtypes = [vp, ctypes.POINTER(_LtArgs), vp]
         lib.pc_profile_begin.argtypes = [vp]
         lib.pc_profile_end.argtypes = [vp, ctypes.POINTER(_KStat), u32, ctypes.POINTER(u32)]
         lib.pc_strerror.argtypes = [i32]
@@ -366,6 +376,50 @@ def hmult(prm: Params, ct_a, ct_b, evk_b, seed: bytes, level: int, out=None):
                            _dev_ptr(ct_b, "ct_b", (batch, 2, level, prm.N), prm.device), batch,
                            _dev_ptr(evk_b, "evk_b", prm.key_shape(level), prm.device), _seed_bytes(seed), level,
                            _dev_ptr(out, "out", (batch, 2, level - 1, prm.N), prm.device), _stream()), "pc_hmult")
+    return out
+
+
+def linear_transform(prm: Params, ct, diag, level: int, baby_b: Sequence = (), baby_seeds: Sequence = (),
+                     baby_galois: Sequence[int] = (), giant_b: Sequence = (), giant_seeds: Sequence = (),
+                     giant_galois: Sequence[int] = (), out=None):
+    """Double-hoisted BSGS linear transform of ct [2][level][N] (pc_linear_transform).
+
+    diag: [n2][n1][level+K][N] plaintext diagonals over the extended basis, with
+    n1 = 1 + len(baby keys) and n2 = 1 + len(giant keys); keys are b halves
+    (shape prm.key_shape(level)) with 32-byte seeds and Galois elements.
+    Returns out [2][level][N].
+    """
+    n2, n1 = int(diag.shape[0]), int(diag.shape[1])
+    if len(baby_b) != n1 - 1 or len(baby_seeds) != n1 - 1 or len(baby_galois) != n1 - 1:
+        raise ValueError("diag's second axis must be 1 + the number of baby keys (b, seed, Galois element each)")
+    if len(giant_b) != n2 - 1 or len(giant_seeds) != n2 - 1 or len(giant_galois) != n2 - 1:
+        raise ValueError("diag's first axis must be 1 + the number of giant keys (b, seed, Galois element each)")
+    kshape = prm.key_shape(level)
+    lk = level + prm.K
+    if out is None:
+        out = _new((2, level, prm.N), prm.device)
+    args = _LtArgs()
+    args.ct = _dev_ptr(ct, "ct", (2, level, prm.N), prm.device)
+    args.level = level
+    args.n1 = n1
+    args.n2 = n2
+    args.diag = _dev_ptr(diag, "diag", (n2, n1, lk, prm.N), prm.device)
+    keep = []
+
+    def keys(bs, seeds, galois, name):
+        n = len(bs)
+        if n == 0:
+            return None, None, None
+        ptrs = (ctypes.c_void_p * n)(*[_dev_ptr(b, name, kshape, prm.device).value for b in bs])
+        blob = b"".join(_seed_bytes(x) for x in seeds)
+        gal = (ctypes.c_uint32 * n)(*[int(g) for g in galois])
+        keep.extend([ptrs, blob, gal])
+        return ptrs, blob, gal
+
+    args.baby_b, args.baby_seeds, args.baby_galois = keys(baby_b, baby_seeds, baby_galois, "baby_b")
+    args.giant_b, args.giant_seeds, args.giant_galois = keys(giant_b, giant_seeds, giant_galois, "giant_b")
+    args.out = _dev_ptr(out, "out", (2, level, prm.N), prm.device)
+    _check(_lib().pc_linear_transform(prm.handle, ctypes.byref(args), _stream()), "pc_linear_transform")
     return out
 
 

@@ -333,11 +333,25 @@ size_t hm_workspace_bytes(const pc_params* p, uint32_t level, uint32_t batch) {
   return align256(batch * 3 * l * N * 4) + align256(batch * 2 * l * N * 4) + std::max(ks, rs);
 }
 
+// Workspace of a linear transform with n1 baby and n2 giant steps at level l:
+// the key-switch workspace of the baby steps (one ciphertext, n1 - 1 keys; its
+// ModDown buffers also serve the final ModDown), inner [2][n2][l+K][N], the
+// giant-step sum [2][l+K][N], and for n2 > 1 the ModDown outputs
+// [n2-1][l][N] and the key-switch workspace of the giant steps.
+size_t lt_workspace_bytes(const pc_params* p, uint32_t level, uint32_t n1, uint32_t n2) {
+  const size_t N = p->N, lk = level + p->K;
+  size_t b = ks_workspace_bytes(p, level, 1, std::max<uint32_t>(1, n1 - 1));
+  b += align256(2 * n2 * lk * N * 4) + align256(2 * lk * N * 4);
+  if (n2 > 1) b += align256((n2 - 1) * (size_t)level * N * 4) + ks_workspace_bytes(p, level, n2 - 1, n2 - 1);
+  return b;
+}
+
 const char* const kKernelNames[KID_COUNT] = {
     "ntt_fwd_col",     "ntt_fwd_blk",     "ntt_inv_blk",     "ntt_inv_col",    "modup_inv_blk",
     "modup_inv_col",   "modup_bconv",     "modup_fwd_blk",   "inner_product",  "moddown_inv_blk",
     "moddown_inv_col", "moddown_bconv",   "moddown_fwd_blk", "chacha_expand",  "keygen",
-    "tensor",          "rescale_gather",  "rescale_col",     "rescale_blk"};
+    "tensor",          "rescale_gather",  "rescale_col",     "rescale_blk",    "bsgs_baby",
+    "bsgs_giant"};
 
 static hipEvent_t prof_event(const pc_params* p) {
   if (p->prof_used == p->prof_pool.size()) {
@@ -799,6 +813,90 @@ int pc_hmult(const pc_params* p, const uint32_t* ct_a, const uint32_t* ct_b, uin
   if (launch_keyswitch(p, T, 3 * ln, (uint32_t)ln, batch, level, &key, 1, &one, c, R, s) != hipSuccess)
     return PC_EDEVICE;
   if (launch_rescale(p, R, 2 * ln, (uint32_t)ln, T + 2 * ln, 3 * ln, batch, level, x, tmp, out, s) != hipSuccess)
+    return PC_EDEVICE;
+  return PC_OK;
+}
+
+static bool lt_keys(const pc_params* p, uint32_t n, const uint32_t* const* b, const uint8_t* seeds,
+                    const uint32_t* galois, std::vector<KeyRef>& out) {
+  out.resize(n);
+  if (n == 0) return true;
+  if (b == nullptr || seeds == nullptr || galois == nullptr) return false;
+  for (uint32_t k = 0; k < n; ++k) {
+    if (b[k] == nullptr || (galois[k] & 1u) == 0 || galois[k] >= 2 * p->N) return false;
+    out[k].b = b[k];
+    out[k].a = nullptr;
+    for (int w = 0; w < 8; ++w) {
+      const uint8_t* sb = seeds + 32 * k + 4 * w;
+      out[k].seed[w] = (uint32_t)sb[0] | ((uint32_t)sb[1] << 8) | ((uint32_t)sb[2] << 16) | ((uint32_t)sb[3] << 24);
+    }
+    out[k].galois = galois[k];
+  }
+  return true;
+}
+
+int pc_linear_transform(const pc_params* p, const pc_lt_args* a, void* stream) {
+  if (p == nullptr || a == nullptr || a->ct == nullptr || a->diag == nullptr || a->out == nullptr) return PC_EINVAL;
+  const uint32_t level = a->level, n1 = a->n1, n2 = a->n2;
+  if (level < 1 || level > p->L || n1 < 1 || n1 > 8 || n2 < 1 || n2 > 32 || level + p->K > 64) return PC_EINVAL;
+  std::vector<KeyRef> baby, giant;
+  if (!lt_keys(p, n1 - 1, a->baby_b, a->baby_seeds, a->baby_galois, baby)) return PC_EINVAL;
+  if (!lt_keys(p, n2 - 1, a->giant_b, a->giant_seeds, a->giant_galois, giant)) return PC_EINVAL;
+  if (p->device < 0) return PC_EDEVICE;
+  if (lt_workspace_bytes(p, level, n1, n2) > p->arena_bytes) return PC_EINVAL;
+  const size_t N = p->N, l = level, lk = level + p->K;
+  // per extended-basis limb: P 2^64 (q-limbs), 2^96 and 2^128 mod r
+  std::vector<uint32_t> pm(lk, 0), m96(lk), m128(lk);
+  for (uint32_t t = 0; t < lk; ++t) {
+    const uint32_t r = t < level ? p->primes[t] : p->primes[p->L + t - level];
+    if (t < level) pm[t] = mulmod(prod_mod(p, (int)p->L, (int)(p->L + p->K), -1, r), powmod(2, 64, r), r);
+    m96[t] = powmod(2, 96, r);
+    m128[t] = powmod(2, 128, r);
+  }
+  uint8_t* c = static_cast<uint8_t*>(p->arena);
+  const KsWorkspace ws1 = ks_workspace_carve(p, c, level, 1, std::max<uint32_t>(1, n1 - 1));
+  c += ks_workspace_bytes(p, level, 1, std::max<uint32_t>(1, n1 - 1));
+  uint32_t* inner = reinterpret_cast<uint32_t*>(c);
+  c += align256(2 * n2 * lk * N * 4);
+  uint32_t* accqp = reinterpret_cast<uint32_t*>(c);
+  c += align256(2 * lk * N * 4);
+  uint32_t* d1 = reinterpret_cast<uint32_t*>(c);
+  KsWorkspace ws2{};
+  if (n2 > 1) {
+    c += align256((n2 - 1) * l * N * 4);
+    ws2 = ks_workspace_carve(p, c, level, n2 - 1, n2 - 1);
+  }
+  DeviceGuard g(p->device);
+  if (!g.ok) return PC_EDEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  const uint64_t ln = (uint64_t)l * N;
+  if (n1 > 1) {
+    if (launch_modup(p, a->ct, 2 * ln, (uint32_t)ln, 1, level, ws1, s) != hipSuccess) return PC_EDEVICE;
+    if (launch_inner_product(p, a->ct, 2 * ln, (uint32_t)ln, 1, level, ws1, baby.data(), n1 - 1, s) != hipSuccess)
+      return PC_EDEVICE;
+  }
+  if (launch_bsgs_baby(p, a->ct, ws1.acc, a->diag, inner, level, n1, n2, a->baby_galois, pm.data(), m96.data(),
+                       m128.data(), s) != hipSuccess)
+    return PC_EDEVICE;
+  if (n2 > 1) {
+    // ModDown of inner_j,1 for j >= 1 (contiguous: inner is [u][j][l+K][N])
+    if (launch_moddown(p, inner + (size_t)(n2 + 1) * lk * N, n2 - 1, 1, level, 0, d1, ws2, nullptr, 0, 1, nullptr, s) !=
+        hipSuccess)
+      return PC_EDEVICE;
+    if (launch_modup(p, d1, ln, 0, n2 - 1, level, ws2, s) != hipSuccess) return PC_EDEVICE;
+    const size_t beta = (size_t)beta_of(p, level);
+    for (uint32_t j = 1; j < n2; ++j) {
+      KsWorkspace wj = ws2;
+      wj.ext = ws2.ext + (size_t)(j - 1) * beta * lk * N;
+      wj.acc = ws2.acc + (size_t)(j - 1) * 2 * lk * N;
+      if (launch_inner_product(p, d1 + (size_t)(j - 1) * ln, ln, 0, 1, level, wj, &giant[j - 1], 1, s) != hipSuccess)
+        return PC_EDEVICE;
+    }
+  }
+  if (launch_bsgs_giant(p, inner, n2 > 1 ? ws2.acc : nullptr, accqp, level, n2, a->giant_galois, pm.data(),
+                        m96.data(), m128.data(), s) != hipSuccess)
+    return PC_EDEVICE;
+  if (launch_moddown(p, accqp, 1, 2, level, 0, a->out, ws1, nullptr, 0, 1, nullptr, s) != hipSuccess)
     return PC_EDEVICE;
   return PC_OK;
 }

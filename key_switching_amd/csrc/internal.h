@@ -149,6 +149,8 @@ enum KernelId {
   KID_RESCALE_GATHER,
   KID_RESCALE_COL,
   KID_RESCALE_BLK,
+  KID_BSGS_BABY,
+  KID_BSGS_GIANT,
   KID_COUNT
 };
 extern const char* const kKernelNames[KID_COUNT];
@@ -195,6 +197,17 @@ hipError_t launch_tensor(const pc_params* p, const uint32_t* a, uint64_t a_strid
 hipError_t launch_rescale(const pc_params* p, const uint32_t* c, uint64_t c_stride, uint32_t c1_off,
                           const uint32_t* add1, uint64_t add_stride, uint32_t batch, uint32_t level, uint32_t* x,
                           uint32_t* tmp, uint32_t* out, hipStream_t s);
+// Baby steps of the double-hoisted linear transform: inner [2][n2][l+K][N] from
+// the ciphertext [2][l][N], the baby inner products acc [n1-1][2][l+K][N] (factor
+// 2^-64) and the diagonals [n2][n1][l+K][N]; per extended-basis limb t:
+// pm = P 2^64 mod r_t (q-limbs), m96 = 2^96 mod r_t, m128 = 2^128 mod r_t.
+hipError_t launch_bsgs_baby(const pc_params* p, const uint32_t* ct, const uint32_t* acc, const uint32_t* diag,
+                            uint32_t* inner, uint32_t level, uint32_t n1, uint32_t n2, const uint32_t* baby_galois,
+                            const uint32_t* pm, const uint32_t* m96, const uint32_t* m128, hipStream_t s);
+// Giant-step sum: accqp [2][l+K][N] = inner_0 + sum_{j>=1} (phi_{G_j}(inner_j,0), 0) + 2^64 accg_j.
+hipError_t launch_bsgs_giant(const pc_params* p, const uint32_t* inner, const uint32_t* accg, uint32_t* accqp,
+                             uint32_t level, uint32_t n2, const uint32_t* giant_galois, const uint32_t* pm,
+                             const uint32_t* m96, const uint32_t* m128, hipStream_t s);
 hipError_t launch_chacha_expand(const pc_params* p, const uint32_t seed[8], uint32_t d, uint32_t j,
                                 uint32_t prime_index, uint32_t* dst, hipStream_t s);
 

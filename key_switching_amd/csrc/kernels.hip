@@ -889,6 +889,138 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_rs_blk(RescaleArgs A) {
 }
 
 // ---------------------------------------------------------------------------
+// baby-step/giant-step linear transform, double hoisted
+// ---------------------------------------------------------------------------
+// One thread owns 4 consecutive positions of one limb t of the extended basis
+// (q_0..q_{l-1}, p_0..p_{K-1}). Values enter Montgomery form (x 2^32) once, so
+// each plaintext product is one REDC and pairs of products share it.
+constexpr int kBsgsThreads = 256;
+constexpr int kMaxBaby = 8;         // n1 (baby steps, identity included)
+constexpr int kMaxGiant = 32;       // n2 (giant steps, identity included)
+constexpr int kMaxBsgsLimbs = 64;   // l + K
+
+struct BsgsArgs {
+  DevTables T;
+  const uint32_t* c;      // ciphertext [2][l][N]
+  const uint32_t* acc;    // baby inner products [n1-1][2][l+K][N], carrying 2^-64
+  const uint32_t* diag;   // [n2][n1][l+K][N] plaintext diagonals
+  uint32_t* inner;        // [2][n2][l+K][N]
+  const uint32_t* accg;   // giant inner products [n2-1][2][l+K][N], carrying 2^-64
+  uint32_t* accqp;        // [2][l+K][N]
+  int N, level, K, L, n2;
+  uint32_t galois[kMaxGiant];           // baby (n1-1) or giant (n2-1) Galois elements
+  uint32_t pm[kMaxBsgsLimbs];           // P 2^64 mod r_t on the q-limbs (REDC(c pm) = P c in Montgomery form)
+  uint32_t m96[kMaxBsgsLimbs];          // 2^96 mod r_t (REDC(acc m96) = 2^64 acc)
+  uint32_t m128[kMaxBsgsLimbs];         // 2^128 mod r_t (REDC(acc m128) = 2^64 acc in Montgomery form)
+};
+
+__device__ __forceinline__ void load4(const uint32_t* base, int pos, uint32_t (&v)[4]) {
+  const uint4 x = *reinterpret_cast<const uint4*>(&at32(base, pos));
+  v[0] = x.x;
+  v[1] = x.y;
+  v[2] = x.z;
+  v[3] = x.w;
+}
+
+__device__ __forceinline__ void store4(uint32_t* base, int pos, const uint32_t (&v)[4]) {
+  *reinterpret_cast<uint4*>(&at32(base, pos)) = make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// inner_j,u = sum_i diag[j][i] R_i,u for every giant step j, with
+// R_0 = (P c0, P c1) and R_i = (P phi_{g_i}(c0) + 2^64 acc_i,0, 2^64 acc_i,1)
+// (P vanishes on the p-limbs).
+template <int N1>
+__global__ void __launch_bounds__(kBsgsThreads) k_bsgs_baby(BsgsArgs A) {
+  const int t = blockIdx.y, lk = A.level + A.K;
+  const int pos = 4 * ((int)blockIdx.x * kBsgsThreads + (int)threadIdx.x);
+  const bool qlimb = t < A.level;
+  const size_t pj = qlimb ? (size_t)t : (size_t)(A.L + t - A.level);
+  const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj];
+  const uint32_t pm = A.pm[t], m128 = A.m128[t];
+  const size_t N = (size_t)A.N;
+  uint32_t R[N1][2][4];  // Montgomery form
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (qlimb) {
+      uint32_t c[4];
+      load4(A.c + ((size_t)u * A.level + t) * N, pos, c);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) R[0][u][k] = redc(mul_wide(c[k], pm), r, rinv);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) R[0][u][k] = 0u;
+    }
+  }
+#pragma unroll
+  for (int i = 1; i < N1; ++i) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t a[4];
+      load4(A.acc + (((size_t)(i - 1) * 2 + u) * lk + t) * N, pos, a);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) R[i][u][k] = redc(mul_wide(a[k], m128), r, rinv);
+    }
+    if (qlimb) {
+      const uint32_t g = A.galois[i - 1], h = (g - 1) >> 1, mask = (uint32_t)A.N - 1;
+      const uint32_t* c0 = A.c + (size_t)t * N;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t x = at32(c0, ((uint32_t)(pos + k) * g + h) & mask);
+        R[i][0][k] = add_mod(R[i][0][k], redc(mul_wide(x, pm), r, rinv), r);
+      }
+    }
+  }
+#pragma unroll 1
+  for (int j = 0; j < A.n2; ++j) {
+    uint32_t d[N1][4];
+#pragma unroll
+    for (int i = 0; i < N1; ++i) load4(A.diag + (((size_t)j * N1 + i) * lk + t) * N, pos, d[i]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t sum = 0;
+#pragma unroll
+        for (int i = 0; i + 1 < N1; i += 2)
+          sum = add_mod(sum, redc(mul_wide(d[i][k], R[i][u][k]) + mul_wide(d[i + 1][k], R[i + 1][u][k]), r, rinv), r);
+        if constexpr (N1 % 2) sum = add_mod(sum, redc(mul_wide(d[N1 - 1][k], R[N1 - 1][u][k]), r, rinv), r);
+        o[k] = sum;
+      }
+      store4(A.inner + (((size_t)u * A.n2 + j) * lk + t) * N, pos, o);
+    }
+  }
+}
+
+// acc = inner_0 + sum_{j>=1} (phi_{G_j}(inner_j,0) on the first component + 2^64 accg_j)
+__global__ void __launch_bounds__(kBsgsThreads) k_bsgs_giant(BsgsArgs A) {
+  const int t = blockIdx.y, lk = A.level + A.K;
+  const int pos = 4 * ((int)blockIdx.x * kBsgsThreads + (int)threadIdx.x);
+  const size_t pj = t < A.level ? (size_t)t : (size_t)(A.L + t - A.level);
+  const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj], m96 = A.m96[t];
+  const size_t N = (size_t)A.N;
+  uint32_t o[2][4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) load4(A.inner + (((size_t)u * A.n2) * lk + t) * N, pos, o[u]);
+#pragma unroll 1
+  for (int j = 1; j < A.n2; ++j) {
+    const uint32_t g = A.galois[j - 1], h = (g - 1) >> 1, mask = (uint32_t)A.N - 1;
+    const uint32_t* in0 = A.inner + ((size_t)j * lk + t) * N;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t a[4];
+      load4(A.accg + (((size_t)(j - 1) * 2 + u) * lk + t) * N, pos, a);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[u][k] = add_mod(o[u][k], redc(mul_wide(a[k], m96), r, rinv), r);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[0][k] = add_mod(o[0][k], at32(in0, ((uint32_t)(pos + k) * g + h) & mask), r);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) store4(A.accqp + ((size_t)u * lk + t) * N, pos, o[u]);
+}
+
+// ---------------------------------------------------------------------------
 // key generation: b_d[j] = -a_d[j] s[j] + e_d[j] + g_{d,j} s'[j] (mod r_j)
 // One thread per 8 consecutive positions of limb j (one ChaCha block per
 // digit). s'[j] is s^2 (Galois element 1) or s at the automorphism's source
@@ -1245,6 +1377,70 @@ hipError_t launch_rescale(const pc_params* p, const uint32_t* c, uint64_t c_stri
     { LaunchTimer tm(p, KID_RESCALE_COL, s); hipLaunchKernelGGL(k_rs_col<LN>, dim3(col_tiles<LN>(), rows), dim3(col_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_RESCALE_BLK, s); hipLaunchKernelGGL(k_rs_blk<LN>, dim3(blk_tiles<LN>(), rows), dim3(blk_threads<LN>()), 0, s, A); }
   });
+  return hipGetLastError();
+}
+
+static void bsgs_args(const pc_params* p, BsgsArgs& A, uint32_t level, uint32_t n2, const uint32_t* galois,
+                      uint32_t ngalois, const uint32_t* pm, const uint32_t* m96, const uint32_t* m128) {
+  A.T = p->tabs;
+  A.N = (int)p->N;
+  A.level = (int)level;
+  A.K = (int)p->K;
+  A.L = (int)p->L;
+  A.n2 = (int)n2;
+  for (uint32_t k = 0; k < (uint32_t)kMaxGiant; ++k) A.galois[k] = k < ngalois ? galois[k] : 1u;
+  const uint32_t lk = level + p->K;
+  for (uint32_t t = 0; t < (uint32_t)kMaxBsgsLimbs; ++t) {
+    A.pm[t] = t < lk ? pm[t] : 0u;
+    A.m96[t] = t < lk ? m96[t] : 0u;
+    A.m128[t] = t < lk ? m128[t] : 0u;
+  }
+}
+
+hipError_t launch_bsgs_baby(const pc_params* p, const uint32_t* ct, const uint32_t* acc, const uint32_t* diag,
+                            uint32_t* inner, uint32_t level, uint32_t n1, uint32_t n2, const uint32_t* baby_galois,
+                            const uint32_t* pm, const uint32_t* m96, const uint32_t* m128, hipStream_t s) {
+  const uint32_t lk = level + p->K;
+  if (n1 < 1 || n1 > (uint32_t)kMaxBaby || n2 < 1 || n2 > (uint32_t)kMaxGiant || lk > (uint32_t)kMaxBsgsLimbs)
+    return hipErrorInvalidValue;
+  BsgsArgs A;
+  bsgs_args(p, A, level, n2, baby_galois, n1 - 1, pm, m96, m128);
+  A.c = ct;
+  A.acc = acc;
+  A.diag = diag;
+  A.inner = inner;
+  A.accg = nullptr;
+  A.accqp = nullptr;
+  const dim3 grid(p->N / (4 * kBsgsThreads), lk);
+  LaunchTimer tm(p, KID_BSGS_BABY, s);
+  switch (n1) {
+#define PC_BSGS_CASE(n) \
+  case n: hipLaunchKernelGGL(k_bsgs_baby<n>, grid, dim3(kBsgsThreads), 0, s, A); break;
+    PC_BSGS_CASE(1) PC_BSGS_CASE(2) PC_BSGS_CASE(3) PC_BSGS_CASE(4)
+    PC_BSGS_CASE(5) PC_BSGS_CASE(6) PC_BSGS_CASE(7) PC_BSGS_CASE(8)
+#undef PC_BSGS_CASE
+    default: return hipErrorInvalidValue;
+  }
+  static_assert(kMaxBaby == 8, "the dispatch above covers n1 = 1..8");
+  return hipGetLastError();
+}
+
+hipError_t launch_bsgs_giant(const pc_params* p, const uint32_t* inner, const uint32_t* accg, uint32_t* accqp,
+                             uint32_t level, uint32_t n2, const uint32_t* giant_galois, const uint32_t* pm,
+                             const uint32_t* m96, const uint32_t* m128, hipStream_t s) {
+  const uint32_t lk = level + p->K;
+  if (n2 < 1 || n2 > (uint32_t)kMaxGiant || lk > (uint32_t)kMaxBsgsLimbs) return hipErrorInvalidValue;
+  BsgsArgs A;
+  bsgs_args(p, A, level, n2, giant_galois, n2 - 1, pm, m96, m128);
+  A.c = nullptr;
+  A.acc = nullptr;
+  A.diag = nullptr;
+  A.inner = const_cast<uint32_t*>(inner);
+  A.accg = accg;
+  A.accqp = accqp;
+  const dim3 grid(p->N / (4 * kBsgsThreads), lk);
+  LaunchTimer tm(p, KID_BSGS_GIANT, s);
+  hipLaunchKernelGGL(k_bsgs_giant, grid, dim3(kBsgsThreads), 0, s, A);
   return hipGetLastError();
 }
 

@@ -152,6 +152,26 @@ def test_compute_calls_validate_before_touching_a_device():
         assert lib.pc_hmult(h, dummy, dummy, 2, dummy, seed, 3, dummy, None) == ksa.PC_EINVAL
         assert lib.pc_hmult(h, dummy, None, 1, dummy, seed, 3, dummy, None) == ksa.PC_EINVAL
         assert lib.pc_hmult(h, dummy, dummy, 1, dummy, seed, 3, dummy, None) == ksa.PC_EDEVICE
+        # pc_linear_transform: sizes, keys, then the device
+        lt = ksa._LtArgs()
+        lt.ct, lt.diag, lt.out, lt.level, lt.n1, lt.n2 = dummy.value, dummy.value, dummy.value, 3, 1, 1
+        assert lib.pc_linear_transform(h, None, None) == ksa.PC_EINVAL
+        assert lib.pc_linear_transform(h, ctypes.byref(lt), None) == ksa.PC_EDEVICE
+        for field, bad in (("n1", 0), ("n1", 9), ("n2", 0), ("n2", 33), ("level", 0), ("level", 4)):
+            good = getattr(lt, field)
+            setattr(lt, field, bad)
+            assert lib.pc_linear_transform(h, ctypes.byref(lt), None) == ksa.PC_EINVAL, (field, bad)
+            setattr(lt, field, good)
+        lt.n1 = 2  # one baby key is now required
+        assert lib.pc_linear_transform(h, ctypes.byref(lt), None) == ksa.PC_EINVAL
+        ptrs = (ctypes.c_void_p * 1)(dummy.value)
+        gal = (ctypes.c_uint32 * 1)(4)
+        lt.baby_b, lt.baby_seeds, lt.baby_galois = ptrs, seed, gal
+        assert lib.pc_linear_transform(h, ctypes.byref(lt), None) == ksa.PC_EINVAL  # even Galois element
+        gal[0] = 5
+        assert lib.pc_linear_transform(h, ctypes.byref(lt), None) == ksa.PC_EDEVICE
+        lt.ct = None
+        assert lib.pc_linear_transform(h, ctypes.byref(lt), None) == ksa.PC_EINVAL
         # params_get argument checks
         buf = (ctypes.c_uint32 * 4)()
         assert lib.pc_params_get(h, ksa.PC_GET_PRIMES, 0, buf, 12) == ksa.PC_EINVAL
