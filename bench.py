@@ -255,6 +255,36 @@ def main():
     hstats = ksa.profile_end(prm)
     hm_kernels = {k: round(1000.0 * t / n, 3) for k, (n, t) in hstats.items()
                   if k in ("tensor", "rescale_gather", "rescale_col", "rescale_blk")}
+    # double-hoisted BSGS linear transform of one ciphertext, 4 x 4 diagonals
+    # (baby X^(5^i), i=1..3; giant X^(5^(4j)), j=1..3), uniform diagonals and key b halves
+    wb = ki.WORKLOADS["bsgs16"]
+    n1, n2 = wb.extra["n1"], wb.extra["n2"]
+    lt_keys = [ksa.to_device(ki.uniform_key_b(wb.index, k, beta, basis, w.N), 0) for k in range(len(wb.galois))]
+    lt_seeds = [ki.key_seed(wb.index, k) for k in range(len(wb.galois))]
+    lt_diag = ksa.to_device(ki.uniform_diagonals(wb.index, n2, n1, basis, w.N), 0)
+    lt_out = torch.empty((2, w.L, w.N), dtype=torch.int32, device="cuda:0")
+
+    def lt_step(i):
+        ksa.linear_transform(prm, cts[i % nbuf][0], lt_diag, w.L,
+                             baby_b=lt_keys[: n1 - 1], baby_seeds=lt_seeds[: n1 - 1],
+                             baby_galois=wb.galois[: n1 - 1], giant_b=lt_keys[n1 - 1:],
+                             giant_seeds=lt_seeds[n1 - 1:], giant_galois=wb.galois[n1 - 1:], out=lt_out)
+
+    for i in range(3):
+        lt_step(i)
+    torch.cuda.synchronize()
+    l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    l0.record()
+    for i in range(args.steps):
+        lt_step(i)
+    l1.record()
+    torch.cuda.synchronize()
+    ms_lt = l0.elapsed_time(l1) / args.steps
+    ksa.profile_begin(prm)
+    for i in range(10):
+        lt_step(i)
+    lstats = ksa.profile_end(prm)
+    lt_kernels = {k: round(1000.0 * t / n, 3) for k, (n, t) in lstats.items() if k in ("bsgs_baby", "bsgs_giant")}
     kernels_stored = {k: round(1000.0 * t / n, 3) for k, (n, t) in sorted(kstats_stored.items(), key=lambda kv: -kv[1][1])}
     dom = next(iter(kernels))
     roofs = {k: kernel_roofline(k, v["avg_us"], w, K8, beta, alpha) for k, v in kernels.items()}
@@ -303,6 +333,8 @@ def main():
             "keygen_relin_key": {"keys_per_s": round(1000.0 / ms_kg, 1), "ms_per_key": round(ms_kg, 4)},
             "hmult_k8": {"hmults_per_s": round(K8 * 1000.0 / ms_hm, 1), "ms_per_call": round(ms_hm, 4),
                          "kernel_avg_us": hm_kernels},
+            "bsgs_4x4": {"transforms_per_s": round(1000.0 / ms_lt, 1), "ms_per_call": round(ms_lt, 4),
+                         "key_switches": (n1 - 1) + (n2 - 1), "kernel_avg_us": lt_kernels},
         },
         "kernels": {k: {**{kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()},
                         "hbm_frac": roofs[k]["hbm_frac"], "alu_frac": roofs[k]["alu_frac"]}

@@ -5,7 +5,8 @@ under profiles/ (each summary records the commands that produced it):
 
 * ``stats``   from ``--kernel-trace --stats --output-format csv``: for every
   kernel family of the N=2^16, L=24, k=8 key switch (regenerated key half)
-  and of the homomorphic multiplication of 8 pairs around it, the average
+  and of the homomorphic multiplication of 8 pairs and the 4 x 4 linear
+  transform around it, the average
   duration over the dispatches of that family's batch-8 launch, plus the
   kernel_stats table of the whole run.
 * ``traffic`` from two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of
@@ -58,6 +59,9 @@ FAMILIES = {
     "rescale_gather": "k_rs_gather",
     "rescale_col": "k_rs_col<16>",
     "rescale_blk": "k_rs_blk<16>",
+    # the 4 x 4 double-hoisted linear transform of one ciphertext
+    "bsgs_baby": "k_bsgs_baby<4>",
+    "bsgs_giant": "k_bsgs_giant",
 }
 
 
