@@ -15,6 +15,12 @@ relinearisation. The key's b half is a uniform draw (a real b half is
 indistinguishable from uniform) so that timing never depends on key
 generation.
 
+Beside the headline the line carries per-step min/median/max, a measured
+stream-copy bandwidth (context for the 8 TB/s peak), the homomorphic
+multiplication, linear-transform and key-generation legs, and the key-switch
+rates of the other workloads (one ciphertext under 16 hoisted rotation keys,
+the level sweep 24..4, the N=2^17 relinearise-then-rotate chain).
+
 Prints one JSON line. `python bench.py --gpus N` with N > 1 exits: this build
 measures one GPU.
 """
@@ -62,6 +68,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--buffers-gib", type=float, default=1.1, help="ciphertext buffer rotation size")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the timings of the other workloads (hoisted 16, level sweep, N=2^17 chain)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB copy kernel (reference for rocprofv3 byte counters)")
     return ap.parse_args()
@@ -185,19 +193,25 @@ def main():
         else:
             ksa.keyswitch_ex(prm, ct, [evk_b], [1], w.L, seeds=[seed], out=out)
 
+    per_step = {}
+
     def timed(batch, stored=False, steps=args.steps):
         for i in range(args.warmup):
             step(i, batch, stored)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
-        e0.record()
+        ev[0].record()
         for i in range(steps):
             step(i, batch, stored)
-        e1.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ms = e0.elapsed_time(e1)
+        ms = ev[0].elapsed_time(ev[-1])
+        d = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        # the first timed region of each variant (the later one runs under the library's profiling)
+        per_step.setdefault((batch, stored), {"min": round(d[0], 4), "median": round(d[len(d) // 2], 4),
+                                              "max": round(d[-1], 4)})
         return ms / steps, wall
 
     ms8, wall8 = timed(K8)
@@ -285,6 +299,21 @@ def main():
         lt_step(i)
     lstats = ksa.profile_end(prm)
     lt_kernels = {k: round(1000.0 * t / n, 3) for k, (n, t) in lstats.items() if k in ("bsgs_baby", "bsgs_giant")}
+    # measured stream-copy bandwidth (context for the 8 TB/s peak): 1 GiB read + 1 GiB write
+    csrc = torch.ones(1 << 28, dtype=torch.int32, device="cuda:0")
+    cdst = torch.empty_like(csrc)
+    for _ in range(3):
+        cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        cdst.copy_(csrc)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * csrc.numel() * 4 / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+    del csrc, cdst
+    others = None if args.no_configs else other_configs(ksa, torch, args)
     kernels_stored = {k: round(1000.0 * t / n, 3) for k, (n, t) in sorted(kstats_stored.items(), key=lambda kv: -kv[1][1])}
     dom = next(iter(kernels))
     roofs = {k: kernel_roofline(k, v["avg_us"], w, K8, beta, alpha) for k, v in kernels.items()}
@@ -336,6 +365,10 @@ def main():
             "bsgs_4x4": {"transforms_per_s": round(1000.0 / ms_lt, 1), "ms_per_call": round(ms_lt, 4),
                          "key_switches": (n1 - 1) + (n2 - 1), "kernel_avg_us": lt_kernels},
         },
+        "ms_per_step_k8": per_step[(K8, False)],
+        "ms_per_step_k1": per_step[(1, False)],
+        "copy_gbs_measured": round(copy_gbs, 1),
+        "other_configs": others,
         "kernels": {k: {**{kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()},
                         "hbm_frac": roofs[k]["hbm_frac"], "alu_frac": roofs[k]["alu_frac"]}
                     for k, v in kernels.items()},
@@ -349,6 +382,80 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     prm.close()
     print(json.dumps(result), flush=True)
+
+
+def _time_calls(torch, fn, steps, warmup=3):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def other_configs(ksa, torch, args, steps=10):
+    """Key switches per second on the other workloads (uniform b halves, ChaCha12 a halves).
+
+    hoist16: one N=2^16 ciphertext, ModUp once, 16 rotation keys; levels16: 8
+    ciphertexts switched independently by X^5 and X^-1 keys at each level;
+    n17: 8 N=2^17, L=40 ciphertexts, relinearised then rotated by X^5.
+    """
+    out = {}
+    # hoisted rotations
+    w = ki.WORKLOADS["hoist16"]
+    with ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=1, max_hoist=len(w.galois), device=0) as prm:
+        basis, beta = prm.basis(w.L), prm.beta(w.L)
+        keys = [ksa.to_device(ki.uniform_key_b(w.index, k, beta, basis, w.N), 0) for k in range(len(w.galois))]
+        seeds = [ki.key_seed(w.index, k) for k in range(len(w.galois))]
+        ct = ksa.to_device(ki.ciphertexts(w.index, prm.primes[: w.L], w.N, 1), 0)
+        res = torch.empty((len(w.galois), 1, 2, w.L, w.N), dtype=torch.int32, device="cuda:0")
+        ms = _time_calls(torch, lambda i: ksa.keyswitch_ex(prm, ct, keys, w.galois, w.L, seeds=seeds, out=res), steps)
+        out["hoist16"] = {"ks_per_s": round(len(w.galois) * 1000.0 / ms, 1), "ms_per_call": round(ms, 4),
+                          "key_switches_per_call": len(w.galois)}
+        del keys, ct, res
+    # level sweep
+    w = ki.WORKLOADS["levels16"]
+    with ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=8, device=0) as prm:
+        base = ki.ciphertexts(w.index, prm.primes[: w.L], w.N, 8)
+        per_level = {}
+        for level in w.levels:
+            basis, beta = prm.basis(level), prm.beta(level)
+            keys = [ksa.to_device(ki.uniform_key_b(w.index, 10 * level + k, beta, basis, w.N), 0) for k in range(2)]
+            seeds = [ki.key_seed(w.index, 10 * level + k) for k in range(2)]
+            ct = ksa.to_device(np.ascontiguousarray(base[:, :, :level]), 0)
+            res = torch.empty((1, 8, 2, level, w.N), dtype=torch.int32, device="cuda:0")
+
+            def one_level(i):
+                for k in range(2):  # each key on its own: 16 single key switches
+                    ksa.keyswitch_ex(prm, ct, [keys[k]], [w.galois[k]], level, seeds=[seeds[k]], out=res)
+
+            ms = _time_calls(torch, one_level, steps)
+            per_level[str(level)] = round(16 * 1000.0 / ms, 1)
+            del keys, ct, res
+        out["levels16"] = {"ks_per_s_by_level": per_level}
+    # N=2^17 chain
+    w = ki.WORKLOADS["n17"]
+    with ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=8, device=0) as prm:
+        basis, beta = prm.basis(w.L), prm.beta(w.L)
+        keys = [ksa.to_device(ki.uniform_key_b(w.index, k, beta, basis, w.N), 0) for k in range(2)]
+        seeds = [ki.key_seed(w.index, k) for k in range(2)]
+        ct = ksa.to_device(ki.ciphertexts(w.index, prm.primes[: w.L], w.N, 8), 0)
+        mid = torch.empty((1, 8, 2, w.L, w.N), dtype=torch.int32, device="cuda:0")
+        res = torch.empty_like(mid)
+
+        def chain(i):
+            ksa.keyswitch_ex(prm, ct, [keys[0]], [w.galois[0]], w.L, seeds=[seeds[0]], out=mid)
+            ksa.keyswitch_ex(prm, mid[0], [keys[1]], [w.galois[1]], w.L, seeds=[seeds[1]], out=res)
+
+        ms = _time_calls(torch, chain, steps)
+        out["n17"] = {"ks_per_s": round(16 * 1000.0 / ms, 1), "ms_per_call": round(ms, 4),
+                      "key_switches_per_call": 16}
+        del keys, ct, mid, res
+    return out
 
 
 def cpu_baseline(w, budget_s):
