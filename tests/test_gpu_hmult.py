@@ -127,3 +127,16 @@ def test_headline_n16_hmult_batch8():
     again = host(ksa.hmult(prm, dev(a), dev(b), kb, key.seed, w.L))
     assert_equal(again, out, "repeat")
     prm.close()
+
+
+def test_n17_hmult():
+    """N=2^17, L=40, dnum=5, K=8: two products at the top level, rescaled to L=39."""
+    w = ki.WORKLOADS["n17"]
+    prm, oprm = params_pair(w.log2n, w.L, w.dnum, w.K, max_batch=2)
+    key = ks.Key(b=ki.uniform_key_b(w.index, 0, len(oprm.digits(w.L)), oprm.basis(w.L), oprm.N),
+                 seed=ki.key_seed(w.index, 0), level=w.L, galois=1)
+    a, b = _pairs(w.index + 9, oprm, w.L, 2)
+    out = host(ksa.hmult(prm, dev(a), dev(b), dev(key.b), key.seed, w.L))
+    assert out.shape == (2, 2, w.L - 1, oprm.N)
+    assert_equal(out[1], hm.hmult(oprm, a[1], b[1], key, w.L), "n17 hmult pair 1")
+    prm.close()
