@@ -105,7 +105,9 @@ enum {
   PC_GET_ALPHA = 4,           /* uint32: alpha at level `arg` */
   PC_GET_BETA = 5,            /* uint32: beta at level `arg` */
   PC_GET_WORKSPACE_BYTES = 6, /* uint64: workspace of pc_keyswitch_ex at level `arg` for max_batch x max_hoist */
-  PC_GET_DEVICE_TABLE = 7     /* uint32[N]: forward twiddles psi^bitrev(k) of prime index `arg` (host copy) */
+  PC_GET_DEVICE_TABLE = 7,    /* uint32[N]: forward twiddles psi^bitrev(k) of prime index `arg` (host copy) */
+  PC_GET_ARENA_BYTES = 8,     /* uint64: size of the workspace arena (allocated only with a device) */
+  PC_GET_LT_WORKSPACE_BYTES = 9 /* uint64: arena bytes pc_linear_transform needs; arg = level | n1 << 8 | n2 << 16 */
 };
 /* Copy a property into host memory dst (bytes must match exactly). */
 int pc_params_get(const pc_params *p, int what, uint32_t arg, void *dst, size_t bytes);
@@ -221,7 +223,8 @@ int pc_hmult(const pc_params *p, const uint32_t *ct_a, const uint32_t *ct_b, uin
  * sum_j phi_{G_j}(sum_i diag[j][i] phi_{g_i}(m)). Keys as in pc_keyswitch_ex
  * (b half in device memory, a half regenerated from its seed). All buffers are
  * the caller's; out must not alias ct or diag. Uses the params' workspace arena
- * (PC_EINVAL if it is too small for level, n1, n2). Returns PC_EINVAL for null
+ * (PC_EINVAL if it is smaller than PC_GET_LT_WORKSPACE_BYTES for level, n1, n2;
+ * a larger max_batch or max_hoist at creation enlarges it). Returns PC_EINVAL for null
  * pointers, sizes out of range, an even Galois element or one >= 2N,
  * PC_EDEVICE on launch failure or a host-only params. */
 typedef struct {

@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpc.so")
 
 PC_OK, PC_EINVAL, PC_ENOMEM, PC_EDEVICE, PC_EUNSUPPORTED = 0, -1, -2, -3, -4
-PC_GET_N, PC_GET_PRIMES, PC_GET_PSI, PC_GET_ALPHA, PC_GET_BETA, PC_GET_WORKSPACE_BYTES, PC_GET_DEVICE_TABLE = range(1, 8)
+(PC_GET_N, PC_GET_PRIMES, PC_GET_PSI, PC_GET_ALPHA, PC_GET_BETA, PC_GET_WORKSPACE_BYTES, PC_GET_DEVICE_TABLE,
+ PC_GET_ARENA_BYTES, PC_GET_LT_WORKSPACE_BYTES) = range(1, 10)
 
 EXPORTED = ("pc_params_create", "pc_params_destroy", "pc_params_get", "pc_ntt", "pc_intt", "pc_modup",
             "pc_keyswitch", "pc_moddown", "pc_keyswitch_ex", "pc_keygen", "pc_tensor", "pc_rescale",
@@ -202,6 +203,21 @@ class Params:
         _check(_lib().pc_params_get(self.handle, PC_GET_WORKSPACE_BYTES, level, ctypes.byref(buf), 8),
                "pc_params_get")
         return int(buf.value)
+
+    def _get_u64(self, what: int, arg: int) -> int:
+        buf = ctypes.c_uint64()
+        _check(_lib().pc_params_get(self.handle, what, arg, ctypes.byref(buf), 8), "pc_params_get")
+        return int(buf.value)
+
+    def arena_bytes(self) -> int:
+        """Size of the workspace arena sized at creation."""
+        return self._get_u64(PC_GET_ARENA_BYTES, 0)
+
+    def lt_workspace_bytes(self, level: int, n1: int, n2: int) -> int:
+        """Arena bytes a linear transform with n1 baby and n2 giant steps needs at ``level``."""
+        if not (0 < level < 256 and 0 < n1 < 256 and 0 < n2 < 65536):
+            raise ValueError("level, n1 or n2 out of range")
+        return self._get_u64(PC_GET_LT_WORKSPACE_BYTES, level | (n1 << 8) | (n2 << 16))
 
     def twiddles(self, prime_index: int):
         return self._get_u32(PC_GET_DEVICE_TABLE, prime_index, self.N)

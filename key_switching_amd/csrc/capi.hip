@@ -470,6 +470,13 @@ int pc_params_create(const pc_params_desc* desc, int device, pc_params** out) {
     }
   }
   build_tables(p);
+  {
+    // the arena fits a key switch of max_batch x max_hoist, an HMult of
+    // max_batch pairs and an NTT of every prime at the top level
+    const size_t ks = ks_workspace_bytes(p, p->L, p->max_batch, p->max_batch * p->max_hoist);
+    const size_t hm = p->L >= 2 ? hm_workspace_bytes(p, p->L, p->max_batch) : 0;
+    p->arena_bytes = std::max<size_t>(std::max(ks, hm), (size_t)2 * count * p->N * 4);
+  }
   if (device >= 0) {
     DeviceGuard g(device);
     if (!g.ok) {
@@ -482,9 +489,6 @@ int pc_params_create(const pc_params_desc* desc, int device, pc_params** out) {
       delete p;
       return rc;
     }
-    const size_t ks = ks_workspace_bytes(p, p->L, p->max_batch, p->max_batch * p->max_hoist);
-    const size_t hm = p->L >= 2 ? hm_workspace_bytes(p, p->L, p->max_batch) : 0;
-    p->arena_bytes = std::max<size_t>(std::max(ks, hm), (size_t)2 * count * p->N * 4);
     if (hipMalloc(&p->arena, p->arena_bytes) != hipSuccess) {
       (void)hipFree(p->d_tables);
       delete p;
@@ -571,6 +575,19 @@ int pc_params_get(const pc_params* p, int what, uint32_t arg, void* dst, size_t 
     case PC_GET_WORKSPACE_BYTES: {
       if (bytes != 8 || arg < 1 || arg > p->L) return PC_EINVAL;
       const uint64_t v = ks_workspace_bytes(p, arg, p->max_batch, p->max_batch * p->max_hoist);
+      memcpy(dst, &v, 8);
+      return PC_OK;
+    }
+    case PC_GET_ARENA_BYTES: {
+      if (bytes != 8) return PC_EINVAL;
+      const uint64_t v = p->arena_bytes;
+      memcpy(dst, &v, 8);
+      return PC_OK;
+    }
+    case PC_GET_LT_WORKSPACE_BYTES: {
+      const uint32_t level = arg & 0xff, n1 = (arg >> 8) & 0xff, n2 = arg >> 16;
+      if (bytes != 8 || level < 1 || level > p->L || n1 < 1 || n2 < 1) return PC_EINVAL;
+      const uint64_t v = lt_workspace_bytes(p, level, n1, n2);
       memcpy(dst, &v, 8);
       return PC_OK;
     }

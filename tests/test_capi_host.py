@@ -180,6 +180,20 @@ def test_compute_calls_validate_before_touching_a_device():
     assert lib.pc_strerror(ksa.PC_EDEVICE).startswith(b"device")
 
 
+def test_arena_and_transform_workspace_sizes():
+    with ksa.Params(16, 24, 4, 6, max_batch=8, device=None) as prm:
+        arena = prm.arena_bytes()
+        assert arena >= prm.workspace_bytes(24)
+        need = prm.lt_workspace_bytes(24, 4, 4)
+        assert 0 < need <= arena  # the 4 x 4 transform fits the batch-8 arena
+        assert prm.lt_workspace_bytes(24, 8, 4) > need and prm.lt_workspace_bytes(24, 4, 8) > need
+        assert prm.lt_workspace_bytes(12, 4, 4) < need
+    with ksa.Params(16, 24, 4, 6, device=None) as small:
+        assert small.lt_workspace_bytes(24, 4, 4) > small.arena_bytes()  # needs a larger arena
+        with pytest.raises(ksa.PcError):
+            small.lt_workspace_bytes(25, 4, 4)
+
+
 def test_workspace_grows_with_level():
     with ksa.Params(16, 24, 4, 6, max_batch=8, device=None) as prm:
         sizes = [prm.workspace_bytes(l) for l in (4, 8, 12, 16, 20, 24)]
