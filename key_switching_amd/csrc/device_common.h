@@ -38,12 +38,6 @@ __device__ __forceinline__ uint32_t mul_shoup(uint32_t x, uint32_t w, uint32_t w
   return min(t, t - r);
 }
 
-// Same, result left in [0, 2r).
-__device__ __forceinline__ uint32_t mul_shoup_lazy(uint32_t x, uint32_t w, uint32_t wp, uint32_t r) {
-  const uint32_t qh = __umulhi(x, wp);
-  return x * w - qh * r;
-}
-
 // Montgomery reduction: x < r 2^32  ->  x 2^-32 mod r, canonical.
 // rinv_neg = -r^-1 mod 2^32.
 __device__ __forceinline__ uint32_t redc(uint64_t x, uint32_t r, uint32_t rinv_neg) {
