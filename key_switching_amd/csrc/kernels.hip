@@ -378,6 +378,7 @@ struct IPArgs {
   uint32_t* acc;        // [items][2][l+K][N], item = key * batch + b
   int N, level, K, L, alpha, batch, nkeys;
   int key_level;  // level of the keys (their limbs are [q_0..q_{key_level-1}, p_0..p_{K-1}])
+  int limb_xcd;   // 0, or the split of limb_xcd_decode: tiles of limb j grouped on XCDs (see below)
   uint32_t key_base;
   const uint32_t* evk_b[kMaxKeysPerLaunch];
   const uint32_t* evk_a[kMaxKeysPerLaunch];
@@ -465,16 +466,41 @@ __device__ __forceinline__ void ip_sums(const uint32_t (&e)[BETA][8], const uint
 
 constexpr int kIpThreads = 256;
 
-// One workgroup per (tile of 8*kIpThreads positions, limb blockIdx.y, key
-// blockIdx.z). STORED: the a half is read; otherwise each thread expands its
+// Placement for gathers under automorphisms: a gather reads the whole source
+// limb, so the tiles of one limb (for every key or item that gathers from it)
+// go to the same XCD, and each limb fills one L2 instead of all eight.
+// Workgroup i of a 1-D grid runs on XCD i mod 8. With few limbs, whole limbs
+// would load the 8 XCDs unevenly, so a limb can be cut into `split` parts of
+// tiles/split tiles: part s of limb j is part j split + s of the walk, on XCD
+// (j split + s) mod 8, and the limb fills `split` L2s. The walk has
+// 8 ceil(limbs split / 8) per_limb tiles/split units; padding units return false.
+__device__ __forceinline__ bool limb_xcd_decode(int u, int tiles, int split, int limbs, int per_limb, int& tile,
+                                                int& limb, int& idx) {
+  const int xcd = u & 7, slot = u >> 3, tps = tiles / split;
+  const int t_in = slot % tps, rest = slot / tps;
+  idx = rest % per_limb;
+  const int part = xcd + 8 * (rest / per_limb);
+  limb = part / split;
+  tile = (part % split) * tps + t_in;
+  return limb < limbs;
+}
+__device__ __forceinline__ bool limb_xcd_unit(int tiles, int split, int limbs, int per_limb, int& tile, int& limb,
+                                              int& idx) {
+  return limb_xcd_decode((int)blockIdx.x, tiles, split, limbs, per_limb, tile, limb, idx);
+}
+
+// One workgroup per (tile of 8*kIpThreads positions, limb, key): a grid
+// (tiles, limbs, keys), or under automorphisms the 1-D walk of
+// limb_xcd_decode. STORED: the a half is read; otherwise each thread expands its
 // ChaCha block per digit. BT: the batch size when known at compile time (1 or
 // 8), else 0.
 template <int BETA, int ROUNDS, bool STORED, int BT>
 __global__ void __launch_bounds__(kIpThreads) k_inner_product(IPArgs A) {
   constexpr int TILE = 8 * kIpThreads;
-  const int j = blockIdx.y, key = blockIdx.z;
   const int lk = A.level + A.K;
-  const int p0 = STORED ? (int)blockIdx.x * TILE + 4 * (int)threadIdx.x : ((int)blockIdx.x * kIpThreads + threadIdx.x) * 8;
+  int tile = (int)blockIdx.x, j = (int)blockIdx.y, key = (int)blockIdx.z;
+  if (A.limb_xcd && !limb_xcd_unit(A.N / TILE, A.limb_xcd, lk, A.nkeys, tile, j, key)) return;
+  const int p0 = STORED ? tile * TILE + 4 * (int)threadIdx.x : (tile * kIpThreads + (int)threadIdx.x) * 8;
   const int p1 = STORED ? p0 + TILE / 2 : p0 + 4;
   const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
   const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj];
@@ -528,23 +554,29 @@ __global__ void __launch_bounds__(2 * kIpHalf) k_ip_regen(IPArgs A) {
   __shared__ uint32_t am_lds[2][BETA][8][kIpHalf];  // [slot][digit][k][consumer thread]
   const int lk = A.level + A.K;
   const int tiles = A.N / TILE;
-  const int units = A.nkeys * lk * tiles;
+  // under automorphisms, units are numbered as in limb_xcd_decode, so that
+  // unit u, walked by workgroup u mod gridDim.x (a multiple of 8), runs on
+  // XCD u mod 8 with its limb's other tiles; the padding units are skipped
+  const int units = A.limb_xcd ? 8 * ((lk * A.limb_xcd + 7) / 8) * A.nkeys * (tiles / A.limb_xcd)
+                               : A.nkeys * lk * tiles;
   const bool producer = threadIdx.x >= kIpHalf;
   const int t = threadIdx.x % kIpHalf;
   int u = blockIdx.x;
   if (u >= units) return;  // uniform over the workgroup
 
   auto decode = [&](int unit, int& key, int& j, int& tile) {
+    if (A.limb_xcd) return limb_xcd_decode(unit, tiles, A.limb_xcd, lk, A.nkeys, tile, j, key);
     tile = unit % tiles;
     j = (unit / tiles) % lk;
     key = unit / (tiles * lk);
+    return true;
   };
   // a half of digits [d0, d1) of `unit`: this thread expands ChaCha block
   // tile*kIpHalf + t (tile positions 8t..8t+7) and files each value under the
   // consumer thread and slot that own its position
   auto produce = [&](int unit, int slot, int d0, int d1) {
     int key, j, tile;
-    decode(unit, key, j, tile);
+    if (!decode(unit, key, j, tile)) return;
     const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
     const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj];
     const int hi = (8 * t) >= TILE / 2;
@@ -561,7 +593,7 @@ __global__ void __launch_bounds__(2 * kIpHalf) k_ip_regen(IPArgs A) {
   };
   auto consume = [&](int unit, int slot) {
     int key, j, tile;
-    decode(unit, key, j, tile);
+    if (!decode(unit, key, j, tile)) return;
     const int p0 = tile * TILE + 4 * t, p1 = p0 + TILE / 2;
     const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
     const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj];
@@ -621,6 +653,7 @@ struct ModDownArgs {
   const uint32_t* c0;   // c0 of ciphertext b at c0 + b * ct_stride, or nullptr
   uint64_t ct_stride;
   int N, level, K, L, polys, variant, batch, rows_ip, ngroups;
+  int limb_xcd;  // combine pass: 0, or the split of limb_xcd_decode (c0 gathered under an automorphism)
   uint32_t galois[kMaxKeysPerLaunch];  // per key = item / batch
 };
 
@@ -692,8 +725,11 @@ template <int LOGN>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_fwd_blk(ModDownArgs A) {
   using C = Cfg<LOGN>;
   const int lk = A.level + A.K;
-  // rows in storage order (see k_modup_inv_blk)
-  const size_t ip = blockIdx.y / A.level, i = blockIdx.y % A.level, z = ip * A.level + i;
+  // rows in storage order (see k_modup_inv_blk); when c0 is gathered under an
+  // automorphism, the tiles of limb i are grouped on XCDs (see limb_xcd_decode)
+  int tile = (int)blockIdx.x, ipi = (int)(blockIdx.y / A.level), ii = (int)(blockIdx.y % A.level);
+  if (A.limb_xcd && !limb_xcd_unit(blk_tiles<LOGN>(), A.limb_xcd, A.level, A.rows_ip, tile, ii, ipi)) return;
+  const size_t ip = (size_t)ipi, i = (size_t)ii, z = ip * A.level + i;
   const size_t item = ip / A.polys, u = ip % A.polys;
   const size_t pi = (size_t)A.variant * A.L + i;
   const uint32_t* c0 = nullptr;
@@ -716,7 +752,7 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_fwd_blk(ModDownArgs 
                 A.out + z * A.N,
                 {},
                 {}};
-  fwd_blk_pass_fetch<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
+  fwd_blk_pass_fetch<C::LRC, C::LRB, C::LEB, C::CB>(L, tile * C::CB);
 }
 
 // ---------------------------------------------------------------------------
@@ -1194,27 +1230,59 @@ static uint32_t resident_workgroups(F kernel, int threads) {
   return n;
 }
 
+// Split of limb_xcd_decode for `limbs` limbs of `tiles` tiles: the smallest of
+// 1, 2, 4, 8 (dividing tiles) whose padding to a multiple of 8 parts costs at
+// most 7%, else the one with the least padding.
+static int xcd_split(uint32_t limbs, uint32_t tiles) {
+  int best = 1;
+  double best_pad = 1e9;
+  for (uint32_t sp = 1; sp <= 8 && sp <= tiles; sp *= 2) {
+    if (tiles % sp) break;
+    const uint32_t parts = limbs * sp, padded = (parts + 7) / 8 * 8;
+    const double pad = (double)padded / parts;
+    if (pad <= 1.07) return (int)sp;
+    if (pad < best_pad) {
+      best_pad = pad;
+      best = (int)sp;
+    }
+  }
+  return best;
+}
+
+static uint32_t blk_tiles_of(uint32_t log2n) {
+  return log2n == 12 ? (uint32_t)blk_tiles<12>() : log2n == 16 ? (uint32_t)blk_tiles<16>() : (uint32_t)blk_tiles<17>();
+}
+
 template <int BETA, int ROUNDS, int BT>
-static void launch_ip_regen(const pc_params* p, const IPArgs& A, hipStream_t s) {
+static void launch_ip_regen(const pc_params* p, const IPArgs& A0, hipStream_t s) {
   auto kern = k_ip_regen<BETA, ROUNDS, BT>;
-  const uint32_t units = (uint32_t)A.nkeys * (uint32_t)(A.level + A.K) * (p->N / (8 * kIpHalf));
-  const uint32_t grid = std::min(units, resident_workgroups(kern, 2 * kIpHalf));
+  const uint32_t lk = (uint32_t)(A0.level + A0.K), tiles = p->N / (8 * kIpHalf);
+  IPArgs A = A0;
+  if (A.limb_xcd) A.limb_xcd = xcd_split(lk, tiles);
+  const uint32_t sp = (uint32_t)A.limb_xcd;
+  const uint32_t units = sp ? 8 * ((lk * sp + 7) / 8) * (uint32_t)A.nkeys * (tiles / sp) : (uint32_t)A.nkeys * lk * tiles;
+  uint32_t grid = std::min(units, resident_workgroups(kern, 2 * kIpHalf));
+  if (sp) grid = std::max<uint32_t>(8, grid & ~7u);  // unit u stays on XCD u mod 8
   LaunchTimer tm(p, KID_INNER_PRODUCT, s);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(2 * kIpHalf), 0, s, A);
 }
 
 template <int BETA, int BT>
-static void launch_ip_bt(const pc_params* p, const IPArgs& A, uint32_t nkeys, bool stored, hipStream_t s) {
+static void launch_ip_bt(const pc_params* p, const IPArgs& A0, uint32_t nkeys, bool stored, hipStream_t s) {
   if constexpr (BT != 1) {
-    if (!stored && A.batch >= 2) {  // regenerated a half and a batch to overlap it with
+    if (!stored && A0.batch >= 2) {  // regenerated a half and a batch to overlap it with
       if (p->chacha_rounds == 20)
-        launch_ip_regen<BETA, 20, BT>(p, A, s);
+        launch_ip_regen<BETA, 20, BT>(p, A0, s);
       else
-        launch_ip_regen<BETA, 12, BT>(p, A, s);
+        launch_ip_regen<BETA, 12, BT>(p, A0, s);
       return;
     }
   }
-  const dim3 grid((p->N / 8 + kIpThreads - 1) / kIpThreads, (uint32_t)(A.level + A.K), nkeys);
+  const uint32_t tiles = (p->N / 8 + kIpThreads - 1) / kIpThreads, lk = (uint32_t)(A0.level + A0.K);
+  IPArgs A = A0;
+  if (A.limb_xcd) A.limb_xcd = xcd_split(lk, tiles);
+  const uint32_t sp = (uint32_t)A.limb_xcd;
+  const dim3 grid = sp ? dim3(8 * ((lk * sp + 7) / 8) * nkeys * (tiles / sp)) : dim3(tiles, lk, nkeys);
   LaunchTimer tm(p, KID_INNER_PRODUCT, s);
   if (stored)
     hipLaunchKernelGGL((k_inner_product<BETA, 12, true, BT>), grid, dim3(kIpThreads), 0, s, A);
@@ -1257,8 +1325,10 @@ hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t
     A.key_level = (int)key_level_of(p, level);
     A.key_base = base;
     bool stored = false;
+    A.limb_xcd = 0;
     for (uint32_t k = 0; k < cnt; ++k) {
       const KeyRef& kr = keys[base + k];
+      if (kr.galois != 1u) A.limb_xcd = -1;  // split chosen below, per kernel
       A.evk_b[k] = kr.b;
       A.evk_a[k] = kr.a;
       stored = stored || kr.a != nullptr;
@@ -1306,6 +1376,10 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
   const uint32_t groups = (level + kBconvGroup - 1) / kBconvGroup;
   A.rows_ip = (int)(items * polys);
   A.ngroups = (int)groups;
+  A.limb_xcd = 0;
+  if (c0 != nullptr)
+    for (uint32_t k = 0; k < nkeys && k < (uint32_t)kMaxKeysPerLaunch; ++k)
+      if (A.galois[k] != 1u) A.limb_xcd = xcd_split(level, (uint32_t)blk_tiles_of(p->log2n));
   PC_DISPATCH_LOGN(p->log2n, {
     { LaunchTimer tm(p, KID_MODDOWN_INV_BLK, s); hipLaunchKernelGGL(k_md_inv_blk<LN>, dim3(blk_tiles<LN>(), rows_p), dim3(blk_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_MODDOWN_INV_COL, s); hipLaunchKernelGGL(k_md_inv_col<LN>, dim3(col_tiles<LN>(), rows_p), dim3(col_threads<LN>()), 0, s, A); }
@@ -1313,7 +1387,13 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
       LaunchTimer tm(p, KID_MODDOWN_BCONV, s);
       hipLaunchKernelGGL((k_md_bconv<LN, CNT>), dim3(xcd_grid(col_tiles<LN>(), (int)(items * polys), (int)groups)), dim3(col_threads<LN>()), 0, s, A);
     });
-    { LaunchTimer tm(p, KID_MODDOWN_FWD_BLK, s); hipLaunchKernelGGL(k_md_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_q), dim3(blk_threads<LN>()), 0, s, A); }
+    {
+      const uint32_t sp = (uint32_t)A.limb_xcd;
+      const dim3 grid = sp ? dim3(8 * ((level * sp + 7) / 8) * items * polys * (blk_tiles<LN>() / sp))
+                           : dim3(blk_tiles<LN>(), rows_q);
+      LaunchTimer tm(p, KID_MODDOWN_FWD_BLK, s);
+      hipLaunchKernelGGL(k_md_fwd_blk<LN>, grid, dim3(blk_threads<LN>()), 0, s, A);
+    }
   });
   return hipGetLastError();
 }
