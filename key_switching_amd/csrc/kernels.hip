@@ -944,6 +944,7 @@ struct BsgsArgs {
   const uint32_t* accg;   // giant inner products [n2-1][2][l+K][N], carrying 2^-64
   uint32_t* accqp;        // [2][l+K][N]
   int N, level, K, L, n2;
+  int split;                            // 0: grid (tiles, limbs); else the 1-D walk of limb_xcd_decode
   uint32_t galois[kMaxGiant];           // baby (n1-1) or giant (n2-1) Galois elements
   uint32_t pm[kMaxBsgsLimbs];           // P 2^64 mod r_t on the q-limbs (REDC(c pm) = P c in Montgomery form)
   uint32_t m96[kMaxBsgsLimbs];          // 2^96 mod r_t (REDC(acc m96) = 2^64 acc)
@@ -967,8 +968,10 @@ __device__ __forceinline__ void store4(uint32_t* base, int pos, const uint32_t (
 // (P vanishes on the p-limbs).
 template <int N1>
 __global__ void __launch_bounds__(kBsgsThreads) k_bsgs_baby(BsgsArgs A) {
-  const int t = blockIdx.y, lk = A.level + A.K;
-  const int pos = 4 * ((int)blockIdx.x * kBsgsThreads + (int)threadIdx.x);
+  const int lk = A.level + A.K;
+  int tile = (int)blockIdx.x, t = (int)blockIdx.y, one = 0;
+  if (A.split && !limb_xcd_unit(A.N / (4 * kBsgsThreads), A.split, lk, 1, tile, t, one)) return;
+  const int pos = 4 * (tile * kBsgsThreads + (int)threadIdx.x);
   const bool qlimb = t < A.level;
   const size_t pj = qlimb ? (size_t)t : (size_t)(A.L + t - A.level);
   const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj];
@@ -1030,8 +1033,10 @@ __global__ void __launch_bounds__(kBsgsThreads) k_bsgs_baby(BsgsArgs A) {
 
 // acc = inner_0 + sum_{j>=1} (phi_{G_j}(inner_j,0) on the first component + 2^64 accg_j)
 __global__ void __launch_bounds__(kBsgsThreads) k_bsgs_giant(BsgsArgs A) {
-  const int t = blockIdx.y, lk = A.level + A.K;
-  const int pos = 4 * ((int)blockIdx.x * kBsgsThreads + (int)threadIdx.x);
+  const int lk = A.level + A.K;
+  int tile = (int)blockIdx.x, t = (int)blockIdx.y, one = 0;
+  if (A.split && !limb_xcd_unit(A.N / (4 * kBsgsThreads), A.split, lk, 1, tile, t, one)) return;
+  const int pos = 4 * (tile * kBsgsThreads + (int)threadIdx.x);
   const size_t pj = t < A.level ? (size_t)t : (size_t)(A.L + t - A.level);
   const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj], m96 = A.m96[t];
   const size_t N = (size_t)A.N;
@@ -1468,7 +1473,10 @@ static void bsgs_args(const pc_params* p, BsgsArgs& A, uint32_t level, uint32_t 
   A.K = (int)p->K;
   A.L = (int)p->L;
   A.n2 = (int)n2;
+  A.split = 0;
   for (uint32_t k = 0; k < (uint32_t)kMaxGiant; ++k) A.galois[k] = k < ngalois ? galois[k] : 1u;
+  for (uint32_t k = 0; k < ngalois; ++k)
+    if (galois[k] != 1u) A.split = xcd_split(level + p->K, p->N / (4 * kBsgsThreads));
   const uint32_t lk = level + p->K;
   for (uint32_t t = 0; t < (uint32_t)kMaxBsgsLimbs; ++t) {
     A.pm[t] = t < lk ? pm[t] : 0u;
@@ -1491,7 +1499,8 @@ hipError_t launch_bsgs_baby(const pc_params* p, const uint32_t* ct, const uint32
   A.inner = inner;
   A.accg = nullptr;
   A.accqp = nullptr;
-  const dim3 grid(p->N / (4 * kBsgsThreads), lk);
+  const uint32_t tiles = p->N / (4 * kBsgsThreads), sp = (uint32_t)A.split;
+  const dim3 grid = sp ? dim3(8 * ((lk * sp + 7) / 8) * (tiles / sp)) : dim3(tiles, lk);
   LaunchTimer tm(p, KID_BSGS_BABY, s);
   switch (n1) {
 #define PC_BSGS_CASE(n) \
@@ -1518,7 +1527,8 @@ hipError_t launch_bsgs_giant(const pc_params* p, const uint32_t* inner, const ui
   A.inner = const_cast<uint32_t*>(inner);
   A.accg = accg;
   A.accqp = accqp;
-  const dim3 grid(p->N / (4 * kBsgsThreads), lk);
+  const uint32_t tiles = p->N / (4 * kBsgsThreads), sp = (uint32_t)A.split;
+  const dim3 grid = sp ? dim3(8 * ((lk * sp + 7) / 8) * (tiles / sp)) : dim3(tiles, lk);
   LaunchTimer tm(p, KID_BSGS_GIANT, s);
   hipLaunchKernelGGL(k_bsgs_giant, grid, dim3(kBsgsThreads), 0, s, A);
   return hipGetLastError();
