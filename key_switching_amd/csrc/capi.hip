@@ -490,6 +490,7 @@ int pc_params_create(const pc_params_desc* desc, int device, pc_params** out) {
       return rc;
     }
     if (hipMalloc(&p->arena, p->arena_bytes) != hipSuccess) {
+      (void)hipGetLastError();  // do not leave the failure for a later launch check to report
       (void)hipFree(p->d_tables);
       delete p;
       return PC_ENOMEM;

@@ -391,3 +391,18 @@ def test_rejected_arguments_on_gpu():
     with pytest.raises(ValueError):
         ksa.keyswitch(prm, ct[:, :2].contiguous(), b, bytes(32), 3, 5)
     prm.close()
+
+
+def test_allocation_failure_reports_enomem():
+    """An arena too large for the device fails creation with PC_ENOMEM, and the
+    library keeps working afterwards (the failure is not left for a later launch)."""
+    with pytest.raises(ksa.PcError) as e:
+        ksa.Params(16, 24, 4, 6, max_batch=1 << 20, device=0)
+    assert e.value.code == ksa.PC_ENOMEM
+    w = ki.WORKLOADS["tiny"]
+    prm, oprm = params_pair(w.log2n, w.L, w.dnum, w.K)
+    s, (key,), _ = _real_keys(oprm, w.index, w.L, (5,), w.h)
+    ct = ki.ciphertexts(w.index, oprm.q, oprm.N, 1)[0]
+    out = host(ksa.keyswitch(prm, dev(ct), dev(key.b), key.seed, w.L, 5))
+    assert_equal(out, ks.keyswitch(oprm, ct, key, w.L), "key switch after a failed creation")
+    prm.close()
