@@ -231,74 +231,80 @@ def main():
     timed(K8, stored=True)
     kstats_stored = ksa.profile_end(prm)
 
-    # key generation of the same relinearisation key on the GPU (pc_keygen): synthetic
-    # secret / error residues of the right shape (timing does not depend on their values)
-    s_coef = ksa.to_device(ki.uniform_key_b(w.index, 2, 1, basis, w.N)[0], 0)
-    e_coef = ksa.to_device(ki.uniform_key_b(w.index, 3, beta, basis, w.N), 0)
-    kg_out = torch.empty((beta, w.L + w.K, w.N), dtype=torch.int32, device="cuda:0")
-    for _ in range(3):
-        ksa.keygen(prm, seed, w.L, 1, s_coef, e_coef, out=kg_out)
-    torch.cuda.synchronize()
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    k0.record()
-    for _ in range(10):
-        ksa.keygen(prm, seed, w.L, 1, s_coef, e_coef, out=kg_out)
-    k1.record()
-    torch.cuda.synchronize()
-    ms_kg = k0.elapsed_time(k1) / 10
-    # homomorphic multiplication of 8 ciphertext pairs at the top level around the same
-    # key switch (pc_hmult: tensor, relinearise d2, rescale); per-kernel shares profiled
-    hm_out = torch.empty((K8, 2, w.L - 1, w.N), dtype=torch.int32, device="cuda:0")
+    def timed_calls(fn, steps):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
 
-    def hm_step(i):
-        ksa.hmult(prm, cts[i % nbuf], cts[(i + 1) % nbuf], evk_b, seed, w.L, out=hm_out)
+    def profiled(fn, families):
+        ksa.profile_begin(prm)
+        try:
+            for i in range(10):
+                fn(i)
+        finally:
+            st = ksa.profile_end(prm)
+        return {k: round(1000.0 * t / n, 3) for k, (n, t) in st.items() if k in families}
 
-    for i in range(3):
-        hm_step(i)
-    torch.cuda.synchronize()
-    h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    h0.record()
-    for i in range(args.steps):
-        hm_step(i)
-    h1.record()
-    torch.cuda.synchronize()
-    ms_hm = h0.elapsed_time(h1) / args.steps
-    ksa.profile_begin(prm)
-    for i in range(10):
-        hm_step(i)
-    hstats = ksa.profile_end(prm)
-    hm_kernels = {k: round(1000.0 * t / n, 3) for k, (n, t) in hstats.items()
-                  if k in ("tensor", "rescale_gather", "rescale_col", "rescale_blk")}
-    # double-hoisted BSGS linear transform of one ciphertext, 4 x 4 diagonals
-    # (baby X^(5^i), i=1..3; giant X^(5^(4j)), j=1..3), uniform diagonals and key b halves
-    wb = ki.WORKLOADS["bsgs16"]
-    n1, n2 = wb.extra["n1"], wb.extra["n2"]
-    lt_keys = [ksa.to_device(ki.uniform_key_b(wb.index, k, beta, basis, w.N), 0) for k in range(len(wb.galois))]
-    lt_seeds = [ki.key_seed(wb.index, k) for k in range(len(wb.galois))]
-    lt_diag = ksa.to_device(ki.uniform_diagonals(wb.index, n2, n1, basis, w.N), 0)
-    lt_out = torch.empty((2, w.L, w.N), dtype=torch.int32, device="cuda:0")
+    def keygen_leg():
+        # key generation of the same relinearisation key on the GPU (pc_keygen): synthetic
+        # secret / error residues of the right shape (timing does not depend on their values)
+        s_coef = ksa.to_device(ki.uniform_key_b(w.index, 2, 1, basis, w.N)[0], 0)
+        e_coef = ksa.to_device(ki.uniform_key_b(w.index, 3, beta, basis, w.N), 0)
+        kg_out = torch.empty((beta, w.L + w.K, w.N), dtype=torch.int32, device="cuda:0")
+        ms = timed_calls(lambda i: ksa.keygen(prm, seed, w.L, 1, s_coef, e_coef, out=kg_out), 10)
+        return {"keys_per_s": round(1000.0 / ms, 1), "ms_per_key": round(ms, 4)}
 
-    def lt_step(i):
-        ksa.linear_transform(prm, cts[i % nbuf][0], lt_diag, w.L,
-                             baby_b=lt_keys[: n1 - 1], baby_seeds=lt_seeds[: n1 - 1],
-                             baby_galois=wb.galois[: n1 - 1], giant_b=lt_keys[n1 - 1:],
-                             giant_seeds=lt_seeds[n1 - 1:], giant_galois=wb.galois[n1 - 1:], out=lt_out)
+    def hmult_leg():
+        # homomorphic multiplication of 8 ciphertext pairs at the top level around the same
+        # key switch (pc_hmult: tensor, relinearise d2, rescale); per-kernel times profiled
+        hm_out = torch.empty((K8, 2, w.L - 1, w.N), dtype=torch.int32, device="cuda:0")
 
-    for i in range(3):
-        lt_step(i)
-    torch.cuda.synchronize()
-    l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    l0.record()
-    for i in range(args.steps):
-        lt_step(i)
-    l1.record()
-    torch.cuda.synchronize()
-    ms_lt = l0.elapsed_time(l1) / args.steps
-    ksa.profile_begin(prm)
-    for i in range(10):
-        lt_step(i)
-    lstats = ksa.profile_end(prm)
-    lt_kernels = {k: round(1000.0 * t / n, 3) for k, (n, t) in lstats.items() if k in ("bsgs_baby", "bsgs_giant")}
+        def hm_step(i):
+            ksa.hmult(prm, cts[i % nbuf], cts[(i + 1) % nbuf], evk_b, seed, w.L, out=hm_out)
+
+        ms = timed_calls(hm_step, args.steps)
+        fams = ("tensor", "rescale_gather", "rescale_col", "rescale_blk")
+        return {"hmults_per_s": round(K8 * 1000.0 / ms, 1), "ms_per_call": round(ms, 4),
+                "kernel_avg_us": profiled(hm_step, fams)}
+
+    def bsgs_leg():
+        # double-hoisted BSGS linear transform of one ciphertext, 4 x 4 diagonals
+        # (baby X^(5^i), i=1..3; giant X^(5^(4j)), j=1..3), uniform diagonals and key b halves
+        wb = ki.WORKLOADS["bsgs16"]
+        n1, n2 = wb.extra["n1"], wb.extra["n2"]
+        lt_keys = [ksa.to_device(ki.uniform_key_b(wb.index, k, beta, basis, w.N), 0) for k in range(len(wb.galois))]
+        lt_seeds = [ki.key_seed(wb.index, k) for k in range(len(wb.galois))]
+        lt_diag = ksa.to_device(ki.uniform_diagonals(wb.index, n2, n1, basis, w.N), 0)
+        lt_out = torch.empty((2, w.L, w.N), dtype=torch.int32, device="cuda:0")
+
+        def lt_step(i):
+            ksa.linear_transform(prm, cts[i % nbuf][0], lt_diag, w.L,
+                                 baby_b=lt_keys[: n1 - 1], baby_seeds=lt_seeds[: n1 - 1],
+                                 baby_galois=wb.galois[: n1 - 1], giant_b=lt_keys[n1 - 1:],
+                                 giant_seeds=lt_seeds[n1 - 1:], giant_galois=wb.galois[n1 - 1:], out=lt_out)
+
+        ms = timed_calls(lt_step, args.steps)
+        return {"transforms_per_s": round(1000.0 / ms, 1), "ms_per_call": round(ms, 4),
+                "key_switches": (n1 - 1) + (n2 - 1), "kernel_avg_us": profiled(lt_step, ("bsgs_baby", "bsgs_giant"))}
+
+    def leg(fn):
+        """An auxiliary measurement; a failure is reported in the line instead of losing it."""
+        try:
+            return fn()
+        except Exception as exc:  # noqa: BLE001 - reported, not hidden
+            print(f"[bench] {fn.__name__} failed: {exc!r}", file=sys.stderr, flush=True)
+            return {"error": repr(exc)}
+
+    keygen_res = leg(keygen_leg)
+    hmult_res = leg(hmult_leg)
+    bsgs_res = leg(bsgs_leg)
     # measured stream-copy bandwidth (context for the 8 TB/s peak): 1 GiB read + 1 GiB write;
     # left out of counter runs, whose byte calibration needs the 256 MiB copy to be the only one
     copy_gbs = None
@@ -316,7 +322,7 @@ def main():
         torch.cuda.synchronize()
         copy_gbs = round(2.0 * csrc.numel() * 4 / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9, 1)
         del csrc, cdst
-    others = None if args.no_configs else other_configs(ksa, torch, args)
+    others = None if args.no_configs else leg(lambda: other_configs(ksa, torch, args))
     kernels_stored = {k: round(1000.0 * t / n, 3) for k, (n, t) in sorted(kstats_stored.items(), key=lambda kv: -kv[1][1])}
     dom = next(iter(kernels))
     roofs = {k: kernel_roofline(k, v["avg_us"], w, K8, beta, alpha) for k, v in kernels.items()}
@@ -362,11 +368,9 @@ def main():
             "k8_stored": {"ks_per_s": round(K8 * 1000.0 / ms8s, 1), "ms_per_call": round(ms8s, 4)},
             "k1_stored": {"ks_per_s": round(1000.0 / ms1s, 1), "ms_per_call": round(ms1s, 4)},
             "k8_chacha_profiled": {"ms_per_call": round(ms8p, 4)},
-            "keygen_relin_key": {"keys_per_s": round(1000.0 / ms_kg, 1), "ms_per_key": round(ms_kg, 4)},
-            "hmult_k8": {"hmults_per_s": round(K8 * 1000.0 / ms_hm, 1), "ms_per_call": round(ms_hm, 4),
-                         "kernel_avg_us": hm_kernels},
-            "bsgs_4x4": {"transforms_per_s": round(1000.0 / ms_lt, 1), "ms_per_call": round(ms_lt, 4),
-                         "key_switches": (n1 - 1) + (n2 - 1), "kernel_avg_us": lt_kernels},
+            "keygen_relin_key": keygen_res,
+            "hmult_k8": hmult_res,
+            "bsgs_4x4": bsgs_res,
         },
         "ms_per_step_k8": per_step[(K8, False)],
         "ms_per_step_k1": per_step[(1, False)],
