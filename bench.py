@@ -75,60 +75,97 @@ def parse():
     return ap.parse_args()
 
 
-def alg_bytes_per_launch(kernel, w, batch, beta, alpha):
+LRC = {12: 6, 16: 8, 17: 9}   # NTT stages in the column pass (the block pass does the rest)
+
+
+def _shape(N, level, K, alpha, beta):
+    digits = [min(alpha, level - d * alpha) for d in range(beta)]
+    lrc = LRC[N.bit_length() - 1]
+    return digits, sum(level + K - a for a in digits), lrc, N.bit_length() - 1 - lrc
+
+
+def alg_bytes(kernel, N, level, K, alpha, beta, batch, nkeys=1):
     """Algorithmic bytes one launch must move: each input limb read once, each output limb written once.
 
-    Limb = N words of 4 bytes. l = level, K special primes, T_d = l - alpha + K
-    targets per digit (the last digit may be shorter; handled exactly below).
+    Limb = N words of 4 bytes; T_d = level - alpha_d + K targets per digit; the
+    inner product reads each key's b half once per batch; ModDown runs on
+    2 polynomials of every (key, ciphertext) item.
     """
-    N, l, K = w.N, w.L, w.K
-    limb = 4 * N
-    digits = [min(alpha, l - d * alpha) for d in range(beta)]
-    targets = sum(l + K - a for a in digits)
+    l, limb = level, 4 * N
+    _, targets, _, _ = _shape(N, level, K, alpha, beta)
+    items = batch * nkeys
     table = {
         # ModUp: c1 in, y' out; y' in place (scaled y); y in, targets out; targets in, ext out
         "modup_inv_blk": batch * (l + l),
         "modup_inv_col": batch * (l + l),
         "modup_bconv": batch * (l + targets),
         "modup_fwd_blk": batch * (targets + targets),
-        # IP: ext (targets) + own c1 limbs read, b read once per batch, acc written
-        "inner_product": batch * (targets + l) + beta * (l + K) + batch * 2 * (l + K),
-        # ModDown on 2 polys per item
-        "moddown_inv_blk": batch * 2 * (K + K),
-        "moddown_inv_col": batch * 2 * (K + K),
-        "moddown_bconv": batch * 2 * (K + l),
-        "moddown_fwd_blk": batch * 2 * (l + l + l) + batch * l,  # tmp2 + acc in, out; c0 in
+        # IP: ext (targets) + own c1 limbs read once per key, b read once per key, acc written
+        "inner_product": nkeys * (batch * (targets + l) + beta * (l + K)) + items * 2 * (l + K),
+        "moddown_inv_blk": items * 2 * (K + K),
+        "moddown_inv_col": items * 2 * (K + K),
+        "moddown_bconv": items * 2 * (K + l),
+        "moddown_fwd_blk": items * 2 * (l + l + l) + items * l,  # tmp2 + acc in, out; c0 in
     }
     return table[kernel] * limb
 
 
-def alg_ops_per_launch(kernel, w, batch, beta, alpha):
+def alg_ops(kernel, N, level, K, alpha, beta, batch, nkeys=1):
     """Algorithmic 32-bit integer operations of one launch (op counts of the primitives above).
 
-    An NTT pass over a limb does N/2 butterflies per stage; the column and block
-    passes of a 2^16-point transform cover 8 stages each.
+    An NTT pass over a limb does N/2 butterflies per stage: the column pass
+    covers the first LRC stages, the block pass the rest.
     """
-    N, l, K = w.N, w.L, w.K
-    digits = [min(alpha, l - d * alpha) for d in range(beta)]
-    half_pass = N // 2 * 8 * OPS_BUTTERFLY          # one 8-stage pass over one limb
+    l = level
+    digits, targets, lrc, lrb = _shape(N, level, K, alpha, beta)
+    col = N // 2 * lrc * OPS_BUTTERFLY
+    blk = N // 2 * lrb * OPS_BUTTERFLY
     conv_targets = sum((l + K - a) * N * dot_ops(a) for a in digits)
-    targets = sum(l + K - a for a in digits)
     lk = l + K
+    items = batch * nkeys
     key_ops = lk * N * beta * (OPS_REDC + OPS_CHACHA12_BLOCK / 8 + OPS_WORDPAIR)  # b to Montgomery form, a regenerated
     pairs = beta // 2 + beta % 2
     ip_item = lk * N * 2 * (pairs * (2 + OPS_REDC + OPS_ADDMOD))                   # both sums, products paired per REDC
     table = {
-        "modup_inv_blk": batch * l * half_pass,
-        "modup_inv_col": batch * l * (half_pass + N * OPS_SHOUP),
-        "modup_bconv": batch * (conv_targets + targets * half_pass),
-        "modup_fwd_blk": batch * targets * half_pass,
-        "inner_product": key_ops + batch * ip_item,
-        "moddown_inv_blk": batch * 2 * K * half_pass,
-        "moddown_inv_col": batch * 2 * K * (half_pass + N * OPS_SHOUP),
-        "moddown_bconv": batch * 2 * l * (N * dot_ops(K) + half_pass),
-        "moddown_fwd_blk": batch * 2 * l * (half_pass + N * (2 * OPS_ADDMOD + OPS_SHOUP)),
+        "modup_inv_blk": batch * l * blk,
+        "modup_inv_col": batch * l * (col + N * OPS_SHOUP),
+        "modup_bconv": batch * (conv_targets + targets * col),
+        "modup_fwd_blk": batch * targets * blk,
+        "inner_product": nkeys * key_ops + items * ip_item,
+        "moddown_inv_blk": items * 2 * K * blk,
+        "moddown_inv_col": items * 2 * K * (col + N * OPS_SHOUP),
+        "moddown_bconv": items * 2 * l * (N * dot_ops(K) + col),
+        "moddown_fwd_blk": items * 2 * l * (blk + N * (2 * OPS_ADDMOD + OPS_SHOUP)),
     }
     return table[kernel]
+
+
+KERNELS = ("modup_inv_blk", "modup_inv_col", "modup_bconv", "modup_fwd_blk", "inner_product",
+           "moddown_inv_blk", "moddown_inv_col", "moddown_bconv", "moddown_fwd_blk")
+
+
+def alg_bytes_per_launch(kernel, w, batch, beta, alpha):
+    return alg_bytes(kernel, w.N, w.L, w.K, alpha, beta, batch)
+
+
+def alg_ops_per_launch(kernel, w, batch, beta, alpha):
+    return alg_ops(kernel, w.N, w.L, w.K, alpha, beta, batch)
+
+
+def path_fractions(calls, ms):
+    """HBM and int32-ALU fractions of a measured call made of the key-switch launches in
+    `calls` (a list of (N, level, K, alpha, beta, batch, nkeys, with_modup) tuples)."""
+    nbytes = nops = 0
+    for (N, level, K, alpha, beta, batch, nkeys, with_modup) in calls:
+        for k in KERNELS:
+            if k.startswith("modup") and not with_modup:
+                continue
+            nbytes += alg_bytes(k, N, level, K, alpha, beta, batch, nkeys)
+            nops += alg_ops(k, N, level, K, alpha, beta, batch, nkeys)
+    t = ms * 1e-3
+    return {"alg_bytes_per_call": int(nbytes), "alg_ops_per_call": int(nops),
+            "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "alu_frac": round(nops / t / 1e12 / INT32_PEAK_TOPS, 4)}
 
 
 def kernel_roofline(kernel, avg_us, w, batch, beta, alpha):
@@ -422,13 +459,14 @@ def other_configs(ksa, torch, args, steps=10):
         res = torch.empty((len(w.galois), 1, 2, w.L, w.N), dtype=torch.int32, device="cuda:0")
         ms = _time_calls(torch, lambda i: ksa.keyswitch_ex(prm, ct, keys, w.galois, w.L, seeds=seeds, out=res), steps)
         out["hoist16"] = {"ks_per_s": round(len(w.galois) * 1000.0 / ms, 1), "ms_per_call": round(ms, 4),
-                          "key_switches_per_call": len(w.galois)}
+                          "key_switches_per_call": len(w.galois),
+                          "path": path_fractions([(w.N, w.L, w.K, prm.alpha(w.L), beta, 1, len(w.galois), True)], ms)}
         del keys, ct, res
     # level sweep
     w = ki.WORKLOADS["levels16"]
     with ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=8, device=0) as prm:
         base = ki.ciphertexts(w.index, prm.primes[: w.L], w.N, 8)
-        per_level = {}
+        per_level, per_level_path = {}, {}
         for level in w.levels:
             basis, beta = prm.basis(level), prm.beta(level)
             keys = [ksa.to_device(ki.uniform_key_b(w.index, 10 * level + k, beta, basis, w.N), 0) for k in range(2)]
@@ -442,8 +480,10 @@ def other_configs(ksa, torch, args, steps=10):
 
             ms = _time_calls(torch, one_level, steps)
             per_level[str(level)] = round(16 * 1000.0 / ms, 1)
+            one = (w.N, level, w.K, prm.alpha(level), beta, 8, 1, True)
+            per_level_path[str(level)] = path_fractions([one, one], ms)
             del keys, ct, res
-        out["levels16"] = {"ks_per_s_by_level": per_level}
+        out["levels16"] = {"ks_per_s_by_level": per_level, "path_by_level": per_level_path}
     # N=2^17 chain
     w = ki.WORKLOADS["n17"]
     with ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=8, device=0) as prm:
@@ -459,8 +499,9 @@ def other_configs(ksa, torch, args, steps=10):
             ksa.keyswitch_ex(prm, mid[0], [keys[1]], [w.galois[1]], w.L, seeds=[seeds[1]], out=res)
 
         ms = _time_calls(torch, chain, steps)
+        one = (w.N, w.L, w.K, prm.alpha(w.L), beta, 8, 1, True)
         out["n17"] = {"ks_per_s": round(16 * 1000.0 / ms, 1), "ms_per_call": round(ms, 4),
-                      "key_switches_per_call": 16}
+                      "key_switches_per_call": 16, "path": path_fractions([one, one], ms)}
         del keys, ct, mid, res
     return out
 
