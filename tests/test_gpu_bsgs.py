@@ -79,7 +79,7 @@ def _run(prm, ct, diag, baby, giant, level):
 
 @pytest.mark.parametrize("level,n1,n2,partition", [
     (7, 3, 3, 0), (5, 2, 3, 0), (4, 4, 2, 0), (2, 1, 4, 0), (7, 3, 2, 1), (3, 2, 2, 1),
-    (6, 8, 2, 0), (7, 1, 8, 0)])
+    (6, 8, 2, 0), (7, 1, 8, 0), (1, 2, 2, 0), (1, 3, 3, 1)])
 def test_small_ring_matches_oracle(level, n1, n2, partition):
     """N=2^12, L=7, dnum=3, K=3 with real rotation keys and small diagonals."""
     prm, oprm = params_pair(12, 7, 3, 3, partition=partition, max_batch=4, max_hoist=8)

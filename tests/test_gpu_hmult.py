@@ -94,7 +94,7 @@ def test_rescale_matches_oracle(log2n, L, dnum, K, level, batch):
     prm.close()
 
 
-@pytest.mark.parametrize("level,partition", [(7, 0), (4, 0), (2, 0), (7, 1), (3, 1)])
+@pytest.mark.parametrize("level,partition", [(7, 0), (4, 0), (2, 0), (7, 1), (3, 1), (2, 1)])
 def test_small_ring_hmult_matches_oracle(level, partition):
     """N=2^12, L=7, dnum=3, K=3 with a real key of s^2 (at the key level the partition asks for)."""
     prm, oprm = params_pair(12, 7, 3, 3, partition=partition, max_batch=3)
