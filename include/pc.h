@@ -47,6 +47,8 @@
  * must not overlap. The library owns a workspace arena inside pc_params, sized
  * at creation for max_batch ciphertexts and max_hoist keys; calls that use it
  * must not run concurrently on different streams for the same pc_params.
+ * pc_keyswitch_ex calls that each bring their own workspace may run
+ * concurrently on different streams (the constant tables are read-only).
  *
  * Errors. Every entry point validates its arguments on the host before any
  * launch and returns PC_EINVAL (null pointer, level outside [1, L], even or
