@@ -117,6 +117,9 @@ struct KsWorkspace {
   uint32_t* acc;   // [items][2][l+K][N]     inner product
   uint32_t* y2;    // [items][2][K][N]       ModDown coefficients of the P limbs
   uint32_t* tmp2;  // [items][2][l][N]       ModDown after the column pass
+  // ext in the segment layout, for inner products that gather under
+  // automorphisms (set before ModUp; ModUp then also files c1's limbs there)
+  bool seg = false;
 };
 size_t ks_workspace_bytes(const pc_params* p, uint32_t level, uint32_t batch, uint32_t items);
 KsWorkspace ks_workspace_carve(const pc_params* p, void* base, uint32_t level, uint32_t batch, uint32_t items);

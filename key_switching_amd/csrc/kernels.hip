@@ -167,6 +167,7 @@ struct ModUpArgs {
   uint32_t* tmp;  // [batch][beta][l+K][N]
   uint32_t* ext;  // [batch][beta][l+K][N]
   int N, level, K, L, alpha, beta, batch, ngroups;
+  int seg;  // ext in the segment layout, the digits' own limbs included (gathers follow)
   size_t scale_off, bconv_off;
 };
 
@@ -178,7 +179,9 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_modup_inv_blk(ModUpArgs
   const size_t b = blockIdx.y / A.level, i = blockIdx.y % A.level, z = b * A.level + i;
   PlainLimb L{A.T.r[i], A.T.rinv[i], A.T.tw_iblk + i * A.N, A.ct + b * A.ct_stride + A.c1_off + i * A.N,
               A.y + z * A.N};
-  inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
+  // with the segment layout, c1's limb i is also the own limb of digit i / alpha
+  uint32_t* own = A.seg ? A.ext + ((b * A.beta + i / A.alpha) * (A.level + A.K) + i) * A.N : nullptr;
+  inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB, own);
 }
 
 template <int LOGN>
@@ -354,7 +357,7 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_modup_fwd_blk(ModUpArgs
   // time, then touch different offsets, while each XCD still serves one tile
   // (one slice of the twiddles) per prime
   const int tile = (int)((blockIdx.x + (uint32_t)j) % (uint32_t)blk_tiles<LOGN>());
-  fwd_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, tile * C::CB);
+  fwd_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, tile * C::CB, A.seg != 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -379,6 +382,7 @@ struct IPArgs {
   int N, level, K, L, alpha, batch, nkeys;
   int key_level;  // level of the keys (their limbs are [q_0..q_{key_level-1}, p_0..p_{K-1}])
   int limb_xcd;   // 0, or the split of limb_xcd_decode: tiles of limb j grouped on XCDs (see below)
+  int lrc, lrb;   // N = 2^(lrc + lrb): columns and rows of the segment layout
   uint32_t key_base;
   const uint32_t* evk_b[kMaxKeysPerLaunch];
   const uint32_t* evk_a[kMaxKeysPerLaunch];
@@ -421,20 +425,30 @@ __device__ __forceinline__ void load_key8(const uint32_t* limb, int p0, int p1, 
 
 // phi(ext_d[j]) of batch item b at the thread's 8 positions: the digit's own
 // limbs come straight from c1, the others from ModUp's output; the automorphism
-// index map is a gather unless the Galois element is 1.
-template <int BETA>
+// index map is a gather unless the Galois element is 1. With the segment
+// layout (SEG) every limb, own ones included, is read from ext at src_idx.
+template <int BETA, bool SEG>
 __device__ __forceinline__ void load_digits(const IPArgs& A, int b, int j, int lk, uint32_t g, int p0, int p1,
                                             const uint32_t (&src_idx)[8], uint32_t (&e)[BETA][8]) {
+  // the offsets are made opaque per call: otherwise the compiler keeps a
+  // 64-bit address per digit and position live across the batch loop
+  uint32_t idx[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    idx[k] = src_idx[k];
+    asm volatile("" : "+v"(idx[k]));
+  }
+  asm volatile("" : "+v"(p0), "+v"(p1));
 #pragma unroll
   for (int d = 0; d < BETA; ++d) {
-    const bool own = j < A.level && j >= d * A.alpha && j < (d + 1) * A.alpha;
+    const bool own = !SEG && j < A.level && j >= d * A.alpha && j < (d + 1) * A.alpha;
     const uint32_t* src = own ? A.ct + b * A.ct_stride + A.c1_off + (size_t)j * A.N
                               : A.ext + (((size_t)b * BETA + d) * lk + j) * A.N;
-    if (g == 1u) {
+    if (!SEG && g == 1u) {
       load8(src, p0, p1, e[d]);
     } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) e[d][k] = at32(src, src_idx[k]);
+      for (int k = 0; k < 8; ++k) e[d][k] = at32(src, idx[k]);
     }
   }
 }
@@ -445,6 +459,34 @@ __device__ __forceinline__ void gather_index(int N, uint32_t g, int p0, int p1, 
   const uint32_t h = (g - 1) >> 1, mask = (uint32_t)N - 1;
 #pragma unroll
   for (int k = 0; k < 8; ++k) idx[k] = ((uint32_t)pos8(p0, p1, k) * g + h) & mask;
+}
+
+// Segment layout (store_tile_segments): a limb of N = 2^(lrc + lrb) words is
+// 2^lrb rows of 2^lrc columns, position row 2^lrc + col; segment col holds
+// column col, natural row bitrev(x) at offset col 2^lrb + x. Under X -> X^g
+// the position p = row 2^lrc + col reads source position g p + h mod N, that
+// is column (g col + h) mod 2^lrc, row (g row + floor((g col + h) / 2^lrc))
+// mod 2^lrb: all rows of one output column come from one source column, one
+// 2^lrb-word segment.
+__device__ __forceinline__ uint32_t seg_src_index(uint32_t p, uint32_t g, uint32_t h, int lrc, int lrb) {
+  const uint32_t cmask = (1u << lrc) - 1, rmask = (1u << lrb) - 1;
+  const uint32_t u = (p & cmask) * g + h;
+  const uint32_t row = ((p >> lrc) * g + (u >> lrc)) & rmask;
+  return ((u & cmask) << lrb) | (__brev(row) >> (32 - lrb));
+}
+
+// Position of run `run` (8 consecutive positions, one ChaCha block) when runs
+// walk each 8-column strip down its rows: the lanes of a wave hold consecutive
+// rows of one strip, so each of a thread's 8 gathers reads, across the wave,
+// a single segment.
+__device__ __forceinline__ int seg_run_pos(int run, int lrc, int lrb) {
+  return ((run & ((1 << lrb) - 1)) << lrc) + ((run >> lrb) << 3);
+}
+
+__device__ __forceinline__ void gather_index_seg(const IPArgs& A, uint32_t g, int p0, uint32_t (&idx)[8]) {
+  const uint32_t h = (g - 1) >> 1;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) idx[k] = seg_src_index((uint32_t)(p0 + k), g, h, A.lrc, A.lrb);
 }
 
 // (sum_d e_d b_d, sum_d e_d a_d) at one position; am(d) gives a_d there.
@@ -493,21 +535,26 @@ __device__ __forceinline__ bool limb_xcd_unit(int tiles, int split, int limbs, i
 // (tiles, limbs, keys), or under automorphisms the 1-D walk of
 // limb_xcd_decode. STORED: the a half is read; otherwise each thread expands its
 // ChaCha block per digit. BT: the batch size when known at compile time (1 or
-// 8), else 0.
-template <int BETA, int ROUNDS, bool STORED, int BT>
+// 8), else 0. SEG: ext is in the segment layout and a tile's runs walk strips
+// (seg_run_pos).
+template <int BETA, int ROUNDS, bool STORED, int BT, bool SEG>
 __global__ void __launch_bounds__(kIpThreads) k_inner_product(IPArgs A) {
   constexpr int TILE = 8 * kIpThreads;
   const int lk = A.level + A.K;
   int tile = (int)blockIdx.x, j = (int)blockIdx.y, key = (int)blockIdx.z;
   if (A.limb_xcd && !limb_xcd_unit(A.N / TILE, A.limb_xcd, lk, A.nkeys, tile, j, key)) return;
-  const int p0 = STORED ? tile * TILE + 4 * (int)threadIdx.x : (tile * kIpThreads + (int)threadIdx.x) * 8;
-  const int p1 = STORED ? p0 + TILE / 2 : p0 + 4;
+  const int run = tile * kIpThreads + (int)threadIdx.x;
+  const int p0 = SEG ? seg_run_pos(run, A.lrc, A.lrb) : STORED ? tile * TILE + 4 * (int)threadIdx.x : run * 8;
+  const int p1 = !SEG && STORED ? p0 + TILE / 2 : p0 + 4;
   const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
   const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj];
   const uint32_t g = A.galois[key];
   const int kj = key_limb(A, j);
   uint32_t src_idx[8];
-  gather_index(A.N, g, p0, p1, src_idx);
+  if constexpr (SEG)
+    gather_index_seg(A, g, p0, src_idx);
+  else
+    gather_index(A.N, g, p0, p1, src_idx);
 
   uint32_t bm[BETA][8], am[BETA][8];
 #pragma unroll
@@ -528,7 +575,7 @@ __global__ void __launch_bounds__(kIpThreads) k_inner_product(IPArgs A) {
 #pragma unroll 1
   for (int b = 0; b < batch; ++b) {
     uint32_t e[BETA][8];
-    load_digits<BETA>(A, b, j, lk, g, p0, p1, src_idx, e);
+    load_digits<BETA, SEG>(A, b, j, lk, g, p0, p1, src_idx, e);
     uint32_t o0[8], o1[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) ip_sums<BETA>(e, bm, k, [&](int d) { return am[d][k]; }, r, rinv, o0[k], o1[k]);
@@ -548,7 +595,7 @@ __global__ void __launch_bounds__(kIpThreads) k_inner_product(IPArgs A) {
 // grid size; both halves expand the first unit together.
 constexpr int kIpHalf = 128;  // consumer threads = producer threads per workgroup
 
-template <int BETA, int ROUNDS, int BT>
+template <int BETA, int ROUNDS, int BT, bool SEG>
 __global__ void __launch_bounds__(2 * kIpHalf) k_ip_regen(IPArgs A) {
   constexpr int TILE = 8 * kIpHalf;
   __shared__ uint32_t am_lds[2][BETA][8][kIpHalf];  // [slot][digit][k][consumer thread]
@@ -573,7 +620,8 @@ __global__ void __launch_bounds__(2 * kIpHalf) k_ip_regen(IPArgs A) {
   };
   // a half of digits [d0, d1) of `unit`: this thread expands ChaCha block
   // tile*kIpHalf + t (tile positions 8t..8t+7) and files each value under the
-  // consumer thread and slot that own its position
+  // consumer thread and slot that own its position; with SEG, consumer t owns
+  // exactly the block of run tile*kIpHalf + t (seg_run_pos)
   auto produce = [&](int unit, int slot, int d0, int d1) {
     int key, j, tile;
     if (!decode(unit, key, j, tile)) return;
@@ -581,25 +629,39 @@ __global__ void __launch_bounds__(2 * kIpHalf) k_ip_regen(IPArgs A) {
     const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj];
     const int hi = (8 * t) >= TILE / 2;
     const int ct0 = (8 * t - hi * (TILE / 2)) >> 2;  // consumer thread of positions 8t..8t+3
+    const int run = tile * kIpHalf + t;
+    const uint32_t block = SEG ? (uint32_t)(seg_run_pos(run, A.lrc, A.lrb) >> 3) : (uint32_t)run;
 #pragma unroll
     for (int d = 0; d < BETA; ++d) {
       if (d < d0 || d >= d1) continue;
       uint32_t w[16];
-      chacha_block<ROUNDS>(A.seed[key], (uint32_t)(tile * kIpHalf + t), 0u, (uint32_t)d, (uint32_t)key_limb(A, j), w);
+      chacha_block<ROUNDS>(A.seed[key], block, 0u, (uint32_t)d, (uint32_t)key_limb(A, j), w);
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        am_lds[slot][d][4 * hi + (k & 3)][ct0 + (k >> 2)] = word_pair_to_mont(w[2 * k], w[2 * k + 1], r, rinv);
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t v = word_pair_to_mont(w[2 * k], w[2 * k + 1], r, rinv);
+        if constexpr (SEG)
+          am_lds[slot][d][k][t] = v;
+        else
+          am_lds[slot][d][4 * hi + (k & 3)][ct0 + (k >> 2)] = v;
+      }
+      // one digit's block at a time: interleaving the digits' ChaCha states
+      // would take every register
+      asm volatile("" ::: "memory");
     }
   };
   auto consume = [&](int unit, int slot) {
     int key, j, tile;
     if (!decode(unit, key, j, tile)) return;
-    const int p0 = tile * TILE + 4 * t, p1 = p0 + TILE / 2;
+    const int p0 = SEG ? seg_run_pos(tile * kIpHalf + t, A.lrc, A.lrb) : tile * TILE + 4 * t;
+    const int p1 = SEG ? p0 + 4 : p0 + TILE / 2;
     const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
     const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj];
     const uint32_t g = A.galois[key];
     uint32_t src_idx[8];
-    gather_index(A.N, g, p0, p1, src_idx);
+    if constexpr (SEG)
+      gather_index_seg(A, g, p0, src_idx);
+    else
+      gather_index(A.N, g, p0, p1, src_idx);
     uint32_t bm[BETA][8];
 #pragma unroll
     for (int d = 0; d < BETA; ++d)
@@ -612,7 +674,7 @@ __global__ void __launch_bounds__(2 * kIpHalf) k_ip_regen(IPArgs A) {
       int sl = slot;
       asm volatile("" : "+s"(sl));
       uint32_t e[BETA][8];
-      load_digits<BETA>(A, b, j, lk, g, p0, p1, src_idx, e);
+      load_digits<BETA, SEG>(A, b, j, lk, g, p0, p1, src_idx, e);
       uint32_t o0[8], o1[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k)
@@ -1196,6 +1258,7 @@ hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stri
   A.scale_off = p->mu_scale_off[level];
   A.bconv_off = p->mu_bconv_off[level];
   A.batch = (int)batch;
+  A.seg = ws.seg ? 1 : 0;
   const uint32_t rows_in = batch * level;
   const uint32_t rows_ext = batch * (uint32_t)A.beta * (level + p->K);
   // the last digit is the shortest, so it has the most targets
@@ -1259,8 +1322,8 @@ static uint32_t blk_tiles_of(uint32_t log2n) {
 }
 
 template <int BETA, int ROUNDS, int BT>
-static void launch_ip_regen(const pc_params* p, const IPArgs& A0, hipStream_t s) {
-  auto kern = k_ip_regen<BETA, ROUNDS, BT>;
+static void launch_ip_regen(const pc_params* p, const IPArgs& A0, bool seg, hipStream_t s) {
+  auto kern = seg ? k_ip_regen<BETA, ROUNDS, BT, true> : k_ip_regen<BETA, ROUNDS, BT, false>;
   const uint32_t lk = (uint32_t)(A0.level + A0.K), tiles = p->N / (8 * kIpHalf);
   IPArgs A = A0;
   if (A.limb_xcd) A.limb_xcd = xcd_split(lk, tiles);
@@ -1272,14 +1335,25 @@ static void launch_ip_regen(const pc_params* p, const IPArgs& A0, hipStream_t s)
   hipLaunchKernelGGL(kern, dim3(grid), dim3(2 * kIpHalf), 0, s, A);
 }
 
+template <int BETA, int BT, bool SEG>
+static void launch_ip_kernel(const IPArgs& A, dim3 grid, bool stored, int rounds, hipStream_t s) {
+  if (stored)
+    hipLaunchKernelGGL((k_inner_product<BETA, 12, true, BT, SEG>), grid, dim3(kIpThreads), 0, s, A);
+  else if (rounds == 20)
+    hipLaunchKernelGGL((k_inner_product<BETA, 20, false, BT, SEG>), grid, dim3(kIpThreads), 0, s, A);
+  else
+    hipLaunchKernelGGL((k_inner_product<BETA, 12, false, BT, SEG>), grid, dim3(kIpThreads), 0, s, A);
+}
+
 template <int BETA, int BT>
-static void launch_ip_bt(const pc_params* p, const IPArgs& A0, uint32_t nkeys, bool stored, hipStream_t s) {
+static void launch_ip_bt(const pc_params* p, const IPArgs& A0, uint32_t nkeys, bool stored, bool seg,
+                         hipStream_t s) {
   if constexpr (BT != 1) {
     if (!stored && A0.batch >= 2) {  // regenerated a half and a batch to overlap it with
       if (p->chacha_rounds == 20)
-        launch_ip_regen<BETA, 20, BT>(p, A0, s);
+        launch_ip_regen<BETA, 20, BT>(p, A0, seg, s);
       else
-        launch_ip_regen<BETA, 12, BT>(p, A0, s);
+        launch_ip_regen<BETA, 12, BT>(p, A0, seg, s);
       return;
     }
   }
@@ -1289,22 +1363,21 @@ static void launch_ip_bt(const pc_params* p, const IPArgs& A0, uint32_t nkeys, b
   const uint32_t sp = (uint32_t)A.limb_xcd;
   const dim3 grid = sp ? dim3(8 * ((lk * sp + 7) / 8) * nkeys * (tiles / sp)) : dim3(tiles, lk, nkeys);
   LaunchTimer tm(p, KID_INNER_PRODUCT, s);
-  if (stored)
-    hipLaunchKernelGGL((k_inner_product<BETA, 12, true, BT>), grid, dim3(kIpThreads), 0, s, A);
-  else if (p->chacha_rounds == 20)
-    hipLaunchKernelGGL((k_inner_product<BETA, 20, false, BT>), grid, dim3(kIpThreads), 0, s, A);
+  if (seg)
+    launch_ip_kernel<BETA, BT, true>(A, grid, stored, (int)p->chacha_rounds, s);
   else
-    hipLaunchKernelGGL((k_inner_product<BETA, 12, false, BT>), grid, dim3(kIpThreads), 0, s, A);
+    launch_ip_kernel<BETA, BT, false>(A, grid, stored, (int)p->chacha_rounds, s);
 }
 
 template <int BETA>
-static void launch_ip_beta(const pc_params* p, const IPArgs& A, uint32_t nkeys, bool stored, hipStream_t s) {
+static void launch_ip_beta(const pc_params* p, const IPArgs& A, uint32_t nkeys, bool stored, bool seg,
+                           hipStream_t s) {
   if (A.batch == 8)
-    launch_ip_bt<BETA, 8>(p, A, nkeys, stored, s);
+    launch_ip_bt<BETA, 8>(p, A, nkeys, stored, seg, s);
   else if (A.batch == 1)
-    launch_ip_bt<BETA, 1>(p, A, nkeys, stored, s);
+    launch_ip_bt<BETA, 1>(p, A, nkeys, stored, seg, s);
   else
-    launch_ip_bt<BETA, 0>(p, A, nkeys, stored, s);
+    launch_ip_bt<BETA, 0>(p, A, nkeys, stored, seg, s);
 }
 
 hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_offset,
@@ -1329,6 +1402,8 @@ hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t
     A.nkeys = (int)cnt;
     A.key_level = (int)key_level_of(p, level);
     A.key_base = base;
+    A.lrc = pass_split_lrc(p->log2n);
+    A.lrb = (int)p->log2n - A.lrc;
     bool stored = false;
     A.limb_xcd = 0;
     for (uint32_t k = 0; k < cnt; ++k) {
@@ -1341,12 +1416,12 @@ hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t
       A.galois[k] = kr.galois;
     }
     switch (beta) {
-      case 1: launch_ip_beta<1>(p, A, cnt, stored, s); break;
-      case 2: launch_ip_beta<2>(p, A, cnt, stored, s); break;
-      case 3: launch_ip_beta<3>(p, A, cnt, stored, s); break;
-      case 4: launch_ip_beta<4>(p, A, cnt, stored, s); break;
-      case 5: launch_ip_beta<5>(p, A, cnt, stored, s); break;
-      case 6: launch_ip_beta<6>(p, A, cnt, stored, s); break;
+      case 1: launch_ip_beta<1>(p, A, cnt, stored, ws.seg, s); break;
+      case 2: launch_ip_beta<2>(p, A, cnt, stored, ws.seg, s); break;
+      case 3: launch_ip_beta<3>(p, A, cnt, stored, ws.seg, s); break;
+      case 4: launch_ip_beta<4>(p, A, cnt, stored, ws.seg, s); break;
+      case 5: launch_ip_beta<5>(p, A, cnt, stored, ws.seg, s); break;
+      case 6: launch_ip_beta<6>(p, A, cnt, stored, ws.seg, s); break;
       default: return hipErrorInvalidValue;
     }
   }

@@ -359,10 +359,28 @@ __device__ __forceinline__ void fwd_col_pass(Limb& L, int col0) {
   (void)R;
 }
 
+// The tile of a block pass in the segment layout: column c0 + k of the limb
+// (natural positions row 2^LOGRC + c0 + k) is the contiguous run of 2^LOGRB
+// words at (c0 + k) 2^LOGRB, element x (natural row bitrev(x)) at offset x.
+// This is the order in which the tile sits in LDS, so consecutive lanes store
+// consecutive words. Every thread of the workgroup stores E words.
+template <int LOGRB, int LOGE, int C>
+__device__ __forceinline__ void store_tile_segments(const uint32_t* lds, uint32_t* __restrict__ dst, int c0) {
+  using Lay = BlkLds<LOGRB, LOGE>;
+  constexpr int R = 1 << LOGRB, E = 1 << LOGE, THREADS = C * (R / E);
+#pragma unroll
+  for (int m = 0; m < E; ++m) {
+    const int idx = (int)threadIdx.x + THREADS * m;
+    const int k = idx >> LOGRB, x = idx & (R - 1);
+    at32(dst, ((c0 + k) << LOGRB) + x) = lds[Lay::row(k) + Lay::col(x)];
+  }
+}
+
 // Forward block pass: stages LOGRC..n-1 on blocks B = bitrev(c0 + k), k < C.
-// Output element x of block B goes to natural position bitrev(x) 2^LOGRC + c0 + k.
+// Output element x of block B goes to natural position bitrev(x) 2^LOGRC + c0 + k,
+// or with `seg` to the segment layout (store_tile_segments).
 template <int LOGRC, int LOGRB, int LOGE, int C, class Limb>
-__device__ __forceinline__ void fwd_blk_pass(Limb& L, int c0) {
+__device__ __forceinline__ void fwd_blk_pass(Limb& L, int c0, bool seg = false) {
   constexpr int R = 1 << LOGRB, E = 1 << LOGE, ROUNDS = LOGRB / LOGE, TPB = R / E;
   static_assert(LOGRB % LOGE == 0, "rounds must tile the pass");
   using Lay = BlkLds<LOGRB, LOGE>;
@@ -378,6 +396,10 @@ __device__ __forceinline__ void fwd_blk_pass(Limb& L, int c0) {
 #pragma unroll
   for (int m = 0; m < E; ++m) lds[Lay::row(k) + Lay::col(elem_index<LOGRB, LOGE, false>(ROUNDS - 1, t, m))] = v[m];
   __syncthreads();
+  if (seg) {
+    store_tile_segments<LOGRB, LOGE, C>(lds, L.dst, c0);
+    return;
+  }
   const int kk = tid % C, rest = tid / C;
 #pragma unroll
   for (int m = 0; m < E; ++m) {
@@ -416,9 +438,10 @@ __device__ __forceinline__ void fwd_blk_pass_fetch(Limb& L, int c0) {
 
 // Inverse block pass: GS stages 0..LOGRB-1 on blocks B = bitrev(c0 + k); element
 // x of block B is read from natural position bitrev(x) 2^LOGRC + c0 + k and
-// written to B 2^LOGRB + x.
+// written to B 2^LOGRB + x. A non-null seg_dst also receives the input tile in
+// the segment layout (store_tile_segments).
 template <int LOGRC, int LOGRB, int LOGE, int C, class Limb>
-__device__ __forceinline__ void inv_blk_pass(Limb& L, int c0) {
+__device__ __forceinline__ void inv_blk_pass(Limb& L, int c0, uint32_t* seg_dst = nullptr) {
   constexpr int R = 1 << LOGRB, E = 1 << LOGE, ROUNDS = LOGRB / LOGE, TPB = R / E;
   static_assert(LOGRB % LOGE == 0, "rounds must tile the pass");
   using Lay = BlkLds<LOGRB, LOGE>;
@@ -433,6 +456,7 @@ __device__ __forceinline__ void inv_blk_pass(Limb& L, int c0) {
     }
   }
   __syncthreads();
+  if (seg_dst != nullptr) store_tile_segments<LOGRB, LOGE, C>(lds, seg_dst, c0);
   const int t = tid % TPB, k = tid / TPB;
   const int B = (int)bitrev((uint32_t)(c0 + k), LOGRC);
   uint32_t v[E];

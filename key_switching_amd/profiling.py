@@ -49,7 +49,7 @@ FAMILIES = {
     "modup_inv_col": "k_modup_inv_col<16>",
     "modup_bconv": "k_modup_bconv<16, 6>",
     "modup_fwd_blk": "k_modup_fwd_blk<16>",
-    "inner_product": "k_ip_regen<4, 12, 8>",
+    "inner_product": "k_ip_regen<4, 12, 8, false>",
     "moddown_inv_blk": "k_md_inv_blk<16>",
     "moddown_inv_col": "k_md_inv_col<16>",
     "moddown_bconv": "k_md_bconv<16, 6>",
@@ -96,8 +96,10 @@ def cmd_stats(a) -> str:
     rows = list(csv.DictReader(open(a.trace)))
     out = [f"# rocprofv3 kernel statistics: {a.title}", "",
            "Commands:", "", "```", a.cmd, "```", "",
-           f"device_sources_hash: {device_source_hash()}", "",
-           "Per kernel family, dispatches of its batch-8 launch (largest grid of that kernel in the run):", "",
+           f"device_sources_hash: {device_source_hash()}", ""]
+    if a.note:
+        out += [a.note, ""]
+    out += ["Per kernel family, dispatches of its batch-8 launch (largest grid of that kernel in the run):", "",
            "| family | dispatch | grid | launches | avg us | median us | min us | max us |",
            "|---|---|---|---|---|---|---|---|"]
     for fam, prefix in FAMILIES.items():
@@ -187,6 +189,7 @@ def main(argv=None):
     s.add_argument("--top", type=int, default=24)
     s.add_argument("--title", default="")
     s.add_argument("--cmd", default="")
+    s.add_argument("--note", default="")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)

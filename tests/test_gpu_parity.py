@@ -361,6 +361,9 @@ def test_n17_rotate_after_relinearise(n17_case):
     step2 = host(ksa.keyswitch_ex(prm, step1[0].contiguous(), [dev(rot.b)], [5], w.L, seeds=[rot.seed]))[0]
     ref2 = ks.keyswitch(c["oprm"], c["ref1"], rot, w.L)
     assert_equal(step2[c["b"]], ref2, "n17 chain")
+    # one ciphertext alone takes the segment-layout gather (2^9 columns of 2^8 rows)
+    one = host(ksa.keyswitch(prm, step1[0][c["b"]].contiguous(), dev(rot.b), rot.seed, w.L, 5))
+    assert_equal(one, ref2, "n17 single rotation")
 
 
 def test_caller_workspace_matches_arena():
@@ -375,6 +378,11 @@ def test_caller_workspace_matches_arena():
     assert_equal(a, b, "caller workspace")
     ref = ks.keyswitch_hoisted(oprm, cts[2], keys, 7)
     assert_equal(a[:, 2], ref, "3-item batch, 2 keys")
+    # one ciphertext: the segment layout, also read by the key with g = 1; a regenerated and stored
+    one = host(ksa.keyswitch_ex(prm, dev(cts[2:3]), kbs, [5, 1], 7, seeds=seeds))
+    assert_equal(one[:, 0], ref, "1 item, 2 keys")
+    one_stored = host(ksa.keyswitch_ex(prm, dev(cts[2:3]), kbs, [5, 1], 7, evk_a=[dev(ks.key_a(oprm, k)) for k in keys]))
+    assert_equal(one_stored, one, "1 item, 2 keys, stored a")
     small = torch.empty(16, dtype=torch.int32, device="cuda:0")
     with pytest.raises(ksa.PcError):
         ksa.keyswitch_ex(prm, dev(cts), kbs, [5, 1], 7, seeds=seeds, workspace=small)
