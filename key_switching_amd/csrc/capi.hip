@@ -351,7 +351,7 @@ const char* const kKernelNames[KID_COUNT] = {
     "modup_inv_col",   "modup_bconv",     "modup_fwd_blk",   "inner_product",  "moddown_inv_blk",
     "moddown_inv_col", "moddown_bconv",   "moddown_fwd_blk", "chacha_expand",  "keygen",
     "tensor",          "rescale_gather",  "rescale_col",     "rescale_blk",    "bsgs_baby",
-    "bsgs_giant"};
+    "bsgs_giant",      "seg_copy"};
 
 static hipEvent_t prof_event(const pc_params* p) {
   if (p->prof_used == p->prof_pool.size()) {
@@ -391,12 +391,18 @@ hipError_t launch_keyswitch(const pc_params* p, const uint32_t* ct, uint64_t ct_
   if (e != hipSuccess) return e;
   e = launch_inner_product(p, ct, ct_stride, c1_off, batch, level, ws, keys, nkeys, s);
   if (e != hipSuccess) return e;
+  // with the segment layout (one ciphertext), the combine pass gathers c0 from
+  // a segment-layout copy in y, which ModUp no longer needs
+  if (ws.seg) {
+    e = launch_seg_copy(p, ct, level, ws.y, s);
+    if (e != hipSuccess) return e;
+  }
   const size_t lk = level + p->K;
   for (uint32_t k0 = 0; k0 < nkeys; k0 += kMaxKeysPerLaunch) {
     const uint32_t nk = std::min<uint32_t>(kMaxKeysPerLaunch, nkeys - k0);
     const size_t item0 = (size_t)k0 * batch;
     e = launch_moddown(p, ws.acc + item0 * 2 * lk * p->N, nk * batch, 2, level, 1, out + item0 * 2 * level * p->N,
-                       ws, ct, ct_stride, batch, galois + k0, s);
+                       ws, ws.seg ? ws.y : ct, ct_stride, batch, galois + k0, s, ws.seg);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -154,6 +154,7 @@ enum KernelId {
   KID_RESCALE_BLK,
   KID_BSGS_BABY,
   KID_BSGS_GIANT,
+  KID_SEG_COPY,
   KID_COUNT
 };
 extern const char* const kKernelNames[KID_COUNT];
@@ -180,7 +181,9 @@ hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t
 // When c0 is non-null, c0 of ciphertext (item % batch) under the item's Galois element is added to u = 0.
 hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t items, uint32_t polys, uint32_t level,
                           int variant, uint32_t* out, const KsWorkspace& ws, const uint32_t* c0, uint64_t ct_stride,
-                          uint32_t batch, const uint32_t* galois_per_key, hipStream_t s);
+                          uint32_t batch, const uint32_t* galois_per_key, hipStream_t s, bool c0_seg = false);
+// Copy of `limbs` limbs from natural order into the segment layout (dst must not overlap src).
+hipError_t launch_seg_copy(const pc_params* p, const uint32_t* src, uint32_t limbs, uint32_t* dst, hipStream_t s);
 // b of a key at `level` from evaluation-form s ([lk][N]) and e ([beta][lk][N]);
 // gm[j] = [P]_{q_j} 2^32 mod q_j (q-limbs).
 hipError_t launch_keygen(const pc_params* p, const uint32_t seed[8], uint32_t level, uint32_t galois,

@@ -67,6 +67,20 @@ constexpr int blk_tiles() {
 // ---------------------------------------------------------------------------
 // limb policies
 // ---------------------------------------------------------------------------
+// Segment layout (store_tile_segments): a limb of N = 2^(lrc + lrb) words is
+// 2^lrb rows of 2^lrc columns, position row 2^lrc + col; segment col holds
+// column col, natural row bitrev(x) at offset col 2^lrb + x. Under X -> X^g
+// the position p = row 2^lrc + col reads source position g p + h mod N, that
+// is column (g col + h) mod 2^lrc, row (g row + floor((g col + h) / 2^lrc))
+// mod 2^lrb: all rows of one output column come from one source column, one
+// 2^lrb-word segment.
+__device__ __forceinline__ uint32_t seg_src_index(uint32_t p, uint32_t g, uint32_t h, int lrc, int lrb) {
+  const uint32_t cmask = (1u << lrc) - 1, rmask = (1u << lrb) - 1;
+  const uint32_t u = (p & cmask) * g + h;
+  const uint32_t row = ((p >> lrc) * g + (u >> lrc)) & rmask;
+  return ((u & cmask) << lrb) | (__brev(row) >> (32 - lrb));
+}
+
 struct PlainLimb {
   uint32_t r, rinv;
   const uint32_t* __restrict__ tw;
@@ -87,8 +101,10 @@ struct ScaledLimb {
 
 // ModDown combine: out = (acc - v) P^-1 (+ c0 at the automorphism's source
 // index). acc and c0 at the E output positions of this thread are fetched
-// before the transform (fwd_blk_pass_fetch).
-template <int E>
+// before the transform (fwd_blk_pass_fetch). c0 is in natural order, or with
+// SEG in the segment layout of a 2^LRB x 2^LRC limb: a thread's E positions
+// are rows of one column, so its gathers stay in one segment.
+template <int E, int LRC, int LRB, bool SEG>
 struct CombineLimb {
   uint32_t r, rinv, pinv, pinvp;
   const uint32_t* __restrict__ tw;
@@ -101,7 +117,8 @@ struct CombineLimb {
   __device__ __forceinline__ uint32_t load(int pos) const { return at32(src, pos); }
   __device__ __forceinline__ void fetch(int m, int pos) {
     av[m] = at32(acc, pos);
-    cv[m] = c0 ? at32(c0, ((uint32_t)pos * g + h) & mask) : 0u;
+    const uint32_t si = SEG ? seg_src_index((uint32_t)pos, g, h, LRC, LRB) : (((uint32_t)pos * g + h) & mask);
+    cv[m] = c0 ? at32(c0, si) : 0u;
   }
   __device__ __forceinline__ void finish(int m, int pos, uint32_t v) const {
     uint32_t o = mul_shoup(sub_mod(av[m], v, r), pinv, pinvp, r);
@@ -430,15 +447,14 @@ __device__ __forceinline__ void load_key8(const uint32_t* limb, int p0, int p1, 
 template <int BETA, bool SEG>
 __device__ __forceinline__ void load_digits(const IPArgs& A, int b, int j, int lk, uint32_t g, int p0, int p1,
                                             const uint32_t (&src_idx)[8], uint32_t (&e)[BETA][8]) {
-  // the offsets are made opaque per call: otherwise the compiler keeps a
-  // 64-bit address per digit and position live across the batch loop
+  // with SEG the offsets are made opaque per call: otherwise the compiler
+  // keeps a 64-bit address per digit and position live across the batch loop
   uint32_t idx[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     idx[k] = src_idx[k];
-    asm volatile("" : "+v"(idx[k]));
+    if constexpr (SEG) asm volatile("" : "+v"(idx[k]));
   }
-  asm volatile("" : "+v"(p0), "+v"(p1));
 #pragma unroll
   for (int d = 0; d < BETA; ++d) {
     const bool own = !SEG && j < A.level && j >= d * A.alpha && j < (d + 1) * A.alpha;
@@ -459,20 +475,6 @@ __device__ __forceinline__ void gather_index(int N, uint32_t g, int p0, int p1, 
   const uint32_t h = (g - 1) >> 1, mask = (uint32_t)N - 1;
 #pragma unroll
   for (int k = 0; k < 8; ++k) idx[k] = ((uint32_t)pos8(p0, p1, k) * g + h) & mask;
-}
-
-// Segment layout (store_tile_segments): a limb of N = 2^(lrc + lrb) words is
-// 2^lrb rows of 2^lrc columns, position row 2^lrc + col; segment col holds
-// column col, natural row bitrev(x) at offset col 2^lrb + x. Under X -> X^g
-// the position p = row 2^lrc + col reads source position g p + h mod N, that
-// is column (g col + h) mod 2^lrc, row (g row + floor((g col + h) / 2^lrc))
-// mod 2^lrb: all rows of one output column come from one source column, one
-// 2^lrb-word segment.
-__device__ __forceinline__ uint32_t seg_src_index(uint32_t p, uint32_t g, uint32_t h, int lrc, int lrb) {
-  const uint32_t cmask = (1u << lrc) - 1, rmask = (1u << lrb) - 1;
-  const uint32_t u = (p & cmask) * g + h;
-  const uint32_t row = ((p >> lrc) * g + (u >> lrc)) & rmask;
-  return ((u & cmask) << lrb) | (__brev(row) >> (32 - lrb));
 }
 
 // Position of run `run` (8 consecutive positions, one ChaCha block) when runs
@@ -783,7 +785,8 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv(ModDownArgs A)
   }
 }
 
-template <int LOGN>
+// SEG: c0 in the segment layout.
+template <int LOGN, bool SEG>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_fwd_blk(ModDownArgs A) {
   using C = Cfg<LOGN>;
   const int lk = A.level + A.K;
@@ -800,7 +803,7 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_fwd_blk(ModDownArgs 
     c0 = A.c0 + (item % A.batch) * A.ct_stride + i * A.N;
     g = A.galois[item / A.batch];
   }
-  CombineLimb<(1 << C::LEB)> L{A.T.r[i],
+  CombineLimb<(1 << C::LEB), C::LRC, C::LRB, SEG> L{A.T.r[i],
                 A.T.rinv[i],
                 A.LT.md_pinv[pi],
                 A.LT.md_pinvp[pi],
@@ -815,6 +818,20 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_fwd_blk(ModDownArgs 
                 {},
                 {}};
   fwd_blk_pass_fetch<C::LRC, C::LRB, C::LEB, C::CB>(L, tile * C::CB);
+}
+
+// Natural order -> segment layout, one limb per row of the grid.
+struct SegCopyArgs {
+  const uint32_t* src;
+  uint32_t* dst;
+  int N;
+};
+
+template <int LOGN>
+__global__ void __launch_bounds__(blk_threads<LOGN>()) k_seg_copy(SegCopyArgs A) {
+  using C = Cfg<LOGN>;
+  const size_t z = blockIdx.y;
+  copy_tile_segments<C::LRC, C::LRB, C::LEB, C::CB>(A.src + z * A.N, A.dst + z * A.N, blockIdx.x * C::CB);
 }
 
 // ---------------------------------------------------------------------------
@@ -1428,9 +1445,21 @@ hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t
   return hipGetLastError();
 }
 
+hipError_t launch_seg_copy(const pc_params* p, const uint32_t* src, uint32_t limbs, uint32_t* dst, hipStream_t s) {
+  SegCopyArgs A;
+  A.src = src;
+  A.dst = dst;
+  A.N = (int)p->N;
+  PC_DISPATCH_LOGN(p->log2n, {
+    LaunchTimer tm(p, KID_SEG_COPY, s);
+    hipLaunchKernelGGL(k_seg_copy<LN>, dim3(blk_tiles<LN>(), limbs), dim3(blk_threads<LN>()), 0, s, A);
+  });
+  return hipGetLastError();
+}
+
 hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t items, uint32_t polys, uint32_t level,
                           int variant, uint32_t* out, const KsWorkspace& ws, const uint32_t* c0, uint64_t ct_stride,
-                          uint32_t batch, const uint32_t* galois_per_key, hipStream_t s) {
+                          uint32_t batch, const uint32_t* galois_per_key, hipStream_t s, bool c0_seg) {
   ModDownArgs A;
   A.T = p->tabs;
   A.LT = p->ltabs;
@@ -1472,7 +1501,10 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
       const dim3 grid = sp ? dim3(8 * ((level * sp + 7) / 8) * items * polys * (blk_tiles<LN>() / sp))
                            : dim3(blk_tiles<LN>(), rows_q);
       LaunchTimer tm(p, KID_MODDOWN_FWD_BLK, s);
-      hipLaunchKernelGGL(k_md_fwd_blk<LN>, grid, dim3(blk_threads<LN>()), 0, s, A);
+      if (c0_seg)
+        hipLaunchKernelGGL((k_md_fwd_blk<LN, true>), grid, dim3(blk_threads<LN>()), 0, s, A);
+      else
+        hipLaunchKernelGGL((k_md_fwd_blk<LN, false>), grid, dim3(blk_threads<LN>()), 0, s, A);
     }
   });
   return hipGetLastError();

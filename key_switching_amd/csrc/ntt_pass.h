@@ -376,6 +376,24 @@ __device__ __forceinline__ void store_tile_segments(const uint32_t* lds, uint32_
   }
 }
 
+// A block-pass tile of columns [c0, c0 + C) copied from natural order into the
+// segment layout, through LDS.
+template <int LOGRC, int LOGRB, int LOGE, int C>
+__device__ __forceinline__ void copy_tile_segments(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
+                                                   int c0) {
+  constexpr int R = 1 << LOGRB, E = 1 << LOGE, TPB = R / E;
+  using Lay = BlkLds<LOGRB, LOGE>;
+  __shared__ uint32_t lds[Lay::words(C)];
+  const int kk = (int)threadIdx.x % C, rest = (int)threadIdx.x / C;
+#pragma unroll
+  for (int m = 0; m < E; ++m) {
+    const int x = rest + TPB * m;
+    lds[Lay::row(kk) + Lay::col(x)] = at32(src, ((int)bitrev((uint32_t)x, LOGRB) << LOGRC) + c0 + kk);
+  }
+  __syncthreads();
+  store_tile_segments<LOGRB, LOGE, C>(lds, dst, c0);
+}
+
 // Forward block pass: stages LOGRC..n-1 on blocks B = bitrev(c0 + k), k < C.
 // Output element x of block B goes to natural position bitrev(x) 2^LOGRC + c0 + k,
 // or with `seg` to the segment layout (store_tile_segments).

@@ -53,7 +53,7 @@ FAMILIES = {
     "moddown_inv_blk": "k_md_inv_blk<16>",
     "moddown_inv_col": "k_md_inv_col<16>",
     "moddown_bconv": "k_md_bconv<16, 6>",
-    "moddown_fwd_blk": "k_md_fwd_blk<16>",
+    "moddown_fwd_blk": "k_md_fwd_blk<16, false>",
     # homomorphic multiplication of 8 pairs around the same key switch
     "tensor": "k_tensor",
     "rescale_gather": "k_rs_gather",
