@@ -427,10 +427,12 @@ __device__ __forceinline__ void fwd_blk_pass(Limb& L, int c0, bool seg = false) 
 }
 
 // Forward block pass whose output stage also reads side inputs at the output
-// positions: L.fetch(m, pos) runs for every output slot m before the
-// transform, so those loads are in flight while it computes, and
-// L.finish(m, pos, v) stores slot m afterwards.
-template <int LOGRC, int LOGRB, int LOGE, int C, class Limb>
+// positions: L.fetch(m, pos) runs for every output slot m, and
+// L.finish(m, pos, v) stores slot m afterwards. EARLY fetches before the
+// transform, so the loads are in flight while it computes (best for small
+// grids and for gathers); otherwise after it, which frees 2E registers during
+// the transform and lets more workgroups share a CU (best for large grids).
+template <int LOGRC, int LOGRB, int LOGE, int C, bool EARLY, class Limb>
 __device__ __forceinline__ void fwd_blk_pass_fetch(Limb& L, int c0) {
   constexpr int R = 1 << LOGRB, E = 1 << LOGE, ROUNDS = LOGRB / LOGE, TPB = R / E;
   static_assert(LOGRB % LOGE == 0, "rounds must tile the pass");
@@ -439,8 +441,10 @@ __device__ __forceinline__ void fwd_blk_pass_fetch(Limb& L, int c0) {
   const int tid = threadIdx.x;
   const int kk = tid % C, rest = tid / C;
   auto out_pos = [&](int m) { return ((int)bitrev((uint32_t)(rest + TPB * m), LOGRB) << LOGRC) + c0 + kk; };
+  if constexpr (EARLY) {
 #pragma unroll
-  for (int m = 0; m < E; ++m) L.fetch(m, out_pos(m));
+    for (int m = 0; m < E; ++m) L.fetch(m, out_pos(m));
+  }
   const int t = tid % TPB, k = tid / TPB;
   const int B = (int)bitrev((uint32_t)(c0 + k), LOGRC);
   uint32_t v[E];
@@ -449,6 +453,11 @@ __device__ __forceinline__ void fwd_blk_pass_fetch(Limb& L, int c0) {
   fwd_blk_compute<LOGRC, LOGRB, LOGE>(v, lds + Lay::row(k), t, B, L.r, L.rinv, L.tw);
 #pragma unroll
   for (int m = 0; m < E; ++m) lds[Lay::row(k) + Lay::col(elem_index<LOGRB, LOGE, false>(ROUNDS - 1, t, m))] = v[m];
+  if constexpr (!EARLY) {
+    asm volatile("" ::: "memory");  // keeps the compiler from hoisting the fetches into the transform
+#pragma unroll
+    for (int m = 0; m < E; ++m) L.fetch(m, out_pos(m));
+  }
   __syncthreads();
 #pragma unroll
   for (int m = 0; m < E; ++m) L.finish(m, out_pos(m), lds[Lay::row(kk) + Lay::col(rest + TPB * m)]);

@@ -53,12 +53,12 @@ FAMILIES = {
     "moddown_inv_blk": "k_md_inv_blk<16>",
     "moddown_inv_col": "k_md_inv_col<16>",
     "moddown_bconv": "k_md_bconv<16, 6>",
-    "moddown_fwd_blk": "k_md_fwd_blk<16, false>",
+    "moddown_fwd_blk": "k_md_fwd_blk<16, false, false>",
     # homomorphic multiplication of 8 pairs around the same key switch
     "tensor": "k_tensor",
     "rescale_gather": "k_rs_gather",
     "rescale_col": "k_rs_col<16>",
-    "rescale_blk": "k_rs_blk<16>",
+    "rescale_blk": "k_rs_blk<16, false>",
     # the 4 x 4 double-hoisted linear transform of one ciphertext
     "bsgs_baby": "k_bsgs_baby<4>",
     "bsgs_giant": "k_bsgs_giant",
