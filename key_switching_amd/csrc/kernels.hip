@@ -59,6 +59,9 @@ template <int LOGN>
 constexpr int col_tiles() {
   return (1 << Cfg<LOGN>::LRB) / Cfg<LOGN>::CC;
 }
+static inline int col_tiles_of(uint32_t log2n) {
+  return log2n == 12 ? col_tiles<12>() : log2n == 16 ? col_tiles<16>() : col_tiles<17>();
+}
 template <int LOGN>
 constexpr int blk_tiles() {
   return (1 << Cfg<LOGN>::LRC) / Cfg<LOGN>::CB;
@@ -309,13 +312,18 @@ __device__ __forceinline__ void grouped_bconv(TargetGroup<G, E>& tg, int cnt, Sr
   }
 }
 
+// Targets per conversion workgroup: 3, or 1 when a grid of 3-target groups
+// would give the chip's 256 CUs fewer than two workgroups each (a single
+// ciphertext): each source tile is then read once per target (from L2), but
+// three times as many workgroups share the work.
 constexpr int kBconvGroup = 3;
+constexpr uint32_t kBconvSmallGrid = 512;
 
 // ModUp conversion: row (b, d), column tile blockIdx.x, target group blockIdx.z.
-template <int LOGN, int CNT>
+template <int LOGN, int CNT, int G>
 __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_bconv(ModUpArgs A) {
   using C = Cfg<LOGN>;
-  constexpr int E = 1 << C::LEC, G = kBconvGroup;
+  constexpr int E = 1 << C::LEC;
   __shared__ uint32_t lds[C::CC * LdsTile<C::LRC, C::LEC>::STRIDE];
   const int lk = A.level + A.K;
   int tile, row, grp;
@@ -744,10 +752,10 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_inv_col(ModDownArgs 
 
 // ModDown conversion P -> q_i: row ip = (item, u), column tile blockIdx.x,
 // group of G target limbs q_i blockIdx.z.
-template <int LOGN, int CNT>
+template <int LOGN, int CNT, int G>
 __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv(ModDownArgs A) {
   using C = Cfg<LOGN>;
-  constexpr int E = 1 << C::LEC, G = kBconvGroup;
+  constexpr int E = 1 << C::LEC;
   __shared__ uint32_t lds[C::CC * LdsTile<C::LRC, C::LEC>::STRIDE];
   int tile, row, grp;
   if (!xcd_unit(col_tiles<LOGN>(), A.rows_ip, A.ngroups, tile, row, grp)) return;
@@ -1281,14 +1289,21 @@ hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stri
   const uint32_t rows_ext = batch * (uint32_t)A.beta * (level + p->K);
   // the last digit is the shortest, so it has the most targets
   const int targets = (int)(level + p->K) - ((int)level - (A.beta - 1) * A.alpha);
-  const uint32_t groups = (uint32_t)((targets + kBconvGroup - 1) / kBconvGroup);
+  const int tiles_c = col_tiles_of(p->log2n);
+  const bool one = xcd_grid(tiles_c, (int)batch * A.beta, (targets + kBconvGroup - 1) / kBconvGroup) < kBconvSmallGrid;
+  const int G = one ? 1 : kBconvGroup;
+  const uint32_t groups = (uint32_t)((targets + G - 1) / G);
   A.ngroups = (int)groups;
   PC_DISPATCH_LOGN(p->log2n, {
     { LaunchTimer tm(p, KID_MODUP_INV_BLK, s); hipLaunchKernelGGL(k_modup_inv_blk<LN>, dim3(blk_tiles<LN>(), rows_in), dim3(blk_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_MODUP_INV_COL, s); hipLaunchKernelGGL(k_modup_inv_col<LN>, dim3(col_tiles<LN>(), rows_in), dim3(col_threads<LN>()), 0, s, A); }
     PC_DISPATCH_CNT(A.alpha, {
       LaunchTimer tm(p, KID_MODUP_BCONV, s);
-      hipLaunchKernelGGL((k_modup_bconv<LN, CNT>), dim3(xcd_grid(col_tiles<LN>(), (int)batch * A.beta, (int)groups)), dim3(col_threads<LN>()), 0, s, A);
+      const dim3 grid(xcd_grid(col_tiles<LN>(), (int)batch * A.beta, (int)groups));
+      if (one)
+        hipLaunchKernelGGL((k_modup_bconv<LN, CNT, 1>), grid, dim3(col_threads<LN>()), 0, s, A);
+      else
+        hipLaunchKernelGGL((k_modup_bconv<LN, CNT, kBconvGroup>), grid, dim3(col_threads<LN>()), 0, s, A);
     });
     { LaunchTimer tm(p, KID_MODUP_FWD_BLK, s); hipLaunchKernelGGL(k_modup_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_ext), dim3(blk_threads<LN>()), 0, s, A); }
   });
@@ -1489,7 +1504,11 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
     A.galois[k] = (galois_per_key != nullptr && k < nkeys) ? galois_per_key[k] : 1u;
   const uint32_t rows_p = items * polys * p->K;
   const uint32_t rows_q = items * polys * level;
-  const uint32_t groups = (level + kBconvGroup - 1) / kBconvGroup;
+  const int tiles_c = col_tiles_of(p->log2n);
+  const bool one = xcd_grid(tiles_c, (int)(items * polys), (int)((level + kBconvGroup - 1) / kBconvGroup)) <
+                   kBconvSmallGrid;
+  const uint32_t G = one ? 1u : (uint32_t)kBconvGroup;
+  const uint32_t groups = (level + G - 1) / G;
   A.rows_ip = (int)(items * polys);
   A.ngroups = (int)groups;
   A.limb_xcd = 0;
@@ -1501,7 +1520,11 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
     { LaunchTimer tm(p, KID_MODDOWN_INV_COL, s); hipLaunchKernelGGL(k_md_inv_col<LN>, dim3(col_tiles<LN>(), rows_p), dim3(col_threads<LN>()), 0, s, A); }
     PC_DISPATCH_CNT(A.K, {
       LaunchTimer tm(p, KID_MODDOWN_BCONV, s);
-      hipLaunchKernelGGL((k_md_bconv<LN, CNT>), dim3(xcd_grid(col_tiles<LN>(), (int)(items * polys), (int)groups)), dim3(col_threads<LN>()), 0, s, A);
+      const dim3 grid(xcd_grid(col_tiles<LN>(), (int)(items * polys), (int)groups));
+      if (one)
+        hipLaunchKernelGGL((k_md_bconv<LN, CNT, 1>), grid, dim3(col_threads<LN>()), 0, s, A);
+      else
+        hipLaunchKernelGGL((k_md_bconv<LN, CNT, kBconvGroup>), grid, dim3(col_threads<LN>()), 0, s, A);
     });
     {
       const uint32_t sp = (uint32_t)A.limb_xcd;
