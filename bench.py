@@ -8,6 +8,11 @@ workload the headline metric (key switches/s at N=2^16, L=24, k=1 and 8) is
 quoted on. `value` is key switches per second at batch k=8; the k=1 rate and
 the stored-key variants are reported beside it.
 
+Consecutive steps are independent batches dealt round-robin to three HIP
+streams, each call with its own caller workspace (`--streams 1` times them on
+one stream, as the per-kernel timings and the profiler runs do); the
+one-stream rates are reported beside the headline.
+
 Inputs are resident in HBM before timing starts. Ciphertext inputs and outputs
 rotate through more than 1 GiB of buffers so that the 256 MB Infinity Cache
 cannot hold them between steps; the key is reused, as in real
@@ -68,7 +73,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--buffers-gib", type=float, default=1.1, help="ciphertext buffer rotation size")
-    ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
+    ap.add_argument("--streams", type=int, default=3, choices=(1, 2, 3),
                     help="HIP streams the timed batches alternate on (each with its own workspace); "
                          "1 for profiler runs, whose per-dispatch times must not overlap")
     ap.add_argument("--no-configs", action="store_true",
@@ -206,7 +211,7 @@ def main():
     # resident inputs: rotating ciphertext / output buffers, one key
     ct_bytes = K8 * 2 * w.L * w.N * 4
     nbuf = max(2, int(np.ceil(args.buffers_gib * (1 << 30) / (2 * ct_bytes))))
-    nbuf += nbuf % 2  # even: a buffer is reused only by the stream that used it last
+    nbuf += -nbuf % args.streams  # a multiple of the streams: a buffer is reused only by the stream that used it last
     base = ki.ciphertexts(w.index, q, w.N, K8)
     cts, outs = [], []
     for i in range(nbuf):
@@ -226,11 +231,13 @@ def main():
         del src, dst
     torch.cuda.synchronize()
 
-    # independent batches in flight on two streams, each call with its own workspace
-    # (the arena serves one stream at a time)
-    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    # independent batches in flight on several streams (default priority), each call
+    # with its own workspace (the arena serves one stream at a time); three measured
+    # fastest: a fourth shares the process's four hardware queues with the null stream
+    S = args.streams
+    streams = [torch.cuda.Stream() for _ in range(S)]
     ws_bytes = prm.workspace_bytes(w.L)
-    workspaces = [torch.empty((ws_bytes + 3) // 4, dtype=torch.int32, device="cuda:0") for _ in range(2)]
+    workspaces = [torch.empty((ws_bytes + 3) // 4, dtype=torch.int32, device="cuda:0") for _ in range(S)]
 
     def step(i, batch, stored=False, ws=None):
         ct = cts[i % nbuf][:batch]
@@ -241,23 +248,25 @@ def main():
             ksa.keyswitch_ex(prm, ct, [evk_b], [1], w.L, seeds=[seed], out=out, workspace=ws)
 
     def timed_streams(batch, stored=False, steps=args.steps):
-        """Steps alternating on two streams; the region opens with an event that both
-        streams wait for and closes when both are done."""
+        """Steps dealt round-robin to the streams; the region opens with an event that
+        every stream waits for and closes when all of them are done."""
         def issue(i):
-            with torch.cuda.stream(streams[i % 2]):
-                step(i, batch, stored, workspaces[i % 2])
+            with torch.cuda.stream(streams[i % S]):
+                step(i, batch, stored, workspaces[i % S])
 
         for i in range(args.warmup):
             issue(i)
         torch.cuda.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(streams[0])
-        streams[1].wait_event(start)
+        for st in streams[1:]:
+            st.wait_event(start)
         for i in range(steps):
             issue(i)
-        joined = torch.cuda.Event()
-        joined.record(streams[1])
-        streams[0].wait_event(joined)
+        for st in streams[1:]:
+            joined = torch.cuda.Event()
+            joined.record(st)
+            streams[0].wait_event(joined)
         end.record(streams[0])
         torch.cuda.synchronize()
         return start.elapsed_time(end) / steps
@@ -289,10 +298,10 @@ def main():
     ms1s, _ = timed(1, stored=True)
     print(f"[bench] one stream: k=8 {ms8:.3f} ms/step, k=1 {ms1:.3f}, stored k=8 {ms8s:.3f}, stored k=1 {ms1s:.3f}",
           file=sys.stderr, flush=True)
-    if args.streams == 2:
+    if S > 1:
         ms8_2, ms1_2 = timed_streams(K8), timed_streams(1)
         ms8s_2, ms1s_2 = timed_streams(K8, stored=True), timed_streams(1, stored=True)
-        print(f"[bench] two streams: k=8 {ms8_2:.3f} ms/step, k=1 {ms1_2:.3f}, stored k=8 {ms8s_2:.3f}, "
+        print(f"[bench] {S} streams: k=8 {ms8_2:.3f} ms/step, k=1 {ms1_2:.3f}, stored k=8 {ms8s_2:.3f}, "
               f"stored k=1 {ms1s_2:.3f}", file=sys.stderr, flush=True)
     else:
         ms8_2, ms1_2, ms8s_2, ms1s_2 = ms8, ms1, ms8s, ms1s

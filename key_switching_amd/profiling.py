@@ -47,12 +47,12 @@ COPY_KERNEL_HINT = "elementwise"  # bench.py --calibrate-copy: torch.bitwise_or(
 FAMILIES = {
     "modup_inv_blk": "k_modup_inv_blk<16>",
     "modup_inv_col": "k_modup_inv_col<16>",
-    "modup_bconv": "k_modup_bconv<16, 6>",
+    "modup_bconv": "k_modup_bconv<16, 6, 3>",
     "modup_fwd_blk": "k_modup_fwd_blk<16>",
     "inner_product": "k_ip_regen<4, 12, 8, false>",
     "moddown_inv_blk": "k_md_inv_blk<16>",
     "moddown_inv_col": "k_md_inv_col<16>",
-    "moddown_bconv": "k_md_bconv<16, 6>",
+    "moddown_bconv": "k_md_bconv<16, 6, 3>",
     "moddown_fwd_blk": "k_md_fwd_blk<16, false, false>",
     # homomorphic multiplication of 8 pairs around the same key switch
     "tensor": "k_tensor",

@@ -389,26 +389,27 @@ def test_caller_workspace_matches_arena():
     prm.close()
 
 
-def test_two_streams_with_caller_workspaces():
-    """N=2^16, L=24, dnum=4, K=6: batches of 8 alternating on two streams, each call with
-    its own workspace, give the bits of the same calls made one at a time."""
+def test_three_streams_with_caller_workspaces():
+    """N=2^16, L=24, dnum=4, K=6: batches of 8 dealt to three streams, each call with
+    its own workspace (the benchmark's launch configuration), give the bits of the
+    same calls made one at a time."""
     w = ki.WORKLOADS["n16"]
     prm, oprm = params_pair(w.log2n, w.L, w.dnum, w.K, max_batch=8)
     (key,) = _uniform_keys(oprm, w.index, w.L, (1,))
     kb = dev(key.b)
-    cts = [dev(ki.ciphertexts(w.index + 20 + i, oprm.q, oprm.N, 8)) for i in range(4)]
+    cts = [dev(ki.ciphertexts(w.index + 20 + i, oprm.q, oprm.N, 8)) for i in range(6)]
     want = [host(ksa.keyswitch_ex(prm, c, [kb], [1], w.L, seeds=[key.seed]))[0] for c in cts]
-    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
-    ws = [torch.empty(prm.workspace_bytes(w.L) // 4, dtype=torch.int32, device="cuda:0") for _ in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    ws = [torch.empty(prm.workspace_bytes(w.L) // 4, dtype=torch.int32, device="cuda:0") for _ in range(3)]
     outs = [torch.empty((1, 8, 2, w.L, oprm.N), dtype=torch.int32, device="cuda:0") for _ in cts]
     torch.cuda.synchronize()
     for rep in range(3):
         for i, c in enumerate(cts):
-            with torch.cuda.stream(streams[i % 2]):
-                ksa.keyswitch_ex(prm, c, [kb], [1], w.L, seeds=[key.seed], out=outs[i], workspace=ws[i % 2])
+            with torch.cuda.stream(streams[i % 3]):
+                ksa.keyswitch_ex(prm, c, [kb], [1], w.L, seeds=[key.seed], out=outs[i], workspace=ws[i % 3])
         torch.cuda.synchronize()
         for i in range(len(cts)):
-            assert_equal(host(outs[i])[0], want[i], f"two streams, repeat {rep}, call {i}")
+            assert_equal(host(outs[i])[0], want[i], f"three streams, repeat {rep}, call {i}")
     ref = ks.keyswitch(oprm, ki.ciphertexts(w.index + 23, oprm.q, oprm.N, 8)[5], key, w.L)
     assert_equal(want[3][5], ref, "call 3 item 5 vs oracle")
     prm.close()
