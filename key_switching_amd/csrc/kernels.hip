@@ -3,14 +3,17 @@
 // Steps (Perseus README, 'Layout': NTT and key-switching kernels; 'What's
 // inside': the a half regenerated in-kernel from a ChaCha12 seed):
 //   ModUp   : k_modup_inv_blk + k_modup_inv_col   iNTT of c1, scaled by N^-1 (Q_d/q_i)^-1
-//             k_modup_bconv_col                   fast base conversion fused into NTT pass 1
+//             k_modup_bconv                       fast base conversion fused into NTT pass 1
 //             k_modup_fwd_blk                     NTT pass 2 -> ext (evaluation form)
-//   IP      : k_inner_product                     automorphism gather, ChaCha12 a half, both sums
+//   IP      : k_inner_product, k_ip_regen         automorphism gather, ChaCha12 a half, both sums
 //   ModDown : k_md_inv_blk + k_md_inv_col         iNTT of the special limbs, scaled by N^-1 (P/p_t)^-1
-//             k_md_bconv_col                      base conversion P -> q_i fused into NTT pass 1
+//             k_md_bconv                          base conversion P -> q_i fused into NTT pass 1
 //             k_md_fwd_blk                        NTT pass 2 fused with (acc - z) P^-1 (+ phi(c0))
-// Every limb of every launch is one grid row (blockIdx.y); blockIdx.x walks the
-// column/block tiles of that limb.
+//             k_seg_copy                          c0 into the segment layout (one ciphertext under
+//                                                 rotation keys; see seg_src_index)
+// The per-limb passes take one limb per grid row (blockIdx.y), blockIdx.x
+// walking its column/block tiles; the conversions and the gathering kernels
+// use 1-D grids placed by XCD (xcd_unit, limb_xcd_decode).
 #include <algorithm>
 #include <map>
 #include <mutex>
