@@ -913,14 +913,9 @@ int pc_linear_transform(const pc_params* p, const pc_lt_args* a, void* stream) {
         hipSuccess)
       return PC_EDEVICE;
     if (launch_modup(p, d1, ln, 0, n2 - 1, level, ws2, s) != hipSuccess) return PC_EDEVICE;
-    const size_t beta = (size_t)beta_of(p, level);
-    for (uint32_t j = 1; j < n2; ++j) {
-      KsWorkspace wj = ws2;
-      wj.ext = ws2.ext + (size_t)(j - 1) * beta * lk * N;
-      wj.acc = ws2.acc + (size_t)(j - 1) * 2 * lk * N;
-      if (launch_inner_product(p, d1 + (size_t)(j - 1) * ln, ln, 0, 1, level, wj, &giant[j - 1], 1, s) != hipSuccess)
-        return PC_EDEVICE;
-    }
+    // giant step j's key switches brought-down component j - 1: one launch, one ciphertext per key
+    if (launch_inner_product(p, d1, ln, 0, 1, level, ws2, giant.data(), n2 - 1, s, true) != hipSuccess)
+      return PC_EDEVICE;
   }
   if (launch_bsgs_giant(p, inner, n2 > 1 ? ws2.acc : nullptr, accqp, level, n2, a->giant_galois, pm.data(),
                         m96.data(), m128.data(), s) != hipSuccess)

@@ -174,9 +174,12 @@ hipError_t launch_ntt(const pc_params* p, uint32_t* data, uint32_t* tmp, const u
                       bool inverse, hipStream_t s);
 hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_offset, uint32_t batch,
                         uint32_t level, const KsWorkspace& ws, hipStream_t s);
+// one_ct_per_key: key k switches its own `batch` ciphertexts, the k-th group
+// (ct + k batch ct_stride, ext of ModUp's items k batch .. k batch + batch - 1);
+// otherwise every key switches the same batch.
 hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_offset,
                                 uint32_t batch, uint32_t level, const KsWorkspace& ws, const KeyRef* keys,
-                                uint32_t nkeys, hipStream_t s);
+                                uint32_t nkeys, hipStream_t s, bool one_ct_per_key = false);
 // ModDown of items*2 accumulators; out[item][u][l][N]. variant: 0 plain acc, 1 acc carrying 2^-64.
 // When c0 is non-null, c0 of ciphertext (item % batch) under the item's Galois element is added to u = 0.
 hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t items, uint32_t polys, uint32_t level,

@@ -412,6 +412,10 @@ struct IPArgs {
   int limb_xcd;   // 0, or the split of limb_xcd_decode: tiles of limb j grouped on XCDs (see below)
   int lrc, lrb;   // N = 2^(lrc + lrb): columns and rows of the segment layout
   uint32_t key_base;
+  // 0: every key reads the same batch; else key k reads the ciphertext and ext
+  // at these offsets (words) times k (one ciphertext per key, as in the giant
+  // steps of a linear transform)
+  uint64_t ct_key_stride, ext_key_stride;
   const uint32_t* evk_b[kMaxKeysPerLaunch];
   const uint32_t* evk_a[kMaxKeysPerLaunch];
   ChaChaKey seed[kMaxKeysPerLaunch];
@@ -456,7 +460,7 @@ __device__ __forceinline__ void load_key8(const uint32_t* limb, int p0, int p1, 
 // index map is a gather unless the Galois element is 1. With the segment
 // layout (SEG) every limb, own ones included, is read from ext at src_idx.
 template <int BETA, bool SEG>
-__device__ __forceinline__ void load_digits(const IPArgs& A, int b, int j, int lk, uint32_t g, int p0, int p1,
+__device__ __forceinline__ void load_digits(const IPArgs& A, int key, int b, int j, int lk, uint32_t g, int p0, int p1,
                                             const uint32_t (&src_idx)[8], uint32_t (&e)[BETA][8]) {
   // with SEG the offsets are made opaque per call: otherwise the compiler
   // keeps a 64-bit address per digit and position live across the batch loop
@@ -469,8 +473,8 @@ __device__ __forceinline__ void load_digits(const IPArgs& A, int b, int j, int l
 #pragma unroll
   for (int d = 0; d < BETA; ++d) {
     const bool own = !SEG && j < A.level && j >= d * A.alpha && j < (d + 1) * A.alpha;
-    const uint32_t* src = own ? A.ct + b * A.ct_stride + A.c1_off + (size_t)j * A.N
-                              : A.ext + (((size_t)b * BETA + d) * lk + j) * A.N;
+    const uint32_t* src = own ? A.ct + key * A.ct_key_stride + b * A.ct_stride + A.c1_off + (size_t)j * A.N
+                              : A.ext + key * A.ext_key_stride + (((size_t)b * BETA + d) * lk + j) * A.N;
     if (!SEG && g == 1u) {
       load8(src, p0, p1, e[d]);
     } else {
@@ -588,7 +592,7 @@ __global__ void __launch_bounds__(kIpThreads) k_inner_product(IPArgs A) {
 #pragma unroll 1
   for (int b = 0; b < batch; ++b) {
     uint32_t e[BETA][8];
-    load_digits<BETA, SEG>(A, b, j, lk, g, p0, p1, src_idx, e);
+    load_digits<BETA, SEG>(A, (int)A.key_base + key, b, j, lk, g, p0, p1, src_idx, e);
     uint32_t o0[8], o1[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) ip_sums<BETA>(e, bm, k, [&](int d) { return am[d][k]; }, r, rinv, o0[k], o1[k]);
@@ -687,7 +691,7 @@ __global__ void __launch_bounds__(2 * kIpHalf) k_ip_regen(IPArgs A) {
       int sl = slot;
       asm volatile("" : "+s"(sl));
       uint32_t e[BETA][8];
-      load_digits<BETA, SEG>(A, b, j, lk, g, p0, p1, src_idx, e);
+      load_digits<BETA, SEG>(A, (int)A.key_base + key, b, j, lk, g, p0, p1, src_idx, e);
       uint32_t o0[8], o1[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k)
@@ -1418,7 +1422,7 @@ static void launch_ip_beta(const pc_params* p, const IPArgs& A, uint32_t nkeys, 
 
 hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_offset,
                                 uint32_t batch, uint32_t level, const KsWorkspace& ws, const KeyRef* keys,
-                                uint32_t nkeys, hipStream_t s) {
+                                uint32_t nkeys, hipStream_t s, bool one_ct_per_key) {
   const int beta = beta_of(p, level);
   for (uint32_t base = 0; base < nkeys; base += kMaxKeysPerLaunch) {
     const uint32_t cnt = (nkeys - base) < (uint32_t)kMaxKeysPerLaunch ? (nkeys - base) : kMaxKeysPerLaunch;
@@ -1438,6 +1442,8 @@ hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t
     A.nkeys = (int)cnt;
     A.key_level = (int)key_level_of(p, level);
     A.key_base = base;
+    A.ct_key_stride = one_ct_per_key ? ct_stride * batch : 0;
+    A.ext_key_stride = one_ct_per_key ? (uint64_t)batch * beta * (level + p->K) * p->N : 0;
     A.lrc = pass_split_lrc(p->log2n);
     A.lrb = (int)p->log2n - A.lrc;
     bool stored = false;
