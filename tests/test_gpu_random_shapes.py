@@ -22,7 +22,7 @@ torch = pytest.importorskip("torch")
 ksa = pytest.importorskip("key_switching_amd")
 
 LOG2N = 12
-CASES = 48
+CASES = 96
 
 
 def _shape(seed):
@@ -70,4 +70,34 @@ def test_random_shape_matches_oracle(seed):
         for r in range(len(keys)):
             bad = np.flatnonzero(got[r, b].reshape(-1) != np.asarray(want[r], dtype=np.uint64).reshape(-1))
             assert bad.size == 0, f"{what}: key {r} item {b}: {bad.size} words differ, first at {bad[0]}"
+    prm.close()
+
+
+@pytest.mark.parametrize("L,dnum", [(10, 5), (12, 6)])
+@pytest.mark.parametrize("batch", [1, 2])
+@pytest.mark.parametrize("stored", [False, True])
+def test_five_and_six_digits(L, dnum, batch, stored):
+    """The largest digit counts in both gather layouts (one ciphertext: segment layout;
+    two: natural order), with a rotation and the conjugation key, a regenerated or stored."""
+    K, level, galois = 3, L, [5, (2 << LOG2N) - 1]
+    prm = ksa.Params(LOG2N, L, dnum, K, device=0, max_batch=batch, max_hoist=2)
+    oprm = ks.Params(LOG2N, L, dnum, K)
+    assert len(oprm.digits(level)) == dnum
+    widx = 400 + 10 * L + batch
+    keys = [ks.Key(b=ki.uniform_key_b(widx, k, dnum, oprm.basis(level), oprm.N), seed=ki.key_seed(widx, k),
+                   level=level, galois=g) for k, g in enumerate(galois)]
+    cts = ki.ciphertexts(widx, oprm.q[:level], oprm.N, batch)
+    kb = [ksa.to_device(k.b, 0) for k in keys]
+    if stored:
+        out = ksa.keyswitch_ex(prm, ksa.to_device(cts, 0), kb, galois, level,
+                               evk_a=[ksa.to_device(ks.key_a(oprm, k), 0) for k in keys])
+    else:
+        out = ksa.keyswitch_ex(prm, ksa.to_device(cts, 0), kb, galois, level, seeds=[k.seed for k in keys])
+    torch.cuda.synchronize()
+    got = ksa.to_host(out).astype(np.uint64)
+    for b in range(batch):
+        want = ks.keyswitch_hoisted(oprm, cts[b], keys, level)
+        for r in range(len(keys)):
+            bad = np.flatnonzero(got[r, b].reshape(-1) != np.asarray(want[r], dtype=np.uint64).reshape(-1))
+            assert bad.size == 0, f"beta {dnum} batch {batch} stored {stored}: key {r} item {b}: {bad.size} differ"
     prm.close()
