@@ -132,3 +132,38 @@ def test_bsgs16_four_by_four():
     again = _run(prm, ct, diag, baby, giant, w.L)
     assert_equal(again, out, "repeat")
     prm.close()
+
+
+def _uniform_case(oprm, widx, level, baby_g, giant_g):
+    kl = oprm.key_level(level)
+    beta = len(oprm.digits(kl))
+    keys = [ks.Key(b=ki.uniform_key_b(widx, k, beta, oprm.basis(kl), oprm.N), seed=ki.key_seed(widx, k),
+                   level=kl, galois=g) for k, g in enumerate(list(baby_g) + list(giant_g))]
+    ct = ki.ciphertexts(widx, oprm.q[:level], oprm.N, 1)[0]
+    diag = ki.uniform_diagonals(widx, len(giant_g) + 1, len(baby_g) + 1, oprm.basis(level), oprm.N)
+    return ct, diag, keys[: len(baby_g)], keys[len(baby_g):]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_match_oracle(seed):
+    """Seeded random N=2^12 chains, levels and step counts with uniform keys and
+    diagonals; Galois elements drawn with 1 and 2N - 1 among them, so that giant
+    steps also run in natural order (every giant element 1) and mixed."""
+    g = np.random.default_rng([11, seed])
+    L = int(g.integers(1, 10))
+    dnum = int(g.integers(-(-L // 8), min(L, 6) + 1))
+    K = int(g.integers(1, 4))
+    partition = int(g.integers(0, 2))
+    level = int(g.integers(1, L + 1))
+    n1, n2 = int(g.integers(1, 6)), int(g.integers(1, 6))
+    n2N = 2 << 12
+    pool = [1, n2N - 1, 5, 25, 3125]
+    baby_g = [pool[int(i)] for i in g.integers(0, len(pool), n1 - 1)]
+    giant_g = [1] * (n2 - 1) if seed % 3 == 0 else [pool[int(i)] for i in g.integers(0, len(pool), n2 - 1)]
+    what = f"seed {seed}: L={L} dnum={dnum} K={K} partition={partition} level={level} baby={baby_g} giant={giant_g}"
+    print(what, flush=True)
+    prm, oprm = params_pair(12, L, dnum, K, partition=partition, max_batch=8, max_hoist=8)
+    ct, diag, baby, giant = _uniform_case(oprm, 500 + seed, level, baby_g, giant_g)
+    out = _run(prm, ct, diag, baby, giant, level)
+    assert_equal(out, bsgs.linear_transform(oprm, ct, diag, baby, giant, level), what)
+    prm.close()
