@@ -140,3 +140,27 @@ def test_n17_hmult():
     assert out.shape == (2, 2, w.L - 1, oprm.N)
     assert_equal(out[1], hm.hmult(oprm, a[1], b[1], key, w.L), "n17 hmult pair 1")
     prm.close()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_match_oracle(seed):
+    """Seeded random N=2^12 chains, partitions, levels (>= 2, so that the rescale
+    keeps a limb) and batches, with a uniform key b half and its ChaCha seed."""
+    g = np.random.default_rng([13, seed])
+    L = int(g.integers(2, 11))
+    dnum = int(g.integers(-(-L // 8), min(L, 6) + 1))
+    K = int(g.integers(1, 4))
+    partition = int(g.integers(0, 2))
+    level = int(g.integers(2, L + 1))
+    batch = int(g.integers(1, 4))
+    what = f"seed {seed}: L={L} dnum={dnum} K={K} partition={partition} level={level} batch={batch}"
+    print(what, flush=True)
+    prm, oprm = params_pair(12, L, dnum, K, partition=partition, max_batch=batch)
+    kl = oprm.key_level(level)
+    key = ks.Key(b=ki.uniform_key_b(600 + seed, 0, len(oprm.digits(kl)), oprm.basis(kl), oprm.N),
+                 seed=ki.key_seed(600 + seed, 0), level=kl, galois=1)
+    a, b = _pairs(600 + seed, oprm, level, batch)
+    out = host(ksa.hmult(prm, dev(a), dev(b), dev(key.b), key.seed, level))
+    for z in range(batch):
+        assert_equal(out[z], hm.hmult(oprm, a[z], b[z], key, level), f"{what} pair {z}")
+    prm.close()
