@@ -132,8 +132,7 @@ def alg_ops(kernel, N, level, K, alpha, beta, batch, nkeys=1):
     lk = l + K
     items = batch * nkeys
     key_ops = lk * N * beta * (OPS_REDC + OPS_CHACHA12_BLOCK / 8 + OPS_WORDPAIR)  # b to Montgomery form, a regenerated
-    pairs = beta // 2 + beta % 2
-    ip_item = lk * N * 2 * (pairs * (2 + OPS_REDC + OPS_ADDMOD))                   # both sums, products paired per REDC
+    ip_item = lk * N * 2 * dot_ops(beta)                                            # both sums, one REDC each
     table = {
         "modup_inv_blk": batch * l * blk,
         "modup_inv_col": batch * l * (col + N * OPS_SHOUP),

@@ -507,20 +507,20 @@ __device__ __forceinline__ void gather_index_seg(const IPArgs& A, uint32_t g, in
 }
 
 // (sum_d e_d b_d, sum_d e_d a_d) at one position; am(d) gives a_d there.
+// Each sum is one dot_redc: the products add up in 64 bits with folds, and a
+// single REDC ends it (b and a are below r, e below 2^31).
 template <int BETA, class AFn>
 __device__ __forceinline__ void ip_sums(const uint32_t (&e)[BETA][8], const uint32_t (&bm)[BETA][8], int k, AFn am,
                                         uint32_t r, uint32_t rinv, uint32_t& s0, uint32_t& s1) {
-  s0 = 0;
-  s1 = 0;
+  uint32_t ev[BETA], bv[BETA], av[BETA];
 #pragma unroll
-  for (int d = 0; d + 1 < BETA; d += 2) {
-    s0 = add_mod(s0, redc(mul_wide(e[d][k], bm[d][k]) + mul_wide(e[d + 1][k], bm[d + 1][k]), r, rinv), r);
-    s1 = add_mod(s1, redc(mul_wide(e[d][k], am(d)) + mul_wide(e[d + 1][k], am(d + 1)), r, rinv), r);
+  for (int d = 0; d < BETA; ++d) {
+    ev[d] = e[d][k];
+    bv[d] = bm[d][k];
+    av[d] = am(d);
   }
-  if constexpr (BETA % 2) {
-    s0 = add_mod(s0, redc(mul_wide(e[BETA - 1][k], bm[BETA - 1][k]), r, rinv), r);
-    s1 = add_mod(s1, redc(mul_wide(e[BETA - 1][k], am(BETA - 1)), r, rinv), r);
-  }
+  s0 = dot_redc<BETA>(ev, bv, r, rinv);
+  s1 = dot_redc<BETA>(ev, av, r, rinv);
 }
 
 constexpr int kIpThreads = 256;

@@ -28,7 +28,11 @@ def test_headline_totals():
     # limbs: ModUp 8*(48 + 48 + 24+96 + 192) = 3264; IP 8*(96+24) + 4*30 + 8*60 = 1560;
     # ModDown 8*2*(12 + 12 + 30 + 72) + 8*24 = 2208 -> 7032 limbs
     assert nbytes == 7032 * LIMB16
-    assert nops == 10991173632
+    # inner product: 2 sums of dot_ops(4) = 10 per position and item, 8 items x 30 limbs
+    assert bench.alg_ops_per_launch("inner_product", w, 8, 4, 6) == (
+        8 * 30 * (1 << 16) * 2 * 10 + 30 * (1 << 16) * 4 * (bench.OPS_REDC + bench.OPS_CHACHA12_BLOCK / 8
+                                                           + bench.OPS_WORDPAIR))
+    assert nops == 10739515392
 
 
 def test_model_scales_with_batch_and_keys():
