@@ -45,7 +45,8 @@
  * `stream` (a hipStream_t; NULL = the null stream) and return without waiting;
  * results are valid once the stream has reached that point. Inputs and outputs
  * must not overlap. The library owns a workspace arena inside pc_params, sized
- * at creation for max_batch ciphertexts and max_hoist keys; calls that use it
+ * at creation for max_batch ciphertexts and max_hoist keys at any level (the
+ * largest of the per-level needs); calls that use it
  * must not run concurrently on different streams for the same pc_params.
  * pc_keyswitch_ex calls that each bring their own workspace may run
  * concurrently on different streams (the constant tables are read-only).
@@ -206,8 +207,8 @@ int pc_rescale(const pc_params *p, const uint32_t *ct, uint32_t batch, uint32_t 
  *   evk_b       device b half of the key (shape as in pc_keyswitch_ex)
  *   evk_seed    host, 32 bytes
  *   out         device [batch][2][level-1][N]
- * Uses the params' workspace arena (sized at create for level L and
- * max_batch). */
+ * Uses the params' workspace arena (sized at create for max_batch at every
+ * level). */
 int pc_hmult(const pc_params *p, const uint32_t *ct_a, const uint32_t *ct_b, uint32_t batch, const uint32_t *evk_b,
              const uint8_t *evk_seed, uint32_t level, uint32_t *out, void *stream);
 

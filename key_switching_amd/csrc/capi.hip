@@ -480,11 +480,16 @@ int pc_params_create(const pc_params_desc* desc, int device, pc_params** out) {
   }
   build_tables(p);
   {
-    // the arena fits a key switch of max_batch x max_hoist, an HMult of
-    // max_batch pairs and an NTT of every prime at the top level
-    const size_t ks = ks_workspace_bytes(p, p->L, p->max_batch, p->max_batch * p->max_hoist);
-    const size_t hm = p->L >= 2 ? hm_workspace_bytes(p, p->L, p->max_batch) : 0;
-    p->arena_bytes = std::max<size_t>(std::max(ks, hm), (size_t)2 * count * p->N * 4);
+    // the arena fits a key switch of max_batch x max_hoist and an HMult of
+    // max_batch pairs at every level (with ceil(l/dnum) primes per digit a
+    // lower level can have more digits, and so a larger ext, than the top),
+    // and an NTT of every prime
+    size_t need = (size_t)2 * count * p->N * 4;
+    for (uint32_t l = 1; l <= p->L; ++l) {
+      need = std::max(need, ks_workspace_bytes(p, l, p->max_batch, p->max_batch * p->max_hoist));
+      if (l >= 2) need = std::max(need, hm_workspace_bytes(p, l, p->max_batch));
+    }
+    p->arena_bytes = need;
   }
   if (device >= 0) {
     DeviceGuard g(device);

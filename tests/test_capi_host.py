@@ -198,3 +198,14 @@ def test_workspace_grows_with_level():
     with ksa.Params(16, 24, 4, 6, max_batch=8, device=None) as prm:
         sizes = [prm.workspace_bytes(l) for l in (4, 8, 12, 16, 20, 24)]
         assert sizes == sorted(sizes) and sizes[0] > 0
+
+
+def test_arena_fits_every_level():
+    """With ceil(l/dnum) primes per digit a lower level can need a larger
+    workspace than the top one (more digits): L = 6, dnum = 5 has 3 digits at
+    level 6 and 5 at level 5. The arena covers every level."""
+    prm = ksa.Params(12, 6, 5, 2, device=None, max_batch=1, max_hoist=2)
+    sizes = [prm.workspace_bytes(level) for level in range(1, 7)]
+    assert max(sizes) > sizes[-1]
+    assert prm.arena_bytes() >= max(sizes)
+    prm.close()

@@ -101,3 +101,11 @@ def test_five_and_six_digits(L, dnum, batch, stored):
             bad = np.flatnonzero(got[r, b].reshape(-1) != np.asarray(want[r], dtype=np.uint64).reshape(-1))
             assert bad.size == 0, f"beta {dnum} batch {batch} stored {stored}: key {r} item {b}: {bad.size} differ"
     prm.close()
+
+
+def test_lower_level_with_more_digits():
+    """Regression: with L = 6 and dnum = 5, level 5 has five digits against the
+    top level's three, so its workspace is larger; the arena must cover it
+    (seed 495 of the same draw: level 5, one ciphertext, two keys, stored a)."""
+    assert _shape(495)[:3] == (6, 5, 2) and _shape(495)[5] == 5
+    test_random_shape_matches_oracle(495)
