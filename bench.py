@@ -355,7 +355,7 @@ def main():
             ksa.hmult(prm, cts[i % nbuf], cts[(i + 1) % nbuf], evk_b, seed, w.L, out=hm_out)
 
         ms = timed_calls(hm_step, args.steps)
-        fams = ("tensor", "rescale_gather", "rescale_col", "rescale_blk")
+        fams = ("tensor", "rescale_gather", "rescale_col", "moddown_fwd_blk", "moddown_rescale")
         return {"hmults_per_s": round(K8 * 1000.0 / ms, 1), "ms_per_call": round(ms, 4),
                 "kernel_avg_us": profiled(hm_step, fams)}
 

@@ -323,14 +323,13 @@ KsWorkspace ks_workspace_carve(const pc_params* p, void* base, uint32_t level, u
 }
 
 // Workspace of a homomorphic multiplication of `batch` pairs at level l: the
-// tensor [batch][3][l][N] (d0, d2, d1), the relinearised pair
-// [batch][2][l][N], then the key switch's own workspace, whose start the
-// rescale reuses afterwards for x [2 batch][N] and tmp [2 batch][l-1][N].
+// tensor [batch][3][l][N] (d0, d2, d1), a [batch][2][l][N] buffer R for the
+// relinearised pair's last limbs and then the rescale's column-pass output
+// [2 batch][l-1][N], then the key switch's own workspace (whose ModUp buffer y,
+// free after ModUp, takes the rescale's dropped limbs [2 batch][N]).
 size_t hm_workspace_bytes(const pc_params* p, uint32_t level, uint32_t batch) {
   const size_t N = p->N, l = level;
-  const size_t ks = ks_workspace_bytes(p, level, batch, batch);
-  const size_t rs = align256(2 * batch * N * 4) + align256(2 * batch * (l - 1) * N * 4);
-  return align256(batch * 3 * l * N * 4) + align256(batch * 2 * l * N * 4) + std::max(ks, rs);
+  return align256(batch * 3 * l * N * 4) + align256(batch * 2 * l * N * 4) + ks_workspace_bytes(p, level, batch, batch);
 }
 
 // Workspace of a linear transform with n1 baby and n2 giant steps at level l:
@@ -351,7 +350,7 @@ const char* const kKernelNames[KID_COUNT] = {
     "modup_inv_col",   "modup_bconv",     "modup_fwd_blk",   "inner_product",  "moddown_inv_blk",
     "moddown_inv_col", "moddown_bconv",   "moddown_fwd_blk", "chacha_expand",  "keygen",
     "tensor",          "rescale_gather",  "rescale_col",     "rescale_blk",    "bsgs_baby",
-    "bsgs_giant",      "seg_copy"};
+    "bsgs_giant",      "seg_copy",        "moddown_rescale"};
 
 static hipEvent_t prof_event(const pc_params* p) {
   if (p->prof_used == p->prof_pool.size()) {
@@ -835,16 +834,25 @@ int pc_hmult(const pc_params* p, const uint32_t* ct_a, const uint32_t* ct_b, uin
   c += align256(batch * 3 * ln * 4);
   uint32_t* R = reinterpret_cast<uint32_t*>(c);  // [batch][2][l][N]: relinearised (d0, d2) without d1
   c += align256(batch * 2 * ln * 4);
-  uint32_t* x = reinterpret_cast<uint32_t*>(c);
-  uint32_t* tmp = x + align256(2 * batch * N * 4) / 4;
   DeviceGuard g(p->device);
   if (!g.ok) return PC_EDEVICE;
   hipStream_t s = (hipStream_t)stream;
   const uint64_t off[3] = {0, 2 * ln, ln};
   if (launch_tensor(p, ct_a, 2 * ln, ct_b, 2 * ln, batch, level, T, 3 * ln, off, s) != hipSuccess) return PC_EDEVICE;
-  if (launch_keyswitch(p, T, 3 * ln, (uint32_t)ln, batch, level, &key, 1, &one, c, R, s) != hipSuccess)
+  // relinearisation of (d0, d2): ModUp and inner product as in a key switch;
+  // ModDown brings down limb l-1 of both components first (into R), the
+  // rescale turns it into the values to subtract (its column pass writes over
+  // R, whose other limbs are never written), and one pass per limb < l-1
+  // finishes ModDown and the rescale together
+  const KsWorkspace ws = ks_workspace_carve(p, c, level, batch, batch);
+  if (launch_modup(p, T, 3 * ln, (uint32_t)ln, batch, level, ws, s) != hipSuccess) return PC_EDEVICE;
+  if (launch_inner_product(p, T, 3 * ln, (uint32_t)ln, batch, level, ws, &key, 1, s) != hipSuccess) return PC_EDEVICE;
+  if (launch_moddown(p, ws.acc, batch, 2, level, 1, R, ws, T, 3 * ln, batch, &one, s, false, level - 1) != hipSuccess)
     return PC_EDEVICE;
-  if (launch_rescale(p, R, 2 * ln, (uint32_t)ln, T + 2 * ln, 3 * ln, batch, level, x, tmp, out, s) != hipSuccess)
+  if (launch_rescale(p, R, 2 * ln, (uint32_t)ln, T + 2 * ln, 3 * ln, batch, level, ws.y, R, out, s, false) !=
+      hipSuccess)
+    return PC_EDEVICE;
+  if (launch_moddown_rescale(p, ws.acc, batch, level, ws, T, 3 * ln, T + 2 * ln, 3 * ln, R, out, s) != hipSuccess)
     return PC_EDEVICE;
   return PC_OK;
 }

@@ -155,6 +155,7 @@ enum KernelId {
   KID_BSGS_BABY,
   KID_BSGS_GIANT,
   KID_SEG_COPY,
+  KID_MODDOWN_RESCALE,
   KID_COUNT
 };
 extern const char* const kKernelNames[KID_COUNT];
@@ -184,7 +185,8 @@ hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t
 // When c0 is non-null, c0 of ciphertext (item % batch) under the item's Galois element is added to u = 0.
 hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t items, uint32_t polys, uint32_t level,
                           int variant, uint32_t* out, const KsWorkspace& ws, const uint32_t* c0, uint64_t ct_stride,
-                          uint32_t batch, const uint32_t* galois_per_key, hipStream_t s, bool c0_seg = false);
+                          uint32_t batch, const uint32_t* galois_per_key, hipStream_t s, bool c0_seg = false,
+                          uint32_t combine_from = 0);
 // Copy of `limbs` limbs from natural order into the segment layout (dst must not overlap src).
 hipError_t launch_seg_copy(const pc_params* p, const uint32_t* src, uint32_t limbs, uint32_t* dst, hipStream_t s);
 // b of a key at `level` from evaluation-form s ([lk][N]) and e ([beta][lk][N]);
@@ -205,7 +207,16 @@ hipError_t launch_tensor(const pc_params* p, const uint32_t* a, uint64_t a_strid
 // and tmp ([2 batch][l-1][N]) are workspace; out is [batch][2][l-1][N].
 hipError_t launch_rescale(const pc_params* p, const uint32_t* c, uint64_t c_stride, uint32_t c1_off,
                           const uint32_t* add1, uint64_t add_stride, uint32_t batch, uint32_t level, uint32_t* x,
-                          uint32_t* tmp, uint32_t* out, hipStream_t s);
+                          uint32_t* tmp, uint32_t* out, hipStream_t s, bool final_pass = true);
+// The ModDown combine of limbs 0..level-2 of a relinearised batch fused with the
+// rescale's last pass: launch_moddown(..., combine_from = level - 1) has
+// written limb level-1 and launch_rescale(..., final_pass = false) has filled
+// tmp; out = [batch][2][level-1][N]. c0 and add1 as in launch_moddown and
+// launch_rescale (d0 and d1 of the tensor).
+hipError_t launch_moddown_rescale(const pc_params* p, const uint32_t* acc, uint32_t batch, uint32_t level,
+                                  const KsWorkspace& ws, const uint32_t* c0, uint64_t ct_stride,
+                                  const uint32_t* add1, uint64_t add_stride, const uint32_t* tmp, uint32_t* out,
+                                  hipStream_t s);
 // Baby steps of the double-hoisted linear transform: inner [2][n2][l+K][N] from
 // the ciphertext [2][l][N], the baby inner products acc [n1-1][2][l+K][N] (factor
 // 2^-64) and the diagonals [n2][n1][l+K][N]; per extended-basis limb t:

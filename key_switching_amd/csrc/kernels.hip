@@ -733,6 +733,7 @@ struct ModDownArgs {
   uint64_t ct_stride;
   int N, level, K, L, polys, variant, batch, rows_ip, ngroups;
   int limb_xcd;  // combine pass: 0, or the split of limb_xcd_decode (c0 gathered under an automorphism)
+  int i0, ni;    // combine pass: limbs i0 .. i0 + ni - 1 of every polynomial (0 and level: all)
   uint32_t galois[kMaxKeysPerLaunch];  // per key = item / batch
 };
 
@@ -808,7 +809,7 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_fwd_blk(ModDownArgs 
   const int lk = A.level + A.K;
   // rows in storage order (see k_modup_inv_blk); when c0 is gathered under an
   // automorphism, the tiles of limb i are grouped on XCDs (see limb_xcd_decode)
-  int tile = (int)blockIdx.x, ipi = (int)(blockIdx.y / A.level), ii = (int)(blockIdx.y % A.level);
+  int tile = (int)blockIdx.x, ipi = (int)(blockIdx.y / A.ni), ii = A.i0 + (int)(blockIdx.y % A.ni);
   if (A.limb_xcd && !limb_xcd_unit(blk_tiles<LOGN>(), A.limb_xcd, A.level, A.rows_ip, tile, ii, ipi)) return;
   const size_t ip = (size_t)ipi, i = (size_t)ii, z = ip * A.level + i;
   const size_t item = ip / A.polys, u = ip % A.polys;
@@ -997,6 +998,98 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_rs_col(RescaleArgs A) {
   RescaleSrcLimb L{A.T.r[i],      A.T.rinv[i], A.T.tw_fwd + (size_t)i * A.N, A.x + (size_t)u * A.N,
                    A.ql_half,     A.ql_mod[i], A.tmp + ((size_t)u * A.lp + i) * A.N};
   fwd_col_pass<C::LRC, C::LEC, C::LRB, C::CC>(L, blockIdx.x * C::CC);
+}
+
+// The ModDown combine of a relinearisation (as k_md_fwd_blk with Galois
+// element 1) and the rescale's last pass (as k_rs_blk) for limb i < l' of
+// polynomial u, in one workgroup: two block passes on the same prime and
+// tile, the relinearised value o kept in registers between them instead of
+// being written and read back.
+//   phase 0: o = (acc - v) P^-1 (+ d0 on u = 0)
+//   phase 1: out = (o (+ d1 on u = 1) - v) q_{l'}^-1
+template <int E>
+struct MdRsLimb {
+  uint32_t r, rinv;
+  const uint32_t* __restrict__ tw;
+  uint32_t pinv, pinvp, inv, invp;
+  const uint32_t* __restrict__ src_md;  // ModDown conversion, after its column pass
+  const uint32_t* __restrict__ src_rs;  // rescale column-pass output
+  const uint32_t* __restrict__ acc;
+  const uint32_t* __restrict__ c0;   // nullptr: nothing to add
+  const uint32_t* __restrict__ add;  // nullptr: nothing to add
+  uint32_t* __restrict__ dst;
+  int phase;
+  uint32_t av[E], cv[E], o[E];
+  __device__ __forceinline__ uint32_t load(int pos) const { return at32(phase ? src_rs : src_md, pos); }
+  __device__ __forceinline__ void fetch(int m, int pos) {
+    if (phase == 0) {
+      av[m] = at32(acc, pos);
+      cv[m] = c0 ? at32(c0, pos) : 0u;
+    } else {
+      cv[m] = add ? at32(add, pos) : 0u;
+    }
+  }
+  __device__ __forceinline__ void finish(int m, int pos, uint32_t v) {
+    if (phase == 0) {
+      uint32_t x = mul_shoup(sub_mod(av[m], v, r), pinv, pinvp, r);
+      if (c0) x = add_mod(x, cv[m], r);
+      asm volatile("" : "+v"(x));  // computed here: only o stays live into the second pass
+      o[m] = x;
+    } else {
+      uint32_t x = o[m];
+      if (add) x = add_mod(x, cv[m], r);
+      at32(dst, pos) = mul_shoup(sub_mod(x, v, r), inv, invp, r);
+    }
+  }
+};
+
+struct MdRsArgs {
+  ModDownArgs M;         // polys = 2, variant 1, c0 = d0
+  const uint32_t* tmp;   // rescale column-pass output [2 batch][l'][N]
+  const uint32_t* add1;  // d1 of pair b at add1 + b * add_stride
+  uint64_t add_stride;
+  uint32_t* out;         // [batch][2][l'][N]
+  uint32_t inv[kMaxRescaleLimbs], invp[kMaxRescaleLimbs];
+};
+
+template <int LOGN, bool EARLY>
+__global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_rs_blk(MdRsArgs A) {
+  using C = Cfg<LOGN>;
+  const ModDownArgs& M = A.M;
+  const int lp = M.level - 1, lk = M.level + M.K;
+  const size_t ip = blockIdx.y / lp, i = blockIdx.y % lp;  // ip = 2 b + u
+  const size_t b = ip >> 1, u = ip & 1;
+  const size_t pi = (size_t)M.variant * M.L + i;
+  MdRsLimb<(1 << C::LEB)> L;
+  L.r = M.T.r[i];
+  L.rinv = M.T.rinv[i];
+  L.tw = M.T.tw_fblk + i * M.N;
+  L.pinv = M.LT.md_pinv[pi];
+  L.pinvp = M.LT.md_pinvp[pi];
+  L.inv = A.inv[i];
+  L.invp = A.invp[i];
+  L.src_md = M.tmp2 + (ip * M.level + i) * M.N;
+  L.src_rs = A.tmp + (ip * lp + i) * M.N;
+  L.acc = M.acc + (ip * lk + i) * M.N;
+  L.c0 = (u == 0 && M.c0 != nullptr) ? M.c0 + b * M.ct_stride + i * M.N : nullptr;
+  L.add = (u == 1 && A.add1 != nullptr) ? A.add1 + b * A.add_stride + i * M.N : nullptr;
+  L.dst = A.out + (ip * lp + i) * M.N;
+  L.phase = 0;
+  fwd_blk_pass_fetch<C::LRC, C::LRB, C::LEB, C::CB, EARLY>(L, blockIdx.x * C::CB);
+  // the second pass reuses the LDS tile; the empty asm keeps its loads (and
+  // the registers they take) out of the first pass
+  asm volatile("" ::: "memory");
+  __syncthreads();
+  {
+    // opaque copies: the second pass's loads cannot be hoisted into the first
+    const uint32_t* src = L.src_rs;
+    const uint32_t* tw = L.tw;
+    asm volatile("" : "+s"(src), "+s"(tw)::"memory");
+    L.src_rs = src;
+    L.tw = tw;
+  }
+  L.phase = 1;
+  fwd_blk_pass_fetch<C::LRC, C::LRB, C::LEB, C::CB, EARLY>(L, blockIdx.x * C::CB);
 }
 
 template <int LOGN, bool EARLY>
@@ -1490,7 +1583,9 @@ hipError_t launch_seg_copy(const pc_params* p, const uint32_t* src, uint32_t lim
 
 hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t items, uint32_t polys, uint32_t level,
                           int variant, uint32_t* out, const KsWorkspace& ws, const uint32_t* c0, uint64_t ct_stride,
-                          uint32_t batch, const uint32_t* galois_per_key, hipStream_t s, bool c0_seg) {
+                          uint32_t batch, const uint32_t* galois_per_key, hipStream_t s, bool c0_seg,
+                          uint32_t combine_from) {
+  if (combine_from >= level) return hipErrorInvalidValue;
   ModDownArgs A;
   A.T = p->tabs;
   A.LT = p->ltabs;
@@ -1512,7 +1607,9 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
   for (uint32_t k = 0; k < (uint32_t)kMaxKeysPerLaunch; ++k)
     A.galois[k] = (galois_per_key != nullptr && k < nkeys) ? galois_per_key[k] : 1u;
   const uint32_t rows_p = items * polys * p->K;
-  const uint32_t rows_q = items * polys * level;
+  A.i0 = (int)combine_from;
+  A.ni = (int)(level - combine_from);
+  const uint32_t rows_q = items * polys * (uint32_t)A.ni;
   const int tiles_c = col_tiles_of(p->log2n);
   const bool one = xcd_grid(tiles_c, (int)(items * polys), (int)((level + kBconvGroup - 1) / kBconvGroup)) <
                    kBconvSmallGrid;
@@ -1524,6 +1621,7 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
   if (c0 != nullptr)
     for (uint32_t k = 0; k < nkeys && k < (uint32_t)kMaxKeysPerLaunch; ++k)
       if (A.galois[k] != 1u) A.limb_xcd = xcd_split(level, (uint32_t)blk_tiles_of(p->log2n));
+  if (A.limb_xcd && combine_from != 0) return hipErrorInvalidValue;  // the XCD walk covers whole polynomials
   PC_DISPATCH_LOGN(p->log2n, {
     { LaunchTimer tm(p, KID_MODDOWN_INV_BLK, s); hipLaunchKernelGGL(k_md_inv_blk<LN>, dim3(blk_tiles<LN>(), rows_p), dim3(blk_threads<LN>()), 0, s, A); }
     { LaunchTimer tm(p, KID_MODDOWN_INV_COL, s); hipLaunchKernelGGL(k_md_inv_col<LN>, dim3(col_tiles<LN>(), rows_p), dim3(col_threads<LN>()), 0, s, A); }
@@ -1571,9 +1669,19 @@ hipError_t launch_tensor(const pc_params* p, const uint32_t* a, uint64_t a_strid
   return hipGetLastError();
 }
 
+// q_{l'}^-1 mod q_i and its Shoup companion for i < l' = level - 1.
+static void rescale_inverses(const pc_params* p, uint32_t level, uint32_t* inv, uint32_t* invp) {
+  const uint32_t lp = level - 1;
+  const size_t off = (size_t)lp * p->L;  // rows of the per-level rescale tables
+  for (uint32_t i = 0; i < (uint32_t)kMaxRescaleLimbs; ++i) {
+    inv[i] = i < lp ? p->h_rs_inv[off + i] : 0u;
+    invp[i] = i < lp ? p->h_rs_invp[off + i] : 0u;
+  }
+}
+
 hipError_t launch_rescale(const pc_params* p, const uint32_t* c, uint64_t c_stride, uint32_t c1_off,
                           const uint32_t* add1, uint64_t add_stride, uint32_t batch, uint32_t level, uint32_t* x,
-                          uint32_t* tmp, uint32_t* out, hipStream_t s) {
+                          uint32_t* tmp, uint32_t* out, hipStream_t s, bool final_pass) {
   const uint32_t lp = level - 1, polys = 2 * batch;
   if (level < 2 || lp > (uint32_t)kMaxRescaleLimbs || polys > (uint32_t)kMaxLimbsPerLaunch) return hipErrorInvalidValue;
   RescaleArgs A;
@@ -1591,12 +1699,8 @@ hipError_t launch_rescale(const pc_params* p, const uint32_t* c, uint64_t c_stri
   A.lp = (int)lp;
   A.ql_half = p->primes[lp] / 2;
   const size_t off = (size_t)lp * p->L;  // rows of the per-level rescale tables
-  for (uint32_t i = 0; i < (uint32_t)kMaxRescaleLimbs; ++i) {
-    const bool on = i < lp;
-    A.ql_mod[i] = on ? p->h_rs_qlmod[off + i] : 0u;
-    A.inv[i] = on ? p->h_rs_inv[off + i] : 0u;
-    A.invp[i] = on ? p->h_rs_invp[off + i] : 0u;
-  }
+  for (uint32_t i = 0; i < (uint32_t)kMaxRescaleLimbs; ++i) A.ql_mod[i] = i < lp ? p->h_rs_qlmod[off + i] : 0u;
+  rescale_inverses(p, level, A.inv, A.invp);
   {
     LaunchTimer tm(p, KID_RESCALE_GATHER, s);
     hipLaunchKernelGGL(k_rs_gather, dim3(p->N / (4 * kGatherThreads), polys), dim3(kGatherThreads), 0, s, A);
@@ -1608,13 +1712,58 @@ hipError_t launch_rescale(const pc_params* p, const uint32_t* c, uint64_t c_stri
   const uint32_t rows = polys * lp;
   PC_DISPATCH_LOGN(p->log2n, {
     { LaunchTimer tm(p, KID_RESCALE_COL, s); hipLaunchKernelGGL(k_rs_col<LN>, dim3(col_tiles<LN>(), rows), dim3(col_threads<LN>()), 0, s, A); }
-    {
+    if (final_pass) {
       LaunchTimer tm(p, KID_RESCALE_BLK, s);
       if (late_fetch(polys))
         hipLaunchKernelGGL((k_rs_blk<LN, false>), dim3(blk_tiles<LN>(), rows), dim3(blk_threads<LN>()), 0, s, A);
       else
         hipLaunchKernelGGL((k_rs_blk<LN, true>), dim3(blk_tiles<LN>(), rows), dim3(blk_threads<LN>()), 0, s, A);
     }
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_moddown_rescale(const pc_params* p, const uint32_t* acc, uint32_t batch, uint32_t level,
+                                  const KsWorkspace& ws, const uint32_t* c0, uint64_t ct_stride,
+                                  const uint32_t* add1, uint64_t add_stride, const uint32_t* tmp, uint32_t* out,
+                                  hipStream_t s) {
+  const uint32_t lp = level - 1, polys = 2 * batch;
+  if (level < 2 || lp > (uint32_t)kMaxRescaleLimbs || polys > (uint32_t)kMaxLimbsPerLaunch) return hipErrorInvalidValue;
+  MdRsArgs A;
+  ModDownArgs& M = A.M;
+  M.T = p->tabs;
+  M.LT = p->ltabs;
+  M.acc = acc;
+  M.y2 = ws.y2;
+  M.tmp2 = ws.tmp2;
+  M.out = nullptr;
+  M.c0 = c0;
+  M.ct_stride = ct_stride;
+  M.N = (int)p->N;
+  M.level = (int)level;
+  M.K = (int)p->K;
+  M.L = (int)p->L;
+  M.polys = 2;
+  M.variant = 1;  // acc carries 2^-64
+  M.batch = (int)batch;
+  M.rows_ip = (int)polys;
+  M.ngroups = 0;
+  M.limb_xcd = 0;
+  M.i0 = 0;
+  M.ni = (int)lp;
+  for (int k = 0; k < kMaxKeysPerLaunch; ++k) M.galois[k] = 1u;
+  A.tmp = tmp;
+  A.add1 = add1;
+  A.add_stride = add_stride;
+  A.out = out;
+  rescale_inverses(p, level, A.inv, A.invp);
+  const uint32_t rows = polys * lp;
+  PC_DISPATCH_LOGN(p->log2n, {
+    LaunchTimer tm(p, KID_MODDOWN_RESCALE, s);
+    if (late_fetch(polys))
+      hipLaunchKernelGGL((k_md_rs_blk<LN, false>), dim3(blk_tiles<LN>(), rows), dim3(blk_threads<LN>()), 0, s, A);
+    else
+      hipLaunchKernelGGL((k_md_rs_blk<LN, true>), dim3(blk_tiles<LN>(), rows), dim3(blk_threads<LN>()), 0, s, A);
   });
   return hipGetLastError();
 }

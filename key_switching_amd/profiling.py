@@ -58,7 +58,7 @@ FAMILIES = {
     "tensor": "k_tensor",
     "rescale_gather": "k_rs_gather",
     "rescale_col": "k_rs_col<16>",
-    "rescale_blk": "k_rs_blk<16, false>",
+    "moddown_rescale": "k_md_rs_blk<16, false>",
     # the 4 x 4 double-hoisted linear transform of one ciphertext
     "bsgs_baby": "k_bsgs_baby<4>",
     "bsgs_giant": "k_bsgs_giant",
