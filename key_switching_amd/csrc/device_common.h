@@ -58,6 +58,16 @@ __device__ __forceinline__ T& at32(T* base, uint32_t idx) {
   return *reinterpret_cast<T*>(reinterpret_cast<B*>(base) + (idx << 2));
 }
 
+// Streaming access for a word that this kernel touches once and no kernel
+// reads again soon (the accumulators that an earlier launch wrote, the final
+// output): the non-temporal hint keeps it from evicting reused lines.
+__device__ __forceinline__ uint32_t load_stream(const uint32_t* base, uint32_t idx) {
+  return __builtin_nontemporal_load(&at32(base, idx));
+}
+__device__ __forceinline__ void store_stream(uint32_t* base, uint32_t idx, uint32_t v) {
+  __builtin_nontemporal_store(v, &at32(base, idx));
+}
+
 // x w 2^-32 mod r for any 32-bit x and w < r, canonical: with w a twiddle in
 // Montgomery form (w0 2^32 mod r) this is x w0 mod r.
 __device__ __forceinline__ uint32_t mul_mont(uint32_t x, uint32_t w, uint32_t r, uint32_t rinv_neg) {

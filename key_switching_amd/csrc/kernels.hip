@@ -109,7 +109,8 @@ struct ScaledLimb {
 // index). acc and c0 at the E output positions of this thread are fetched
 // before the transform (fwd_blk_pass_fetch). c0 is in natural order, or with
 // SEG in the segment layout of a 2^LRB x 2^LRC limb: a thread's E positions
-// are rows of one column, so its gathers stay in one segment.
+// are rows of one column, so its gathers stay in one segment. acc (written by
+// the inner product, read once here) and out take the streaming hint.
 template <int E, int LRC, int LRB, bool SEG>
 struct CombineLimb {
   uint32_t r, rinv, pinv, pinvp;
@@ -122,14 +123,14 @@ struct CombineLimb {
   uint32_t av[E], cv[E];
   __device__ __forceinline__ uint32_t load(int pos) const { return at32(src, pos); }
   __device__ __forceinline__ void fetch(int m, int pos) {
-    av[m] = at32(acc, pos);
+    av[m] = load_stream(acc, pos);
     const uint32_t si = SEG ? seg_src_index((uint32_t)pos, g, h, LRC, LRB) : (((uint32_t)pos * g + h) & mask);
     cv[m] = c0 ? at32(c0, si) : 0u;
   }
   __device__ __forceinline__ void finish(int m, int pos, uint32_t v) const {
     uint32_t o = mul_shoup(sub_mod(av[m], v, r), pinv, pinvp, r);
     if (c0) o = add_mod(o, cv[m], r);
-    at32(dst, pos) = o;
+    store_stream(dst, pos, o);
   }
 };
 
@@ -1007,6 +1008,7 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_rs_col(RescaleArgs A) {
 // being written and read back.
 //   phase 0: o = (acc - v) P^-1 (+ d0 on u = 0)
 //   phase 1: out = (o (+ d1 on u = 1) - v) q_{l'}^-1
+// acc and out take the streaming hint, as in the ModDown combine.
 template <int E>
 struct MdRsLimb {
   uint32_t r, rinv;
@@ -1023,7 +1025,7 @@ struct MdRsLimb {
   __device__ __forceinline__ uint32_t load(int pos) const { return at32(phase ? src_rs : src_md, pos); }
   __device__ __forceinline__ void fetch(int m, int pos) {
     if (phase == 0) {
-      av[m] = at32(acc, pos);
+      av[m] = load_stream(acc, pos);
       cv[m] = c0 ? at32(c0, pos) : 0u;
     } else {
       cv[m] = add ? at32(add, pos) : 0u;
@@ -1038,7 +1040,7 @@ struct MdRsLimb {
     } else {
       uint32_t x = o[m];
       if (add) x = add_mod(x, cv[m], r);
-      at32(dst, pos) = mul_shoup(sub_mod(x, v, r), inv, invp, r);
+      store_stream(dst, pos, mul_shoup(sub_mod(x, v, r), inv, invp, r));
     }
   }
 };
