@@ -365,7 +365,9 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_bconv(ModUpArgs A
       fwd_col_compute<C::LRC, C::LEC, C::CC>(tg.z[g], lds, tg.r[g], tg.rinv[g], A.T.tw_fwd + tg.pidx[g] * A.N);
       uint32_t* dst = A.tmp + ((b * A.beta + d) * lk + tg.j[g]) * A.N;
 #pragma unroll
-      for (int m = 0; m < E; ++m) at32(dst, col_pos_fwd_out<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)) = tg.z[g][m];
+      // streaming stores: the block pass reads them once, and the inner
+      // product's digits (the block pass's output) keep the cache
+      for (int m = 0; m < E; ++m) store_stream(dst, col_pos_fwd_out<C::LRC, C::LEC, C::LRB, C::CC>(col0, m), tg.z[g][m]);
     }
   }
 }
