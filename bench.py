@@ -92,12 +92,12 @@ def _shape(N, level, K, alpha, beta):
     return digits, sum(level + K - a for a in digits), lrc, N.bit_length() - 1 - lrc
 
 
-def alg_bytes(kernel, N, level, K, alpha, beta, batch, nkeys=1):
+def alg_bytes(kernel, N, level, K, alpha, beta, batch, nkeys=1, stored=False):
     """Algorithmic bytes one launch must move: each input limb read once, each output limb written once.
 
     Limb = N words of 4 bytes; T_d = level - alpha_d + K targets per digit; the
-    inner product reads each key's b half once per batch; ModDown runs on
-    2 polynomials of every (key, ciphertext) item.
+    inner product reads each key's b half (and with ``stored`` its a half) once
+    per batch; ModDown runs on 2 polynomials of every (key, ciphertext) item.
     """
     l, limb = level, 4 * N
     _, targets, _, _ = _shape(N, level, K, alpha, beta)
@@ -109,7 +109,8 @@ def alg_bytes(kernel, N, level, K, alpha, beta, batch, nkeys=1):
         "modup_bconv": batch * (l + targets),
         "modup_fwd_blk": batch * (targets + targets),
         # IP: ext (targets) + own c1 limbs read once per key, b read once per key, acc written
-        "inner_product": nkeys * (batch * (targets + l) + beta * (l + K)) + items * 2 * (l + K),
+        "inner_product": nkeys * (batch * (targets + l) + (2 if stored else 1) * beta * (l + K))
+                         + items * 2 * (l + K),
         "moddown_inv_blk": items * 2 * (K + K),
         "moddown_inv_col": items * 2 * (K + K),
         "moddown_bconv": items * 2 * (K + l),
@@ -118,11 +119,12 @@ def alg_bytes(kernel, N, level, K, alpha, beta, batch, nkeys=1):
     return table[kernel] * limb
 
 
-def alg_ops(kernel, N, level, K, alpha, beta, batch, nkeys=1):
+def alg_ops(kernel, N, level, K, alpha, beta, batch, nkeys=1, stored=False):
     """Algorithmic 32-bit integer operations of one launch (op counts of the primitives above).
 
     An NTT pass over a limb does N/2 butterflies per stage: the column pass
-    covers the first LRC stages, the block pass the rest.
+    covers the first LRC stages, the block pass the rest. With ``stored`` the
+    key's a half is read and put in Montgomery form instead of regenerated.
     """
     l = level
     digits, targets, lrc, lrb = _shape(N, level, K, alpha, beta)
@@ -131,7 +133,8 @@ def alg_ops(kernel, N, level, K, alpha, beta, batch, nkeys=1):
     conv_targets = sum((l + K - a) * N * dot_ops(a) for a in digits)
     lk = l + K
     items = batch * nkeys
-    key_ops = lk * N * beta * (OPS_REDC + OPS_CHACHA12_BLOCK / 8 + OPS_WORDPAIR)  # b to Montgomery form, a regenerated
+    a_ops = OPS_REDC if stored else OPS_CHACHA12_BLOCK / 8 + OPS_WORDPAIR
+    key_ops = lk * N * beta * (OPS_REDC + a_ops)  # b to Montgomery form, a regenerated (or read)
     ip_item = lk * N * 2 * dot_ops(beta)                                            # both sums, one REDC each
     table = {
         "modup_inv_blk": batch * l * blk,
@@ -159,7 +162,7 @@ def alg_ops_per_launch(kernel, w, batch, beta, alpha):
     return alg_ops(kernel, w.N, w.L, w.K, alpha, beta, batch)
 
 
-def path_fractions(calls, ms):
+def path_fractions(calls, ms, stored=False):
     """HBM and int32-ALU fractions of a measured call made of the key-switch launches in
     `calls` (a list of (N, level, K, alpha, beta, batch, nkeys, with_modup) tuples)."""
     nbytes = nops = 0
@@ -167,8 +170,8 @@ def path_fractions(calls, ms):
         for k in KERNELS:
             if k.startswith("modup") and not with_modup:
                 continue
-            nbytes += alg_bytes(k, N, level, K, alpha, beta, batch, nkeys)
-            nops += alg_ops(k, N, level, K, alpha, beta, batch, nkeys)
+            nbytes += alg_bytes(k, N, level, K, alpha, beta, batch, nkeys, stored)
+            nops += alg_ops(k, N, level, K, alpha, beta, batch, nkeys, stored)
     t = ms * 1e-3
     return {"alg_bytes_per_call": int(nbytes), "alg_ops_per_call": int(nops),
             "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),

@@ -27,6 +27,8 @@
  *     alpha(l) = ceil(l / dnum) primes, D_d = [d alpha, min((d+1) alpha, l)),
  *     beta(l) = ceil(l / alpha) digits; a key used at level l was generated at
  *     level l and has limbs q_0..q_{l-1}, p_0..p_{K-1} (the "key basis");
+ *     with partition 1 alpha = ceil(L / dnum) at every level and one key
+ *     generated at level L serves every level;
  *   - ciphertext ct = [2][l][N] (c0 then c1), decrypting as c0 + c1 s;
  *   - key b half: [beta][l+K][N] evaluation form (digit, key-basis limb,
  *     position); the a half of digit d, limb j, position i is
@@ -40,23 +42,26 @@
  *   - ModDown uses the floor form (acc - Conv_{P->Q}([acc]_P)) * P^-1.
  *
  * Memory and streams. Every device pointer is a plain device address
- * (hipMalloc or PyTorch memory), 16-byte aligned, on the device the params
- * were created for; host pointers are marked "host". Calls enqueue work on
- * `stream` (a hipStream_t; NULL = the null stream) and return without waiting;
- * results are valid once the stream has reached that point. Inputs and outputs
- * must not overlap. The library owns a workspace arena inside pc_params, sized
- * at creation for max_batch ciphertexts and max_hoist keys at any level (the
- * largest of the per-level needs); calls that use it
- * must not run concurrently on different streams for the same pc_params.
- * pc_keyswitch_ex calls that each bring their own workspace may run
- * concurrently on different streams (the constant tables are read-only).
+ * (hipMalloc or PyTorch memory) on the device the params were created for,
+ * 16-byte aligned (the kernels move limbs in 16-byte vectors; a misaligned
+ * pointer is rejected with PC_EINVAL); host pointers are marked "host". The
+ * caller owns every ciphertext, key, output and workspace buffer; the library
+ * owns what its create calls return. Calls enqueue work on `stream` (a
+ * hipStream_t; NULL = the null stream) and return without waiting; results
+ * are valid once the stream has reached that point. Inputs and outputs must
+ * not overlap. The library owns a workspace arena inside pc_params, sized at
+ * creation for max_batch ciphertexts and max_hoist keys at any level (the
+ * largest of the per-level needs); calls that use it must not run
+ * concurrently on different streams for the same pc_params. pc_keyswitch_ex
+ * calls that each bring their own workspace may run concurrently on
+ * different streams (the constant tables are read-only).
  *
  * Errors. Every entry point validates its arguments on the host before any
- * launch and returns PC_EINVAL (null pointer, level outside [1, L], even or
- * out-of-range Galois element, batch above max_batch, ...), PC_EUNSUPPORTED
- * (a shape the kernels do not cover), PC_ENOMEM (allocation at creation) or
- * PC_EDEVICE (a HIP error, including no usable device). No call aborts the
- * process; pc_strerror gives a static message.
+ * launch and returns PC_EINVAL (null or misaligned pointer, level outside
+ * [1, L], even or out-of-range Galois element, batch above max_batch, ...),
+ * PC_EUNSUPPORTED (a shape the kernels do not cover), PC_ENOMEM (allocation at
+ * creation) or PC_EDEVICE (a HIP error, including no usable device). No call
+ * aborts the process; pc_strerror gives a static message.
  */
 #ifndef PC_H
 #define PC_H
@@ -93,12 +98,19 @@ typedef struct {
   const uint32_t *primes; /* host; NULL = the descending rule, else L + K primes (q's then p's) */
 } pc_params_desc;
 
-/* Build the prime chain, psi and every constant table on the host; with
- * device >= 0, also upload them and allocate the workspace arena on that
- * device. device = -1 builds the host tables only (pc_params_get works; every
- * compute call returns PC_EDEVICE). The caller owns *out and frees it with
- * pc_params_destroy. */
+/* Parameters, constant tables and the workspace arena (Perseus README,
+ * 'Layout': the CUDA-free core holds the parameters and the device runtime
+ * one frozen device arena; 'What's inside': programs replay from one device
+ * arena sized at setup). Builds the prime chain, psi and every constant table
+ * on the host; with device >= 0 also uploads them and allocates the arena on
+ * that device. device = -1 builds the host tables only (pc_params_get works;
+ * every compute call returns PC_EDEVICE). *out receives a library-owned
+ * handle, freed by pc_params_destroy. Errors: PC_EINVAL (null desc or out,
+ * L, K or dnum out of range, a bad user prime), PC_EUNSUPPORTED (ring size,
+ * digit, special-prime or key limits above), PC_ENOMEM, PC_EDEVICE. */
 int pc_params_create(const pc_params_desc *desc, int device, pc_params **out);
+/* Frees the tables and the arena of p (Perseus README, Python example under
+ * 'Reproduce': a session's resources end with close()). NULL is ignored. */
 void pc_params_destroy(pc_params *p);
 
 enum {
@@ -112,36 +124,61 @@ enum {
   PC_GET_ARENA_BYTES = 8,     /* uint64: size of the workspace arena (allocated only with a device) */
   PC_GET_LT_WORKSPACE_BYTES = 9 /* uint64: arena bytes pc_linear_transform needs; arg = level | n1 << 8 | n2 << 16 */
 };
-/* Copy a property into host memory dst (bytes must match exactly). */
+/* Copies property `what` (argument `arg`) into host memory dst; bytes must be
+ * the property's exact size (Perseus README, 'Layout': the core's parameters,
+ * here the chain, psi and the digit split). PC_EINVAL for a null pointer, an
+ * unknown property, a wrong size or an argument out of range. */
 int pc_params_get(const pc_params *p, int what, uint32_t arg, void *dst, size_t bytes);
 
-/* Negacyclic NTT in place: coefficients -> natural-order evaluations, for
- * nlimbs limbs of `data` ([nlimbs][N], device); limb z uses the prime with
- * chain index prime_idx[z] (host array, values < L + K). Uses the arena. */
-int pc_ntt(const pc_params *p, uint32_t *data, const uint32_t *prime_idx, uint32_t nlimbs, void *stream);
-/* Inverse of pc_ntt (includes the N^-1 scale). */
-int pc_intt(const pc_params *p, uint32_t *data, const uint32_t *prime_idx, uint32_t nlimbs, void *stream);
+/* Negacyclic NTT in place (Perseus README, 'Layout': the device runtime's NTT
+ * kernels). data is [count][nlimbs][N] (device, coefficients in, natural-order
+ * evaluations out); limb z of every one of the count polynomials uses the
+ * prime with chain index prime_idx[z] (host array of nlimbs values < L + K).
+ * count or nlimbs 0 does nothing. Uses the arena as scratch. PC_EINVAL for a
+ * null or misaligned data, a null prime_idx or an index out of range. */
+int pc_ntt(const pc_params *p, uint32_t *data, const uint32_t *prime_idx, uint32_t nlimbs, uint32_t count,
+           void *stream);
+/* Inverse of pc_ntt (Perseus README, 'Layout'), with the N^-1 scale; same
+ * arguments and errors. */
+int pc_intt(const pc_params *p, uint32_t *data, const uint32_t *prime_idx, uint32_t nlimbs, uint32_t count,
+            void *stream);
 
-/* ModUp of c1 ([level][N], evaluation form, device) into
- * ext ([beta][level+K][N], evaluation form, device): for digit d, limbs of D_d
- * are copied from c1, the others are the fast base conversion of the digit
- * ((sum_i [c1_i (Q_d/q_i)^-1]_{q_i} (Q_d/q_i)) mod r_j), taken to evaluation form. */
+/* ModUp (Perseus README, 'Layout': the device runtime's key switching; its
+ * first step) of c1 ([level][N], evaluation form, device) into ext
+ * ([beta][level+K][N], evaluation form, device): for digit d, limbs of D_d are
+ * copied from c1, the others are the fast base conversion of the digit
+ * ((sum_i [c1_i (Q_d/q_i)^-1]_{q_i} (Q_d/q_i)) mod r_j), taken to evaluation
+ * form. Uses the arena. PC_EINVAL for null or misaligned pointers or a level
+ * outside [1, L]. */
 int pc_modup(const pc_params *p, const uint32_t *c1, uint32_t level, uint32_t *ext, void *stream);
 
-/* One key switch: out ([2][level][N], device) from ct ([2][level][N], device)
- * with the key whose b half is evk_b ([beta][level+K][N], device) and whose
- * a half is regenerated from evk_seed (32 bytes, host). automorphism_idx is
- * the key's Galois element (1 for relinearisation). */
+/* One key switch (Perseus README, 'Layout': key switching kernels; 'What's
+ * inside': half of every key-switching key regenerated on the GPU from a
+ * ChaCha12 seed; arXiv summary page, methodology item (i)): out
+ * ([2][level][N], device) from ct ([2][level][N], device) with the key whose
+ * b half is evk_b ([beta][kl+K][N], device, kl = the key level) and whose a
+ * half is regenerated from evk_seed (32 bytes, host). automorphism_idx is the
+ * key's Galois element (1 for relinearisation). Uses the arena. PC_EINVAL
+ * for null or misaligned pointers, a null seed, a level outside [1, L], an
+ * even Galois element or one >= 2N. */
 int pc_keyswitch(const pc_params *p, const uint32_t *ct, const uint32_t *evk_b, const uint8_t *evk_seed,
                  uint32_t level, uint32_t automorphism_idx, uint32_t *out, void *stream);
 
-/* ModDown of one accumulator acc ([level+K][N], evaluation form, device) into
- * out ([level][N], device): (acc - Conv_{P->Q}([acc]_P)) * P^-1 on the q limbs. */
+/* ModDown (Perseus README, 'Layout': the device runtime's key switching; its
+ * last step) of one accumulator acc ([level+K][N], evaluation form, device)
+ * into out ([level][N], device): (acc - Conv_{P->Q}([acc]_P)) * P^-1 on the q
+ * limbs. Uses the arena. PC_EINVAL for null or misaligned pointers or a level
+ * outside [1, L]. */
 int pc_moddown(const pc_params *p, const uint32_t *acc, uint32_t level, uint32_t *out, void *stream);
 
-/* Batched / hoisted / stored-key key switching. Every ciphertext of the batch
- * is key-switched by every key; ModUp runs once per ciphertext and is shared
- * by all keys (hoisting). */
+/* Batched / hoisted / stored-key key switching (Perseus README, 'Runtime': the
+ * primitives are timed at batches k = 1 and 8; 'Layout' and 'What's inside' as
+ * for pc_keyswitch). Every ciphertext of the batch is key-switched by every
+ * key; ModUp runs once per ciphertext and is shared by all keys (hoisting).
+ * The a halves are regenerated from the seeds, or read from evk_a (the
+ * stored-key variant, which gives the same bits). PC_EINVAL for null or
+ * misaligned pointers, batch or nkeys out of range, a bad Galois element,
+ * neither seeds nor evk_a, or a workspace below PC_GET_WORKSPACE_BYTES. */
 typedef struct {
   const uint32_t *ct;             /* device [batch][2][level][N] */
   uint32_t batch;                 /* 1..max_batch */
@@ -171,19 +208,21 @@ int pc_keyswitch_ex(const pc_params *p, const pc_ks_args *args, void *stream);
  *   s_coef   device [lk][N]: the secret's coefficients as residues mod each r_j
  *   e_coef   device [beta][lk][N]: digit d's error coefficients, residues mod r_j
  *   evk_b    device [beta][lk][N] output (beta = digits at `level`)
- * Uses the params' workspace arena ((beta + 2) lk N words, PC_EINVAL if it is
- * smaller). Returns PC_EINVAL for null pointers, level outside [1, L] or an even
+ * Uses the params' workspace arena ((2 beta + 1) lk N words: the secret, the
+ * errors and the transform's scratch; PC_EINVAL if it is smaller). Returns
+ * PC_EINVAL for null or misaligned pointers, level outside [1, L] or an even
  * Galois element or one >= 2N, PC_EDEVICE on launch failure. */
 int pc_keygen(const pc_params *p, const uint8_t *seed, uint32_t level, uint32_t galois, const uint32_t *s_coef,
               const uint32_t *e_coef, uint32_t *evk_b, void *stream);
 
-/* Homomorphic multiplication around the key switch (Perseus README, 'What's
- * inside': squaring a ciphertext is one of the session's ops; the pages leave
- * its steps to the textbook RNS-CKKS product). Ciphertexts are in evaluation
- * form, 256-byte aligned device buffers owned by the caller; no input may alias
- * an output. All three run on `stream` (hipStream_t or NULL) and return PC_OK,
- * PC_EINVAL for null pointers or sizes out of range, PC_EDEVICE on launch
- * failure or a host-only params.
+/* Homomorphic multiplication around the key switch (Perseus README, Python
+ * example under 'Reproduce': squaring a ciphertext is one of the session's
+ * ops; the pages leave its steps to the textbook RNS-CKKS product).
+ * Ciphertexts are in evaluation form, device buffers owned by the caller; no
+ * input may alias an output. All three run on `stream` (hipStream_t or NULL)
+ * and return PC_OK, PC_EINVAL for null or misaligned pointers or sizes out of
+ * range, PC_EUNSUPPORTED for level - 1 > 64 or 2 batch > 256 (rescale and
+ * multiplication only), PC_EDEVICE on launch failure or a host-only params.
  *
  * pc_tensor: per limb i and position, d0 = a0 b0, d1 = a0 b1 + a1 b0,
  * d2 = a1 b1 (mod q_i).
@@ -192,17 +231,20 @@ int pc_keygen(const pc_params *p, const uint8_t *seed, uint32_t level, uint32_t 
 int pc_tensor(const pc_params *p, const uint32_t *ct_a, const uint32_t *ct_b, uint32_t batch, uint32_t level,
               uint32_t *d, void *stream);
 
-/* pc_rescale: divides by the last prime q_{l-1} (l = level >= 2), rounding to
- * nearest: with x the coefficients of limb l-1 centred into (-q_{l-1}/2,
- * q_{l-1}/2], limb i < l-1 becomes (c_i - NTT_i(x mod q_i)) q_{l-1}^-1 mod q_i.
+/* pc_rescale (Perseus README, 'What's inside': the session's CKKS ops; the
+ * textbook rescale): divides by the last prime q_{l-1} (l = level >= 2),
+ * rounding to nearest: with x the coefficients of limb l-1 centred into
+ * (-q_{l-1}/2, q_{l-1}/2], limb i < l-1 becomes
+ * (c_i - NTT_i(x mod q_i)) q_{l-1}^-1 mod q_i.
  *   ct   device [batch][2][level][N]
  *   out  device [batch][2][level-1][N]
  * Uses the params' workspace arena. */
 int pc_rescale(const pc_params *p, const uint32_t *ct, uint32_t batch, uint32_t level, uint32_t *out, void *stream);
 
-/* pc_hmult: tensor product, relinearisation of d2 with the key of s^2
- * (Galois element 1; its a half regenerated from evk_seed as in pc_keyswitch),
- * then pc_rescale: out = rescale(d0 + KS_0(d2), d1 + KS_1(d2)).
+/* pc_hmult (Perseus README, Python example under 'Reproduce': fhe.square):
+ * tensor product, relinearisation of d2 with the key of s^2 (Galois element
+ * 1; its a half regenerated from evk_seed as in pc_keyswitch), then
+ * pc_rescale: out = rescale(d0 + KS_0(d2), d1 + KS_1(d2)).
  *   ct_a, ct_b  device [batch][2][level][N], 2 <= level <= L
  *   evk_b       device b half of the key (shape as in pc_keyswitch_ex)
  *   evk_seed    host, 32 bytes
@@ -228,7 +270,7 @@ int pc_hmult(const pc_params *p, const uint32_t *ct_a, const uint32_t *ct_b, uin
  * the caller's; out must not alias ct or diag. Uses the params' workspace arena
  * (PC_EINVAL if it is smaller than PC_GET_LT_WORKSPACE_BYTES for level, n1, n2;
  * a larger max_batch or max_hoist at creation enlarges it). Returns PC_EINVAL for null
- * pointers, sizes out of range, an even Galois element or one >= 2N,
+ * or misaligned pointers, sizes out of range, an even Galois element or one >= 2N,
  * PC_EDEVICE on launch failure or a host-only params. */
 typedef struct {
   const uint32_t *ct;             /* device [2][level][N], evaluation form */
@@ -245,15 +287,77 @@ typedef struct {
 } pc_lt_args;
 int pc_linear_transform(const pc_params *p, const pc_lt_args *args, void *stream);
 
-/* Debug / parity: limb j (key-basis index at `level`) of digit d of the a half
- * regenerated from seed (32 bytes, host): dst ([N], device) canonical mod r_j. */
+/* Packed key storage: a key bundle (Perseus README, 'Layout': the server runs
+ * on the client's key bundle; 'Runtime': the bootstrap benchmark runs with its
+ * keys packed; 'What's inside': half of every key is regenerated from a
+ * ChaCha12 seed instead of being stored). Reading: a bundle holds nkeys keys
+ * of one key level, in one device allocation made at creation -- for each key
+ * its b half [beta][kl+K][N], its 32-byte seed and its Galois element (host) --
+ * so that the a halves cost 32 bytes each. With PC_KEYSET_FULL the bundle also
+ * stores every key's expanded a half beside its b half (twice the device
+ * memory: the unpacked form, for comparison); key switches from either form
+ * give the same bits. The bundle is library-owned; its keys are written by
+ * pc_keyset_set or pc_keyset_keygen and read by pc_keyswitch_keyset. */
+typedef struct pc_keyset pc_keyset;
+enum { PC_KEYSET_PACKED = 0, PC_KEYSET_FULL = 1 };
+/* Creates a bundle (Perseus README, 'Layout': the key bundle; 'Runtime': keys
+ * packed) of nkeys (1..256) keys for the key level of ciphertexts at
+ * `level` (level itself, or L with partition 1), Galois elements galois
+ * (host [nkeys], odd, < 2N, pairwise distinct), on the params' device. Errors:
+ * PC_EINVAL (null pointers, sizes, bad or repeated Galois elements, a mode
+ * other than the two above), PC_ENOMEM, PC_EDEVICE (host-only params). */
+int pc_keyset_create(const pc_params *p, uint32_t level, uint32_t nkeys, const uint32_t *galois, uint32_t mode,
+                     pc_keyset **out);
+/* Frees the bundle's device allocation (Perseus README, 'Layout': the key
+ * bundle). NULL is ignored. */
+void pc_keyset_destroy(pc_keyset *ks);
+/* Stores key idx (Perseus README, 'Layout': the key bundle): its b half is
+ * copied from evk_b (device [beta][kl+K][N]) and its seed (host, 32 bytes)
+ * recorded; a FULL bundle also expands the a half on the GPU. PC_EINVAL for a
+ * null or misaligned pointer or idx >= nkeys. */
+int pc_keyset_set(pc_keyset *ks, uint32_t idx, const uint32_t *evk_b, const uint8_t *seed, void *stream);
+/* Generates key idx in place with pc_keygen's equation (Perseus README, 'What's
+ * inside'), for the bundle's Galois element of idx: s_coef, e_coef as in
+ * pc_keygen. Uses the params' arena. Errors as pc_keygen, and PC_EINVAL for
+ * idx >= nkeys. */
+int pc_keyset_keygen(pc_keyset *ks, uint32_t idx, const uint8_t *seed, const uint32_t *s_coef, const uint32_t *e_coef,
+                     void *stream);
+enum {
+  PC_KEYSET_DEVICE_BYTES = 1,  /* uint64: device memory the bundle holds */
+  PC_KEYSET_KEY_BYTES = 2,     /* uint64: bytes of one b half (and of one stored a half) */
+  PC_KEYSET_GALOIS = 3,        /* uint32: Galois element of key `arg` */
+  PC_KEYSET_B_POINTER = 4      /* uint64: device address of key `arg`'s b half */
+};
+/* Copies a property of the bundle (Perseus README, 'Layout': the key bundle)
+ * into host memory dst (bytes exact). PC_EINVAL for a null pointer, an
+ * unknown property, a wrong size or a key index out of range. */
+int pc_keyset_get(const pc_keyset *ks, int what, uint32_t arg, void *dst, size_t bytes);
+/* Key switching with keys drawn from a bundle (Perseus README, 'Layout' and
+ * 'Runtime'): ciphertexts ct [batch][2][level][N] (device) under the nsel
+ * keys key_idx (host [nsel], indices into the bundle), hoisted as in
+ * pc_keyswitch_ex, into out [nsel][batch][2][level][N]; a halves regenerated
+ * from the bundle's seeds, or read from a FULL bundle. workspace: NULL for the
+ * params arena, else device memory of workspace_bytes >=
+ * PC_GET_WORKSPACE_BYTES. PC_EINVAL for null or misaligned pointers, an index
+ * out of range, nsel above max_hoist, batch above max_batch, a bundle of
+ * another params or key level. */
+int pc_keyswitch_keyset(const pc_params *p, const pc_keyset *ks, const uint32_t *ct, uint32_t batch,
+                        const uint32_t *key_idx, uint32_t nsel, uint32_t level, uint32_t *out, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Debug / parity (Perseus README, 'What's inside'; arXiv summary page,
+ * methodology item (i): the ChaCha12 expander): limb j (key-basis index at
+ * `level`) of digit d of the a half regenerated from seed (32 bytes, host):
+ * dst ([N], device) canonical mod r_j. PC_EINVAL for a null or misaligned
+ * pointer, level out of range, d >= beta or j >= level + K. */
 int pc_chacha_expand(const pc_params *p, const uint8_t *seed, uint32_t d, uint32_t j, uint32_t level, uint32_t *dst,
                      void *stream);
 
-/* Measurement support. Between pc_profile_begin and pc_profile_end every
- * kernel the library launches for p is bracketed by two hipEvents recorded on
- * the stream it runs on. pc_profile_end waits for those events and writes, per
- * kernel family (stats[k].name is a static string), the number of launches and
+/* Measurement support (the pages time their primitives, Perseus README,
+ * 'Runtime'). Between pc_profile_begin and pc_profile_end every kernel the
+ * library launches for p is bracketed by two hipEvents recorded on the stream
+ * it runs on. pc_profile_end waits for those events and writes, per kernel
+ * family (stats[k].name is a static string), the number of launches and
  * their summed event-to-event milliseconds; *count receives the number of
  * families written (at most max_stats). Not thread-safe; one profiling window
  * per params at a time. */
@@ -265,6 +369,8 @@ typedef struct {
 int pc_profile_begin(const pc_params *p);
 int pc_profile_end(const pc_params *p, pc_kernel_stat *stats, uint32_t max_stats, uint32_t *count);
 
+/* Static message for an error code (this ABI's own convention; the pages
+ * define none). */
 const char *pc_strerror(int code);
 
 #ifdef __cplusplus

@@ -21,9 +21,14 @@ PC_OK, PC_EINVAL, PC_ENOMEM, PC_EDEVICE, PC_EUNSUPPORTED = 0, -1, -2, -3, -4
 (PC_GET_N, PC_GET_PRIMES, PC_GET_PSI, PC_GET_ALPHA, PC_GET_BETA, PC_GET_WORKSPACE_BYTES, PC_GET_DEVICE_TABLE,
  PC_GET_ARENA_BYTES, PC_GET_LT_WORKSPACE_BYTES) = range(1, 10)
 
+PC_KEYSET_PACKED, PC_KEYSET_FULL = 0, 1
+PC_KEYSET_DEVICE_BYTES, PC_KEYSET_KEY_BYTES, PC_KEYSET_GALOIS, PC_KEYSET_B_POINTER = 1, 2, 3, 4
+
 EXPORTED = ("pc_params_create", "pc_params_destroy", "pc_params_get", "pc_ntt", "pc_intt", "pc_modup",
             "pc_keyswitch", "pc_moddown", "pc_keyswitch_ex", "pc_keygen", "pc_tensor", "pc_rescale",
             "pc_hmult", "pc_linear_transform", "pc_chacha_expand",
+            "pc_keyset_create", "pc_keyset_destroy", "pc_keyset_set", "pc_keyset_keygen", "pc_keyset_get",
+            "pc_keyswitch_keyset",
             "pc_profile_begin", "pc_profile_end", "pc_strerror")
 
 
@@ -75,8 +80,8 @@ def _lib():
         lib.pc_params_destroy.argtypes = [vp]
         lib.pc_params_destroy.restype = None
         lib.pc_params_get.argtypes = [vp, i32, u32, vp, ctypes.c_size_t]
-        lib.pc_ntt.argtypes = [vp, vp, ctypes.POINTER(u32), u32, vp]
-        lib.pc_intt.argtypes = [vp, vp, ctypes.POINTER(u32), u32, vp]
+        lib.pc_ntt.argtypes = [vp, vp, ctypes.POINTER(u32), u32, u32, vp]
+        lib.pc_intt.argtypes = [vp, vp, ctypes.POINTER(u32), u32, u32, vp]
         lib.pc_modup.argtypes = [vp, vp, u32, vp, vp]
         lib.pc_keyswitch.argtypes = [vp, vp, vp, ctypes.c_char_p, u32, u32, vp, vp]
         lib.pc_moddown.argtypes = [vp, vp, u32, vp, vp]
@@ -87,12 +92,23 @@ def _lib():
         lib.pc_rescale.argtypes = [vp, vp, u32, u32, vp, vp]
         lib.pc_hmult.argtypes = [vp, vp, vp, u32, vp, ctypes.c_char_p, u32, vp, vp]
         lib.pc_linear_transform.argtypes = [vp, ctypes.POINTER(_LtArgs), vp]
+        lib.pc_keyset_create.argtypes = [vp, u32, u32, ctypes.POINTER(u32), u32, ctypes.POINTER(vp)]
+        lib.pc_keyset_destroy.argtypes = [vp]
+        lib.pc_keyset_destroy.restype = None
+        lib.pc_keyset_set.argtypes = [vp, u32, vp, ctypes.c_char_p, vp]
+        lib.pc_keyset_keygen.argtypes = [vp, u32, ctypes.c_char_p, vp, vp, vp]
+        lib.pc_keyset_get.argtypes = [vp, i32, u32, vp, ctypes.c_size_t]
+        lib.pc_keyswitch_keyset.argtypes = [vp, vp, vp, u32, ctypes.POINTER(u32), u32, u32, vp, vp,
+                                            ctypes.c_size_t, vp]
         lib.pc_profile_begin.argtypes = [vp]
         lib.pc_profile_end.argtypes = [vp, ctypes.POINTER(_KStat), u32, ctypes.POINTER(u32)]
         lib.pc_strerror.argtypes = [i32]
         lib.pc_strerror.restype = ctypes.c_char_p
         for name in ("pc_params_create", "pc_params_get", "pc_ntt", "pc_intt", "pc_modup", "pc_keyswitch",
-                     "pc_moddown", "pc_keyswitch_ex", "pc_chacha_expand", "pc_profile_begin", "pc_profile_end"):
+                     "pc_moddown", "pc_keyswitch_ex", "pc_chacha_expand", "pc_profile_begin", "pc_profile_end",
+                     "pc_keygen", "pc_tensor", "pc_rescale", "pc_hmult", "pc_linear_transform",
+                     "pc_keyset_create", "pc_keyset_set", "pc_keyset_keygen", "pc_keyset_get",
+                     "pc_keyswitch_keyset"):
             getattr(lib, name).restype = i32
         _LIB = lib
     return _LIB
@@ -120,6 +136,8 @@ def _dev_ptr(t, name: str, shape=None, device=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if device is not None and t.device.index != device:
         raise ValueError(f"{name} is on cuda:{t.device.index}, the params on cuda:{device}")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name} must start at a 16-byte aligned address")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -233,20 +251,27 @@ def _new(shape, like_device: int):
     return torch.empty(shape, dtype=torch.int32, device=f"cuda:{like_device}")
 
 
-def ntt(prm: Params, data, prime_idx: Sequence[int]):
-    """In-place negacyclic NTT of data [len(prime_idx)][N] (pc_ntt)."""
-    idx = (ctypes.c_uint32 * len(prime_idx))(*[int(i) for i in prime_idx])
-    ptr = _dev_ptr(data, "data", (len(prime_idx), prm.N), prm.device)
-    _check(_lib().pc_ntt(prm.handle, ptr, idx, len(prime_idx), _stream()), "pc_ntt")
+def _transform(prm: Params, data, prime_idx: Sequence[int], fn, name: str):
+    n = len(prime_idx)
+    idx = (ctypes.c_uint32 * n)(*[int(i) for i in prime_idx])
+    if data.dim() == 2:
+        count, shape = 1, (n, prm.N)
+    else:
+        count, shape = int(data.shape[0]), (int(data.shape[0]), n, prm.N)
+    ptr = _dev_ptr(data, "data", shape, prm.device)
+    _check(fn(prm.handle, ptr, idx, n, count, _stream()), name)
     return data
+
+
+def ntt(prm: Params, data, prime_idx: Sequence[int]):
+    """In-place negacyclic NTT (pc_ntt) of data [len(prime_idx)][N], or of
+    [count][len(prime_idx)][N] (limb z of every polynomial uses prime_idx[z])."""
+    return _transform(prm, data, prime_idx, _lib().pc_ntt, "pc_ntt")
 
 
 def intt(prm: Params, data, prime_idx: Sequence[int]):
-    """In-place inverse NTT (pc_intt)."""
-    idx = (ctypes.c_uint32 * len(prime_idx))(*[int(i) for i in prime_idx])
-    ptr = _dev_ptr(data, "data", (len(prime_idx), prm.N), prm.device)
-    _check(_lib().pc_intt(prm.handle, ptr, idx, len(prime_idx), _stream()), "pc_intt")
-    return data
+    """In-place inverse NTT (pc_intt); shapes as in ntt()."""
+    return _transform(prm, data, prime_idx, _lib().pc_intt, "pc_intt")
 
 
 def modup(prm: Params, c1, level: int, ext=None):
@@ -436,6 +461,88 @@ def linear_transform(prm: Params, ct, diag, level: int, baby_b: Sequence = (), b
     args.giant_b, args.giant_seeds, args.giant_galois = keys(giant_b, giant_seeds, giant_galois, "giant_b")
     args.out = _dev_ptr(out, "out", (2, level, prm.N), prm.device)
     _check(_lib().pc_linear_transform(prm.handle, ctypes.byref(args), _stream()), "pc_linear_transform")
+    return out
+
+
+class KeySet:
+    """A key bundle (pc_keyset_create): nkeys keys of the key level serving
+    ``level``, each its b half plus a 32-byte seed (``full=True`` also stores
+    the expanded a halves), in one device allocation."""
+
+    def __init__(self, prm: Params, level: int, galois: Sequence[int], full: bool = False):
+        n = len(galois)
+        gal = (ctypes.c_uint32 * n)(*[int(g) for g in galois])
+        h = ctypes.c_void_p()
+        _check(_lib().pc_keyset_create(prm.handle, level, n, gal, PC_KEYSET_FULL if full else PC_KEYSET_PACKED,
+                                       ctypes.byref(h)), "pc_keyset_create")
+        self._h, self.prm, self.level, self.galois, self.full = h, prm, level, list(galois), full
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("key set closed")
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            _lib().pc_keyset_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def _get_u64(self, what: int, arg: int = 0) -> int:
+        buf = ctypes.c_uint64()
+        _check(_lib().pc_keyset_get(self.handle, what, arg, ctypes.byref(buf), 8), "pc_keyset_get")
+        return int(buf.value)
+
+    def device_bytes(self) -> int:
+        return self._get_u64(PC_KEYSET_DEVICE_BYTES)
+
+    def key_bytes(self) -> int:
+        return self._get_u64(PC_KEYSET_KEY_BYTES)
+
+    def set(self, idx: int, evk_b, seed: bytes):
+        """Store key idx: its b half (device, the key shape) and its seed (pc_keyset_set)."""
+        ptr = _dev_ptr(evk_b, "evk_b", self.prm.key_shape(self.level), self.prm.device)
+        _check(_lib().pc_keyset_set(self.handle, idx, ptr, _seed_bytes(seed), _stream()), "pc_keyset_set")
+
+    def keygen(self, idx: int, seed: bytes, s_coef, e_coef):
+        """Generate key idx in place (pc_keyset_keygen); s_coef, e_coef as in keygen()."""
+        kl = self.prm.key_level(self.level)
+        lk = kl + self.prm.K
+        beta = self.prm.beta(kl)
+        _check(_lib().pc_keyset_keygen(self.handle, idx, _seed_bytes(seed),
+                                       _dev_ptr(s_coef, "s_coef", (lk, self.prm.N), self.prm.device),
+                                       _dev_ptr(e_coef, "e_coef", (beta, lk, self.prm.N), self.prm.device),
+                                       _stream()), "pc_keyset_keygen")
+
+
+def keyswitch_keyset(prm: Params, keyset: KeySet, ct, key_idx: Sequence[int], level: int, out=None, workspace=None):
+    """ct [batch][2][level][N] under the bundle's keys key_idx (pc_keyswitch_keyset);
+    returns out [len(key_idx)][batch][2][level][N]."""
+    batch, nsel = int(ct.shape[0]), len(key_idx)
+    if out is None:
+        out = _new((nsel, batch, 2, level, prm.N), prm.device)
+    idx = (ctypes.c_uint32 * nsel)(*[int(i) for i in key_idx])
+    ws, ws_bytes = None, 0
+    if workspace is not None:
+        ws = _dev_ptr(workspace, "workspace", None, prm.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib().pc_keyswitch_keyset(prm.handle, keyset.handle, _dev_ptr(ct, "ct", (batch, 2, level, prm.N),
+                                                                           prm.device),
+                                      batch, idx, nsel, level,
+                                      _dev_ptr(out, "out", (nsel, batch, 2, level, prm.N), prm.device), ws,
+                                      ws_bytes, _stream()), "pc_keyswitch_keyset")
     return out
 
 

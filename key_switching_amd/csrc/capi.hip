@@ -291,6 +291,10 @@ struct DeviceGuard {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Device buffers are moved in 16-byte vectors: every device pointer of the ABI
+// must be 16-byte aligned.
+bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15u) != 0; }
+
 }  // namespace
 
 size_t ks_workspace_bytes(const pc_params* p, uint32_t level, uint32_t batch, uint32_t items) {
@@ -350,7 +354,7 @@ const char* const kKernelNames[KID_COUNT] = {
     "modup_inv_col",   "modup_bconv",     "modup_fwd_blk",   "inner_product",  "moddown_inv_blk",
     "moddown_inv_col", "moddown_bconv",   "moddown_fwd_blk", "chacha_expand",  "keygen",
     "tensor",          "rescale_gather",  "rescale_col",     "rescale_blk",    "bsgs_baby",
-    "bsgs_giant",      "seg_copy",        "moddown_rescale"};
+    "bsgs_giant",      "seg_copy",        "moddown_rescale", "expand_key"};
 
 static hipEvent_t prof_event(const pc_params* p) {
   if (p->prof_used == p->prof_pool.size()) {
@@ -614,35 +618,42 @@ int pc_params_get(const pc_params* p, int what, uint32_t arg, void* dst, size_t 
   }
 }
 
-static int ntt_common(const pc_params* p, uint32_t* data, const uint32_t* prime_idx, uint32_t nlimbs, void* stream,
-                      bool inverse) {
-  if (p == nullptr || data == nullptr || prime_idx == nullptr) return PC_EINVAL;
+static int ntt_common(const pc_params* p, uint32_t* data, const uint32_t* prime_idx, uint32_t nlimbs, uint32_t count,
+                      void* stream, bool inverse) {
+  if (p == nullptr || data == nullptr || prime_idx == nullptr || misaligned(data)) return PC_EINVAL;
   for (uint32_t z = 0; z < nlimbs; ++z)
     if (prime_idx[z] >= p->L + p->K) return PC_EINVAL;
   if (p->device < 0) return PC_EDEVICE;
-  if (nlimbs == 0) return PC_OK;
+  const size_t total = (size_t)nlimbs * count;
+  if (total == 0) return PC_OK;
+  if (total > 0xffffffffull) return PC_EINVAL;
   DeviceGuard g(p->device);
   if (!g.ok) return PC_EDEVICE;
-  const uint32_t chunk = (uint32_t)std::min<size_t>(nlimbs, p->arena_bytes / ((size_t)p->N * 4));
-  for (uint32_t base = 0; base < nlimbs; base += chunk) {
-    const uint32_t cnt = std::min(chunk, nlimbs - base);
-    if (launch_ntt(p, data + (size_t)base * p->N, static_cast<uint32_t*>(p->arena), prime_idx + base, cnt, inverse,
+  // polynomial c, limb z uses prime_idx[z]; the arena holds the transform's scratch
+  std::vector<uint32_t> idx(total);
+  for (size_t k = 0; k < total; ++k) idx[k] = prime_idx[k % nlimbs];
+  const uint32_t chunk = (uint32_t)std::min<size_t>(total, p->arena_bytes / ((size_t)p->N * 4));
+  for (size_t base = 0; base < total; base += chunk) {
+    const uint32_t cnt = (uint32_t)std::min<size_t>(chunk, total - base);
+    if (launch_ntt(p, data + base * p->N, static_cast<uint32_t*>(p->arena), idx.data() + base, cnt, inverse,
                    (hipStream_t)stream) != hipSuccess)
       return PC_EDEVICE;
   }
   return PC_OK;
 }
 
-int pc_ntt(const pc_params* p, uint32_t* data, const uint32_t* prime_idx, uint32_t nlimbs, void* stream) {
-  return ntt_common(p, data, prime_idx, nlimbs, stream, false);
+int pc_ntt(const pc_params* p, uint32_t* data, const uint32_t* prime_idx, uint32_t nlimbs, uint32_t count,
+           void* stream) {
+  return ntt_common(p, data, prime_idx, nlimbs, count, stream, false);
 }
 
-int pc_intt(const pc_params* p, uint32_t* data, const uint32_t* prime_idx, uint32_t nlimbs, void* stream) {
-  return ntt_common(p, data, prime_idx, nlimbs, stream, true);
+int pc_intt(const pc_params* p, uint32_t* data, const uint32_t* prime_idx, uint32_t nlimbs, uint32_t count,
+            void* stream) {
+  return ntt_common(p, data, prime_idx, nlimbs, count, stream, true);
 }
 
 int pc_modup(const pc_params* p, const uint32_t* c1, uint32_t level, uint32_t* ext, void* stream) {
-  if (p == nullptr || c1 == nullptr || ext == nullptr) return PC_EINVAL;
+  if (p == nullptr || c1 == nullptr || ext == nullptr || misaligned(c1) || misaligned(ext)) return PC_EINVAL;
   if (level < 1 || level > p->L) return PC_EINVAL;
   if (p->device < 0) return PC_EDEVICE;
   DeviceGuard g(p->device);
@@ -663,7 +674,7 @@ int pc_modup(const pc_params* p, const uint32_t* c1, uint32_t level, uint32_t* e
 }
 
 int pc_moddown(const pc_params* p, const uint32_t* acc, uint32_t level, uint32_t* out, void* stream) {
-  if (p == nullptr || acc == nullptr || out == nullptr) return PC_EINVAL;
+  if (p == nullptr || acc == nullptr || out == nullptr || misaligned(acc) || misaligned(out)) return PC_EINVAL;
   if (level < 1 || level > p->L) return PC_EINVAL;
   if (p->device < 0) return PC_EDEVICE;
   DeviceGuard g(p->device);
@@ -674,23 +685,25 @@ int pc_moddown(const pc_params* p, const uint32_t* acc, uint32_t level, uint32_t
   return PC_OK;
 }
 
-int pc_keyswitch_ex(const pc_params* p, const pc_ks_args* a, void* stream) {
+// Validates the arguments of a batched / hoisted key switch and fills keys[]
+// (a->nkeys entries; nkeys <= max_hoist <= kMaxKeysPerLaunch). No allocation.
+static int ks_args_keys(const pc_params* p, const pc_ks_args* a, KeyRef* keys) {
   if (p == nullptr || a == nullptr || a->ct == nullptr || a->out == nullptr || a->evk_b == nullptr ||
       a->galois == nullptr)
     return PC_EINVAL;
+  if (misaligned(a->ct) || misaligned(a->out) || misaligned(a->workspace)) return PC_EINVAL;
   if (a->level < 1 || a->level > p->L) return PC_EINVAL;
   if (a->batch < 1 || a->batch > p->max_batch) return PC_EINVAL;
-  if (a->nkeys < 1 || a->nkeys > p->max_hoist) return PC_EINVAL;
+  if (a->nkeys < 1 || a->nkeys > p->max_hoist || a->nkeys > (uint32_t)kMaxKeysPerLaunch) return PC_EINVAL;
   if (a->evk_a == nullptr && a->seeds == nullptr) return PC_EINVAL;
-  std::vector<KeyRef> keys(a->nkeys);
   for (uint32_t k = 0; k < a->nkeys; ++k) {
     const uint32_t gk = a->galois[k];
     if ((gk & 1u) == 0 || gk >= 2 * p->N) return PC_EINVAL;
-    if (a->evk_b[k] == nullptr) return PC_EINVAL;
+    if (a->evk_b[k] == nullptr || misaligned(a->evk_b[k])) return PC_EINVAL;
     keys[k].b = a->evk_b[k];
     keys[k].a = nullptr;
     if (a->evk_a != nullptr) {
-      if (a->evk_a[k] == nullptr) return PC_EINVAL;
+      if (a->evk_a[k] == nullptr || misaligned(a->evk_a[k])) return PC_EINVAL;
       keys[k].a = a->evk_a[k];
     }
     if (a->seeds != nullptr) {
@@ -703,6 +716,13 @@ int pc_keyswitch_ex(const pc_params* p, const pc_ks_args* a, void* stream) {
     }
     keys[k].galois = gk;
   }
+  return PC_OK;
+}
+
+int pc_keyswitch_ex(const pc_params* p, const pc_ks_args* a, void* stream) {
+  KeyRef keys[kMaxKeysPerLaunch];
+  const int rc = ks_args_keys(p, a, keys);
+  if (rc != PC_OK) return rc;
   if (p->device < 0) return PC_EDEVICE;
   const uint32_t items = a->nkeys * a->batch;
   const size_t need = ks_workspace_bytes(p, a->level, a->batch, items);
@@ -716,8 +736,8 @@ int pc_keyswitch_ex(const pc_params* p, const pc_ks_args* a, void* stream) {
   DeviceGuard g(p->device);
   if (!g.ok) return PC_EDEVICE;
   const uint64_t ct_stride = 2ull * a->level * p->N;
-  if (launch_keyswitch(p, a->ct, ct_stride, a->level * p->N, a->batch, a->level, keys.data(), a->nkeys, a->galois,
-                       base, a->out, (hipStream_t)stream) != hipSuccess)
+  if (launch_keyswitch(p, a->ct, ct_stride, a->level * p->N, a->batch, a->level, keys, a->nkeys, a->galois, base,
+                       a->out, (hipStream_t)stream) != hipSuccess)
     return PC_EDEVICE;
   return PC_OK;
 }
@@ -744,6 +764,7 @@ int pc_keyswitch(const pc_params* p, const uint32_t* ct, const uint32_t* evk_b, 
 int pc_keygen(const pc_params* p, const uint8_t* seed, uint32_t level, uint32_t galois, const uint32_t* s_coef,
               const uint32_t* e_coef, uint32_t* evk_b, void* stream) {
   if (p == nullptr || seed == nullptr || s_coef == nullptr || e_coef == nullptr || evk_b == nullptr) return PC_EINVAL;
+  if (misaligned(s_coef) || misaligned(e_coef) || misaligned(evk_b)) return PC_EINVAL;
   if (level < 1 || level > p->L) return PC_EINVAL;
   if ((galois & 1u) == 0 || galois >= 2 * p->N) return PC_EINVAL;
   if (p->device < 0) return PC_EDEVICE;
@@ -783,6 +804,7 @@ int pc_keygen(const pc_params* p, const uint8_t* seed, uint32_t level, uint32_t 
 int pc_tensor(const pc_params* p, const uint32_t* ct_a, const uint32_t* ct_b, uint32_t batch, uint32_t level,
               uint32_t* d, void* stream) {
   if (p == nullptr || ct_a == nullptr || ct_b == nullptr || d == nullptr) return PC_EINVAL;
+  if (misaligned(ct_a) || misaligned(ct_b) || misaligned(d)) return PC_EINVAL;
   if (level < 1 || level > p->L || batch < 1 || batch > p->max_batch) return PC_EINVAL;
   if (p->device < 0) return PC_EDEVICE;
   DeviceGuard g(p->device);
@@ -795,8 +817,9 @@ int pc_tensor(const pc_params* p, const uint32_t* ct_a, const uint32_t* ct_b, ui
 }
 
 int pc_rescale(const pc_params* p, const uint32_t* ct, uint32_t batch, uint32_t level, uint32_t* out, void* stream) {
-  if (p == nullptr || ct == nullptr || out == nullptr) return PC_EINVAL;
+  if (p == nullptr || ct == nullptr || out == nullptr || misaligned(ct) || misaligned(out)) return PC_EINVAL;
   if (level < 2 || level > p->L || batch < 1 || batch > p->max_batch) return PC_EINVAL;
+  if (level - 1 > (uint32_t)kMaxRescaleLimbs || 2 * batch > (uint32_t)kMaxLimbsPerLaunch) return PC_EUNSUPPORTED;
   if (p->device < 0) return PC_EDEVICE;
   const size_t N = p->N;
   uint32_t* x = static_cast<uint32_t*>(p->arena);
@@ -815,7 +838,9 @@ int pc_hmult(const pc_params* p, const uint32_t* ct_a, const uint32_t* ct_b, uin
              const uint8_t* evk_seed, uint32_t level, uint32_t* out, void* stream) {
   if (p == nullptr || ct_a == nullptr || ct_b == nullptr || evk_b == nullptr || evk_seed == nullptr || out == nullptr)
     return PC_EINVAL;
+  if (misaligned(ct_a) || misaligned(ct_b) || misaligned(evk_b) || misaligned(out)) return PC_EINVAL;
   if (level < 2 || level > p->L || batch < 1 || batch > p->max_batch) return PC_EINVAL;
+  if (level - 1 > (uint32_t)kMaxRescaleLimbs || 2 * batch > (uint32_t)kMaxLimbsPerLaunch) return PC_EUNSUPPORTED;
   if (p->device < 0) return PC_EDEVICE;
   if (hm_workspace_bytes(p, level, batch) > p->arena_bytes) return PC_EINVAL;
   KeyRef key;
@@ -863,7 +888,7 @@ static bool lt_keys(const pc_params* p, uint32_t n, const uint32_t* const* b, co
   if (n == 0) return true;
   if (b == nullptr || seeds == nullptr || galois == nullptr) return false;
   for (uint32_t k = 0; k < n; ++k) {
-    if (b[k] == nullptr || (galois[k] & 1u) == 0 || galois[k] >= 2 * p->N) return false;
+    if (b[k] == nullptr || misaligned(b[k]) || (galois[k] & 1u) == 0 || galois[k] >= 2 * p->N) return false;
     out[k].b = b[k];
     out[k].a = nullptr;
     for (int w = 0; w < 8; ++w) {
@@ -877,6 +902,7 @@ static bool lt_keys(const pc_params* p, uint32_t n, const uint32_t* const* b, co
 
 int pc_linear_transform(const pc_params* p, const pc_lt_args* a, void* stream) {
   if (p == nullptr || a == nullptr || a->ct == nullptr || a->diag == nullptr || a->out == nullptr) return PC_EINVAL;
+  if (misaligned(a->ct) || misaligned(a->diag) || misaligned(a->out)) return PC_EINVAL;
   const uint32_t level = a->level, n1 = a->n1, n2 = a->n2;
   if (level < 1 || level > p->L || n1 < 1 || n1 > 8 || n2 < 1 || n2 > 32 || level + p->K > 64) return PC_EINVAL;
   std::vector<KeyRef> baby, giant;
@@ -938,9 +964,161 @@ int pc_linear_transform(const pc_params* p, const pc_lt_args* a, void* stream) {
   return PC_OK;
 }
 
+// ---------------------------------------------------------------------------
+// key bundles
+// ---------------------------------------------------------------------------
+
+static void seed_words(const uint8_t* seed, uint32_t out[8]) {
+  for (int w = 0; w < 8; ++w)
+    out[w] = (uint32_t)seed[4 * w] | ((uint32_t)seed[4 * w + 1] << 8) | ((uint32_t)seed[4 * w + 2] << 16) |
+             ((uint32_t)seed[4 * w + 3] << 24);
+}
+
+int pc_keyset_create(const pc_params* p, uint32_t level, uint32_t nkeys, const uint32_t* galois, uint32_t mode,
+                     pc_keyset** out) {
+  if (p == nullptr || galois == nullptr || out == nullptr) return PC_EINVAL;
+  *out = nullptr;
+  if (level < 1 || level > p->L || nkeys < 1 || nkeys > 256 || mode > PC_KEYSET_FULL) return PC_EINVAL;
+  for (uint32_t k = 0; k < nkeys; ++k) {
+    if ((galois[k] & 1u) == 0 || galois[k] >= 2 * p->N) return PC_EINVAL;
+    for (uint32_t u = 0; u < k; ++u)
+      if (galois[u] == galois[k]) return PC_EINVAL;
+  }
+  if (p->device < 0) return PC_EDEVICE;
+  pc_keyset* ks = new (std::nothrow) pc_keyset();
+  if (ks == nullptr) return PC_ENOMEM;
+  ks->p = p;
+  ks->key_level = key_level_of(p, level);
+  ks->nkeys = nkeys;
+  ks->mode = mode;
+  ks->beta = (uint32_t)beta_of(p, ks->key_level);
+  ks->lk = ks->key_level + p->K;
+  ks->key_words = (size_t)ks->beta * ks->lk * p->N;
+  ks->galois.assign(galois, galois + nkeys);
+  ks->seeds.assign((size_t)nkeys * 32, 0);
+  DeviceGuard g(p->device);
+  if (!g.ok) {
+    delete ks;
+    return PC_EDEVICE;
+  }
+  const size_t bytes = (size_t)nkeys * (mode ? 2 : 1) * ks->key_words * 4;
+  if (hipMalloc(&ks->mem, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    delete ks;
+    return PC_ENOMEM;
+  }
+  *out = ks;
+  return PC_OK;
+}
+
+void pc_keyset_destroy(pc_keyset* ks) {
+  if (ks == nullptr) return;
+  if (ks->mem != nullptr) {
+    DeviceGuard g(ks->p->device);
+    (void)hipFree(ks->mem);
+  }
+  delete ks;
+}
+
+int pc_keyset_set(pc_keyset* ks, uint32_t idx, const uint32_t* evk_b, const uint8_t* seed, void* stream) {
+  if (ks == nullptr || evk_b == nullptr || seed == nullptr || misaligned(evk_b) || idx >= ks->nkeys) return PC_EINVAL;
+  const pc_params* p = ks->p;
+  DeviceGuard g(p->device);
+  if (!g.ok) return PC_EDEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  memcpy(&ks->seeds[(size_t)idx * 32], seed, 32);
+  if (hipMemcpyAsync(ks->b_of(idx), evk_b, ks->key_words * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return PC_EDEVICE;
+  if (ks->mode == PC_KEYSET_FULL) {
+    uint32_t key[8];
+    seed_words(seed, key);
+    if (launch_expand_key(p, key, ks->key_level, ks->a_of(idx), s) != hipSuccess) return PC_EDEVICE;
+  }
+  return PC_OK;
+}
+
+int pc_keyset_keygen(pc_keyset* ks, uint32_t idx, const uint8_t* seed, const uint32_t* s_coef, const uint32_t* e_coef,
+                     void* stream) {
+  if (ks == nullptr || seed == nullptr || idx >= ks->nkeys) return PC_EINVAL;
+  const pc_params* p = ks->p;
+  const int rc = pc_keygen(p, seed, ks->key_level, ks->galois[idx], s_coef, e_coef, ks->b_of(idx), stream);
+  if (rc != PC_OK) return rc;
+  memcpy(&ks->seeds[(size_t)idx * 32], seed, 32);
+  if (ks->mode == PC_KEYSET_FULL) {
+    DeviceGuard g(p->device);
+    if (!g.ok) return PC_EDEVICE;
+    uint32_t key[8];
+    seed_words(seed, key);
+    if (launch_expand_key(p, key, ks->key_level, ks->a_of(idx), (hipStream_t)stream) != hipSuccess)
+      return PC_EDEVICE;
+  }
+  return PC_OK;
+}
+
+int pc_keyset_get(const pc_keyset* ks, int what, uint32_t arg, void* dst, size_t bytes) {
+  if (ks == nullptr || dst == nullptr) return PC_EINVAL;
+  uint64_t v = 0;
+  switch (what) {
+    case PC_KEYSET_DEVICE_BYTES:
+      v = (uint64_t)ks->nkeys * (ks->mode ? 2 : 1) * ks->key_words * 4;
+      break;
+    case PC_KEYSET_KEY_BYTES:
+      v = (uint64_t)ks->key_words * 4;
+      break;
+    case PC_KEYSET_GALOIS: {
+      if (bytes != 4 || arg >= ks->nkeys) return PC_EINVAL;
+      memcpy(dst, &ks->galois[arg], 4);
+      return PC_OK;
+    }
+    case PC_KEYSET_B_POINTER:
+      if (arg >= ks->nkeys) return PC_EINVAL;
+      v = (uint64_t)(uintptr_t)ks->b_of(arg);
+      break;
+    default:
+      return PC_EINVAL;
+  }
+  if (bytes != 8) return PC_EINVAL;
+  memcpy(dst, &v, 8);
+  return PC_OK;
+}
+
+int pc_keyswitch_keyset(const pc_params* p, const pc_keyset* ks, const uint32_t* ct, uint32_t batch,
+                        const uint32_t* key_idx, uint32_t nsel, uint32_t level, uint32_t* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (p == nullptr || ks == nullptr || key_idx == nullptr || ks->p != p) return PC_EINVAL;
+  if (level < 1 || level > p->L || key_level_of(p, level) != ks->key_level) return PC_EINVAL;
+  if (nsel < 1 || nsel > p->max_hoist) return PC_EINVAL;
+  const uint32_t* bptr[kMaxKeysPerLaunch];
+  const uint32_t* aptr[kMaxKeysPerLaunch];
+  uint32_t gal[kMaxKeysPerLaunch];
+  uint8_t seeds[kMaxKeysPerLaunch * 32];
+  for (uint32_t k = 0; k < nsel; ++k) {
+    const uint32_t i = key_idx[k];
+    if (i >= ks->nkeys) return PC_EINVAL;
+    bptr[k] = ks->b_of(i);
+    aptr[k] = ks->a_of(i);
+    gal[k] = ks->galois[i];
+    memcpy(seeds + 32 * k, &ks->seeds[(size_t)i * 32], 32);
+  }
+  pc_ks_args a;
+  memset(&a, 0, sizeof(a));
+  a.ct = ct;
+  a.batch = batch;
+  a.nkeys = nsel;
+  a.evk_b = bptr;
+  a.evk_a = ks->mode == PC_KEYSET_FULL ? aptr : nullptr;
+  a.seeds = seeds;
+  a.galois = gal;
+  a.level = level;
+  a.out = out;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  return pc_keyswitch_ex(p, &a, stream);
+}
+
 int pc_chacha_expand(const pc_params* p, const uint8_t* seed, uint32_t d, uint32_t j, uint32_t level, uint32_t* dst,
                      void* stream) {
-  if (p == nullptr || seed == nullptr || dst == nullptr) return PC_EINVAL;
+  if (p == nullptr || seed == nullptr || dst == nullptr || misaligned(dst)) return PC_EINVAL;
   if (level < 1 || level > p->L) return PC_EINVAL;
   if (d >= (uint32_t)beta_of(p, level) || j >= level + p->K) return PC_EINVAL;
   if (p->device < 0) return PC_EDEVICE;

@@ -16,6 +16,7 @@ constexpr int kMaxKeysPerLaunch = 32;    // keys (seeds, pointers, Galois elemen
 constexpr int kMaxDigits = 6;            // digits supported by the inner-product kernel
 constexpr int kMaxSpecial = 8;           // special primes (ModDown)
 constexpr int kMaxAlpha = 8;             // primes per digit (ModUp)
+constexpr int kMaxRescaleLimbs = 64;     // limbs kept by a rescale (constants travel in kernel arguments)
 
 // Device pointers to the per-prime tables (prime index = position in the chain:
 // q_0..q_{L-1} then p_0..p_{K-1}).
@@ -94,6 +95,19 @@ struct pc_params {
   mutable std::vector<ProfRec> prof_recs;
 };
 
+// A key bundle (pc_keyset): nkeys keys of one key level in one device
+// allocation, each key's b half and, in the FULL mode, its expanded a half.
+struct pc_keyset {
+  const pc_params* p = nullptr;
+  uint32_t key_level = 0, nkeys = 0, mode = 0, beta = 0, lk = 0;
+  size_t key_words = 0;          // beta * lk * N: one key half
+  uint32_t* mem = nullptr;       // [nkeys][halves][beta][lk][N], halves = 1 (b) or 2 (b, a)
+  std::vector<uint32_t> galois;  // [nkeys]
+  std::vector<uint8_t> seeds;    // [nkeys][32]
+  uint32_t* b_of(uint32_t k) const { return mem + (size_t)k * (mode ? 2 : 1) * key_words; }
+  uint32_t* a_of(uint32_t k) const { return mode ? mem + ((size_t)k * 2 + 1) * key_words : nullptr; }
+};
+
 namespace pc {
 
 // Digit size and count at a level, and the level of the key that serves it
@@ -156,6 +170,7 @@ enum KernelId {
   KID_BSGS_GIANT,
   KID_SEG_COPY,
   KID_MODDOWN_RESCALE,
+  KID_EXPAND_KEY,
   KID_COUNT
 };
 extern const char* const kKernelNames[KID_COUNT];
@@ -230,5 +245,7 @@ hipError_t launch_bsgs_giant(const pc_params* p, const uint32_t* inner, const ui
                              const uint32_t* m96, const uint32_t* m128, hipStream_t s);
 hipError_t launch_chacha_expand(const pc_params* p, const uint32_t seed[8], uint32_t d, uint32_t j,
                                 uint32_t prime_index, uint32_t* dst, hipStream_t s);
+// Every limb of a key's a half at key level kl: dst [beta][kl+K][N], canonical.
+hipError_t launch_expand_key(const pc_params* p, const uint32_t seed[8], uint32_t kl, uint32_t* dst, hipStream_t s);
 
 }  // namespace pc

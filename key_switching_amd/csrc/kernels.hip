@@ -15,7 +15,6 @@
 // walking its column/block tiles; the conversions and the gathering kernels
 // use 1-D grids placed by XCD (xcd_unit, limb_xcd_decode).
 #include <algorithm>
-#include <map>
 #include <mutex>
 
 #include "internal.h"
@@ -871,6 +870,32 @@ __global__ void __launch_bounds__(256) k_chacha_expand(ChaChaKey key, uint32_t d
   }
 }
 
+// Every limb of a key's a half: grid (N / 2048, kl + K, beta), one ChaCha block
+// (8 positions) per thread; limb j of the key basis at key level kl.
+struct ExpandKeyArgs {
+  DevTables T;
+  ChaChaKey key;
+  uint32_t* dst;  // [beta][kl+K][N]
+  int N, kl, L;
+};
+
+template <int ROUNDS>
+__global__ void __launch_bounds__(256) k_expand_key(ExpandKeyArgs A) {
+  const int i0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i0 >= A.N) return;
+  const int j = blockIdx.y, d = blockIdx.z, lk = gridDim.y;
+  const size_t pj = j < A.kl ? (size_t)j : (size_t)(A.L + j - A.kl);
+  const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj], r2 = A.T.r2[pj];
+  uint32_t w[16];
+  chacha_block<ROUNDS>(A.key, (uint32_t)(i0 >> 3), 0u, (uint32_t)d, (uint32_t)j, w);
+  uint32_t v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = redc(mul_wide(word_pair_to_mont(w[2 * k], w[2 * k + 1], r, rinv), r2), r, rinv);
+  uint32_t* out = A.dst + ((size_t)d * lk + j) * A.N + i0;
+  *reinterpret_cast<uint4*>(out) = make_uint4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<uint4*>(out + 4) = make_uint4(v[4], v[5], v[6], v[7]);
+}
+
 // ---------------------------------------------------------------------------
 // homomorphic multiplication around the key switch
 // ---------------------------------------------------------------------------
@@ -924,8 +949,6 @@ __global__ void __launch_bounds__(kTensorThreads) k_tensor(TensorArgs A) {
 // centred residue. The column pass loads [x] mod q_i, the block pass fetches
 // c_i (plus an optional addend on the second polynomial) at its output
 // positions and stores the division.
-constexpr int kMaxRescaleLimbs = 64;
-
 struct RescaleArgs {
   DevTables T;
   const uint32_t* x;  // [polys][N] limb l' of every polynomial, coefficient form
@@ -1415,23 +1438,29 @@ hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stri
 }
 
 // Workgroups of `kernel` resident on the current device at once, cached per
-// (kernel, device).
+// (kernel, device) in a fixed table (no allocation after the first lookup).
 template <class F>
 static uint32_t resident_workgroups(F kernel, int threads) {
+  struct Entry {
+    const void* kernel;
+    int dev;
+    uint32_t n;
+  };
   static std::mutex mu;
-  static std::map<std::pair<const void*, int>, uint32_t> cache;
+  static Entry cache[64];
+  static int used = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  const auto key = std::make_pair(reinterpret_cast<const void*>(kernel), dev);
+  const void* kp = reinterpret_cast<const void*>(kernel);
   std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find(key);
-  if (it != cache.end()) return it->second;
+  for (int i = 0; i < used; ++i)
+    if (cache[i].kernel == kp && cache[i].dev == dev) return cache[i].n;
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
     per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
   const uint32_t n = (uint32_t)(per_cu * cus);
-  cache[key] = n;
+  if (used < 64) cache[used++] = Entry{kp, dev, n};
   return n;
 }
 
@@ -1881,6 +1910,23 @@ hipError_t launch_chacha_expand(const pc_params* p, const uint32_t seed[8], uint
     hipLaunchKernelGGL(k_chacha_expand<20>, grid, dim3(256), 0, s, key, d, j, r, rinv, r2, dst, (int)p->N);
   else
     hipLaunchKernelGGL(k_chacha_expand<12>, grid, dim3(256), 0, s, key, d, j, r, rinv, r2, dst, (int)p->N);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_key(const pc_params* p, const uint32_t seed[8], uint32_t kl, uint32_t* dst, hipStream_t s) {
+  ExpandKeyArgs A;
+  A.T = p->tabs;
+  for (int w = 0; w < 8; ++w) A.key.k[w] = seed[w];
+  A.dst = dst;
+  A.N = (int)p->N;
+  A.kl = (int)kl;
+  A.L = (int)p->L;
+  const dim3 grid((p->N / 8 + 255) / 256, kl + p->K, (uint32_t)beta_of(p, kl));
+  LaunchTimer tm(p, KID_EXPAND_KEY, s);
+  if (p->chacha_rounds == 20)
+    hipLaunchKernelGGL(k_expand_key<20>, grid, dim3(256), 0, s, A);
+  else
+    hipLaunchKernelGGL(k_expand_key<12>, grid, dim3(256), 0, s, A);
   return hipGetLastError();
 }
 

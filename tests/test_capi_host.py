@@ -103,10 +103,10 @@ def test_compute_calls_validate_before_touching_a_device():
         dummy = ctypes.c_void_p(0x1000)  # never dereferenced: validation or the device check fails first
         idx = (ctypes.c_uint32 * 1)(0)
         bad_idx = (ctypes.c_uint32 * 1)(4)
-        assert lib.pc_ntt(h, None, idx, 1, None) == ksa.PC_EINVAL
-        assert lib.pc_ntt(h, dummy, bad_idx, 1, None) == ksa.PC_EINVAL
-        assert lib.pc_ntt(h, dummy, idx, 1, None) == ksa.PC_EDEVICE
-        assert lib.pc_intt(h, dummy, idx, 1, None) == ksa.PC_EDEVICE
+        assert lib.pc_ntt(h, None, idx, 1, 1, None) == ksa.PC_EINVAL
+        assert lib.pc_ntt(h, dummy, bad_idx, 1, 1, None) == ksa.PC_EINVAL
+        assert lib.pc_ntt(h, dummy, idx, 1, 1, None) == ksa.PC_EDEVICE
+        assert lib.pc_intt(h, dummy, idx, 1, 3, None) == ksa.PC_EDEVICE
         assert lib.pc_modup(h, dummy, 0, dummy, None) == ksa.PC_EINVAL
         assert lib.pc_modup(h, dummy, 4, dummy, None) == ksa.PC_EINVAL
         assert lib.pc_modup(h, dummy, 3, dummy, None) == ksa.PC_EDEVICE
@@ -178,6 +178,88 @@ def test_compute_calls_validate_before_touching_a_device():
         assert lib.pc_params_get(h, ksa.PC_GET_ALPHA, 0, buf, 4) == ksa.PC_EINVAL
         assert lib.pc_params_get(h, 99, 0, buf, 4) == ksa.PC_EINVAL
     assert lib.pc_strerror(ksa.PC_EDEVICE).startswith(b"device")
+
+
+def test_misaligned_pointers_rejected():
+    """The kernels move limbs in 16-byte vectors: a device pointer off a 16-byte
+    boundary is refused before anything else (here a host-only params, which
+    would otherwise answer PC_EDEVICE)."""
+    lib = ksa._lib()
+    with ksa.Params(12, 3, 3, 1, device=None, max_batch=2) as prm:
+        h = prm.handle
+        ok, bad = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1004)
+        idx = (ctypes.c_uint32 * 1)(0)
+        seed = bytes(32)
+        assert lib.pc_ntt(h, bad, idx, 1, 1, None) == ksa.PC_EINVAL
+        assert lib.pc_modup(h, ok, 3, bad, None) == ksa.PC_EINVAL
+        assert lib.pc_moddown(h, bad, 3, ok, None) == ksa.PC_EINVAL
+        assert lib.pc_keyswitch(h, bad, ok, seed, 3, 5, ok, None) == ksa.PC_EINVAL
+        assert lib.pc_keyswitch(h, ok, bad, seed, 3, 5, ok, None) == ksa.PC_EINVAL
+        assert lib.pc_keyswitch(h, ok, ok, seed, 3, 5, bad, None) == ksa.PC_EINVAL
+        assert lib.pc_keyswitch(h, ok, ok, seed, 3, 5, ok, None) == ksa.PC_EDEVICE
+        args = ksa._KsArgs()
+        bp = (ctypes.c_void_p * 1)(0x1000)
+        gal = (ctypes.c_uint32 * 1)(5)
+        args.ct, args.batch, args.nkeys, args.level, args.out = ok, 1, 1, 3, ok
+        args.evk_b, args.galois, args.seeds = bp, gal, seed
+        args.workspace, args.workspace_bytes = ctypes.c_void_p(0x2008), 1 << 30
+        assert lib.pc_keyswitch_ex(h, ctypes.byref(args), None) == ksa.PC_EINVAL
+        args.workspace = ctypes.c_void_p(0x2000)
+        assert lib.pc_keyswitch_ex(h, ctypes.byref(args), None) == ksa.PC_EDEVICE
+        assert lib.pc_keygen(h, seed, 3, 5, ok, bad, ok, None) == ksa.PC_EINVAL
+        assert lib.pc_tensor(h, ok, ok, 1, 3, bad, None) == ksa.PC_EINVAL
+        assert lib.pc_rescale(h, bad, 1, 3, ok, None) == ksa.PC_EINVAL
+        assert lib.pc_hmult(h, ok, ok, 1, bad, seed, 3, ok, None) == ksa.PC_EINVAL
+        assert lib.pc_chacha_expand(h, seed, 0, 0, 3, bad, None) == ksa.PC_EINVAL
+
+
+def test_rescale_and_hmult_launch_limits_checked_on_the_host():
+    """A rescale launch carries the constants of at most 256 polynomials: a params
+    set whose max_batch allows more is refused with PC_EUNSUPPORTED before any work."""
+    lib = ksa._lib()
+    with ksa.Params(12, 3, 3, 1, device=None, max_batch=200) as prm:
+        h, ok, seed = prm.handle, ctypes.c_void_p(0x1000), bytes(32)
+        assert lib.pc_rescale(h, ok, 129, 3, ok, None) == ksa.PC_EUNSUPPORTED
+        assert lib.pc_hmult(h, ok, ok, 129, ok, seed, 3, ok, None) == ksa.PC_EUNSUPPORTED
+        assert lib.pc_rescale(h, ok, 128, 3, ok, None) == ksa.PC_EDEVICE
+        assert lib.pc_hmult(h, ok, ok, 128, ok, seed, 3, ok, None) == ksa.PC_EDEVICE
+
+
+def test_keyset_calls_validate_before_touching_a_device():
+    lib = ksa._lib()
+    with ksa.Params(12, 3, 3, 1, device=None) as prm:
+        h = prm.handle
+        out = ctypes.c_void_p()
+        gal = (ctypes.c_uint32 * 3)(5, 25, 1)
+        assert lib.pc_keyset_create(h, 3, 3, gal, 0, ctypes.byref(out)) == ksa.PC_EDEVICE
+        assert lib.pc_keyset_create(h, 3, 3, gal, 2, ctypes.byref(out)) == ksa.PC_EINVAL
+        assert lib.pc_keyset_create(h, 4, 3, gal, 0, ctypes.byref(out)) == ksa.PC_EINVAL
+        assert lib.pc_keyset_create(h, 3, 0, gal, 0, ctypes.byref(out)) == ksa.PC_EINVAL
+        dup = (ctypes.c_uint32 * 2)(5, 5)
+        assert lib.pc_keyset_create(h, 3, 2, dup, 0, ctypes.byref(out)) == ksa.PC_EINVAL
+        even = (ctypes.c_uint32 * 1)(4)
+        assert lib.pc_keyset_create(h, 3, 1, even, 0, ctypes.byref(out)) == ksa.PC_EINVAL
+        assert lib.pc_keyset_create(None, 3, 1, gal, 0, ctypes.byref(out)) == ksa.PC_EINVAL
+        assert out.value is None
+        assert lib.pc_keyset_set(None, 0, ctypes.c_void_p(0x1000), bytes(32), None) == ksa.PC_EINVAL
+        idx = (ctypes.c_uint32 * 1)(0)
+        assert lib.pc_keyswitch_keyset(h, None, ctypes.c_void_p(0x1000), 1, idx, 1, 3, ctypes.c_void_p(0x1000),
+                                       None, 0, None) == ksa.PC_EINVAL
+
+
+def test_every_declaration_cites_the_pages():
+    """Each entry point's comment in include/pc.h names the page and section that
+    defines the operation (the error-text helper excepted: no page defines it)."""
+    text = open(os.path.join(ROOT, "include", "pc.h")).read()
+    blocks = [(m.end(), m.group(0)) for m in re.finditer(r"^/\*.*?\*/", text, flags=re.M | re.S)]
+    code = re.sub(r"/\*.*?\*/", lambda m: " " * len(m.group(0)), text, flags=re.S)
+    for name in sorted(declared_functions() - {"pc_strerror"}):
+        pos = code.index(name + "(")
+        before = [b for end, b in blocks if end <= pos]
+        assert before, name
+        comment = before[-1]
+        assert "Perseus README" in comment or "arXiv summary page" in comment, name
+        assert re.search(r"'[A-Z][^']*'", comment), f"{name}: no section named"
 
 
 def test_arena_and_transform_workspace_sizes():

@@ -109,3 +109,47 @@ def test_lower_level_with_more_digits():
     (seed 495 of the same draw: level 5, one ciphertext, two keys, stored a)."""
     assert _shape(495)[:3] == (6, 5, 2) and _shape(495)[5] == 5
     test_random_shape_matches_oracle(495)
+
+
+def _shape8(seed):
+    g = np.random.default_rng([8, seed])
+    L = int(g.integers(2, 13))
+    dnum = int(g.integers(-(-L // 8), min(L, 6) + 1))
+    K = int(g.integers(1, 5))
+    level = int(g.integers(1, L + 1))
+    nkeys = int(g.integers(1, 3))
+    n2 = 2 << LOG2N
+    pool = [1, n2 - 1, 5, int(2 * g.integers(1, n2 // 2) + 1) % n2]
+    galois = [pool[int(i)] for i in g.integers(0, len(pool), nkeys)]
+    return L, dnum, K, level, galois, bool(seed % 2)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_batch8_random_shapes_match_oracle(seed):
+    """Batches of exactly 8 ciphertexts (the batch size the inner-product kernels are
+    specialised for) over random chains, levels, digit counts and keys, the a half
+    regenerated (even seeds) or stored (odd seeds); every output word."""
+    L, dnum, K, level, galois, stored = _shape8(seed)
+    what = f"seed {seed}: L={L} dnum={dnum} K={K} level={level} galois={galois} stored={stored}"
+    print(what, flush=True)
+    prm = ksa.Params(LOG2N, L, dnum, K, device=0, max_batch=8, max_hoist=len(galois))
+    oprm = ks.Params(LOG2N, L, dnum, K)
+    assert tuple(prm.primes) == oprm.primes
+    beta = len(oprm.digits(level))
+    keys = [ks.Key(b=ki.uniform_key_b(600 + seed, k, beta, oprm.basis(level), oprm.N),
+                   seed=ki.key_seed(600 + seed, k), level=level, galois=gal) for k, gal in enumerate(galois)]
+    cts = ki.ciphertexts(600 + seed, oprm.q[:level], oprm.N, 8)
+    kb = [ksa.to_device(k.b, 0) for k in keys]
+    if stored:
+        out = ksa.keyswitch_ex(prm, ksa.to_device(cts, 0), kb, galois, level,
+                               evk_a=[ksa.to_device(ks.key_a(oprm, k), 0) for k in keys])
+    else:
+        out = ksa.keyswitch_ex(prm, ksa.to_device(cts, 0), kb, galois, level, seeds=[k.seed for k in keys])
+    torch.cuda.synchronize()
+    got = ksa.to_host(out).astype(np.uint64)
+    for b in range(8):
+        want = ks.keyswitch_hoisted(oprm, cts[b], keys, level)
+        for r in range(len(keys)):
+            bad = np.flatnonzero(got[r, b].reshape(-1) != np.asarray(want[r], dtype=np.uint64).reshape(-1))
+            assert bad.size == 0, f"{what}: key {r} item {b}: {bad.size} words differ, first at {bad[0]}"
+    prm.close()
