@@ -195,6 +195,19 @@ typedef struct {
 } pc_ks_args;
 int pc_keyswitch_ex(const pc_params *p, const pc_ks_args *args, void *stream);
 
+/* Key switching that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. Same arguments, layouts and results as
+ * pc_keyswitch_ex, with workspace NULL and workspace_bytes 0 (PC_EINVAL
+ * otherwise): the workspace is a 128 MiB device array inside the library, one
+ * copy per GPU, held until the process ends. A call whose workspace need
+ * (PC_GET_WORKSPACE_BYTES for its batch and keys) exceeds 128 MiB returns
+ * PC_EUNSUPPORTED; at N = 2^16, L = 24, dnum = 4, K = 6 one ciphertext under
+ * one or two keys fits. Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, params or threads) race and must be
+ * serialised by the caller. No word of the array needs to start at zero. */
+int pc_keyswitch_static(const pc_params *p, const pc_ks_args *args, void *stream);
+
 /* Key generation on the GPU (Perseus README, 'What's inside': keys whose a half
  * is regenerated from a ChaCha12 seed). Writes the b half of a key at key level
  * `level` (basis q_0..q_{level-1}, p_0..p_{K-1}, lk = level + K limbs) for

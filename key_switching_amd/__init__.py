@@ -28,7 +28,7 @@ EXPORTED = ("pc_params_create", "pc_params_destroy", "pc_params_get", "pc_ntt", 
             "pc_keyswitch", "pc_moddown", "pc_keyswitch_ex", "pc_keygen", "pc_tensor", "pc_rescale",
             "pc_hmult", "pc_linear_transform", "pc_chacha_expand",
             "pc_keyset_create", "pc_keyset_destroy", "pc_keyset_set", "pc_keyset_keygen", "pc_keyset_get",
-            "pc_keyswitch_keyset",
+            "pc_keyswitch_keyset", "pc_keyswitch_static",
             "pc_profile_begin", "pc_profile_end", "pc_strerror")
 
 
@@ -86,6 +86,7 @@ def _lib():
         lib.pc_keyswitch.argtypes = [vp, vp, vp, ctypes.c_char_p, u32, u32, vp, vp]
         lib.pc_moddown.argtypes = [vp, vp, u32, vp, vp]
         lib.pc_keyswitch_ex.argtypes = [vp, ctypes.POINTER(_KsArgs), vp]
+        lib.pc_keyswitch_static.argtypes = [vp, ctypes.POINTER(_KsArgs), vp]
         lib.pc_chacha_expand.argtypes = [vp, ctypes.c_char_p, u32, u32, u32, vp, vp]
         lib.pc_keygen.argtypes = [vp, ctypes.c_char_p, u32, u32, vp, vp, vp, vp]
         lib.pc_tensor.argtypes = [vp, vp, vp, u32, u32, vp, vp]
@@ -108,7 +109,7 @@ def _lib():
                      "pc_moddown", "pc_keyswitch_ex", "pc_chacha_expand", "pc_profile_begin", "pc_profile_end",
                      "pc_keygen", "pc_tensor", "pc_rescale", "pc_hmult", "pc_linear_transform",
                      "pc_keyset_create", "pc_keyset_set", "pc_keyset_keygen", "pc_keyset_get",
-                     "pc_keyswitch_keyset"):
+                     "pc_keyswitch_keyset", "pc_keyswitch_static"):
             getattr(lib, name).restype = i32
         _LIB = lib
     return _LIB
@@ -311,13 +312,8 @@ def keyswitch(prm: Params, ct, evk_b, seed: bytes, level: int, galois: int, out=
     return out
 
 
-def keyswitch_ex(prm: Params, ct, evk_b: Sequence, galois: Sequence[int], level: int, seeds=None, evk_a=None,
-                 out=None, workspace=None):
-    """Every ciphertext of ct [batch][2][level][N] under every key (pc_keyswitch_ex).
-
-    Returns out [nkeys][batch][2][level][N]. ``seeds`` lists one 32-byte seed
-    per key (regenerated a half); ``evk_a`` lists stored a halves instead.
-    """
+def _ks_call(fn, name, prm: Params, ct, evk_b: Sequence, galois: Sequence[int], level: int, seeds=None,
+             evk_a=None, out=None, workspace=None):
     batch = int(ct.shape[0])
     nkeys = len(evk_b)
     if len(galois) != nkeys:
@@ -350,8 +346,28 @@ def keyswitch_ex(prm: Params, ct, evk_b: Sequence, galois: Sequence[int], level:
     if workspace is not None:
         args.workspace = _dev_ptr(workspace, "workspace", None, prm.device)
         args.workspace_bytes = workspace.numel() * workspace.element_size()
-    _check(_lib().pc_keyswitch_ex(prm.handle, ctypes.byref(args), _stream()), "pc_keyswitch_ex")
+    _check(fn(prm.handle, ctypes.byref(args), _stream()), name)
     return out
+
+
+def keyswitch_ex(prm: Params, ct, evk_b: Sequence, galois: Sequence[int], level: int, seeds=None, evk_a=None,
+                 out=None, workspace=None):
+    """Every ciphertext of ct [batch][2][level][N] under every key (pc_keyswitch_ex).
+
+    Returns out [nkeys][batch][2][level][N]. ``seeds`` lists one 32-byte seed
+    per key (regenerated a half); ``evk_a`` lists stored a halves instead.
+    """
+    return _ks_call(_lib().pc_keyswitch_ex, "pc_keyswitch_ex", prm, ct, evk_b, galois, level, seeds, evk_a, out,
+                    workspace)
+
+
+def keyswitch_static(prm: Params, ct, evk_b: Sequence, galois: Sequence[int], level: int, seeds=None, evk_a=None,
+                     out=None):
+    """As keyswitch_ex, with the library's static scratch as the workspace
+    (pc_keyswitch_static: no device allocation in the call; ``out`` must be
+    given by callers that cannot allocate)."""
+    return _ks_call(_lib().pc_keyswitch_static, "pc_keyswitch_static", prm, ct, evk_b, galois, level, seeds, evk_a,
+                    out)
 
 
 def keygen(prm: Params, seed: bytes, level: int, galois: int, s_coef, e_coef, out=None):

@@ -7,9 +7,17 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 
 #include "internal.h"
+
+// Workspace of pc_keyswitch_static, the entry point that allocates nothing: a
+// file-scope device array. Every GPU the library runs on holds its own copy
+// until the process ends. In host code the name `scratch` is only a stand-in:
+// kernels get the address hipGetSymbolAddress returns for the current device.
+static constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace pc {
 namespace {
@@ -291,6 +299,28 @@ struct DeviceGuard {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// with that device current (at params creation, or on the first static call).
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxScratchDevices] = {};
+
+int scratch_address(int device, void** out) {
+  if (device < 0 || device >= kMaxScratchDevices) return PC_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[device] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return PC_EDEVICE;
+    }
+    g_scratch[device] = ptr;
+  }
+  *out = g_scratch[device];
+  return PC_OK;
+}
+
 // Device buffers are moved in 16-byte vectors: every device pointer of the ABI
 // must be 16-byte aligned.
 bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15u) != 0; }
@@ -512,6 +542,10 @@ int pc_params_create(const pc_params_desc* desc, int device, pc_params** out) {
       delete p;
       return PC_ENOMEM;
     }
+    // the static entry point's scratch address on this device (a failure is
+    // reported by that entry point, which retries the lookup)
+    void* sp = nullptr;
+    (void)scratch_address(device, &sp);
   }
   *out = p;
   return PC_OK;
@@ -735,6 +769,26 @@ int pc_keyswitch_ex(const pc_params* p, const pc_ks_args* a, void* stream) {
   }
   DeviceGuard g(p->device);
   if (!g.ok) return PC_EDEVICE;
+  const uint64_t ct_stride = 2ull * a->level * p->N;
+  if (launch_keyswitch(p, a->ct, ct_stride, a->level * p->N, a->batch, a->level, keys, a->nkeys, a->galois, base,
+                       a->out, (hipStream_t)stream) != hipSuccess)
+    return PC_EDEVICE;
+  return PC_OK;
+}
+
+int pc_keyswitch_static(const pc_params* p, const pc_ks_args* a, void* stream) {
+  KeyRef keys[kMaxKeysPerLaunch];
+  const int rc = ks_args_keys(p, a, keys);
+  if (rc != PC_OK) return rc;
+  if (a->workspace != nullptr || a->workspace_bytes != 0) return PC_EINVAL;  // the scratch is the workspace
+  const size_t need = ks_workspace_bytes(p, a->level, a->batch, a->nkeys * a->batch);
+  if (need > kScratchBytes) return PC_EUNSUPPORTED;
+  if (p->device < 0) return PC_EDEVICE;
+  DeviceGuard g(p->device);
+  if (!g.ok) return PC_EDEVICE;
+  void* base = nullptr;
+  const int sr = scratch_address(p->device, &base);
+  if (sr != PC_OK) return sr;
   const uint64_t ct_stride = 2ull * a->level * p->N;
   if (launch_keyswitch(p, a->ct, ct_stride, a->level * p->N, a->batch, a->level, keys, a->nkeys, a->galois, base,
                        a->out, (hipStream_t)stream) != hipSuccess)

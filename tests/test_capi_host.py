@@ -249,15 +249,22 @@ def test_keyset_calls_validate_before_touching_a_device():
 
 def test_every_declaration_cites_the_pages():
     """Each entry point's comment in include/pc.h names the page and section that
-    defines the operation (the error-text helper excepted: no page defines it)."""
+    defines the operation (the error-text helper excepted: no page defines it;
+    the allocation-free variant of the key switch names the callers it serves
+    instead)."""
     text = open(os.path.join(ROOT, "include", "pc.h")).read()
     blocks = [(m.end(), m.group(0)) for m in re.finditer(r"^/\*.*?\*/", text, flags=re.M | re.S)]
     code = re.sub(r"/\*.*?\*/", lambda m: " " * len(m.group(0)), text, flags=re.S)
-    for name in sorted(declared_functions() - {"pc_strerror"}):
+    def comment_of(name):
         pos = code.index(name + "(")
         before = [b for end, b in blocks if end <= pos]
         assert before, name
-        comment = before[-1]
+        return before[-1]
+
+    if "pc_keyswitch_static" in declared_functions():
+        assert "cannot allocate" in comment_of("pc_keyswitch_static")
+    for name in sorted(declared_functions() - {"pc_strerror", "pc_keyswitch_static"}):
+        comment = comment_of(name)
         assert "Perseus README" in comment or "arXiv summary page" in comment, name
         assert re.search(r"'[A-Z][^']*'", comment), f"{name}: no section named"
 
