@@ -70,7 +70,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline leg")
+    ap.add_argument("--long-steps", type=int, default=2000,
+                    help="steps of the steady-state leg (batch 8, one stream, ~1 s of GPU time)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="per-leg budget of the oracle baseline (one core, then every core)")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="processes of the all-core oracle leg (0: this process's CPU share, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--buffers-gib", type=float, default=1.1, help="ciphertext buffer rotation size")
     ap.add_argument("--streams", type=int, default=3, choices=(1, 2, 3),
@@ -78,6 +83,8 @@ def parse():
                          "1 for profiler runs, whose per-dispatch times must not overlap")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the timings of the other workloads (hoisted 16, level sweep, N=2^17 chain)")
+    ap.add_argument("--only", choices=("hoist16", "levels16", "n17"), default=None,
+                    help="time only this workload (regenerated and stored key halves), for profiler runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB copy kernel (reference for rocprofv3 byte counters)")
     return ap.parse_args()
@@ -190,19 +197,113 @@ def kernel_roofline(kernel, avg_us, w, batch, beta, alpha):
             "alg_bytes": nbytes, "alg_ops": int(nops), "avg_us": round(avg_us, 3)}
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_share():
+    """Cores this process may use: its affinity set, capped by the thread budget the
+    environment sets (OMP_NUM_THREADS) and by 16."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    try:
+        env = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        env = 0
+    if env > 0:
+        n = min(n, env)
+    return max(1, min(n, 16))
+
+
+_ORACLE = {}
+
+
+def _oracle_setup(w):
+    from oracle import keyswitch as ks
+    oprm = ks.Params(w.log2n, w.L, w.dnum, w.K)
+    beta = len(oprm.digits(w.L))
+    key = ks.Key(b=ki.uniform_key_b(w.index, 0, beta, oprm.basis(w.L), w.N), seed=ki.key_seed(w.index, 0),
+                 level=w.L, galois=1)
+    cts = ki.ciphertexts(w.index, oprm.q, w.N, 4)
+    ks.keyswitch(oprm, cts[0], key, w.L)  # warms the oracle's table caches (not timed)
+    _ORACLE.update(ks=ks, oprm=oprm, key=key, cts=cts, w=w)
+
+
+def _oracle_worker(budget_s):
+    """Whole single-ciphertext key switches of the headline shape until the budget is
+    used; returns (key switches, seconds)."""
+    o = _ORACLE
+    n, t0 = 0, time.perf_counter()
+    while True:
+        o["ks"].keyswitch(o["oprm"], o["cts"][n % 4], o["key"], o["w"].L)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 400:
+            return n, el
+
+
+def cpu_baseline(w, budget_s, workers):
+    """The oracle as it stands (numpy, one thread per process) on a bounded sample of the
+    headline workload: single N=2^16, L=24 key switches with the same key shape, first in
+    this process on one core, then in `workers` processes at once (fork, before the GPU is
+    initialised). Rate = key switches per second of wall time."""
+    import multiprocessing as mp
+    _oracle_setup(w)
+    n1, t1 = _oracle_worker(budget_s)
+    one = n1 / t1
+    allc, nall, wall = None, 0, 0.0
+    if workers > 1:
+        with mp.get_context("fork").Pool(workers) as pool:
+            t0 = time.perf_counter()
+            res = pool.map(_oracle_worker, [budget_s] * workers)
+            wall = time.perf_counter() - t0
+        nall = sum(n for n, _ in res)
+        allc = sum(n / t for n, t in res)
+    cores = workers if allc is not None else 1
+    return {"value": round(allc if allc is not None else one, 4), "unit": "key switches/s", "cores": cores,
+            "kind": "oracle",
+            "sample": (f"{nall} single-ciphertext key switches (N=2^16, L=24, dnum=4, K=6, ChaCha12 a half) by "
+                       f"{workers} oracle processes at once in {wall:.1f} s; one core alone: {n1} in {t1:.1f} s"
+                       if allc is not None else
+                       f"{n1} single-ciphertext key switches (N=2^16, L=24, dnum=4, K=6) in {t1:.1f} s on one core"),
+            "one_core_value": round(one, 4), "cpu_model": _cpu_model(), "host_cpu_count": os.cpu_count()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
               "(key switching shards by ciphertext batch; see the design notes).", file=sys.stderr)
         sys.exit(2)
+    w = ki.WORKLOADS["n16"]
+    # the oracle baseline runs first: its worker processes fork before the GPU is touched
+    cpu = None
+    if not args.no_cpu_baseline and args.only is None:
+        cpu = cpu_baseline(w, args.cpu_seconds, args.cpu_workers or _cpu_share())
+        print(f"[bench] cpu baseline: {cpu['value']} ks/s on {cpu['cores']} cores, {cpu['one_core_value']} on one",
+              file=sys.stderr, flush=True)
 
     import torch
     import key_switching_amd as ksa
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
-    w = ki.WORKLOADS["n16"]
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.bitwise_or(src, 0, out=dst)
+        del src, dst
+        torch.cuda.synchronize()
+    if args.only is not None:
+        res = other_configs(ksa, torch, args, only=args.only)
+        print(json.dumps({"only": args.only, "other_configs": res}), flush=True)
+        return
     K8 = 8
     prm = ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=K8, device=0)
     primes = prm.primes
@@ -225,12 +326,6 @@ def main():
     evk_b = ksa.to_device(ki.uniform_key_b(w.index, 0, beta, basis, w.N), 0)
     evk_a = ksa.to_device(ki.uniform_key_b(w.index, 1, beta, basis, w.N), 0)  # stands in for a stored a half
     seed = ki.key_seed(w.index, 0)
-    if args.calibrate_copy:
-        src = torch.ones(64 << 20, dtype=torch.int32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.bitwise_or(src, 0, out=dst)
-        del src, dst
     torch.cuda.synchronize()
 
     # independent batches in flight on several streams (default priority), each call
@@ -275,7 +370,7 @@ def main():
 
     per_step = {}
 
-    def timed(batch, stored=False, steps=args.steps):
+    def timed(batch, stored=False, steps=args.steps, record=True):
         for i in range(args.warmup):
             step(i, batch, stored)
         torch.cuda.synchronize()
@@ -290,8 +385,9 @@ def main():
         ms = ev[0].elapsed_time(ev[-1])
         d = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
         # the first timed region of each variant (the later one runs under the library's profiling)
-        per_step.setdefault((batch, stored), {"min": round(d[0], 4), "median": round(d[len(d) // 2], 4),
-                                              "max": round(d[-1], 4)})
+        if record:
+            per_step.setdefault((batch, stored), {"min": round(d[0], 4), "median": round(d[len(d) // 2], 4),
+                                                  "max": round(d[-1], 4)})
         return ms / steps, wall
 
     ms8, wall8 = timed(K8)
@@ -309,6 +405,14 @@ def main():
         ms8_2, ms1_2, ms8s_2, ms1s_2 = ms8, ms1, ms8s, ms1s
     head = ms8_2  # the headline: whole-job throughput of batch-8 key switches
 
+    # steady state: many consecutive batch-8 steps on one stream (the clock settles
+    # under sustained load)
+    long_ms = None
+    if args.long_steps > 0:
+        long_ms, _ = timed(K8, steps=args.long_steps, record=False)
+        print(f"[bench] steady state: k=8 {long_ms:.3f} ms/step over {args.long_steps} steps", file=sys.stderr,
+              flush=True)
+
     # per-kernel HIP-event timings over a timed region of the same k=8 steps
     ksa.profile_begin(prm)
     ms8p, _ = timed(K8)
@@ -318,6 +422,9 @@ def main():
     ksa.profile_begin(prm)
     timed(K8, stored=True)
     kstats_stored = ksa.profile_end(prm)
+    ksa.profile_begin(prm)
+    ms1p, _ = timed(1)
+    kstats_k1 = ksa.profile_end(prm)
 
     def timed_calls(fn, steps):
         for i in range(3):
@@ -410,12 +517,17 @@ def main():
         torch.cuda.synchronize()
         copy_gbs = round(2.0 * csrc.numel() * 4 / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9, 1)
         del csrc, cdst
+    prm.close()
+    del cts, outs, workspaces
+    torch.cuda.empty_cache()
     others = None if args.no_configs else leg(lambda: other_configs(ksa, torch, args))
     kernels_stored = {k: round(1000.0 * t / n, 3) for k, (n, t) in sorted(kstats_stored.items(), key=lambda kv: -kv[1][1])}
+    kernels_k1 = {k: round(1000.0 * t / n, 3) for k, (n, t) in sorted(kstats_k1.items(), key=lambda kv: -kv[1][1])}
     dom = next(iter(kernels))
     roofs = {k: kernel_roofline(k, v["avg_us"], w, K8, beta, alpha) for k, v in kernels.items()}
     from key_switching_amd import profiling
     traffic_md = os.path.join(ROOT, "profiles", "keyswitch_n16_k8_traffic.md")
+    valu_md = os.path.join(ROOT, "profiles", "keyswitch_n16_k8_valu.md")
     rd = roofs[dom]
     if rd["alu_frac"] >= rd["hbm_frac"]:
         roofline = {"bound": "alu", "achieved": rd["alu_tops"], "peak": round(INT32_PEAK_TOPS, 2), "unit": "TOP/s",
@@ -424,16 +536,21 @@ def main():
         roofline = {"bound": "hbm", "achieved": rd["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": rd["hbm_frac"]}
     traffic = profiling.read_traffic(traffic_md, dom)
-    roofline.update({"traffic": None if traffic is None else round(traffic), "kernel": dom,
-                     "alg_bytes_per_launch": rd["alg_bytes"], "alg_ops_per_launch": rd["alg_ops"],
-                     "hbm_frac": rd["hbm_frac"], "alu_frac": rd["alu_frac"], "avg_us": rd["avg_us"]})
     step_s = head * 1e-3
     path_bytes = sum(r["alg_bytes"] for r in roofs.values())
     path_ops = sum(r["alg_ops"] for r in roofs.values())
     path = {"alg_bytes_per_step": path_bytes, "alg_ops_per_step": path_ops,
             "hbm_frac": round(path_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
             "alu_frac": round(path_ops / step_s / 1e12 / INT32_PEAK_TOPS, 4),
-            "alu_frac_one_stream": round(path_ops / (ms8 * 1e-3) / 1e12 / INT32_PEAK_TOPS, 4)}
+            "alu_frac_one_stream": round(path_ops / (ms8 * 1e-3) / 1e12 / INT32_PEAK_TOPS, 4),
+            "alu_frac_steady_state": (round(path_ops / (long_ms * 1e-3) / 1e12 / INT32_PEAK_TOPS, 4)
+                                      if long_ms else None),
+            "k1_alu_frac_one_stream": path_fractions([(w.N, w.L, w.K, alpha, beta, 1, 1, True)], ms1)["alu_frac"]}
+    roofline.update({"traffic": None if traffic is None else round(traffic), "kernel": dom,
+                     "alg_bytes_per_launch": rd["alg_bytes"], "alg_ops_per_launch": rd["alg_ops"],
+                     "hbm_frac": rd["hbm_frac"], "alu_frac": rd["alu_frac"], "avg_us": rd["avg_us"],
+                     "valu_issued_over_alg": profiling.read_valu_ratio(valu_md, dom),
+                     "path_alu_frac": path["alu_frac"]})
 
     result = {
         "metric": METRIC,
@@ -451,17 +568,25 @@ def main():
         "config": {"workload": "n16: N=2^16, L=24 q-primes (31-bit), dnum=4 (alpha=6), K=6, relinearisation key, "
                                "a half regenerated in-kernel (ChaCha12), batch k=8",
                    "N": w.N, "L": w.L, "dnum": w.dnum, "K": w.K, "batch": K8, "buffers": nbuf},
+        "k1_ks_per_s": round(1000.0 / ms1, 1),
+        "k1_note": "batch 1, one call at a time on one stream (each call's kernels wait for the previous call)",
         "variants": {
             "streams": args.streams,
             "k8_chacha": {"ks_per_s": round(K8 * 1000.0 / ms8_2, 1), "ms_per_call": round(ms8_2, 4)},
-            "k1_chacha": {"ks_per_s": round(1000.0 / ms1_2, 1), "ms_per_call": round(ms1_2, 4)},
             "k8_stored": {"ks_per_s": round(K8 * 1000.0 / ms8s_2, 1), "ms_per_call": round(ms8s_2, 4)},
-            "k1_stored": {"ks_per_s": round(1000.0 / ms1s_2, 1), "ms_per_call": round(ms1s_2, 4)},
+            "k1_chacha_independent_calls_on_streams": {
+                "ks_per_s": round(1000.0 / ms1_2, 1), "ms_per_call": round(ms1_2, 4),
+                "note": f"independent batch-1 calls dealt to {args.streams} streams (up to {args.streams} in flight)"},
+            "k1_stored_independent_calls_on_streams": {"ks_per_s": round(1000.0 / ms1s_2, 1),
+                                                       "ms_per_call": round(ms1s_2, 4)},
             "k8_chacha_one_stream": {"ks_per_s": round(K8 * 1000.0 / ms8, 1), "ms_per_call": round(ms8, 4)},
             "k1_chacha_one_stream": {"ks_per_s": round(1000.0 / ms1, 1), "ms_per_call": round(ms1, 4)},
             "k8_stored_one_stream": {"ks_per_s": round(K8 * 1000.0 / ms8s, 1), "ms_per_call": round(ms8s, 4)},
             "k1_stored_one_stream": {"ks_per_s": round(1000.0 / ms1s, 1), "ms_per_call": round(ms1s, 4)},
+            "k8_chacha_steady_state": ({"ks_per_s": round(K8 * 1000.0 / long_ms, 1), "ms_per_call": round(long_ms, 4),
+                                        "steps": args.long_steps} if long_ms else None),
             "k8_chacha_profiled": {"ms_per_call": round(ms8p, 4)},
+            "k1_chacha_profiled": {"ms_per_call": round(ms1p, 4)},
             "keygen_relin_key": keygen_res,
             "hmult_k8": hmult_res,
             "bsgs_4x4": bsgs_res,
@@ -475,13 +600,12 @@ def main():
                     for k, v in kernels.items()},
         "path_roofline": path,
         "kernels_k8_stored_avg_us": kernels_stored,
+        "kernels_k1_avg_us": kernels_k1,
         "roofline": roofline,
         "wall_s_k8": round(wall8, 3),
     }
-
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    prm.close()
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
@@ -498,91 +622,104 @@ def _time_calls(torch, fn, steps, warmup=3):
     return e0.elapsed_time(e1) / steps
 
 
-def other_configs(ksa, torch, args, steps=10):
-    """Key switches per second on the other workloads (uniform b halves, ChaCha12 a halves).
+def other_configs(ksa, torch, args, steps=10, only=None):
+    """Key switches per second on the other workloads (uniform b halves standing in for
+    real ones; the a halves regenerated in-kernel, or read from a stored copy).
 
-    hoist16: one N=2^16 ciphertext, ModUp once, 16 rotation keys; levels16: 8
-    ciphertexts switched independently by X^5 and X^-1 keys at each level;
-    n17: 8 N=2^17, L=40 ciphertexts, relinearised then rotated by X^5.
+    hoist16: one N=2^16 ciphertext, ModUp once, 16 rotation keys (also drawn from a
+    packed and a full key bundle); levels16: 8 ciphertexts switched independently by the
+    X^5 and X^-1 keys at each level; n17: 8 N=2^17, L=40 ciphertexts, relinearised then
+    rotated by X^5. ``only`` limits the run to one of them (profiler runs).
     """
     out = {}
-    # hoisted rotations
-    w = ki.WORKLOADS["hoist16"]
-    with ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=1, max_hoist=len(w.galois), device=0) as prm:
-        basis, beta = prm.basis(w.L), prm.beta(w.L)
-        keys = [ksa.to_device(ki.uniform_key_b(w.index, k, beta, basis, w.N), 0) for k in range(len(w.galois))]
-        seeds = [ki.key_seed(w.index, k) for k in range(len(w.galois))]
-        ct = ksa.to_device(ki.ciphertexts(w.index, prm.primes[: w.L], w.N, 1), 0)
-        res = torch.empty((len(w.galois), 1, 2, w.L, w.N), dtype=torch.int32, device="cuda:0")
-        ms = _time_calls(torch, lambda i: ksa.keyswitch_ex(prm, ct, keys, w.galois, w.L, seeds=seeds, out=res), steps)
-        out["hoist16"] = {"ks_per_s": round(len(w.galois) * 1000.0 / ms, 1), "ms_per_call": round(ms, 4),
-                          "key_switches_per_call": len(w.galois),
-                          "path": path_fractions([(w.N, w.L, w.K, prm.alpha(w.L), beta, 1, len(w.galois), True)], ms)}
-        del keys, ct, res
-    # level sweep
-    w = ki.WORKLOADS["levels16"]
-    with ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=8, device=0) as prm:
-        base = ki.ciphertexts(w.index, prm.primes[: w.L], w.N, 8)
-        per_level, per_level_path = {}, {}
-        for level in w.levels:
-            basis, beta = prm.basis(level), prm.beta(level)
-            keys = [ksa.to_device(ki.uniform_key_b(w.index, 10 * level + k, beta, basis, w.N), 0) for k in range(2)]
-            seeds = [ki.key_seed(w.index, 10 * level + k) for k in range(2)]
-            ct = ksa.to_device(np.ascontiguousarray(base[:, :, :level]), 0)
-            res = torch.empty((1, 8, 2, level, w.N), dtype=torch.int32, device="cuda:0")
+    if only in (None, "hoist16"):
+        w = ki.WORKLOADS["hoist16"]
+        R = len(w.galois)
+        with ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=1, max_hoist=R, device=0) as prm:
+            basis, beta = prm.basis(w.L), prm.beta(w.L)
+            keys = [ksa.to_device(ki.uniform_key_b(w.index, k, beta, basis, w.N), 0) for k in range(R)]
+            akeys = [ksa.to_device(ki.uniform_key_b(w.index, 100 + k, beta, basis, w.N), 0) for k in range(R)]
+            seeds = [ki.key_seed(w.index, k) for k in range(R)]
+            ct = ksa.to_device(ki.ciphertexts(w.index, prm.primes[: w.L], w.N, 1), 0)
+            res = torch.empty((R, 1, 2, w.L, w.N), dtype=torch.int32, device="cuda:0")
+            one = (w.N, w.L, w.K, prm.alpha(w.L), beta, 1, R, True)
+            ms = _time_calls(torch, lambda i: ksa.keyswitch_ex(prm, ct, keys, w.galois, w.L, seeds=seeds, out=res),
+                             steps)
+            mss = _time_calls(torch, lambda i: ksa.keyswitch_ex(prm, ct, keys, w.galois, w.L, evk_a=akeys, out=res),
+                              steps)
+            d = {"ks_per_s": round(R * 1000.0 / ms, 1), "ms_per_call": round(ms, 4), "key_switches_per_call": R,
+                 "path": path_fractions([one], ms),
+                 "stored": {"ks_per_s": round(R * 1000.0 / mss, 1), "ms_per_call": round(mss, 4),
+                            "path": path_fractions([one], mss, stored=True)}}
+            # the same keys from key bundles: packed (b halves + seeds) and full (a halves stored too)
+            for name, full in (("bundle_packed", False), ("bundle_full", True)):
+                with ksa.KeySet(prm, w.L, w.galois, full=full) as bundle:
+                    for k in range(R):
+                        bundle.set(k, keys[k], seeds[k])
+                    idx = list(range(R))
+                    msb = _time_calls(torch, lambda i: ksa.keyswitch_keyset(prm, bundle, ct, idx, w.L, out=res),
+                                      steps)
+                    d[name] = {"ks_per_s": round(R * 1000.0 / msb, 1), "ms_per_call": round(msb, 4),
+                               "device_bytes": bundle.device_bytes(), "key_half_bytes": bundle.key_bytes()}
+            out["hoist16"] = d
+            del keys, akeys, ct, res
+    if only in (None, "levels16"):
+        w = ki.WORKLOADS["levels16"]
+        with ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=8, device=0) as prm:
+            base = ki.ciphertexts(w.index, prm.primes[: w.L], w.N, 8)
+            per_level, per_level_path = {}, {}
+            for level in w.levels:
+                basis, beta = prm.basis(level), prm.beta(level)
+                keys = [ksa.to_device(ki.uniform_key_b(w.index, 10 * level + k, beta, basis, w.N), 0)
+                        for k in range(2)]
+                seeds = [ki.key_seed(w.index, 10 * level + k) for k in range(2)]
+                ct = ksa.to_device(np.ascontiguousarray(base[:, :, :level]), 0)
+                res = torch.empty((1, 8, 2, level, w.N), dtype=torch.int32, device="cuda:0")
 
-            def one_level(i):
-                for k in range(2):  # each key on its own: 16 single key switches
-                    ksa.keyswitch_ex(prm, ct, [keys[k]], [w.galois[k]], level, seeds=[seeds[k]], out=res)
+                def one_level(i):
+                    for k in range(2):  # each key on its own: 16 single key switches
+                        ksa.keyswitch_ex(prm, ct, [keys[k]], [w.galois[k]], level, seeds=[seeds[k]], out=res)
 
-            ms = _time_calls(torch, one_level, steps)
-            per_level[str(level)] = round(16 * 1000.0 / ms, 1)
-            one = (w.N, level, w.K, prm.alpha(level), beta, 8, 1, True)
-            per_level_path[str(level)] = path_fractions([one, one], ms)
-            del keys, ct, res
-        out["levels16"] = {"ks_per_s_by_level": per_level, "path_by_level": per_level_path}
-    # N=2^17 chain
-    w = ki.WORKLOADS["n17"]
-    with ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=8, device=0) as prm:
-        basis, beta = prm.basis(w.L), prm.beta(w.L)
-        keys = [ksa.to_device(ki.uniform_key_b(w.index, k, beta, basis, w.N), 0) for k in range(2)]
-        seeds = [ki.key_seed(w.index, k) for k in range(2)]
-        ct = ksa.to_device(ki.ciphertexts(w.index, prm.primes[: w.L], w.N, 8), 0)
-        mid = torch.empty((1, 8, 2, w.L, w.N), dtype=torch.int32, device="cuda:0")
-        res = torch.empty_like(mid)
+                ms = _time_calls(torch, one_level, steps)
+                per_level[str(level)] = round(16 * 1000.0 / ms, 1)
+                one = (w.N, level, w.K, prm.alpha(level), beta, 8, 1, True)
+                per_level_path[str(level)] = path_fractions([one, one], ms)
+                del keys, ct, res
+            out["levels16"] = {"ks_per_s_by_level": per_level, "path_by_level": per_level_path}
+    if only in (None, "n17"):
+        w = ki.WORKLOADS["n17"]
+        with ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=8, device=0) as prm:
+            basis, beta = prm.basis(w.L), prm.beta(w.L)
+            keys = [ksa.to_device(ki.uniform_key_b(w.index, k, beta, basis, w.N), 0) for k in range(2)]
+            akeys = [ksa.to_device(ki.uniform_key_b(w.index, 100 + k, beta, basis, w.N), 0) for k in range(2)]
+            seeds = [ki.key_seed(w.index, k) for k in range(2)]
+            ct = ksa.to_device(ki.ciphertexts(w.index, prm.primes[: w.L], w.N, 8), 0)
+            mid = torch.empty((1, 8, 2, w.L, w.N), dtype=torch.int32, device="cuda:0")
+            res = torch.empty_like(mid)
 
-        def chain(i):
-            ksa.keyswitch_ex(prm, ct, [keys[0]], [w.galois[0]], w.L, seeds=[seeds[0]], out=mid)
-            ksa.keyswitch_ex(prm, mid[0], [keys[1]], [w.galois[1]], w.L, seeds=[seeds[1]], out=res)
+            def chain(i, stored=False):
+                kw0 = {"evk_a": [akeys[0]]} if stored else {"seeds": [seeds[0]]}
+                kw1 = {"evk_a": [akeys[1]]} if stored else {"seeds": [seeds[1]]}
+                ksa.keyswitch_ex(prm, ct, [keys[0]], [w.galois[0]], w.L, out=mid, **kw0)
+                ksa.keyswitch_ex(prm, mid[0], [keys[1]], [w.galois[1]], w.L, out=res, **kw1)
 
-        ms = _time_calls(torch, chain, steps)
-        one = (w.N, w.L, w.K, prm.alpha(w.L), beta, 8, 1, True)
-        out["n17"] = {"ks_per_s": round(16 * 1000.0 / ms, 1), "ms_per_call": round(ms, 4),
-                      "key_switches_per_call": 16, "path": path_fractions([one, one], ms)}
-        del keys, ct, mid, res
+            ms = _time_calls(torch, chain, steps)
+            mss = _time_calls(torch, lambda i: chain(i, stored=True), steps)
+            one = (w.N, w.L, w.K, prm.alpha(w.L), beta, 8, 1, True)
+            traffic = None
+            try:
+                from key_switching_amd import profiling
+                traffic = profiling.read_ip_traffic(os.path.join(ROOT, "profiles", "keyswitch_n17_chain_traffic.md"))
+            except Exception:  # noqa: BLE001 - the summary is optional context
+                traffic = None
+            out["n17"] = {"ks_per_s": round(16 * 1000.0 / ms, 1), "ms_per_call": round(ms, 4),
+                          "key_switches_per_call": 16, "path": path_fractions([one, one], ms),
+                          "stored": {"ks_per_s": round(16 * 1000.0 / mss, 1), "ms_per_call": round(mss, 4),
+                                     "path": path_fractions([one, one], mss, stored=True)},
+                          "key_half_bytes": beta * (w.L + w.K) * w.N * 4,
+                          "inner_product_traffic_bytes": traffic}
+            del keys, akeys, ct, mid, res
     return out
-
-
-def cpu_baseline(w, budget_s):
-    """The oracle as it stands, one thread, on a bounded sample: whole key switches of single
-    N=2^16, L=24 ciphertexts (k=1) with the same key shape, repeated until the budget is used."""
-    from oracle import keyswitch as ks
-    oprm = ks.Params(w.log2n, w.L, w.dnum, w.K)
-    beta = len(oprm.digits(w.L))
-    key = ks.Key(b=ki.uniform_key_b(w.index, 0, beta, oprm.basis(w.L), w.N), seed=ki.key_seed(w.index, 0),
-                 level=w.L, galois=1)
-    cts = ki.ciphertexts(w.index, oprm.q, w.N, 4)
-    ks.keyswitch(oprm, cts[0], key, w.L)  # warm the oracle's table caches
-    n, t0 = 0, time.perf_counter()
-    while True:
-        ks.keyswitch(oprm, cts[n % 4], key, w.L)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 50:
-            break
-    return {"value": round(n / el, 4), "unit": "key switches/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} single-ciphertext key switches (N=2^16, L=24, dnum=4, K=6, ChaCha12 a half) "
-                      f"in {el:.1f} s on one host core (numpy, single-threaded)"}
 
 
 if __name__ == "__main__":

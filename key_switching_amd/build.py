@@ -11,6 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["csrc/kernels.hip", "csrc/capi.hip"]
 LIB = os.path.join(HERE, "libpc.so")
+PROBE_SRC = os.path.join(HERE, "rate_probe.hip")
+PROBE = os.path.join(HERE, "rate_probe")  # instruction-rate probe (measurement tool, not part of the library)
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -45,6 +47,19 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_probe(verbose: bool = False) -> str:
+    """Compile the instruction-rate probe (key_switching_amd/rate_probe)."""
+    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    cmd = [hipcc(), *flags, PROBE_SRC, "-o", PROBE]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}")
+    return PROBE
+
+
 if __name__ == "__main__":
     build(verbose=True)
-    print("built", LIB, file=sys.stderr)
+    build_probe(verbose=True)
+    print("built", LIB, "and", PROBE, file=sys.stderr)

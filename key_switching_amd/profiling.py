@@ -65,6 +65,19 @@ FAMILIES = {
 }
 
 
+# the N=2^17, L=40 chain (bench.py --only n17): batch-8 launches, a half
+# regenerated or stored
+FAMILIES_N17 = {
+    "modup_bconv": "k_modup_bconv<17, 8, 3>",
+    "modup_fwd_blk": "k_modup_fwd_blk<17>",
+    "inner_product_chacha": "k_ip_regen<5, 12, 8, false>",
+    "inner_product_stored": "k_inner_product<5, 12, true, 8, false>",
+    "moddown_bconv": "k_md_bconv<17, 8, 3>",
+    "moddown_fwd_blk": "k_md_fwd_blk<17, false, false>",
+}
+FAMILY_SETS = {"n16": FAMILIES, "n17": FAMILIES_N17}
+
+
 def device_source_hash() -> str:
     h = hashlib.sha256()
     for rel in DEVICE_SOURCES:
@@ -147,7 +160,7 @@ def cmd_traffic(a) -> str:
            "Per kernel family, batch-8 launch (largest grid of that kernel), medians over its dispatches:", "",
            "| family | dispatch | grid | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetch bytes | write bytes | traffic bytes |",
            "|---|---|---|---|---|---|---|---|---|"]
-    for fam, prefix in FAMILIES.items():
+    for fam, prefix in FAMILY_SETS[a.families].items():
         fk = {(d, g): v for (d, k, g), v in f.items() if k == prefix}
         wk = {(d, g): v for (d, k, g), v in w.items() if k == prefix}
         if not fk or not wk:
@@ -180,6 +193,132 @@ def read_traffic(path: str, family: str):
     return None
 
 
+def read_valu_ratio(path: str, family: str):
+    """Issued VALU lane-operations over the model's algorithmic operations for one
+    family, from a VALU summary (None if absent or stale)."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read().splitlines()
+    if not any(line.strip() == f"device_sources_hash: {device_source_hash()}" for line in text):
+        return None
+    for line in text:
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 5 and cells[0] == family:
+            try:
+                return float(cells[4])
+            except ValueError:
+                return None
+    return None
+
+
+def read_ip_traffic(path: str):
+    """Inner-product traffic per batch-8 launch of the N=2^17 chain, regenerated and
+    stored a halves, from its traffic summary (None if absent or stale)."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read().splitlines()
+    if not any(line.strip() == f"device_sources_hash: {device_source_hash()}" for line in text):
+        return None
+    out = {}
+    for line in text:
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 9 and cells[0] in ("inner_product_chacha", "inner_product_stored"):
+            out[cells[0].split("_")[-1]] = {"fetch": float(cells[6]), "write": float(cells[7]),
+                                            "total": float(cells[8])}
+    return out or None
+
+
+# SQ counters of the VALU summary (one rocprofv3 pass: at most 8 SQ and 2 GRBM counters)
+VALU_COUNTERS = ("SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES",
+                 "SQ_INSTS_LDS", "SQ_WAIT_INST_ANY", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE")
+
+
+def _per_dispatch(path: str):
+    rows, meta = {}, {}
+    for r in csv.DictReader(open(path)):
+        d = r["Dispatch_Id"]
+        rows.setdefault(d, {})[r["Counter_Name"]] = rows.get(d, {}).get(r["Counter_Name"], 0.0) + float(
+            r["Counter_Value"])
+        meta[d] = (_short(r["Kernel_Name"]), _grid(r), int(r.get("VGPR_Count", 0) or 0),
+                   (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3, r["Kernel_Name"])
+    return rows, meta
+
+
+def cmd_valu(a) -> str:
+    """Issued VALU instructions per kernel family against the model's algorithmic
+    int32 operations (bench.alg_ops at N=2^16, L=24, dnum=4, K=6, batch 8)."""
+    sys.path.insert(0, os.path.dirname(HERE))
+    import bench
+    rows, meta = _per_dispatch(a.pmc)
+    clock = bench.CLOCK_GHZ * 1e3  # MHz -> cycles per us
+    simds = bench.CUS * 4
+    out = [f"# VALU instruction counts: {a.title}", "", "Commands:", "", "```", a.cmd, "```", "",
+           f"device_sources_hash: {device_source_hash()}", "",
+           "Per kernel family, batch-8 launch (largest grid of that kernel), medians over its dispatches.",
+           "`issued/alg` = SQ_INSTS_VALU x 64 lanes / the model's algorithmic int32 operations of the launch; "
+           "`issue us` = SQ_INSTS_VALU x 4 cycles / 1024 SIMDs / 2.4 GHz, the launch's time if the VALU issued "
+           "every cycle at the peak clock; `busy` = issue us / the launch's duration in this counter run "
+           "(serialised dispatches); `wait` = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; `bank` = "
+           "SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS.", "",
+           "| family | dispatch | grid | VALU wave-instr (M) | issued/alg | issue us | duration us | busy | "
+           "LDS instr (M) | bank | wait | VGPRs |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    N, L, K, alpha, beta, batch = 1 << 16, 24, 6, 6, 4, 8
+    for fam, prefix in FAMILIES.items():
+        if fam not in bench.KERNELS:
+            continue
+        ds = [d for d, m in meta.items() if m[0] == prefix]
+        if not ds:
+            continue
+        g = max(meta[d][1] for d in ds)
+        ds = [d for d in ds if meta[d][1] == g]
+
+        def med(c):
+            return statistics.median(rows[d].get(c, 0.0) for d in ds)
+
+        valu = med("SQ_INSTS_VALU")
+        alg = bench.alg_ops(fam, N, L, K, alpha, beta, batch)
+        issue_us = valu * 4 / simds / clock
+        dur = statistics.median(meta[d][3] for d in ds)
+        lds = med("SQ_INSTS_LDS")
+        out.append(f"| {fam} | `{prefix}` | {g} | {valu / 1e6:.2f} | {valu * 64 / alg:.3f} | {issue_us:.1f} | "
+                   f"{dur:.1f} | {issue_us / dur:.2f} | {lds / 1e6:.2f} | "
+                   f"{med('SQ_LDS_BANK_CONFLICT') / max(lds, 1):.3f} | "
+                   f"{med('SQ_WAIT_INST_ANY') / max(med('SQ_WAVE_CYCLES'), 1):.2f} | {meta[ds[0]][2]} |")
+    return "\n".join(out) + "\n"
+
+
+PROBE_NAMES = {"0": "v_add_u32", "1": "v_mul_lo_u32", "2": "v_mul_hi_u32", "3": "v_mad_u64_u32", "4": "v_add3_u32",
+               "5": "v_min_u32", "6": "v_xor_b32", "7": "v_alignbit_b32", "8": "butterfly (11 instructions)"}
+
+
+def cmd_rates(a) -> str:
+    """Issue rates of the instruction-rate probe (key_switching_amd/rate_probe) from a
+    `rocprofv3 --pmc SQ_INSTS_VALU GRBM_GUI_ACTIVE` run. GRBM_GUI_ACTIVE is summed over
+    the 8 XCDs, so GUI_ACTIVE / 8 / duration is the engine clock during the dispatch."""
+    rows, meta = _per_dispatch(a.pmc)
+    out = [f"# VALU issue rates of 32-bit integer instructions: {a.title}", "", "Commands:", "", "```", a.cmd,
+           "```", "",
+           "Each probe kernel runs 8 independent chains of one operation per thread (2048 workgroups of 256 "
+           "threads, 4096 iterations); its loop body is that operation alone (checked in the gfx950 assembly "
+           "of the build). `rate` = SQ_INSTS_VALU / (256 CUs x clock x duration), in wave-instructions per CU "
+           "per clock; 1.0 is the four SIMD16s each issuing one wave64 instruction every 4 clocks. "
+           "`clock` = GRBM_GUI_ACTIVE / 8 XCDs / duration.", "",
+           "| instruction | dispatches | VALU wave-instr (M) | duration us | clock GHz | rate at 2.4 GHz | "
+           "rate at the measured clock |", "|---|---|---|---|---|---|---|"]
+    for op, name in PROBE_NAMES.items():
+        ds = [d for d, m in meta.items() if f"k_probe<{op}>(" in m[4]]
+        if not ds:
+            continue
+        valu = statistics.median(rows[d]["SQ_INSTS_VALU"] for d in ds)
+        dur = statistics.median(meta[d][3] for d in ds)
+        gui = statistics.median(rows[d]["GRBM_GUI_ACTIVE"] for d in ds)
+        clk = gui / 8 / (dur * 1e3)
+        out.append(f"| {name} | {len(ds)} | {valu / 1e6:.1f} | {dur:.1f} | {clk:.3f} | "
+                   f"{valu / (256 * 2.4e3 * dur):.3f} | {valu / (256 * clk * 1e3 * dur):.3f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -195,8 +334,18 @@ def main(argv=None):
     t.add_argument("--write", required=True)
     t.add_argument("--title", default="")
     t.add_argument("--cmd", default="")
+    t.add_argument("--families", choices=sorted(FAMILY_SETS), default="n16")
+    v = sub.add_parser("valu")
+    v.add_argument("--pmc", required=True)
+    v.add_argument("--title", default="")
+    v.add_argument("--cmd", default="")
+    q = sub.add_parser("rates")
+    q.add_argument("--pmc", required=True)
+    q.add_argument("--title", default="")
+    q.add_argument("--cmd", default="")
     a = ap.parse_args(argv)
-    sys.stdout.write(cmd_stats(a) if a.cmd_name == "stats" else cmd_traffic(a))
+    fn = {"stats": cmd_stats, "traffic": cmd_traffic, "valu": cmd_valu, "rates": cmd_rates}[a.cmd_name]
+    sys.stdout.write(fn(a))
 
 
 if __name__ == "__main__":
