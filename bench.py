@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--spinup-ms", type=float, default=300.0,
+                    help="untimed batch-8 key switches (about this much GPU time) before the first timed leg and "
+                         "before the multi-stream legs, so that every leg runs at the clock of a loaded GPU")
     ap.add_argument("--long-steps", type=int, default=2000,
                     help="steps of the steady-state leg (batch 8, one stream, ~1 s of GPU time)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -390,6 +393,14 @@ def main():
                                                   "max": round(d[-1], 4)})
         return ms / steps, wall
 
+    def spin_up():
+        """Untimed batch-8 steps: the engine clock ramps up over the first milliseconds
+        of sustained load, and every timed leg should see the loaded GPU."""
+        for i in range(int(args.spinup_ms / 0.5)):
+            step(i, K8)
+        torch.cuda.synchronize()
+
+    spin_up()
     ms8, wall8 = timed(K8)
     ms1, _ = timed(1)
     ms8s, _ = timed(K8, stored=True)
@@ -397,6 +408,7 @@ def main():
     print(f"[bench] one stream: k=8 {ms8:.3f} ms/step, k=1 {ms1:.3f}, stored k=8 {ms8s:.3f}, stored k=1 {ms1s:.3f}",
           file=sys.stderr, flush=True)
     if S > 1:
+        spin_up()
         ms8_2, ms1_2 = timed_streams(K8), timed_streams(1)
         ms8s_2, ms1s_2 = timed_streams(K8, stored=True), timed_streams(1, stored=True)
         print(f"[bench] {S} streams: k=8 {ms8_2:.3f} ms/step, k=1 {ms1_2:.3f}, stored k=8 {ms8s_2:.3f}, "

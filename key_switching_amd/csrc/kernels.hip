@@ -106,11 +106,17 @@ struct ScaledLimb {
 
 // ModDown combine: out = (acc - v) P^-1 (+ c0 at the automorphism's source
 // index). acc and c0 at the E output positions of this thread are fetched
-// before the transform (fwd_blk_pass_fetch). c0 is in natural order, or with
-// SEG in the segment layout of a 2^LRB x 2^LRC limb: a thread's E positions
-// are rows of one column, so its gathers stay in one segment. acc (written by
-// the inner product, read once here) and out take the streaming hint.
-template <int E, int LRC, int LRB, bool SEG>
+// around the transform (fwd_blk_pass_fetch). C0 selects how c0 is read:
+// kNoC0 (nothing to add), kC0Same (Galois element 1: c0 at the output
+// position itself), kC0Gather (natural order, source index i g + h) and
+// kC0Seg (the segment layout of a 2^LRB x 2^LRC limb: a thread's E positions
+// are rows of one column, so its gathers stay in one segment). The first
+// polynomial of each item adds c0, the second does not (c0 is nullptr there).
+// acc (written by the inner product, read once here) and out take the
+// streaming hint.
+constexpr int kNoC0 = 0, kC0Same = 1, kC0Gather = 2, kC0Seg = 3;
+
+template <int E, int LRC, int LRB, int C0>
 struct CombineLimb {
   uint32_t r, rinv, pinv, pinvp;
   const uint32_t* __restrict__ tw;
@@ -123,12 +129,20 @@ struct CombineLimb {
   __device__ __forceinline__ uint32_t load(int pos) const { return at32(src, pos); }
   __device__ __forceinline__ void fetch(int m, int pos) {
     av[m] = load_stream(acc, pos);
-    const uint32_t si = SEG ? seg_src_index((uint32_t)pos, g, h, LRC, LRB) : (((uint32_t)pos * g + h) & mask);
-    cv[m] = c0 ? at32(c0, si) : 0u;
+    if constexpr (C0 != kNoC0) {
+      if (c0 != nullptr) {
+        uint32_t si = (uint32_t)pos;
+        if constexpr (C0 == kC0Gather) si = ((uint32_t)pos * g + h) & mask;
+        if constexpr (C0 == kC0Seg) si = seg_src_index((uint32_t)pos, g, h, LRC, LRB);
+        cv[m] = at32(c0, si);
+      }
+    }
   }
   __device__ __forceinline__ void finish(int m, int pos, uint32_t v) const {
     uint32_t o = mul_shoup(sub_mod(av[m], v, r), pinv, pinvp, r);
-    if (c0) o = add_mod(o, cv[m], r);
+    if constexpr (C0 != kNoC0) {
+      if (c0 != nullptr) o = add_mod(o, cv[m], r);
+    }
     store_stream(dst, pos, o);
   }
 };
@@ -260,6 +274,10 @@ __device__ __forceinline__ uint64_t fold_hi(uint64_t x, uint32_t r) {
 // c[k] < r, with one REDC: four products sum below 2r 2^32, and after each
 // fold (high word below r) two more do, so the sum is folded after the fourth
 // product, after every further pair and once more after an odd tail.
+// The running sum is pinned to one 64-bit register pair after every step, so
+// that each product is one multiply-add into it: left free, the compiler
+// splits the sum into separate chains and high-word sums, which costs moves
+// and 64-bit adds (18 instructions instead of 14 at CNT = 6).
 template <int CNT>
 __device__ __forceinline__ uint32_t dot_redc(const uint32_t (&v)[CNT], const uint32_t (&c)[CNT], uint32_t r,
                                              uint32_t rinv) {
@@ -267,10 +285,17 @@ __device__ __forceinline__ uint32_t dot_redc(const uint32_t (&v)[CNT], const uin
 #pragma unroll
   for (int k = 0; k < CNT; ++k) {
     acc += mul_wide(v[k], c[k]);
-    if (k == 3 || (k > 3 && (k & 1))) acc = fold_hi(acc, r);
+    asm volatile("" : "+v"(acc));
+    if (k == 3 || (k > 3 && (k & 1))) {
+      acc = fold_hi(acc, r);
+      asm volatile("" : "+v"(acc));
+    }
   }
   constexpr bool folded_last = CNT == 4 || (CNT > 4 && !(CNT & 1));
-  if constexpr (CNT > 2 && !folded_last) acc = fold_hi(acc, r);
+  if constexpr (CNT > 2 && !folded_last) {
+    acc = fold_hi(acc, r);
+    asm volatile("" : "+v"(acc));
+  }
   return redc(acc, r, rinv);
 }
 
@@ -803,9 +828,9 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv(ModDownArgs A)
   }
 }
 
-// SEG: c0 in the segment layout. EARLY: side inputs fetched before the
+// C0: how c0 is read (CombineLimb). EARLY: side inputs fetched before the
 // transform (fwd_blk_pass_fetch).
-template <int LOGN, bool SEG, bool EARLY>
+template <int LOGN, int C0, bool EARLY>
 __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_fwd_blk(ModDownArgs A) {
   using C = Cfg<LOGN>;
   const int lk = A.level + A.K;
@@ -822,7 +847,7 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_fwd_blk(ModDownArgs 
     c0 = A.c0 + (item % A.batch) * A.ct_stride + i * A.N;
     g = A.galois[item / A.batch];
   }
-  CombineLimb<(1 << C::LEB), C::LRC, C::LRB, SEG> L{A.T.r[i],
+  CombineLimb<(1 << C::LEB), C::LRC, C::LRB, C0> L{A.T.r[i],
                 A.T.rinv[i],
                 A.LT.md_pinv[pi],
                 A.LT.md_pinvp[pi],
@@ -1671,12 +1696,23 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
       const dim3 grid = sp ? dim3(8 * ((level * sp + 7) / 8) * items * polys * (blk_tiles<LN>() / sp))
                            : dim3(blk_tiles<LN>(), rows_q);
       LaunchTimer tm(p, KID_MODDOWN_FWD_BLK, s);
-      if (c0_seg)
-        hipLaunchKernelGGL((k_md_fwd_blk<LN, true, true>), grid, dim3(blk_threads<LN>()), 0, s, A);
-      else if (sp == 0 && late_fetch(items * polys))
-        hipLaunchKernelGGL((k_md_fwd_blk<LN, false, false>), grid, dim3(blk_threads<LN>()), 0, s, A);
-      else
-        hipLaunchKernelGGL((k_md_fwd_blk<LN, false, true>), grid, dim3(blk_threads<LN>()), 0, s, A);
+      const dim3 bt(blk_threads<LN>());
+      bool gather = false;
+      for (uint32_t k = 0; k < nkeys && k < (uint32_t)kMaxKeysPerLaunch; ++k) gather = gather || A.galois[k] != 1u;
+      if (c0 == nullptr) {
+        if (late_fetch(items * polys))
+          hipLaunchKernelGGL((k_md_fwd_blk<LN, kNoC0, false>), grid, bt, 0, s, A);
+        else
+          hipLaunchKernelGGL((k_md_fwd_blk<LN, kNoC0, true>), grid, bt, 0, s, A);
+      } else if (c0_seg) {
+        hipLaunchKernelGGL((k_md_fwd_blk<LN, kC0Seg, true>), grid, bt, 0, s, A);
+      } else if (gather) {
+        hipLaunchKernelGGL((k_md_fwd_blk<LN, kC0Gather, true>), grid, bt, 0, s, A);
+      } else if (late_fetch(items * polys)) {
+        hipLaunchKernelGGL((k_md_fwd_blk<LN, kC0Same, false>), grid, bt, 0, s, A);
+      } else {
+        hipLaunchKernelGGL((k_md_fwd_blk<LN, kC0Same, true>), grid, bt, 0, s, A);
+      }
     }
   });
   return hipGetLastError();

@@ -229,15 +229,40 @@ struct IdentityCol {
   __device__ __forceinline__ static int col(int x) { return x; }
 };
 
-template <int LOGR, int LOGE, bool GS, class Col = IdentityCol>
+// Orders this wave's LDS accesses around an exchange among its own lanes: a
+// wave's LDS instructions execute in program order, so only the compiler has
+// to be kept from moving accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// WAVE: every thread that touches lds_row belongs to the calling thread's wave
+// (a block pass: the 2^(LOGR-LOGE) threads of a block are consecutive lanes
+// of one wave), so the exchange needs no workgroup barrier.
+template <int LOGR, int LOGE, bool GS, class Col = IdentityCol, bool WAVE = false>
 __device__ __forceinline__ void exchange(uint32_t (&v)[1 << LOGE], uint32_t* lds_row, int from_round, int t) {
   constexpr int E = 1 << LOGE;
 #pragma unroll
   for (int m = 0; m < E; ++m) lds_row[Col::col(elem_index<LOGR, LOGE, GS>(from_round, t, m))] = v[m];
-  __syncthreads();
+  if constexpr (WAVE)
+    wave_lds_sync();
+  else
+    __syncthreads();
 #pragma unroll
   for (int m = 0; m < E; ++m) v[m] = lds_row[Col::col(elem_index<LOGR, LOGE, GS>(from_round + 1, t, m))];
-  __syncthreads();
+  if constexpr (WAVE)
+    wave_lds_sync();
+  else
+    __syncthreads();
+}
+
+// The threads of one block-pass block fit in one wave (and blocks never
+// straddle waves).
+template <int LOGR, int LOGE>
+constexpr bool block_in_wave() {
+  return (1 << (LOGR - LOGE)) <= 64 && 64 % (1 << (LOGR - LOGE)) == 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -316,7 +341,8 @@ __device__ __forceinline__ void fwd_blk_compute(uint32_t (&v)[1 << LOGE], uint32
   for (int rd = 0; rd < ROUNDS; ++rd) load_round_tw<LOGRB, LOGE, false>(rd, t, tw, twb, W[rd]);
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
-    if (rd > 0) exchange<LOGRB, LOGE, false, BlkLds<LOGRB, LOGE>>(v, lds_row, rd - 1, t);
+    if (rd > 0)
+      exchange<LOGRB, LOGE, false, BlkLds<LOGRB, LOGE>, block_in_wave<LOGRB, LOGE>()>(v, lds_row, rd - 1, t);
     ct_round_w<LOGE>(v, W[rd], r, rinv);
   }
 }
@@ -331,7 +357,8 @@ __device__ __forceinline__ void inv_blk_compute(uint32_t (&v)[1 << LOGE], uint32
   for (int rd = 0; rd < ROUNDS; ++rd) load_round_tw<LOGRB, LOGE, true>(rd, t, tw, twb, W[rd]);
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
-    if (rd > 0) exchange<LOGRB, LOGE, true, BlkLds<LOGRB, LOGE>>(v, lds_row, rd - 1, t);
+    if (rd > 0)
+      exchange<LOGRB, LOGE, true, BlkLds<LOGRB, LOGE>, block_in_wave<LOGRB, LOGE>()>(v, lds_row, rd - 1, t);
     gs_round_w<LOGE>(v, W[rd], r, rinv);
   }
 }
@@ -489,7 +516,12 @@ __device__ __forceinline__ void inv_blk_pass(Limb& L, int c0, uint32_t* seg_dst 
   uint32_t v[E];
 #pragma unroll
   for (int m = 0; m < E; ++m) v[m] = lds[Lay::row(k) + Lay::col(elem_index<LOGRB, LOGE, true>(0, t, m))];
-  __syncthreads();
+  // from here on each wave touches only its own blocks' rows, unless the
+  // segment copy above read other waves' rows
+  if (!block_in_wave<LOGRB, LOGE>() || seg_dst != nullptr)
+    __syncthreads();
+  else
+    wave_lds_sync();
   inv_blk_compute<LOGRC, LOGRB, LOGE>(v, lds + Lay::row(k), t, B, L.r, L.rinv, L.tw);
 #pragma unroll
   for (int m = 0; m < E; ++m) L.store((B << LOGRB) + elem_index<LOGRB, LOGE, true>(ROUNDS - 1, t, m), v[m]);
