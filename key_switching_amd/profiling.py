@@ -53,7 +53,7 @@ FAMILIES = {
     "moddown_inv_blk": "k_md_inv_blk<16>",
     "moddown_inv_col": "k_md_inv_col<16>",
     "moddown_bconv": "k_md_bconv<16, 6, 3>",
-    "moddown_fwd_blk": "k_md_fwd_blk<16, false, false>",
+    "moddown_fwd_blk": "k_md_fwd_blk<16, 1, false>",
     # homomorphic multiplication of 8 pairs around the same key switch
     "tensor": "k_tensor",
     "rescale_gather": "k_rs_gather",
@@ -73,7 +73,7 @@ FAMILIES_N17 = {
     "inner_product_chacha": "k_ip_regen<5, 12, 8, false>",
     "inner_product_stored": "k_inner_product<5, 12, true, 8, false>",
     "moddown_bconv": "k_md_bconv<17, 8, 3>",
-    "moddown_fwd_blk": "k_md_fwd_blk<17, false, false>",
+    "moddown_fwd_blk": "k_md_fwd_blk<17, 1, false>",
 }
 FAMILY_SETS = {"n16": FAMILIES, "n17": FAMILIES_N17}
 
