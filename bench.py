@@ -96,7 +96,7 @@ def parse():
     return ap.parse_args()
 
 
-LRC = {12: 6, 16: 8, 17: 9}   # NTT stages in the column pass (the block pass does the rest)
+LRC = {12: 6, 16: 8, 17: 8}   # NTT stages in the column pass (the block pass does the rest)
 
 
 def _shape(N, level, K, alpha, beta):

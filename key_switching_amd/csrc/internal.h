@@ -39,7 +39,7 @@ struct DevTables {
 
 // Split of the n = log2 N NTT stages into a column pass of 2^lrc points and a
 // block pass of 2^lrb points (must match the kernels' pass shapes).
-constexpr int pass_split_lrc(uint32_t log2n) { return log2n == 12 ? 6 : log2n == 16 ? 8 : log2n == 17 ? 9 : -1; }
+constexpr int pass_split_lrc(uint32_t log2n) { return log2n == 12 ? 6 : log2n == 16 ? 8 : log2n == 17 ? 8 : -1; }
 inline bool pass_split(uint32_t log2n, int* lrc, int* lrb) {
   const int c = pass_split_lrc(log2n);
   if (c < 0) return false;

@@ -37,9 +37,12 @@ template <>
 struct Cfg<16> {
   static constexpr int LRC = 8, LEC = 4, LRB = 8, LEB = 4, CC = 32, CB = 32;
 };
+// N = 2^17: 256-point columns as at 2^16 (two radix-16 rounds, the shape the
+// fused conversion runs best with) and 512-point blocks in three radix-8
+// rounds, one block per wave, 16 blocks per workgroup (64-byte runs).
 template <>
 struct Cfg<17> {
-  static constexpr int LRC = 9, LEC = 3, LRB = 8, LEB = 4, CC = 16, CB = 32;
+  static constexpr int LRC = 8, LEC = 4, LRB = 9, LEB = 3, CC = 32, CB = 16;
 };
 
 template <int LOGN>

@@ -65,15 +65,21 @@ struct LdsTile {
 // 256-point blocks with 16 elements per thread, row(k) = 272k + k/2 and
 // col(x) = x + x/16 put every one of them on 32 distinct banks (the pad makes
 // 16t + m distinct over t, the stride of 16 mod 32 separates the two blocks, and
-// the k/2 skew separates all 32 blocks of the transpose). Other shapes keep a
-// plain padded stride.
+// the k/2 skew separates all 32 blocks of the transpose). 512-point blocks
+// with 8 elements per thread (one block per wave) are touched as x = 64m + t,
+// x = 64(t/8) + 8m + t%8 and x = 8t + m; col(x) = x + x/8 puts the last two
+// on 32 distinct banks (the first has three 2-way pairs), and a row stride of
+// 578 (2 mod 32) puts the two x of the 16-block transpose on even and odd
+// banks. Other shapes keep a plain padded stride.
 template <int LOGRB, int LOGE>
 struct BlkLds {
   static constexpr int R = 1 << LOGRB;
   static constexpr bool SWZ = LOGRB == 8 && LOGE == 4;
-  static constexpr int S = SWZ ? R + R / 16 : R + 4;
+  static constexpr bool SWZ9 = LOGRB == 9 && LOGE == 3;
+  static constexpr int S = SWZ ? R + R / 16 : SWZ9 ? 578 : R + 4;
+  static_assert(!SWZ9 || S >= R + R / 8, "padded row must hold x + x/8");
   __device__ __forceinline__ static int row(int k) { return SWZ ? k * S + (k >> 1) : k * S; }
-  __device__ __forceinline__ static int col(int x) { return SWZ ? x + (x >> 4) : x; }
+  __device__ __forceinline__ static int col(int x) { return SWZ ? x + (x >> 4) : SWZ9 ? x + (x >> 3) : x; }
   static constexpr int words(int c) { return SWZ ? c * S + c / 2 : c * S; }
 };
 

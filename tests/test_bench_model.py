@@ -52,11 +52,11 @@ def test_model_scales_with_batch_and_keys():
 
 
 def test_n17_passes_split_stages():
-    """N=2^17 has a 9-stage column pass and an 8-stage block pass."""
+    """N=2^17 has an 8-stage column pass and a 9-stage block pass."""
     N = 1 << 17
     col = bench.alg_ops("modup_inv_col", N, 40, 8, 8, 5, 1) - 40 * N * bench.OPS_SHOUP
     blk = bench.alg_ops("modup_inv_blk", N, 40, 8, 8, 5, 1)
-    assert col * 8 == blk * 9
+    assert col * 9 == blk * 8
 
 
 def test_more_than_one_gpu_exits_with_a_message():
