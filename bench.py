@@ -723,6 +723,13 @@ def other_configs(ksa, torch, args, steps=10, only=None):
 
             ms = _time_calls(torch, chain, steps)
             mss = _time_calls(torch, lambda i: chain(i, stored=True), steps)
+            ksa.profile_begin(prm)
+            try:
+                for i in range(3):
+                    chain(i)
+            finally:
+                kst = ksa.profile_end(prm)
+            chain_kernels = {k: round(1000.0 * t / n, 2) for k, (n, t) in sorted(kst.items(), key=lambda kv: -kv[1][1])}
             one = (w.N, w.L, w.K, prm.alpha(w.L), beta, 8, 1, True)
             traffic = None
             try:
@@ -735,6 +742,7 @@ def other_configs(ksa, torch, args, steps=10, only=None):
                           "stored": {"ks_per_s": round(16 * 1000.0 / mss, 1), "ms_per_call": round(mss, 4),
                                      "path": path_fractions([one, one], mss, stored=True)},
                           "key_half_bytes": beta * (w.L + w.K) * w.N * 4,
+                          "kernel_avg_us": chain_kernels,
                           "inner_product_traffic_bytes": traffic}
             del keys, akeys, ct, mid, res
     return out
