@@ -162,6 +162,42 @@ def test_top_level_partition_needs_the_key_basis_index(monkeypatch):
     assert e is None or np.abs(e).max() > ks.error_bound(prm, level, emax, 8)
 
 
+@pytest.mark.parametrize("L,dnum,K,h", [(6, 3, 2, 8), (5, 2, 3, 12), (4, 4, 1, 4)])
+def test_error_bound_is_reached_by_a_worst_case_input(L, dnum, K, h):
+    """The bound holds and is nearly attained, so a dropped or extra factor fails.
+
+    Every coefficient of c1 is the integer whose residue on each q_i of digit D
+    is [-(Q_d/q_i)]_{q_i}. Fast base conversion then sums alpha_d terms
+    (q_i - 1) Q_d/q_i, so every ModUp coefficient is alpha_d Q_d - sum_i Q_d/q_i,
+    the top of its range. With every key error equal to E_max, coefficient N-1
+    of ext_d * e_d adds N equal positive terms (no negacyclic wrap reaches it),
+    and after the division by P the error there is
+    sum_d N alpha_d (Q_d/P) E_max up to the ModDown term, which lies in
+    [-K h, K (1 + h)] by the floor form's range [0, K P) per coefficient.
+    """
+    prm = small_params(log2n=6, L=L, dnum=dnum, K=K)
+    N, level, emax = prm.N, L, 19
+    digits = prm.digits(level)
+    c1 = np.empty((level, N), dtype=np.uint64)
+    for D in digits:
+        Qd = math.prod(prm.q[i] for i in D)
+        for i in D:
+            c1[i] = rns.ntt(np.full(N, (-(Qd // prm.q[i])) % prm.q[i], dtype=np.uint64), prm.q[i])
+    ct = np.stack([np.zeros_like(c1), c1])
+    s = ki.ternary_secret(L * 100 + K, N, h)
+    errs = np.full((len(digits), N), emax, dtype=np.int64)
+    key = ks.keygen(prm, s, errs, ki.key_seed(L, K), level, 1)
+    out = ks.keyswitch(prm, ct, key, level)
+    e = ks.decryption_error(prm, ct, out, s, 1, level)
+    assert e is not None
+    B = ks.error_bound(prm, level, emax, h)
+    assert np.abs(e).max() <= B
+    assert int(np.argmax(e)) == N - 1
+    assert e[N - 1] >= B - 2 * K * (1 + h) - 1
+    # the top term alone is a large share of the bound (the bound is not loose)
+    assert B - K * (1 + h) > 50 * K * (1 + h)
+
+
 def test_planted_mistakes_fail_the_decryption_check(monkeypatch):
     """Mistakes planted in the oracle (on the CPU) must break the decryption check."""
     prm = small_params(log2n=6, L=4, dnum=2, K=2)
