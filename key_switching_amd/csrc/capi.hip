@@ -176,6 +176,7 @@ int build_tables(pc_params* p) {
   p->h_mu_scale.assign(so, 0);
   p->h_mu_scalep.assign(so, 0);
   p->h_mu_bconv.assign(bo, 0);
+  p->h_mu_bconvw.assign(bo, 0);
   for (uint32_t l = 1; l <= L; ++l) {
     const int a = alpha_of(p, l);
     const uint32_t lk = l + K;
@@ -191,7 +192,10 @@ int build_tables(pc_params* p) {
         if ((int)j >= i0 && (int)j < i1) continue;
         const uint32_t rj = j < l ? p->primes[j] : p->primes[L + (j - l)];
         const uint32_t qhat = prod_mod(p, i0, i1, (int)i, rj);
-        p->h_mu_bconv[p->mu_bconv_off[l] + (size_t)i * lk + j] = mulmod(qhat, pow2_32(rj), rj);
+        const uint32_t pj = j < l ? j : L + (j - l);
+        const size_t at = p->mu_bconv_off[l] + (size_t)i * lk + j;
+        p->h_mu_bconv[at] = mulmod(qhat, pow2_32(rj), rj);
+        p->h_mu_bconvw[at] = mulmod(p->h_mu_bconv[at], p->h_tw_fwd[(size_t)pj * N + 1], rj);
       }
     }
   }
@@ -199,6 +203,7 @@ int build_tables(pc_params* p) {
   p->h_md_scale.assign(2 * K, 0);
   p->h_md_scalep.assign(2 * K, 0);
   p->h_md_bconv.assign((size_t)2 * K * L, 0);
+  p->h_md_bconvw.assign((size_t)2 * K * L, 0);
   p->h_md_pinv.assign(2 * L, 0);
   p->h_md_pinvp.assign(2 * L, 0);
   for (int v = 0; v < 2; ++v) {
@@ -218,7 +223,9 @@ int build_tables(pc_params* p) {
           if (u != t) ph = mulmod(ph, p->primes[L + u] % qi, qi);
         // (P/p_t) 2^32 S^-1 with S = 1 or 2^64, i.e. times 2^32 or 2^-32
         const uint32_t f = v == 0 ? pow2_32(qi) : invmod(pow2_32(qi), qi);
-        p->h_md_bconv[((size_t)v * K + t) * L + i] = mulmod(ph, f, qi);
+        const size_t at = ((size_t)v * K + t) * L + i;
+        p->h_md_bconv[at] = mulmod(ph, f, qi);
+        p->h_md_bconvw[at] = mulmod(p->h_md_bconv[at], p->h_tw_fwd[(size_t)i * N + 1], qi);
       }
     }
     for (uint32_t i = 0; i < L; ++i) {
@@ -267,6 +274,7 @@ int upload_tables(pc_params* p) {
   const size_t o_ds = append(blob, p->h_md_scale), o_dsp = append(blob, p->h_md_scalep),
                o_db = append(blob, p->h_md_bconv), o_dp = append(blob, p->h_md_pinv),
                o_dpp = append(blob, p->h_md_pinvp);
+  const size_t o_mbw = append(blob, p->h_mu_bconvw), o_dbw = append(blob, p->h_md_bconvw);
   void* d = nullptr;
   if (hipMalloc(&d, blob.size()) != hipSuccess) return PC_ENOMEM;
   if (hipMemcpy(d, blob.data(), blob.size(), hipMemcpyHostToDevice) != hipSuccess) {
@@ -277,7 +285,8 @@ int upload_tables(pc_params* p) {
   auto at = [d](size_t off) { return reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(d) + off); };
   p->tabs = DevTables{at(o_r), at(o_rinv), at(o_ninv), at(o_ninvp), at(o_r2),
                       at(o_tf), at(o_ti),   at(o_bf),   at(o_bi)};
-  p->ltabs = DevLevelTables{at(o_ms), at(o_msp), at(o_mb), at(o_ds), at(o_dsp), at(o_db), at(o_dp), at(o_dpp)};
+  p->ltabs = DevLevelTables{at(o_ms), at(o_msp), at(o_mb),  at(o_ds),  at(o_dsp),
+                            at(o_db), at(o_dp),  at(o_dpp), at(o_mbw), at(o_dbw)};
   return PC_OK;
 }
 

@@ -59,6 +59,11 @@ struct DevLevelTables {
   const uint32_t* md_bconv;   // [2][K][L] (P/p_t) 2^32 S^-1 mod q_i
   const uint32_t* md_pinv;    // [2][L] S P^-1 mod q_i
   const uint32_t* md_pinvp;
+  // the conversion constants times the target's first forward twiddle
+  // psi^bitrev(1) (plain): the upper half of a column, which the NTT's first
+  // stage multiplies by that twiddle, is converted already multiplied by it
+  const uint32_t* mu_bconvw;  // as mu_bconv
+  const uint32_t* md_bconvw;  // as md_bconv
 };
 
 }  // namespace pc
@@ -76,6 +81,7 @@ struct pc_params {
   std::vector<uint32_t> h_mu_scale, h_mu_scalep, h_mu_bconv;
   std::vector<size_t> mu_scale_off, mu_bconv_off;  // by level (index l, 1..L)
   std::vector<uint32_t> h_md_scale, h_md_scalep, h_md_bconv, h_md_pinv, h_md_pinvp;
+  std::vector<uint32_t> h_mu_bconvw, h_md_bconvw;  // the conversion constants times psi^bitrev(1) of the target
   // rescale by q_{l'} (row l' = level - 1, entry i < l'): q_{l'} mod q_i, q_{l'}^-1 mod q_i, its Shoup companion
   std::vector<uint32_t> h_rs_qlmod, h_rs_inv, h_rs_invp;  // [L][L]
   // device state

@@ -308,17 +308,21 @@ __device__ __forceinline__ uint32_t dot_redc(const uint32_t (&v)[CNT], const uin
 // keep it from hoisting every load and spending a register on each).
 // CNT is the source count the kernel is built for; a row with cnt < CNT
 // sources (the last, shorter digit) repeats its last source with constant 0.
-template <int G, int E, int CNT, class SrcFn, class ConstFn>
-__device__ __forceinline__ void grouped_bconv(TargetGroup<G, E>& tg, int cnt, SrcFn src, ConstFn cst) {
+// Slots m >= E/2 (the upper half of the column's first NTT stage) use the
+// constants cstw, which carry that stage's twiddle.
+template <int G, int E, int CNT, class SrcFn, class ConstFn, class ConstWFn>
+__device__ __forceinline__ void grouped_bconv(TargetGroup<G, E>& tg, int cnt, SrcFn src, ConstFn cst,
+                                              ConstWFn cstw) {
   constexpr int MC = 2, CHUNKS = E / MC;
-  static_assert(E % MC == 0, "positions must tile into chunks");
-  uint32_t c[G][CNT];
+  static_assert(E % MC == 0 && (E / 2) % MC == 0, "positions must tile into chunks");
+  uint32_t c[G][CNT], cw[G][CNT];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int k = 0; k < CNT; ++k) {
-      const uint32_t x = cst(min(k, cnt - 1), g);
+      const uint32_t x = cst(min(k, cnt - 1), g), xw = cstw(min(k, cnt - 1), g);
       c[g][k] = k < cnt ? x : 0u;
+      cw[g][k] = k < cnt ? xw : 0u;
     }
   uint32_t v[2][MC][CNT];
   auto load = [&](int chunk, uint32_t (&buf)[MC][CNT]) {
@@ -336,7 +340,7 @@ __device__ __forceinline__ void grouped_bconv(TargetGroup<G, E>& tg, int cnt, Sr
     for (int i = 0; i < MC; ++i)
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        tg.z[g][ch * MC + i] = dot_redc<CNT>(v[ch & 1][i], c[g], tg.r[g], tg.rinv[g]);
+        tg.z[g][ch * MC + i] = dot_redc<CNT>(v[ch & 1][i], ch * MC < E / 2 ? c[g] : cw[g], tg.r[g], tg.rinv[g]);
         asm volatile("" : "+v"(tg.z[g][ch * MC + i]));  // computed here, before the next loads
       }
     asm volatile("" ::: "memory");
@@ -379,17 +383,20 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_bconv(ModUpArgs A
   }
   const uint32_t* ybase = A.y + (b * A.level + i0) * A.N;
   const uint32_t* cbase = A.LT.mu_bconv + A.bconv_off + (size_t)i0 * lk;
+  const uint32_t* cwbase = A.LT.mu_bconvw + A.bconv_off + (size_t)i0 * lk;
   grouped_bconv<G, E, CNT>(
       tg, cnt,
       [&](int k, int m) {
         const uint32_t* yk = ybase + (size_t)k * A.N;  // uniform limb base, 32-bit offset
         return at32(yk, col_pos_fwd_in<C::LRC, C::LEC, C::LRB, C::CC>(col0, m));
       },
-      [&](int k, int g) { return cbase[(size_t)k * lk + tg.j[g]]; });
+      [&](int k, int g) { return cbase[(size_t)k * lk + tg.j[g]]; },
+      [&](int k, int g) { return cwbase[(size_t)k * lk + tg.j[g]]; });
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (g < tg.n) {
-      fwd_col_compute<C::LRC, C::LEC, C::CC>(tg.z[g], lds, tg.r[g], tg.rinv[g], A.T.tw_fwd + tg.pidx[g] * A.N);
+      fwd_col_compute<C::LRC, C::LEC, C::CC, true>(tg.z[g], lds, tg.r[g], tg.rinv[g],
+                                                   A.T.tw_fwd + tg.pidx[g] * A.N);
       uint32_t* dst = A.tmp + ((b * A.beta + d) * lk + tg.j[g]) * A.N;
 #pragma unroll
       // streaming stores: the block pass reads them once, and the inner
@@ -813,17 +820,20 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv(ModDownArgs A)
   }
   const uint32_t* ybase = A.y2 + ip * A.K * A.N;
   const uint32_t* cbase = A.LT.md_bconv + (size_t)A.variant * A.K * A.L;
+  const uint32_t* cwbase = A.LT.md_bconvw + (size_t)A.variant * A.K * A.L;
   grouped_bconv<G, E, CNT>(
       tg, A.K,
       [&](int k, int m) {
         const uint32_t* yk = ybase + (size_t)k * A.N;  // uniform limb base, 32-bit offset
         return at32(yk, col_pos_fwd_in<C::LRC, C::LEC, C::LRB, C::CC>(col0, m));
       },
-      [&](int k, int g) { return cbase[(size_t)k * A.L + tg.j[g]]; });
+      [&](int k, int g) { return cbase[(size_t)k * A.L + tg.j[g]]; },
+      [&](int k, int g) { return cwbase[(size_t)k * A.L + tg.j[g]]; });
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (g < tg.n) {
-      fwd_col_compute<C::LRC, C::LEC, C::CC>(tg.z[g], lds, tg.r[g], tg.rinv[g], A.T.tw_fwd + tg.pidx[g] * A.N);
+      fwd_col_compute<C::LRC, C::LEC, C::CC, true>(tg.z[g], lds, tg.r[g], tg.rinv[g],
+                                                   A.T.tw_fwd + tg.pidx[g] * A.N);
       uint32_t* dst = A.tmp2 + (ip * A.level + tg.j[g]) * A.N;
 #pragma unroll
       for (int m = 0; m < E; ++m) at32(dst, col_pos_fwd_out<C::LRC, C::LEC, C::LRB, C::CC>(col0, m)) = tg.z[g][m];

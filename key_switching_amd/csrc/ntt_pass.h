@@ -108,8 +108,9 @@ __device__ __forceinline__ void load_run(const uint32_t* __restrict__ p, int n, 
 // Montgomery form (one REDC per product). TwBase(s) returns the table offset of
 // group 0 of stage s for this thread's row/block (the part that does not depend
 // on the slot m); the 2^sl twiddles of stage sl are the run starting at
-// TwBase(s) + (t_high << sl), indexed by m >> (LOGE - sl).
-template <int LOGR, int LOGE, class TwBase>
+// TwBase(s) + (t_high << sl), indexed by m >> (LOGE - sl). FOLD0: the upper
+// half of round 0 arrives already multiplied by stage 0's single twiddle.
+template <int LOGR, int LOGE, bool FOLD0 = false, class TwBase>
 __device__ __forceinline__ void ct_round(uint32_t (&v)[1 << LOGE], int round, int t, uint32_t r, uint32_t rinv,
                                          const uint32_t* __restrict__ tw, TwBase twbase) {
   constexpr int E = 1 << LOGE;
@@ -119,15 +120,16 @@ __device__ __forceinline__ void ct_round(uint32_t (&v)[1 << LOGE], int round, in
   for (int sl = 0; sl < LOGE; ++sl) {
     const int s = round * LOGE + sl;
     const int half = E >> (sl + 1);
+    const bool folded = FOLD0 && s == 0;
     uint32_t w[E / 2];
-    load_run(tw + twbase(s) + (thigh << sl), 1 << sl, w);
+    if (!folded) load_run(tw + twbase(s) + (thigh << sl), 1 << sl, w);
 #pragma unroll
     for (int g = 0; g < (1 << sl); ++g) {
 #pragma unroll
       for (int j = 0; j < half; ++j) {
         const int m0 = g * 2 * half + j;
         const uint32_t u = v[m0];
-        const uint32_t x = mul_mont(v[m0 + half], w[g], r, rinv);
+        const uint32_t x = folded ? v[m0 + half] : mul_mont(v[m0 + half], w[g], r, rinv);
         v[m0] = add_mod(u, x, r);
         v[m0 + half] = sub_mod(u, x, r);
       }
@@ -284,8 +286,10 @@ constexpr bool block_in_wave() {
 // (threadIdx.x % C); the input layout is round 0, the output layout the last
 // round. The inverse pass's output layout equals the forward pass's input
 // layout (both put slot m at x = (m << (LOGRC - LOGE)) | t), so an inverse
-// column pass can feed a forward column pass without an exchange.
-template <int LOGRC, int LOGE, int C>
+// column pass can feed a forward column pass without an exchange. In round 0
+// slots m and m + E/2 are stage 0's pairs (x and x + 2^(LOGRC-1)), all with
+// twiddle entry 1; FOLD0: slots m >= E/2 already carry that factor.
+template <int LOGRC, int LOGE, int C, bool FOLD0 = false>
 __device__ __forceinline__ void fwd_col_compute(uint32_t (&v)[1 << LOGE], uint32_t* lds, uint32_t r, uint32_t rinv,
                                                 const uint32_t* __restrict__ tw) {
   constexpr int ROUNDS = LOGRC / LOGE;
@@ -294,7 +298,7 @@ __device__ __forceinline__ void fwd_col_compute(uint32_t (&v)[1 << LOGE], uint32
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     if (rd > 0) exchange<LOGRC, LOGE, false>(v, lds + col * LdsTile<LOGRC, LOGE>::STRIDE, rd - 1, t);
-    ct_round<LOGRC, LOGE>(v, rd, t, r, rinv, tw, twb);
+    ct_round<LOGRC, LOGE, FOLD0>(v, rd, t, r, rinv, tw, twb);
   }
 }
 
