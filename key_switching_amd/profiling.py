@@ -66,14 +66,19 @@ FAMILIES = {
 
 
 # the N=2^17, L=40 chain (bench.py --only n17): batch-8 launches, a half
-# regenerated or stored
+# regenerated or stored. Each chain call relinearises, then rotates, so the
+# inner product's dispatches of one kind alternate between the two keys: a
+# (prefix, parity) entry takes every other dispatch in dispatch order.
 FAMILIES_N17 = {
     "modup_bconv": "k_modup_bconv<17, 8, 3>",
     "modup_fwd_blk": "k_modup_fwd_blk<17>",
-    "inner_product_chacha": "k_ip_regen<5, 12, 8, false>",
-    "inner_product_stored": "k_inner_product<5, 12, true, 8, false>",
+    "inner_product_chacha_relin": ("k_ip_regen<5, 12, 8, false>", 0),
+    "inner_product_chacha_rotate": ("k_ip_regen<5, 12, 8, false>", 1),
+    "inner_product_stored_relin": ("k_inner_product<5, 12, true, 8, false>", 0),
+    "inner_product_stored_rotate": ("k_inner_product<5, 12, true, 8, false>", 1),
     "moddown_bconv": "k_md_bconv<17, 8, 3>",
-    "moddown_fwd_blk": "k_md_fwd_blk<17, 1, false>",
+    "moddown_fwd_blk_relin": "k_md_fwd_blk<17, 1, false>",
+    "moddown_fwd_blk_rotate": "k_md_fwd_blk<17, 2, true>",
 }
 FAMILY_SETS = {"n16": FAMILIES, "n17": FAMILIES_N17}
 
@@ -160,14 +165,21 @@ def cmd_traffic(a) -> str:
            "Per kernel family, batch-8 launch (largest grid of that kernel), medians over its dispatches:", "",
            "| family | dispatch | grid | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetch bytes | write bytes | traffic bytes |",
            "|---|---|---|---|---|---|---|---|---|"]
-    for fam, prefix in FAMILY_SETS[a.families].items():
+    for fam, spec in FAMILY_SETS[a.families].items():
+        prefix, parity = (spec, None) if isinstance(spec, str) else spec
         fk = {(d, g): v for (d, k, g), v in f.items() if k == prefix}
         wk = {(d, g): v for (d, k, g), v in w.items() if k == prefix}
         if not fk or not wk:
             continue
         g = max(gg for (_, gg) in fk)
-        kf = [v for (d, gg), v in fk.items() if gg == g]
-        kw = [v for (d, gg), v in wk.items() if gg == g]
+
+        def pick(m):
+            ds = sorted((d for (d, gg) in m if gg == g), key=int)
+            if parity is not None:
+                ds = ds[parity::2]
+            return [m[(d, g)] for d in ds]
+
+        kf, kw = pick(fk), pick(wk)
         fb = statistics.median(kf) * 1024.0 * rf
         wb = statistics.median(kw) * 1024.0 * rw
         out.append(f"| {fam} | `{prefix}` | {g} | {len(kf)} | {statistics.median(kf):.0f} | "
@@ -222,9 +234,10 @@ def read_ip_traffic(path: str):
     out = {}
     for line in text:
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
-        if len(cells) == 9 and cells[0] in ("inner_product_chacha", "inner_product_stored"):
-            out[cells[0].split("_")[-1]] = {"fetch": float(cells[6]), "write": float(cells[7]),
-                                            "total": float(cells[8])}
+        if len(cells) == 9 and cells[0].startswith("inner_product_"):
+            _, _, half, step = cells[0].split("_")
+            out.setdefault(half, {})[step] = {"fetch": float(cells[6]), "write": float(cells[7]),
+                                              "total": float(cells[8])}
     return out or None
 
 
@@ -261,8 +274,8 @@ def cmd_valu(a) -> str:
            "(serialised dispatches); `wait` = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; `bank` = "
            "SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS.", "",
            "| family | dispatch | grid | VALU wave-instr (M) | issued/alg | issue us | duration us | busy | "
-           "LDS instr (M) | bank | wait | VGPRs |",
-           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+           "LDS instr (M) | bank | wait |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
     N, L, K, alpha, beta, batch = 1 << 16, 24, 6, 6, 4, 8
     for fam, prefix in FAMILIES.items():
         if fam not in bench.KERNELS:
@@ -284,7 +297,7 @@ def cmd_valu(a) -> str:
         out.append(f"| {fam} | `{prefix}` | {g} | {valu / 1e6:.2f} | {valu * 64 / alg:.3f} | {issue_us:.1f} | "
                    f"{dur:.1f} | {issue_us / dur:.2f} | {lds / 1e6:.2f} | "
                    f"{med('SQ_LDS_BANK_CONFLICT') / max(lds, 1):.3f} | "
-                   f"{med('SQ_WAIT_INST_ANY') / max(med('SQ_WAVE_CYCLES'), 1):.2f} | {meta[ds[0]][2]} |")
+                   f"{med('SQ_WAIT_INST_ANY') / max(med('SQ_WAVE_CYCLES'), 1):.2f} |")
     return "\n".join(out) + "\n"
 
 
