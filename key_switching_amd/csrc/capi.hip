@@ -339,10 +339,10 @@ bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15u) != 0; }
 size_t ks_workspace_bytes(const pc_params* p, uint32_t level, uint32_t batch, uint32_t items) {
   const size_t N = p->N, l = level, K = p->K, lk = l + K, beta = (size_t)beta_of(p, level);
   size_t b = 0;
-  b += align256(batch * l * N * 4);
+  b += align256(batch * l * (N + kLimbPad) * 4);
   b += 2 * align256(batch * beta * lk * N * 4);
   b += align256(items * 2 * lk * N * 4);
-  b += align256(items * 2 * K * N * 4);
+  b += align256(items * 2 * K * (N + kLimbPad) * 4);
   b += align256(items * 2 * l * N * 4);
   return b;
 }
@@ -356,11 +356,11 @@ KsWorkspace ks_workspace_carve(const pc_params* p, void* base, uint32_t level, u
     c += align256(bytes);
     return r;
   };
-  w.y = take(batch * l * N * 4);
+  w.y = take(batch * l * (N + kLimbPad) * 4);
   w.tmp = take(batch * beta * lk * N * 4);
   w.ext = take(batch * beta * lk * N * 4);
   w.acc = take(items * 2 * lk * N * 4);
-  w.y2 = take(items * 2 * K * N * 4);
+  w.y2 = take(items * 2 * K * (N + kLimbPad) * 4);
   w.tmp2 = take(items * 2 * l * N * 4);
   return w;
 }

@@ -17,6 +17,10 @@ constexpr int kMaxDigits = 6;            // digits supported by the inner-produc
 constexpr int kMaxSpecial = 8;           // special primes (ModDown)
 constexpr int kMaxAlpha = 8;             // primes per digit (ModUp)
 constexpr int kMaxRescaleLimbs = 64;     // limbs kept by a rescale (constants travel in kernel arguments)
+// Words between consecutive limbs of the inverse passes' buffers (ModUp's y,
+// ModDown's y2) beyond N: with limbs a power of two apart, the workgroups
+// that walk many limbs at the same offsets meet on the same HBM channels.
+constexpr uint32_t kLimbPad = 32;
 
 // Device pointers to the per-prime tables (prime index = position in the chain:
 // q_0..q_{L-1} then p_0..p_{K-1}).
@@ -131,11 +135,11 @@ inline uint32_t key_level_of(const pc_params* p, uint32_t level) { return p->par
 // Workspace carve-up for a key switch of `items` (ciphertext, key) pairs over a
 // batch of `batch` ciphertexts at level l.
 struct KsWorkspace {
-  uint32_t* y;     // [batch][l][N]          ModUp coefficients (scaled)
+  uint32_t* y;     // [batch][l][N + kLimbPad] ModUp coefficients (scaled)
   uint32_t* tmp;   // [batch][beta][l+K][N]  ModUp after the column pass
   uint32_t* ext;   // [batch][beta][l+K][N]  ModUp output (evaluation form)
   uint32_t* acc;   // [items][2][l+K][N]     inner product
-  uint32_t* y2;    // [items][2][K][N]       ModDown coefficients of the P limbs
+  uint32_t* y2;    // [items][2][K][N + kLimbPad] ModDown coefficients of the P limbs
   uint32_t* tmp2;  // [items][2][l][N]       ModDown after the column pass
   // ext in the segment layout, for inner products that gather under
   // automorphisms (set before ModUp; ModUp then also files c1's limbs there)

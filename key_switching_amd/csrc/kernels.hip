@@ -203,11 +203,12 @@ struct ModUpArgs {
   const uint32_t* ct;  // c1 of batch item b at ct + b * ct_stride + c1_off
   uint64_t ct_stride;
   uint32_t c1_off;
-  uint32_t* y;    // [batch][l][N]
+  uint32_t* y;    // [batch][l][ys]
   uint32_t* tmp;  // [batch][beta][l+K][N]
   uint32_t* ext;  // [batch][beta][l+K][N]
   int N, level, K, L, alpha, beta, batch, ngroups;
   int seg;  // ext in the segment layout, the digits' own limbs included (gathers follow)
+  int ys;   // words between limbs of y (N + kLimbPad)
   size_t scale_off, bconv_off;
 };
 
@@ -218,7 +219,7 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_modup_inv_blk(ModUpArgs
   // are neighbours in memory
   const size_t b = blockIdx.y / A.level, i = blockIdx.y % A.level, z = b * A.level + i;
   PlainLimb L{A.T.r[i], A.T.rinv[i], A.T.tw_iblk + i * A.N, A.ct + b * A.ct_stride + A.c1_off + i * A.N,
-              A.y + z * A.N};
+              A.y + z * A.ys};
   // with the segment layout, c1's limb i is also the own limb of digit i / alpha
   uint32_t* own = A.seg ? A.ext + ((b * A.beta + i / A.alpha) * (A.level + A.K) + i) * A.N : nullptr;
   inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB, own);
@@ -229,7 +230,7 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_inv_col(ModUpArgs
   using C = Cfg<LOGN>;
   const size_t z = blockIdx.y, i = z % A.level;
   ScaledLimb L{A.T.r[i],          A.T.rinv[i], A.LT.mu_scale[A.scale_off + i], A.LT.mu_scalep[A.scale_off + i],
-               A.T.tw_inv + i * A.N, A.y + z * A.N, A.y + z * A.N};
+               A.T.tw_inv + i * A.N, A.y + z * A.ys, A.y + z * A.ys};
   inv_col_pass<C::LRC, C::LEC, C::LRB, C::CC>(L, blockIdx.x * C::CC);
 }
 
@@ -381,13 +382,13 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_modup_bconv(ModUpArgs A
     tg.r[g] = A.T.r[tg.pidx[g]];
     tg.rinv[g] = A.T.rinv[tg.pidx[g]];
   }
-  const uint32_t* ybase = A.y + (b * A.level + i0) * A.N;
+  const uint32_t* ybase = A.y + (b * A.level + i0) * A.ys;
   const uint32_t* cbase = A.LT.mu_bconv + A.bconv_off + (size_t)i0 * lk;
   const uint32_t* cwbase = A.LT.mu_bconvw + A.bconv_off + (size_t)i0 * lk;
   grouped_bconv<G, E, CNT>(
       tg, cnt,
       [&](int k, int m) {
-        const uint32_t* yk = ybase + (size_t)k * A.N;  // uniform limb base, 32-bit offset
+        const uint32_t* yk = ybase + (size_t)k * A.ys;  // uniform limb base, 32-bit offset
         return at32(yk, col_pos_fwd_in<C::LRC, C::LEC, C::LRB, C::CC>(col0, m));
       },
       [&](int k, int g) { return cbase[(size_t)k * lk + tg.j[g]]; },
@@ -763,7 +764,7 @@ struct ModDownArgs {
   DevTables T;
   DevLevelTables LT;
   const uint32_t* acc;  // [items][polys][l+K][N]
-  uint32_t* y2;         // [items][polys][K][N]
+  uint32_t* y2;         // [items][polys][K][y2s]
   uint32_t* tmp2;       // [items][polys][l][N]
   uint32_t* out;        // [items][polys][l][N]
   const uint32_t* c0;   // c0 of ciphertext b at c0 + b * ct_stride, or nullptr
@@ -771,6 +772,7 @@ struct ModDownArgs {
   int N, level, K, L, polys, variant, batch, rows_ip, ngroups;
   int limb_xcd;  // combine pass: 0, or the split of limb_xcd_decode (c0 gathered under an automorphism)
   int i0, ni;    // combine pass: limbs i0 .. i0 + ni - 1 of every polynomial (0 and level: all)
+  int y2s;       // words between limbs of y2 (N + kLimbPad)
   uint32_t galois[kMaxKeysPerLaunch];  // per key = item / batch
 };
 
@@ -781,7 +783,7 @@ __global__ void __launch_bounds__(blk_threads<LOGN>()) k_md_inv_blk(ModDownArgs 
   // rows in storage order (see k_modup_inv_blk)
   const size_t ip = blockIdx.y / A.K, t = blockIdx.y % A.K, z = ip * A.K + t, pt = A.L + t;
   PlainLimb L{A.T.r[pt], A.T.rinv[pt], A.T.tw_iblk + pt * A.N, A.acc + (ip * lk + A.level + t) * A.N,
-              A.y2 + z * A.N};
+              A.y2 + z * A.y2s};
   inv_blk_pass<C::LRC, C::LRB, C::LEB, C::CB>(L, blockIdx.x * C::CB);
 }
 
@@ -791,7 +793,7 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_inv_col(ModDownArgs 
   const size_t z = blockIdx.y, t = z % A.K, pt = A.L + t;
   const size_t si = (size_t)A.variant * A.K + t;
   ScaledLimb L{A.T.r[pt], A.T.rinv[pt], A.LT.md_scale[si], A.LT.md_scalep[si], A.T.tw_inv + pt * A.N,
-               A.y2 + z * A.N, A.y2 + z * A.N};
+               A.y2 + z * A.y2s, A.y2 + z * A.y2s};
   inv_col_pass<C::LRC, C::LEC, C::LRB, C::CC>(L, blockIdx.x * C::CC);
 }
 
@@ -818,13 +820,13 @@ __global__ void __launch_bounds__(col_threads<LOGN>()) k_md_bconv(ModDownArgs A)
     tg.r[g] = A.T.r[i];
     tg.rinv[g] = A.T.rinv[i];
   }
-  const uint32_t* ybase = A.y2 + ip * A.K * A.N;
+  const uint32_t* ybase = A.y2 + ip * A.K * A.y2s;
   const uint32_t* cbase = A.LT.md_bconv + (size_t)A.variant * A.K * A.L;
   const uint32_t* cwbase = A.LT.md_bconvw + (size_t)A.variant * A.K * A.L;
   grouped_bconv<G, E, CNT>(
       tg, A.K,
       [&](int k, int m) {
-        const uint32_t* yk = ybase + (size_t)k * A.N;  // uniform limb base, 32-bit offset
+        const uint32_t* yk = ybase + (size_t)k * A.y2s;  // uniform limb base, 32-bit offset
         return at32(yk, col_pos_fwd_in<C::LRC, C::LEC, C::LRB, C::CC>(col0, m));
       },
       [&](int k, int g) { return cbase[(size_t)k * A.L + tg.j[g]]; },
@@ -1438,6 +1440,7 @@ hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stri
   A.ct_stride = ct_stride;
   A.c1_off = c1_offset;
   A.y = ws.y;
+  A.ys = (int)(p->N + kLimbPad);
   A.tmp = ws.tmp;
   A.ext = ws.ext;
   A.N = (int)p->N;
@@ -1662,6 +1665,7 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
   A.LT = p->ltabs;
   A.acc = acc;
   A.y2 = ws.y2;
+  A.y2s = (int)(p->N + kLimbPad);
   A.tmp2 = ws.tmp2;
   A.out = out;
   A.c0 = c0;
@@ -1817,6 +1821,7 @@ hipError_t launch_moddown_rescale(const pc_params* p, const uint32_t* acc, uint3
   M.LT = p->ltabs;
   M.acc = acc;
   M.y2 = ws.y2;
+  M.y2s = (int)(p->N + kLimbPad);
   M.tmp2 = ws.tmp2;
   M.out = nullptr;
   M.c0 = c0;
