@@ -282,11 +282,9 @@ constexpr bool block_in_wave() {
 // Positions are limb offsets in [0, N).
 // ---------------------------------------------------------------------------
 
-// Register-level column passes: v holds this thread's E elements of column
-// (threadIdx.x % C); the input layout is round 0, the output layout the last
-// round. The inverse pass's output layout equals the forward pass's input
-// layout (both put slot m at x = (m << (LOGRC - LOGE)) | t), so an inverse
-// column pass can feed a forward column pass without an exchange. In round 0
+// Register-level forward column pass (the conversion kernels' transform): v
+// holds this thread's E elements of column (threadIdx.x % C); the input
+// layout is round 0, the output layout the last round. In round 0
 // slots m and m + E/2 are stage 0's pairs (x and x + 2^(LOGRC-1)), all with
 // twiddle entry 1; FOLD0: slots m >= E/2 already carry that factor.
 template <int LOGRC, int LOGE, int C, bool FOLD0 = false>
@@ -302,19 +300,6 @@ __device__ __forceinline__ void fwd_col_compute(uint32_t (&v)[1 << LOGE], uint32
   }
 }
 
-template <int LOGRC, int LOGE, int C>
-__device__ __forceinline__ void inv_col_compute(uint32_t (&v)[1 << LOGE], uint32_t* lds, uint32_t r, uint32_t rinv,
-                                                const uint32_t* __restrict__ tw) {
-  constexpr int ROUNDS = LOGRC / LOGE;
-  const int col = threadIdx.x % C, t = threadIdx.x / C;
-  auto twb = [](int u) { return 1 << (LOGRC - u - 1); };
-#pragma unroll
-  for (int rd = 0; rd < ROUNDS; ++rd) {
-    if (rd > 0) exchange<LOGRC, LOGE, true>(v, lds + col * LdsTile<LOGRC, LOGE>::STRIDE, rd - 1, t);
-    gs_round<LOGRC, LOGE>(v, rd, t, r, rinv, tw, twb);
-  }
-}
-
 // Limb position of slot m of this thread in a column pass: input layout (round 0)
 // of a forward pass / output layout (last round) of an inverse pass.
 template <int LOGRC, int LOGE, int LOGRB, int C>
@@ -326,11 +311,6 @@ template <int LOGRC, int LOGE, int LOGRB, int C>
 __device__ __forceinline__ int col_pos_fwd_out(int col0, int m) {
   const int col = threadIdx.x % C, t = threadIdx.x / C;
   return col0 + col + (elem_index<LOGRC, LOGE, false>(LOGRC / LOGE - 1, t, m) << LOGRB);
-}
-template <int LOGRC, int LOGE, int LOGRB, int C>
-__device__ __forceinline__ int col_pos_inv_in(int col0, int m) {
-  const int col = threadIdx.x % C, t = threadIdx.x / C;
-  return col0 + col + (elem_index<LOGRC, LOGE, true>(0, t, m) << LOGRB);
 }
 
 // Register-level block passes on block B (LOGRB-point, TPB = 2^(LOGRB-LOGE)
