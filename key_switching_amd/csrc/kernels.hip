@@ -1552,11 +1552,22 @@ static void launch_ip_kernel(const IPArgs& A, dim3 grid, bool stored, int rounds
     hipLaunchKernelGGL((k_inner_product<BETA, 12, false, BT, SEG>), grid, dim3(kIpThreads), 0, s, A);
 }
 
+// Source bytes per limb above which a gathering batch takes one workgroup per
+// inner-product unit (4 x an XCD's 4 MB L2).
+constexpr size_t kGatherSetBytes = size_t(16) << 20;
+
 template <int BETA, int BT>
 static void launch_ip_bt(const pc_params* p, const IPArgs& A0, uint32_t nkeys, bool stored, bool seg,
                          hipStream_t s) {
   if constexpr (BT != 1) {
-    if (!stored && A0.batch >= 2) {  // regenerated a half and a batch to overlap it with
+    // regenerated a half and a batch to overlap it with: the producer/consumer
+    // kernel, unless the call gathers from more than kGatherSetBytes of
+    // sources per limb (batch x digits x limb bytes), where its persistent walk
+    // refetches them more than one workgroup per unit does (measured: the
+    // N = 2^17 relinearise-and-rotate chain, 20 MB, 3.57K -> 3.68K key
+    // switches/s; the N = 2^16 level sweep, 8 MB, slower)
+    const size_t gather_set = (size_t)A0.batch * BETA * p->N * 4;
+    if (!stored && A0.batch >= 2 && (A0.limb_xcd == 0 || gather_set <= kGatherSetBytes)) {
       if (p->chacha_rounds == 20)
         launch_ip_regen<BETA, 20, BT>(p, A0, seg, s);
       else
