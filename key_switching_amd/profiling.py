@@ -66,14 +66,16 @@ FAMILIES = {
 
 
 # the N=2^17, L=40 chain (bench.py --only n17): batch-8 launches, a half
-# regenerated or stored. Each chain call relinearises, then rotates, so the
-# inner product's dispatches of one kind alternate between the two keys: a
+# regenerated or stored. Each chain call relinearises, then rotates. With a
+# regenerated half the two steps run different kernels (the rotation's
+# gathers take one workgroup per unit); with a stored half they run the same
+# kernel, whose dispatches then alternate between the two keys: a
 # (prefix, parity) entry takes every other dispatch in dispatch order.
 FAMILIES_N17 = {
     "modup_bconv": "k_modup_bconv<17, 8, 3>",
     "modup_fwd_blk": "k_modup_fwd_blk<17>",
-    "inner_product_chacha_relin": ("k_ip_regen<5, 12, 8, false>", 0),
-    "inner_product_chacha_rotate": ("k_ip_regen<5, 12, 8, false>", 1),
+    "inner_product_chacha_relin": "k_ip_regen<5, 12, 8, false>",
+    "inner_product_chacha_rotate": "k_inner_product<5, 12, false, 8, false>",
     "inner_product_stored_relin": ("k_inner_product<5, 12, true, 8, false>", 0),
     "inner_product_stored_rotate": ("k_inner_product<5, 12, true, 8, false>", 1),
     "moddown_bconv": "k_md_bconv<17, 8, 3>",
