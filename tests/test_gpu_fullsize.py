@@ -200,6 +200,25 @@ def test_n17_relinearise_then_rotate_every_item(digests):
     prm.close()
 
 
+def test_n17_rotation_batch7_matches_single_calls():
+    """A batch of 7 under the X^5 key at N=2^17 gathers from more than 16 MB of
+    sources per limb and takes the inner product's one-workgroup-per-unit kernel
+    with each thread expanding its ChaCha blocks, at a batch size the kernel is
+    not specialised for. Every item must equal the single-ciphertext call on it,
+    the path that the chain's digests pin to the oracle (item 13 above)."""
+    c = cases.case_n17_chain()
+    rot = c.keys[1]
+    prm = params_for(c, max_batch=8)
+    kb = dev(rot.b)
+    cts = dev(c.cts[:7])
+    batch = host(ksa.keyswitch_ex(prm, cts, [kb], [5], c.level, seeds=[rot.seed]))[0]
+    for b in range(7):
+        one = host(ksa.keyswitch(prm, cts[b].contiguous(), kb, rot.seed, c.level, 5))
+        diff = np.flatnonzero(batch[b].reshape(-1) != one.reshape(-1))
+        assert diff.size == 0, f"item {b}: {diff.size} words differ from the single call, first at {diff[0]}"
+    prm.close()
+
+
 def test_n16_live_oracle_item_and_decryption():
     """One item compared word for word with a live oracle run, and its decryption under
     the real secret within the bound (the digests pin the rest)."""
