@@ -68,6 +68,8 @@ def dot_ops(alpha):
     the 64-bit sum after the fourth product and every further pair (two ops each), REDC."""
     folds = 0 if alpha <= 2 else 1 + (alpha - 3) // 2
     return alpha + 2 * folds + OPS_REDC
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,8 +87,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--buffers-gib", type=float, default=1.1, help="ciphertext buffer rotation size")
     ap.add_argument("--streams", type=int, default=3, choices=(1, 2, 3),
-                    help="HIP streams the timed batches alternate on (each with its own workspace); "
-                         "1 for profiler runs, whose per-dispatch times must not overlap")
+                    help="streams of the labelled variants with independent calls in flight (each call with "
+                         "its own workspace; the headline is one stream); 1 skips them, as profiler runs "
+                         "need, whose per-dispatch times must not overlap")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the timings of the other workloads (hoisted 16, level sweep, N=2^17 chain)")
     ap.add_argument("--only", choices=("hoist16", "levels16", "n17"), default=None,
