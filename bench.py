@@ -10,8 +10,7 @@ the stored-key variants are reported beside it.
 
 The headline runs the batches one after another on one HIP stream: with the
 clock up, a batch of 8 fills the chip and one stream measured faster than two
-or three (each extra stream brings its own 770 MB workspace, and the Infinity
-Cache then holds less of each). Independent calls dealt round-robin to
+or three (0.47-0.49 against 0.50-0.53 ms per batch). Independent calls dealt round-robin to
 several streams (`--streams`, each call with its own caller workspace) are
 reported beside it; at batch 1 they overlap calls that each leave most of the
 chip idle.
@@ -29,8 +28,8 @@ multiplication, linear-transform and key-generation legs, and the key-switch
 rates of the other workloads (one ciphertext under 16 hoisted rotation keys,
 the level sweep 24..4, the N=2^17 relinearise-then-rotate chain).
 
-Prints one JSON line. `python bench.py --gpus N` with N > 1 exits: this build
-measures one GPU.
+Prints one JSON line. `python bench.py --gpus N` with N > 1 exits: the
+benchmark measures one GPU.
 """
 
 import argparse
@@ -286,7 +285,7 @@ def cpu_baseline(w, budget_s, workers):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(key switching shards by ciphertext batch; see the design notes).", file=sys.stderr)
         sys.exit(2)
     w = ki.WORKLOADS["n16"]

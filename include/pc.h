@@ -2,13 +2,14 @@
  * pc.h -- C ABI of the MI355X (gfx950) CKKS hybrid key-switching library.
  *
  * What it computes. The Perseus README ('What's inside') describes a CKKS
- * runtime whose key switching regenerates half of every key-switching key on
- * the GPU from a ChaCha12 seed instead of storing it, and ('Layout') whose
- * device runtime provides NTT and key-switching kernels over a 32-bit prime
- * chain (opening paragraph: 32-bit kernels). The arXiv summary page of the
- * Perseus paper (methodology, item (i)) calls the regeneration a ChaCha12
- * counter-mode expander. The pages do not write the algorithm out; this
- * library implements textbook RNS-CKKS hybrid key switching:
+ * runtime whose key switching re-creates one half of each key-switching key
+ * in its GPU kernels out of a ChaCha12 seed rather than keeping it in memory,
+ * and ('Layout') whose device runtime has NTT and key-switching kernels over
+ * a 32-bit prime chain (opening paragraph: 32-bit kernels). The arXiv summary
+ * page of the Perseus paper (methodology, item (i)) describes that
+ * re-creation as ChaCha12 run in counter mode. The pages do not write the
+ * algorithm out; this library implements textbook RNS-CKKS hybrid key
+ * switching:
  *
  *   ModUp (iNTT, fast base conversion per digit, NTT) -> automorphism ->
  *   inner product with the key (b half read, a half regenerated) ->
@@ -101,7 +102,7 @@ typedef struct {
 /* Parameters, constant tables and the workspace arena (Perseus README,
  * 'Layout': the CUDA-free core holds the parameters and the device runtime
  * one frozen device arena; 'What's inside': programs replay from one device
- * arena sized at setup). Builds the prime chain, psi and every constant table
+ * arena whose size is fixed when it starts). Builds the prime chain, psi and every constant table
  * on the host; with device >= 0 also uploads them and allocates the arena on
  * that device. device = -1 builds the host tables only (pc_params_get works;
  * every compute call returns PC_EDEVICE). *out receives a library-owned
@@ -153,8 +154,8 @@ int pc_intt(const pc_params *p, uint32_t *data, const uint32_t *prime_idx, uint3
 int pc_modup(const pc_params *p, const uint32_t *c1, uint32_t level, uint32_t *ext, void *stream);
 
 /* One key switch (Perseus README, 'Layout': key switching kernels; 'What's
- * inside': half of every key-switching key regenerated on the GPU from a
- * ChaCha12 seed; arXiv summary page, methodology item (i)): out
+ * inside': one half of each key re-created in the kernels out of a ChaCha12 seed;
+ * arXiv summary page, methodology item (i)): out
  * ([2][level][N], device) from ct ([2][level][N], device) with the key whose
  * b half is evk_b ([beta][kl+K][N], device, kl = the key level) and whose a
  * half is regenerated from evk_seed (32 bytes, host). automorphism_idx is the
@@ -302,8 +303,8 @@ int pc_linear_transform(const pc_params *p, const pc_lt_args *args, void *stream
 
 /* Packed key storage: a key bundle (Perseus README, 'Layout': the server runs
  * on the client's key bundle; 'Runtime': the bootstrap benchmark runs with its
- * keys packed; 'What's inside': half of every key is regenerated from a
- * ChaCha12 seed instead of being stored). Reading: a bundle holds nkeys keys
+ * keys packed; 'What's inside': one half of each key is re-created from a
+ * ChaCha12 seed rather than kept). Reading: a bundle holds nkeys keys
  * of one key level, in one device allocation made at creation -- for each key
  * its b half [beta][kl+K][N], its 32-byte seed and its Galois element (host) --
  * so that the a halves cost 32 bytes each. With PC_KEYSET_FULL the bundle also

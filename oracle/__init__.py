@@ -16,8 +16,8 @@ integers, written for a reader who checks it against the definitions:
                 product, ModDown, key switch (single, batched, hoisted),
                 key generation and the decryption check with its error bound.
 
-Source of the method: the Perseus README ('What's inside': half of every
-key-switching key is regenerated on the GPU from a ChaCha12 seed; 'Layout':
+Source of the method: the Perseus README ('What's inside': the GPU re-creates
+one half of each key-switching key from a ChaCha12 seed; 'Layout':
 the runtime's NTT and key-switching kernels) and the arXiv summary page of the
 Perseus paper (methodology item (i)). The pages do not spell out hybrid key
 switching itself; every step here is the textbook RNS-CKKS algorithm under

@@ -1,9 +1,9 @@
 """ChaCha block function and the key-half expander (oracle; test infrastructure only).
 
-The Perseus README ('What's inside') states that half of every key-switching
-key is regenerated on the GPU from a ChaCha12 seed instead of being stored;
-the arXiv summary page (methodology, item (i)) calls it a counter-mode
-expander. The pages fix neither the state layout nor how keystream words
+Per the Perseus README ('What's inside'), the GPU re-creates one of the two
+halves of each key-switching key from a ChaCha12 seed, so that half never
+sits in memory; the arXiv summary page (methodology, item (i)) describes the
+generator as ChaCha12 run in counter mode. The pages fix neither the state layout nor how keystream words
 become residues. Reading taken here:
 
 * state: the standard ChaCha layout -- four constant words spelling

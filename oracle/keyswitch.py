@@ -23,7 +23,7 @@ at level l (l active ciphertext primes) and a key with Galois element k
    rounding term).
 6. out0 += the automorphism of c0.
 
-Readings where the pages are silent (all listed in the design notes):
+Readings where the pages are silent:
 by default (partition 0) digits at level l have alpha(l) = ceil(l/dnum)
 primes each, D_d = [d*alpha, min((d+1)*alpha, l)), and the key is generated at
 level l; with partition 1 alpha = ceil(L/dnum) at every level, the digits are
