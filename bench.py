@@ -80,9 +80,9 @@ def parse():
     ap.add_argument("--long-steps", type=int, default=2000,
                     help="steps of the steady-state leg (batch 8, one stream, ~1 s of GPU time)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="per-leg budget of the oracle baseline (one core, then every core)")
-    ap.add_argument("--cpu-workers", type=int, default=0,
-                    help="processes of the all-core oracle leg (0: this process's CPU share, at most 16)")
+                    help="per-leg budget of the oracle baseline (one thread, then every thread)")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="OpenMP threads of the all-core oracle leg (0: this process's CPU share, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--buffers-gib", type=float, default=1.1, help="ciphertext buffer rotation size")
     ap.add_argument("--streams", type=int, default=3, choices=(1, 2, 3),
@@ -228,58 +228,58 @@ def _cpu_share():
     return max(1, min(n, 16))
 
 
-_ORACLE = {}
+def _o2_sample(O, w, ct, b, seed, threads, budget_s, max_calls=400):
+    """Key switches by the C++ oracle until the budget is used: (calls, seconds)."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        O.keyswitch(ct[n % len(ct)], w.L, 1, b, seed=seed, threads=threads, validate=False)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= max_calls:
+            return n, el
 
 
-def _oracle_setup(w):
+def _numpy_oracle_one_core(w, calls=2):
+    """The numpy oracle on one core, a few calls (context for the C++ figure)."""
     from oracle import keyswitch as ks
     oprm = ks.Params(w.log2n, w.L, w.dnum, w.K)
     beta = len(oprm.digits(w.L))
     key = ks.Key(b=ki.uniform_key_b(w.index, 0, beta, oprm.basis(w.L), w.N), seed=ki.key_seed(w.index, 0),
                  level=w.L, galois=1)
-    cts = ki.ciphertexts(w.index, oprm.q, w.N, 4)
-    ks.keyswitch(oprm, cts[0], key, w.L)  # warms the oracle's table caches (not timed)
-    _ORACLE.update(ks=ks, oprm=oprm, key=key, cts=cts, w=w)
+    cts = ki.ciphertexts(w.index, oprm.q, w.N, calls)
+    ks.keyswitch(oprm, cts[0], key, w.L)  # fills the oracle's table caches (not timed)
+    t0 = time.perf_counter()
+    for c in cts:
+        ks.keyswitch(oprm, c, key, w.L)
+    return calls / (time.perf_counter() - t0)
 
 
-def _oracle_worker(budget_s):
-    """Whole single-ciphertext key switches of the headline shape until the budget is
-    used; returns (key switches, seconds)."""
-    o = _ORACLE
-    n, t0 = 0, time.perf_counter()
-    while True:
-        o["ks"].keyswitch(o["oprm"], o["cts"][n % 4], o["key"], o["w"].L)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 400:
-            return n, el
-
-
-def cpu_baseline(w, budget_s, workers):
-    """The oracle as it stands (numpy, one thread per process) on a bounded sample of the
-    headline workload: single N=2^16, L=24 key switches with the same key shape, first in
-    this process on one core, then in `workers` processes at once (fork, before the GPU is
-    initialised). Rate = key switches per second of wall time."""
-    import multiprocessing as mp
-    _oracle_setup(w)
-    n1, t1 = _oracle_worker(budget_s)
-    one = n1 / t1
-    allc, nall, wall = None, 0, 0.0
-    if workers > 1:
-        with mp.get_context("fork").Pool(workers) as pool:
-            t0 = time.perf_counter()
-            res = pool.map(_oracle_worker, [budget_s] * workers)
-            wall = time.perf_counter() - t0
-        nall = sum(n for n, _ in res)
-        allc = sum(n / t for n, t in res)
-    cores = workers if allc is not None else 1
-    return {"value": round(allc if allc is not None else one, 4), "unit": "key switches/s", "cores": cores,
-            "kind": "oracle",
-            "sample": (f"{nall} single-ciphertext key switches (N=2^16, L=24, dnum=4, K=6, ChaCha12 a half) by "
-                       f"{workers} oracle processes at once in {wall:.1f} s; one core alone: {n1} in {t1:.1f} s"
-                       if allc is not None else
-                       f"{n1} single-ciphertext key switches (N=2^16, L=24, dnum=4, K=6) in {t1:.1f} s on one core"),
-            "one_core_value": round(one, 4), "cpu_model": _cpu_model(), "host_cpu_count": os.cpu_count()}
+def cpu_baseline(w, budget_s, threads):
+    """The C++ oracle tier as it stands (oracle/ks_o2.cpp: plain C++, every product a 64-bit
+    `%`, OpenMP over independent (digit, limb) items) on a bounded sample of the headline
+    workload: single-ciphertext N=2^16, L=24 key switches with the workload's key shape and a
+    ChaCha12-regenerated a half, first on one thread, then on `threads` threads, each leg until
+    its budget is used (at most 400 calls); then the numpy oracle on one core for two calls.
+    The clock brackets the key-switch calls only. Rate = key switches per second."""
+    from oracle import o2
+    O = o2.O2(w.log2n, w.L, w.dnum, w.K)
+    basis = O.primes[: w.L] + O.primes[w.L:]
+    alpha = -(-w.L // w.dnum)
+    beta = -(-w.L // alpha)
+    b = np.ascontiguousarray(ki.uniform_key_b(w.index, 0, beta, basis, w.N), dtype=np.uint32)
+    seed = ki.key_seed(w.index, 0)
+    ct = [np.ascontiguousarray(x, dtype=np.uint32) for x in ki.ciphertexts(w.index, O.primes[: w.L], w.N, 4)]
+    O.keyswitch(ct[0], w.L, 1, b, seed=seed, threads=threads)  # checks the inputs once (not timed)
+    n1, t1 = _o2_sample(O, w, ct, b, seed, 1, budget_s)
+    nall, tall = _o2_sample(O, w, ct, b, seed, threads, budget_s) if threads > 1 else (n1, t1)
+    O.close()
+    one, allc = n1 / t1, nall / tall
+    numpy_one = _numpy_oracle_one_core(w)
+    return {"value": round(allc, 4), "unit": "key switches/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{nall} single-ciphertext key switches (N=2^16, L=24, dnum=4, K=6, ChaCha12 a half) by the "
+                       f"C++ oracle tier on {threads} OpenMP threads in {tall:.1f} s; one thread: {n1} in {t1:.1f} s"),
+            "one_core_value": round(one, 4), "numpy_oracle_one_core_value": round(numpy_one, 4),
+            "cpu_model": _cpu_model(), "host_cpu_count": os.cpu_count()}
 
 
 def main():
@@ -289,10 +289,10 @@ def main():
               "(key switching shards by ciphertext batch; see the design notes).", file=sys.stderr)
         sys.exit(2)
     w = ki.WORKLOADS["n16"]
-    # the oracle baseline runs first: its worker processes fork before the GPU is touched
+    # the oracle baseline runs first, before the GPU is touched
     cpu = None
     if not args.no_cpu_baseline and args.only is None:
-        cpu = cpu_baseline(w, args.cpu_seconds, args.cpu_workers or _cpu_share())
+        cpu = cpu_baseline(w, args.cpu_seconds, args.cpu_threads or _cpu_share())
         print(f"[bench] cpu baseline: {cpu['value']} ks/s on {cpu['cores']} cores, {cpu['one_core_value']} on one",
               file=sys.stderr, flush=True)
 

@@ -16,6 +16,12 @@ integers, written for a reader who checks it against the definitions:
                 product, ModDown, key switch (single, batched, hoisted),
                 key generation and the decryption check with its error bound.
 
+A second tier, ``ks_o2.cpp`` (plain C++17 with OpenMP, loaded through
+``o2``), computes the same key switch from the same definitions with its own
+primes, roots, NTT and ChaCha, sharing no code with the numpy modules. The
+tests compare the two word for word, at small and full sizes; the benchmark
+times the C++ tier as its CPU baseline.
+
 Source of the method: the Perseus README ('What's inside': the GPU re-creates
 one half of each key-switching key from a ChaCha12 seed; 'Layout':
 the runtime's NTT and key-switching kernels) and the arXiv summary page of the
