@@ -131,6 +131,9 @@ def alg_bytes(kernel, N, level, K, alpha, beta, batch, nkeys=1, stored=False):
         "moddown_bconv": items * 2 * (K + l),
         "moddown_fwd_blk": items * 2 * (l + l + l) + items * l,  # tmp2 + acc in, out; c0 in
     }
+    # the fused block pass and inner product (one key of Galois element 1): the
+    # column-pass output and c1's own limbs in, the key once, acc out
+    table["modup_ip"] = (batch * (targets + l) + (2 if stored else 1) * beta * (l + K)) + items * 2 * (l + K)
     return table[kernel] * limb
 
 
@@ -162,6 +165,7 @@ def alg_ops(kernel, N, level, K, alpha, beta, batch, nkeys=1, stored=False):
         "moddown_bconv": items * 2 * l * (N * dot_ops(K) + col),
         "moddown_fwd_blk": items * 2 * l * (blk + N * (2 * OPS_ADDMOD + OPS_SHOUP)),
     }
+    table["modup_ip"] = table["modup_fwd_blk"] + table["inner_product"]
     return table[kernel]
 
 

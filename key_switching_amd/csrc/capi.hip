@@ -393,7 +393,7 @@ const char* const kKernelNames[KID_COUNT] = {
     "modup_inv_col",   "modup_bconv",     "modup_fwd_blk",   "inner_product",  "moddown_inv_blk",
     "moddown_inv_col", "moddown_bconv",   "moddown_fwd_blk", "chacha_expand",  "keygen",
     "tensor",          "rescale_gather",  "rescale_col",     "rescale_blk",    "bsgs_baby",
-    "bsgs_giant",      "seg_copy",        "moddown_rescale", "expand_key"};
+    "bsgs_giant",      "seg_copy",        "moddown_rescale", "expand_key",     "modup_ip"};
 
 static hipEvent_t prof_event(const pc_params* p) {
   if (p->prof_used == p->prof_pool.size()) {
@@ -429,9 +429,7 @@ hipError_t launch_keyswitch(const pc_params* p, const uint32_t* ct, uint64_t ct_
   // segment layout for gathers of single ciphertexts (hoisted keys); a batch
   // spreads its stores over more lines than the gathers save (measured slower)
   for (uint32_t k = 0; k < nkeys; ++k) ws.seg = ws.seg || (batch == 1 && keys[k].galois != 1u);
-  hipError_t e = launch_modup(p, ct, ct_stride, c1_off, batch, level, ws, s);
-  if (e != hipSuccess) return e;
-  e = launch_inner_product(p, ct, ct_stride, c1_off, batch, level, ws, keys, nkeys, s);
+  hipError_t e = launch_modup_ip(p, ct, ct_stride, c1_off, batch, level, ws, keys, nkeys, s);
   if (e != hipSuccess) return e;
   // with the segment layout (one ciphertext), the combine pass gathers c0 from
   // a segment-layout copy in y, which ModUp no longer needs
@@ -933,8 +931,7 @@ int pc_hmult(const pc_params* p, const uint32_t* ct_a, const uint32_t* ct_b, uin
   // R, whose other limbs are never written), and one pass per limb < l-1
   // finishes ModDown and the rescale together
   const KsWorkspace ws = ks_workspace_carve(p, c, level, batch, batch);
-  if (launch_modup(p, T, 3 * ln, (uint32_t)ln, batch, level, ws, s) != hipSuccess) return PC_EDEVICE;
-  if (launch_inner_product(p, T, 3 * ln, (uint32_t)ln, batch, level, ws, &key, 1, s) != hipSuccess) return PC_EDEVICE;
+  if (launch_modup_ip(p, T, 3 * ln, (uint32_t)ln, batch, level, ws, &key, 1, s) != hipSuccess) return PC_EDEVICE;
   if (launch_moddown(p, ws.acc, batch, 2, level, 1, R, ws, T, 3 * ln, batch, &one, s, false, level - 1) != hipSuccess)
     return PC_EDEVICE;
   if (launch_rescale(p, R, 2 * ln, (uint32_t)ln, T + 2 * ln, 3 * ln, batch, level, ws.y, R, out, s, false) !=

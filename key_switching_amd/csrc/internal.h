@@ -181,6 +181,7 @@ enum KernelId {
   KID_SEG_COPY,
   KID_MODDOWN_RESCALE,
   KID_EXPAND_KEY,
+  KID_MODUP_IP,
   KID_COUNT
 };
 extern const char* const kKernelNames[KID_COUNT];
@@ -198,8 +199,17 @@ struct LaunchTimer {
 // Launchers (return hipError_t of the last launch).
 hipError_t launch_ntt(const pc_params* p, uint32_t* data, uint32_t* tmp, const uint32_t* prime_idx, uint32_t nlimbs,
                       bool inverse, hipStream_t s);
+// fwd_blk = false stops after the conversion's column pass (tmp), for the fused
+// block pass and inner product.
 hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_offset, uint32_t batch,
-                        uint32_t level, const KsWorkspace& ws, hipStream_t s);
+                        uint32_t level, const KsWorkspace& ws, hipStream_t s, bool fwd_blk = true);
+// ModUp and the inner product of `batch` ciphertexts under `nkeys` keys (every
+// key on the same batch). One key of Galois element 1 takes the fused block
+// pass and inner product (no ext round trip through memory) when its key tile
+// fits a thread's budget; other calls run ModUp to ext and the inner product.
+hipError_t launch_modup_ip(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_offset,
+                           uint32_t batch, uint32_t level, const KsWorkspace& ws, const KeyRef* keys, uint32_t nkeys,
+                           hipStream_t s);
 // one_ct_per_key: key k switches its own `batch` ciphertexts, the k-th group
 // (ct + k batch ct_stride, ext of ModUp's items k batch .. k batch + batch - 1);
 // otherwise every key switches the same batch.

@@ -758,6 +758,229 @@ __global__ void __launch_bounds__(2 * kIpHalf) k_ip_regen(IPArgs A) {
 }
 
 // ---------------------------------------------------------------------------
+// ModUp's forward block pass fused with the inner product, for one key of
+// Galois element 1 (the relinearisation shape). With no automorphism the
+// inner product is pointwise, and a block-pass tile of columns [c0, c0 + CF)
+// covers the same positions (row bitrev(x) 2^LRC + column) for every digit and
+// item. A workgroup owns one tile of one limb j of the extended basis: it puts
+// the key's values at its positions on chip once (b in registers; a in
+// registers for the first AREG digits and in LDS for the others, regenerated
+// from ChaCha or read from the stored half), then for each batch item runs the
+// block pass of every digit's column-pass output (the digit that owns j reads
+// c1's limb instead), adds the products into 64-bit sums and stores only the
+// two accumulators. ext is neither stored nor read back.
+// ---------------------------------------------------------------------------
+struct ModUpIPArgs {
+  DevTables T;
+  const uint32_t* ct;  // c1 of batch item b at ct + b * ct_stride + c1_off
+  uint64_t ct_stride;
+  uint32_t c1_off;
+  const uint32_t* tmp;  // [batch][beta][l+K][N] ModUp after the column pass
+  uint32_t* acc;        // [batch][2][l+K][N]
+  const uint32_t* evk_b;  // [beta_key][key_level+K][N]
+  const uint32_t* evk_a;  // same shape, or nullptr: regenerated from seed
+  ChaChaKey seed;
+  int N, level, K, L, alpha, batch, key_level;
+};
+
+// Columns per fused tile: one ChaCha block (8 consecutive positions) per row.
+constexpr int kFusedCols = 8;
+// Key values a thread keeps per half (beta digits x its E positions): larger
+// shapes take the separate block pass and inner product.
+constexpr int kFusedKeyValues = 64;
+
+template <int LOGN>
+constexpr int fused_threads() {
+  return kFusedCols << (Cfg<LOGN>::LRB - Cfg<LOGN>::LEB);
+}
+// a-half digits kept in registers (the rest sit in LDS), and the waves per
+// SIMD the register budget is cut for: at N = 2^16 a 4-digit tile in 128
+// threads then takes 33 KB of LDS and at most 256 registers, so that four
+// workgroups share a CU and the 960 tiles of 30 limbs run in one wave of
+// workgroups
+template <int LOGN, int BETA>
+constexpr int fused_areg() {
+  return LOGN == 16 ? 1 : LOGN == 17 ? (BETA < 3 ? BETA : 3) : 0;
+}
+template <int LOGN>
+constexpr int fused_waves() {
+  return 2;
+}
+
+// Tile quads: the four tiles that share each row's 128-byte line run on one
+// XCD in consecutive slots (xcd_unit with 4 groups), so the 32-byte runs of
+// their loads and stores meet in that XCD's L2.
+template <int LOGN, int BETA, int ROUNDS, bool STORED>
+__global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_modup_ip(ModUpIPArgs A) {
+  using C = Cfg<LOGN>;
+  constexpr int LRC = C::LRC, LRB = C::LRB, LEB = C::LEB, CF = kFusedCols;
+  constexpr int E = 1 << LEB, TPB = 1 << (LRB - LEB), THREADS = CF * TPB, RB = LRB / LEB;
+  constexpr int AREG = fused_areg<LOGN, BETA>(), NS = BETA - AREG > 0 ? BETA - AREG : 1;
+  static_assert(CF == 8, "a tile row is one ChaCha block");
+  static_assert(((1 << LRC) / CF) % 4 == 0, "tiles group into quads");
+  using Lay = BlkLds<LRB, LEB>;
+  __shared__ uint32_t lds[Lay::words(CF)];
+  __shared__ uint32_t am_lds[NS][E][THREADS];  // [digit - AREG][slot][consumer thread]
+  const int tid = (int)threadIdx.x;
+  const int lk = A.level + A.K;
+  int quad, j, g;
+  if (!xcd_unit((1 << LRC) / CF / 4, lk, 4, quad, j, g)) return;
+  const int c0 = (quad * 4 + g) * CF;
+  // consumer layout (after the block pass's transpose): column c0 + kk, rows
+  // bitrev(rest + TPB m). rest fills the low LRB - LEB bits and TPB m the top
+  // LEB, so position m = pos0 + (bitrev(m, LEB) << LRC): one per-lane offset,
+  // and the constant goes into the uniform base (slot_of).
+  const int kk = tid % CF, rest = tid / CF;
+  const uint32_t pos0 = (bitrev((uint32_t)rest, LRB) << LRC) + (uint32_t)(c0 + kk);
+  auto slot_of = [](int m) { return (size_t)bitrev((uint32_t)m, LEB) << LRC; };
+  const size_t pj = j < A.level ? (size_t)j : (size_t)(A.L + j - A.level);
+  const uint32_t r = A.T.r[pj], rinv = A.T.rinv[pj];
+  const int kj = j < A.level ? j : A.key_level + (j - A.level);
+  const size_t kdig = (size_t)(A.key_level + A.K) * A.N;  // words per digit of the key
+
+  uint32_t am[AREG > 0 ? AREG : 1][E];
+  if constexpr (STORED) {
+#pragma unroll
+    for (int d = 0; d < BETA; ++d)
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        const uint32_t v = redc(at32(A.evk_a + d * kdig + (size_t)kj * A.N + slot_of(m), pos0), r, rinv);
+        if (d < AREG)
+          am[d < AREG ? d : 0][m] = v;
+        else
+          am_lds[d < AREG ? 0 : d - AREG][m][tid] = v;  // read back by this thread only
+      }
+  } else {
+    // row x of the tile (natural row bitrev(x)) is one ChaCha block per digit;
+    // thread i expands rows i + THREADS s and files value k under consumer
+    // thread (x mod TPB) CF + k, slot x / TPB
+    auto fill = [&](int d, int slot) {
+#pragma unroll
+      for (int s = 0; s < ((1 << LRB) + THREADS - 1) / THREADS; ++s) {
+        const int x = tid + THREADS * s;
+        if (x >= (1 << LRB)) break;
+        const int p = (int)(bitrev((uint32_t)x, LRB) << LRC) + c0;
+        uint32_t w[16];
+        chacha_block<ROUNDS>(A.seed, (uint32_t)(p >> 3), 0u, (uint32_t)d, (uint32_t)kj, w);
+        uint32_t v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = word_pair_to_mont(w[2 * k], w[2 * k + 1], r, rinv);
+        uint4* dst = reinterpret_cast<uint4*>(&am_lds[slot][x / TPB][(x % TPB) * CF]);
+        dst[0] = make_uint4(v[0], v[1], v[2], v[3]);
+        dst[1] = make_uint4(v[4], v[5], v[6], v[7]);
+        // one block at a time: interleaved ChaCha states would take every register
+        asm volatile("" ::: "memory");
+      }
+    };
+#pragma unroll
+    for (int d = 0; d < AREG; ++d) {
+      fill(d, 0);
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < E; ++m) am[d][m] = am_lds[0][m][tid];
+      __syncthreads();
+    }
+#pragma unroll
+    for (int d = AREG; d < BETA; ++d) fill(d, d - AREG);
+    __syncthreads();
+  }
+  // b after the a half, so that its loads are not held in registers across the
+  // ChaCha expansion
+  asm volatile("" ::: "memory");
+  uint32_t bm[BETA][E];
+#pragma unroll
+  for (int d = 0; d < BETA; ++d)
+#pragma unroll
+    for (int m = 0; m < E; ++m) bm[d][m] = redc(at32(A.evk_b + d * kdig + (size_t)kj * A.N + slot_of(m), pos0), r, rinv);
+
+  // block-pass layout: block k of the tile, thread t within it; the round-0
+  // input of slot m is word blk0 + TPB m of the limb
+  const int t = tid % TPB, k = tid / TPB;
+  const int B = (int)bitrev((uint32_t)(c0 + k), LRC);
+  const uint32_t blk0 = ((uint32_t)B << LRB) + (uint32_t)t;
+  // the block's twiddles (the same for every digit and item) are re-read per
+  // round from L1: held across the batch loop they would take 2^LEB - 1
+  // registers per round
+  const uint32_t* const tw = A.T.tw_fblk + pj * A.N;
+  auto twb = [B](int st) { return (B << LRB) + (1 << st); };  // block-major table
+  uint32_t* const lrow = lds + Lay::row(k);
+  // the transposed tile: slot m of this thread at row(kk) + col(rest) + m col(TPB)
+  // (col(x) adds x/16 or x/8, and TPB is a multiple of that divisor)
+  const uint32_t* const tcol = lds + Lay::row(kk) + Lay::col(rest);
+  constexpr int TSTEP = (1 << LRB) / E == TPB ? TPB + (Lay::SWZ ? TPB / 16 : Lay::SWZ9 ? TPB / 8 : 0) : 0;
+  static_assert(TSTEP > 0, "transposed slot stride");
+  const int own_d = j < A.level ? j / A.alpha : -1;  // the digit whose own limb is j
+  constexpr bool folded_last = BETA == 4 || (BETA > 4 && !(BETA & 1));
+#pragma unroll 1
+  for (int b = 0; b < A.batch; ++b) {
+    // the a values in LDS are re-read for every item (an opaque base keeps the
+    // compiler from hoisting them into registers across the batch loop)
+    int am_base = tid;
+    asm volatile("" : "+v"(am_base));
+    uint64_t s0[E], s1[E];
+#pragma unroll
+    for (int m = 0; m < E; ++m) s0[m] = s1[m] = 0;
+#pragma unroll
+    for (int d = 0; d < BETA; ++d) {
+      uint32_t e[E];
+      if (d == own_d) {
+        const uint32_t* c1 = A.ct + b * A.ct_stride + A.c1_off + (size_t)j * A.N;
+#pragma unroll
+        for (int m = 0; m < E; ++m) e[m] = at32(c1 + slot_of(m), pos0);
+      } else {
+        const uint32_t* src = A.tmp + (((size_t)b * BETA + d) * lk + j) * A.N;
+#pragma unroll
+        for (int m = 0; m < E; ++m) e[m] = at32(src, blk0 + (uint32_t)(TPB * m));
+        int zero = 0;
+        asm volatile("" : "+s"(zero));  // keeps the twiddle loads in the loop
+#pragma unroll
+        for (int rd = 0; rd < RB; ++rd) {
+          uint32_t W[E - 1];
+          load_round_tw<LRB, LEB, false>(rd, t, tw + zero, twb, W);
+          if (rd > 0) exchange<LRB, LEB, false, Lay, block_in_wave<LRB, LEB>()>(e, lrow, rd - 1, t);
+          ct_round_w<LEB>(e, W, r, rinv);
+        }
+#pragma unroll
+        for (int m = 0; m < E; ++m) lrow[Lay::col(elem_index<LRB, LEB, false>(RB - 1, t, m))] = e[m];
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < E; ++m) e[m] = tcol[TSTEP * m];
+        __syncthreads();
+      }
+      // the sums of dot_redc, one digit at a time: products below r 2^31, a
+      // fold after the fourth and after every further pair
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        uint32_t av = d < AREG ? am[d < AREG ? d : 0][m] : (&am_lds[d < AREG ? 0 : d - AREG][m][0])[am_base];
+        uint32_t bv = bm[d][m];
+        // 32-bit here: otherwise the compiler hoists their 64-bit extensions
+        // out of the batch loop, two registers per key value
+        asm volatile("" : "+v"(av), "+v"(bv));
+        s0[m] += mul_wide(e[m], bv);
+        s1[m] += mul_wide(e[m], av);
+        asm volatile("" : "+v"(s0[m]), "+v"(s1[m]));
+        if (d == 3 || (d > 3 && (d & 1))) {
+          s0[m] = fold_hi(s0[m], r);
+          s1[m] = fold_hi(s1[m], r);
+          asm volatile("" : "+v"(s0[m]), "+v"(s1[m]));
+        }
+      }
+    }
+    uint32_t* a0 = A.acc + (((size_t)b * 2 + 0) * lk + j) * A.N;
+    uint32_t* a1 = A.acc + (((size_t)b * 2 + 1) * lk + j) * A.N;
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      if constexpr (BETA > 2 && !folded_last) {
+        s0[m] = fold_hi(s0[m], r);
+        s1[m] = fold_hi(s1[m], r);
+      }
+      at32(a0 + slot_of(m), pos0) = redc(s0[m], r, rinv);
+      at32(a1 + slot_of(m), pos0) = redc(s1[m], r, rinv);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // ModDown
 // ---------------------------------------------------------------------------
 struct ModDownArgs {
@@ -1432,7 +1655,7 @@ hipError_t launch_ntt(const pc_params* p, uint32_t* data, uint32_t* tmp, const u
 }
 
 hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_offset, uint32_t batch,
-                        uint32_t level, const KsWorkspace& ws, hipStream_t s) {
+                        uint32_t level, const KsWorkspace& ws, hipStream_t s, bool fwd_blk) {
   ModUpArgs A;
   A.T = p->tabs;
   A.LT = p->ltabs;
@@ -1473,7 +1696,7 @@ hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stri
       else
         hipLaunchKernelGGL((k_modup_bconv<LN, CNT, kBconvGroup>), grid, dim3(col_threads<LN>()), 0, s, A);
     });
-    { LaunchTimer tm(p, KID_MODUP_FWD_BLK, s); hipLaunchKernelGGL(k_modup_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_ext), dim3(blk_threads<LN>()), 0, s, A); }
+    if (fwd_blk) { LaunchTimer tm(p, KID_MODUP_FWD_BLK, s); hipLaunchKernelGGL(k_modup_fwd_blk<LN>, dim3(blk_tiles<LN>(), rows_ext), dim3(blk_threads<LN>()), 0, s, A); }
   });
   return hipGetLastError();
 }
@@ -1645,6 +1868,62 @@ hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t
       default: return hipErrorInvalidValue;
     }
   }
+  return hipGetLastError();
+}
+
+template <int LN, int BETA>
+static void launch_modup_ip_kernel(const pc_params* p, const ModUpIPArgs& A, dim3 grid, hipStream_t s) {
+  if constexpr (BETA * (1 << Cfg<LN>::LEB) <= kFusedKeyValues) {
+    const dim3 block(fused_threads<LN>());
+    if (A.evk_a != nullptr)
+      hipLaunchKernelGGL((k_modup_ip<LN, BETA, 12, true>), grid, block, 0, s, A);
+    else if (p->chacha_rounds == 20)
+      hipLaunchKernelGGL((k_modup_ip<LN, BETA, 20, false>), grid, block, 0, s, A);
+    else
+      hipLaunchKernelGGL((k_modup_ip<LN, BETA, 12, false>), grid, block, 0, s, A);
+  }
+}
+
+hipError_t launch_modup_ip(const pc_params* p, const uint32_t* ct, uint64_t ct_stride, uint32_t c1_offset,
+                           uint32_t batch, uint32_t level, const KsWorkspace& ws, const KeyRef* keys, uint32_t nkeys,
+                           hipStream_t s) {
+  const int beta = beta_of(p, level);
+  const int per_thread = p->log2n == 16 ? 1 << Cfg<16>::LEB : p->log2n == 17 ? 1 << Cfg<17>::LEB : 1 << Cfg<12>::LEB;
+  const bool fused = nkeys == 1 && keys[0].galois == 1u && !ws.seg && beta * per_thread <= kFusedKeyValues;
+  hipError_t e = launch_modup(p, ct, ct_stride, c1_offset, batch, level, ws, s, !fused);
+  if (e != hipSuccess || !fused) return e != hipSuccess ? e : launch_inner_product(p, ct, ct_stride, c1_offset, batch,
+                                                                                   level, ws, keys, nkeys, s);
+  ModUpIPArgs A;
+  A.T = p->tabs;
+  A.ct = ct;
+  A.ct_stride = ct_stride;
+  A.c1_off = c1_offset;
+  A.tmp = ws.tmp;
+  A.acc = ws.acc;
+  A.evk_b = keys[0].b;
+  A.evk_a = keys[0].a;
+  for (int w = 0; w < 8; ++w) A.seed.k[w] = keys[0].seed[w];
+  A.N = (int)p->N;
+  A.level = (int)level;
+  A.K = (int)p->K;
+  A.L = (int)p->L;
+  A.alpha = alpha_of(p, level);
+  A.batch = (int)batch;
+  A.key_level = (int)key_level_of(p, level);
+  const int lk = (int)(level + p->K);
+  LaunchTimer tm(p, KID_MODUP_IP, s);
+  PC_DISPATCH_LOGN(p->log2n, {
+    const dim3 grid(xcd_grid((1 << Cfg<LN>::LRC) / kFusedCols / 4, lk, 4));
+    switch (beta) {
+      case 1: launch_modup_ip_kernel<LN, 1>(p, A, grid, s); break;
+      case 2: launch_modup_ip_kernel<LN, 2>(p, A, grid, s); break;
+      case 3: launch_modup_ip_kernel<LN, 3>(p, A, grid, s); break;
+      case 4: launch_modup_ip_kernel<LN, 4>(p, A, grid, s); break;
+      case 5: launch_modup_ip_kernel<LN, 5>(p, A, grid, s); break;
+      case 6: launch_modup_ip_kernel<LN, 6>(p, A, grid, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  });
   return hipGetLastError();
 }
 
