@@ -807,6 +807,22 @@ constexpr int fused_waves() {
   return 2;
 }
 
+// LDS layout of a fused tile (8 blocks): the block pass's padded rows, col(x) =
+// x + x/16 at N = 2^16, with row(k) = 272 k + 4 (k >> 1). The exchange's two
+// patterns put the blocks k, k + 1 of a half-wave 16 banks apart, as in the
+// pass's own layout, and the transposed read of x = rest + 16 m across the 8
+// blocks (4 rests per half-wave) starts the blocks on the 8 distinct multiples
+// of 4, so every access covers 32 distinct banks (the pass's own skew, k/2, is
+// made for 32 blocks and conflicts up to 4 ways here). Other shapes keep the
+// pass's layout.
+template <int LRB, int LEB>
+struct FusedLay : BlkLds<LRB, LEB> {
+  using Base = BlkLds<LRB, LEB>;
+  static constexpr bool K8 = Base::SWZ;
+  __device__ __forceinline__ static int row(int k) { return K8 ? k * Base::S + 4 * (k >> 1) : Base::row(k); }
+  static constexpr int words(int c) { return K8 ? c * Base::S + 4 * ((c - 1) >> 1) : Base::words(c); }
+};
+
 // Tile quads: the four tiles that share each row's 128-byte line run on one
 // XCD in consecutive slots (xcd_unit with 4 groups), so the 32-byte runs of
 // their loads and stores meet in that XCD's L2.
@@ -818,7 +834,7 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
   constexpr int AREG = fused_areg<LOGN, BETA>(), NS = BETA - AREG > 0 ? BETA - AREG : 1;
   static_assert(CF == 8, "a tile row is one ChaCha block");
   static_assert(((1 << LRC) / CF) % 4 == 0, "tiles group into quads");
-  using Lay = BlkLds<LRB, LEB>;
+  using Lay = FusedLay<LRB, LEB>;
   __shared__ uint32_t lds[Lay::words(CF)];
   __shared__ uint32_t am_lds[NS][E][THREADS];  // [digit - AREG][slot][consumer thread]
   const int tid = (int)threadIdx.x;

@@ -48,8 +48,8 @@ FAMILIES = {
     "modup_inv_blk": "k_modup_inv_blk<16>",
     "modup_inv_col": "k_modup_inv_col<16>",
     "modup_bconv": "k_modup_bconv<16, 6, 3>",
-    "modup_fwd_blk": "k_modup_fwd_blk<16>",
-    "inner_product": "k_ip_regen<4, 12, 8, false>",
+    # the relinearisation key (Galois element 1): block pass and inner product fused
+    "modup_ip": "k_modup_ip<16, 4, 12, false>",
     "moddown_inv_blk": "k_md_inv_blk<16>",
     "moddown_inv_col": "k_md_inv_col<16>",
     "moddown_bconv": "k_md_bconv<16, 6, 3>",
@@ -66,18 +66,19 @@ FAMILIES = {
 
 
 # the N=2^17, L=40 chain (bench.py --only n17): batch-8 launches, a half
-# regenerated or stored. Each chain call relinearises, then rotates. With a
-# regenerated half the two steps run different kernels (the rotation's
-# gathers take one workgroup per unit); with a stored half they run the same
-# kernel, whose dispatches then alternate between the two keys: a
-# (prefix, parity) entry takes every other dispatch in dispatch order.
+# regenerated or stored. Each chain call relinearises (the fused block pass
+# and inner product), then rotates (block pass to ext, then the gathering
+# inner product). A (prefix, parity) entry would take every other dispatch of
+# a kernel in dispatch order, for two steps that run the same kernel.
 FAMILIES_N17 = {
     "modup_bconv": "k_modup_bconv<17, 8, 3>",
-    "modup_fwd_blk": "k_modup_fwd_blk<17>",
-    "inner_product_chacha_relin": "k_ip_regen<5, 12, 8, false>",
+    # relinearisation step: the fused block pass and inner product; rotation
+    # step: the block pass to ext, then the gathering inner product
+    "modup_ip_chacha_relin": "k_modup_ip<17, 5, 12, false>",
+    "modup_ip_stored_relin": "k_modup_ip<17, 5, 12, true>",
+    "modup_fwd_blk_rotate": "k_modup_fwd_blk<17>",
     "inner_product_chacha_rotate": "k_inner_product<5, 12, false, 8, false>",
-    "inner_product_stored_relin": ("k_inner_product<5, 12, true, 8, false>", 0),
-    "inner_product_stored_rotate": ("k_inner_product<5, 12, true, 8, false>", 1),
+    "inner_product_stored_rotate": "k_inner_product<5, 12, true, 8, false>",
     "moddown_bconv": "k_md_bconv<17, 8, 3>",
     "moddown_fwd_blk_relin": "k_md_fwd_blk<17, 1, false>",
     "moddown_fwd_blk_rotate": "k_md_fwd_blk<17, 2, true>",
@@ -226,8 +227,9 @@ def read_valu_ratio(path: str, family: str):
 
 
 def read_ip_traffic(path: str):
-    """Inner-product traffic per batch-8 launch of the N=2^17 chain, regenerated and
-    stored a halves, from its traffic summary (None if absent or stale)."""
+    """Inner-product traffic per batch-8 launch of the N=2^17 chain (the fused launch
+    for the relinearisation step), regenerated and stored a halves, from its
+    traffic summary (None if absent or stale)."""
     if not os.path.exists(path):
         return None
     text = open(path).read().splitlines()
@@ -236,7 +238,7 @@ def read_ip_traffic(path: str):
     out = {}
     for line in text:
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
-        if len(cells) == 9 and cells[0].startswith("inner_product_"):
+        if len(cells) == 9 and cells[0].startswith(("inner_product_", "modup_ip_")):
             _, _, half, step = cells[0].split("_")
             out.setdefault(half, {})[step] = {"fetch": float(cells[6]), "write": float(cells[7]),
                                               "total": float(cells[8])}
@@ -280,7 +282,7 @@ def cmd_valu(a) -> str:
            "|---|---|---|---|---|---|---|---|---|---|---|"]
     N, L, K, alpha, beta, batch = 1 << 16, 24, 6, 6, 4, 8
     for fam, prefix in FAMILIES.items():
-        if fam not in bench.KERNELS:
+        if fam not in bench.KERNELS and fam != "modup_ip":
             continue
         ds = [d for d, m in meta.items() if m[0] == prefix]
         if not ds:
