@@ -20,6 +20,16 @@
 #include "internal.h"
 #include "ntt_pass.h"
 
+// The launchers fall into five groups (NTT and ModUp, inner product, fused
+// ModUp/inner product, ModDown, HMult/BSGS/keygen). Built with PC_PART = 1..5
+// this file holds one group, so that the groups compile in parallel and link
+// into one library; built without it, it holds all five.
+#ifdef PC_PART
+#define PC_IN_PART(n) (PC_PART == (n))
+#else
+#define PC_IN_PART(n) 1
+#endif
+
 namespace pc {
 
 // ---------------------------------------------------------------------------
@@ -1195,6 +1205,7 @@ struct TensorArgs {
 
 constexpr int kTensorThreads = 256;
 
+#if PC_IN_PART(5)
 __global__ void __launch_bounds__(kTensorThreads) k_tensor(TensorArgs A) {
   constexpr int TILE = 8 * kTensorThreads;
   const int i = blockIdx.y;
@@ -1221,6 +1232,7 @@ __global__ void __launch_bounds__(kTensorThreads) k_tensor(TensorArgs A) {
   store8(dz + A.d_off[1], p0, p1, d1);
   store8(dz + A.d_off[2], p0, p1, d2);
 }
+#endif
 
 // Rescale by the last prime q_l' (l' = level - 1) of 2*batch polynomials:
 // out_i = (c_i - NTT_i([x]_{q_l'} mod q_i)) q_l'^-1 mod q_i for i < l', with x
@@ -1247,6 +1259,7 @@ struct RescaleArgs {
 // x[u] = limb l' of polynomial u (plus the addend's limb l' on odd u).
 constexpr int kGatherThreads = 256;
 
+#if PC_IN_PART(5)
 __global__ void __launch_bounds__(kGatherThreads) k_rs_gather(RescaleArgs A) {
   const size_t u = blockIdx.y, b = u >> 1, v = u & 1;
   const int pos = 4 * ((int)blockIdx.x * kGatherThreads + (int)threadIdx.x);
@@ -1262,6 +1275,7 @@ __global__ void __launch_bounds__(kGatherThreads) k_rs_gather(RescaleArgs A) {
   }
   *reinterpret_cast<uint4*>(A.x_out + u * A.N + pos) = w;
 }
+#endif
 
 struct RescaleSrcLimb {
   uint32_t r, rinv;
@@ -1526,6 +1540,7 @@ __global__ void __launch_bounds__(kBsgsThreads) k_bsgs_baby(BsgsArgs A) {
 }
 
 // acc = inner_0 + sum_{j>=1} (phi_{G_j}(inner_j,0) on the first component + 2^64 accg_j)
+#if PC_IN_PART(5)
 __global__ void __launch_bounds__(kBsgsThreads) k_bsgs_giant(BsgsArgs A) {
   const int lk = A.level + A.K;
   int tile = (int)blockIdx.x, t = (int)blockIdx.y, one = 0;
@@ -1554,6 +1569,7 @@ __global__ void __launch_bounds__(kBsgsThreads) k_bsgs_giant(BsgsArgs A) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) store4(A.accqp + ((size_t)u * lk + t) * N, pos, o[u]);
 }
+#endif
 
 // ---------------------------------------------------------------------------
 // key generation: b_d[j] = -a_d[j] s[j] + e_d[j] + g_{d,j} s'[j] (mod r_j)
@@ -1647,6 +1663,7 @@ __global__ void __launch_bounds__(256) k_keygen(KeygenArgs A) {
   }
 static_assert(kMaxAlpha == 8 && kMaxSpecial == 8, "PC_DISPATCH_CNT covers 1..8");
 
+#if PC_IN_PART(1)
 hipError_t launch_ntt(const pc_params* p, uint32_t* data, uint32_t* tmp, const uint32_t* prime_idx, uint32_t nlimbs,
                       bool inverse, hipStream_t s) {
   for (uint32_t base = 0; base < nlimbs; base += kMaxLimbsPerLaunch) {
@@ -1717,6 +1734,7 @@ hipError_t launch_modup(const pc_params* p, const uint32_t* ct, uint64_t ct_stri
   return hipGetLastError();
 }
 
+#endif
 // Workgroups of `kernel` resident on the current device at once, cached per
 // (kernel, device) in a fixed table (no allocation after the first lookup).
 template <class F>
@@ -1747,7 +1765,7 @@ static uint32_t resident_workgroups(F kernel, int threads) {
 // Split of limb_xcd_decode for `limbs` limbs of `tiles` tiles: the smallest of
 // 1, 2, 4, 8 (dividing tiles) whose padding to a multiple of 8 parts costs at
 // most 7%, else the one with the least padding.
-static int xcd_split(uint32_t limbs, uint32_t tiles) {
+[[maybe_unused]] static int xcd_split(uint32_t limbs, uint32_t tiles) {
   int best = 1;
   double best_pad = 1e9;
   for (uint32_t sp = 1; sp <= 8 && sp <= tiles; sp *= 2) {
@@ -1763,10 +1781,11 @@ static int xcd_split(uint32_t limbs, uint32_t tiles) {
   return best;
 }
 
-static uint32_t blk_tiles_of(uint32_t log2n) {
+[[maybe_unused]] static uint32_t blk_tiles_of(uint32_t log2n) {
   return log2n == 12 ? (uint32_t)blk_tiles<12>() : log2n == 16 ? (uint32_t)blk_tiles<16>() : (uint32_t)blk_tiles<17>();
 }
 
+#if PC_IN_PART(2)
 template <int BETA, int ROUNDS, int BT>
 static void launch_ip_regen(const pc_params* p, const IPArgs& A0, bool seg, hipStream_t s) {
   auto kern = seg ? k_ip_regen<BETA, ROUNDS, BT, true> : k_ip_regen<BETA, ROUNDS, BT, false>;
@@ -1887,6 +1906,8 @@ hipError_t launch_inner_product(const pc_params* p, const uint32_t* ct, uint64_t
   return hipGetLastError();
 }
 
+#endif
+#if PC_IN_PART(3)
 template <int LN, int BETA>
 static void launch_modup_ip_kernel(const pc_params* p, const ModUpIPArgs& A, dim3 grid, hipStream_t s) {
   if constexpr (BETA * (1 << Cfg<LN>::LEB) <= kFusedKeyValues) {
@@ -1943,12 +1964,14 @@ hipError_t launch_modup_ip(const pc_params* p, const uint32_t* ct, uint64_t ct_s
   return hipGetLastError();
 }
 
+#endif
 // Fetch the side inputs of a combining block pass after the transform when the
 // grid has at least 8 polynomials of rows (measured: ModDown combine of 8 key
 // switches 87 -> 84 us, rescale of 8 products 96 -> 83 us); smaller grids and
 // gathers keep the early fetch, which hides their latency better.
-static bool late_fetch(uint32_t polys) { return polys >= 8; }
+[[maybe_unused]] static bool late_fetch(uint32_t polys) { return polys >= 8; }
 
+#if PC_IN_PART(4)
 hipError_t launch_seg_copy(const pc_params* p, const uint32_t* src, uint32_t limbs, uint32_t* dst, hipStream_t s) {
   SegCopyArgs A;
   A.src = src;
@@ -2041,6 +2064,8 @@ hipError_t launch_moddown(const pc_params* p, const uint32_t* acc, uint32_t item
   return hipGetLastError();
 }
 
+#endif
+#if PC_IN_PART(5)
 hipError_t launch_tensor(const pc_params* p, const uint32_t* a, uint64_t a_stride, const uint32_t* b,
                          uint64_t b_stride, uint32_t batch, uint32_t level, uint32_t* d, uint64_t d_stride,
                          const uint64_t d_off[3], hipStream_t s) {
@@ -2290,4 +2315,5 @@ hipError_t launch_expand_key(const pc_params* p, const uint32_t seed[8], uint32_
   return hipGetLastError();
 }
 
+#endif
 }  // namespace pc
