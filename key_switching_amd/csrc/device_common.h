@@ -49,6 +49,21 @@ __device__ __forceinline__ uint32_t redc(uint64_t x, uint32_t r, uint32_t rinv_n
 
 __device__ __forceinline__ uint64_t mul_wide(uint32_t a, uint32_t b) { return (uint64_t)a * b; }
 
+// acc = a b (first) and acc += a b (mac): one 32 x 32 + 64 -> 64 multiply-add
+// each, written as the instruction itself so that the compiler cannot widen
+// the operands to 64 bits ahead of a loop (a register pair per kept operand).
+// The carry-out goes to a scratch scalar pair; the caller keeps acc + a b below
+// 2^64.
+__device__ __forceinline__ uint64_t mul_wide_op(uint32_t a, uint32_t b) {
+  uint64_t acc, cc;
+  asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(acc), "=s"(cc) : "v"(a), "v"(b));
+  return acc;
+}
+__device__ __forceinline__ void mac_wide_op(uint64_t& acc, uint32_t a, uint32_t b) {
+  uint64_t cc;
+  asm("v_mad_u64_u32 %0, %1, %2, %3, %0" : "+v"(acc), "=s"(cc) : "v"(a), "v"(b));
+}
+
 // base[idx] addressed through a 32-bit byte offset (idx < 2^30): the compiler
 // can then use a uniform 64-bit base plus a 32-bit per-lane offset instead of
 // a full 64-bit address per lane.

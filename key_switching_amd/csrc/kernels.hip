@@ -937,6 +937,26 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
   static_assert(TSTEP > 0, "transposed slot stride");
   const int own_d = j < A.level ? j / A.alpha : -1;  // the digit whose own limb is j
   constexpr bool folded_last = BETA == 4 || (BETA > 4 && !(BETA & 1));
+  // the next digit's inputs are loaded one step ahead, into en: c1's limb j at
+  // the consumer positions for the digit that owns j, else the column-pass
+  // output at the block pass's round-0 positions. A digit's loads are issued
+  // after the last twiddle loads of the step before, so that waiting for
+  // those twiddles (the counter of outstanding loads is in order) never waits
+  // for them; they land while that step finishes its butterflies, transpose
+  // and products.
+  auto issue = [&](int bn, int dn, uint32_t (&x)[E]) {
+    if (dn == own_d) {
+      const uint32_t* c1 = A.ct + bn * A.ct_stride + A.c1_off + (size_t)j * A.N;
+#pragma unroll
+      for (int m = 0; m < E; ++m) x[m] = at32(c1 + slot_of(m), pos0);
+    } else {
+      const uint32_t* src = A.tmp + (((size_t)bn * BETA + dn) * lk + j) * A.N;
+#pragma unroll
+      for (int m = 0; m < E; ++m) x[m] = at32(src, blk0 + (uint32_t)(TPB * m));
+    }
+  };
+  uint32_t en[E];
+  issue(0, 0, en);
 #pragma unroll 1
   for (int b = 0; b < A.batch; ++b) {
     // the a values in LDS are re-read for every item (an opaque base keeps the
@@ -945,24 +965,21 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
     asm volatile("" : "+v"(am_base));
     uint64_t s0[E], s1[E];
 #pragma unroll
-    for (int m = 0; m < E; ++m) s0[m] = s1[m] = 0;
-#pragma unroll
     for (int d = 0; d < BETA; ++d) {
+      const int bn = d + 1 < BETA ? b : b + 1, dn = d + 1 < BETA ? d + 1 : 0;
       uint32_t e[E];
+#pragma unroll
+      for (int m = 0; m < E; ++m) e[m] = en[m];
       if (d == own_d) {
-        const uint32_t* c1 = A.ct + b * A.ct_stride + A.c1_off + (size_t)j * A.N;
-#pragma unroll
-        for (int m = 0; m < E; ++m) e[m] = at32(c1 + slot_of(m), pos0);
+        if (bn < A.batch) issue(bn, dn, en);
       } else {
-        const uint32_t* src = A.tmp + (((size_t)b * BETA + d) * lk + j) * A.N;
-#pragma unroll
-        for (int m = 0; m < E; ++m) e[m] = at32(src, blk0 + (uint32_t)(TPB * m));
         int zero = 0;
         asm volatile("" : "+s"(zero));  // keeps the twiddle loads in the loop
 #pragma unroll
         for (int rd = 0; rd < RB; ++rd) {
           uint32_t W[E - 1];
           load_round_tw<LRB, LEB, false>(rd, t, tw + zero, twb, W);
+          if (rd == RB - 1 && bn < A.batch) issue(bn, dn, en);
           if (rd > 0) exchange<LRB, LEB, false, Lay, block_in_wave<LRB, LEB>()>(e, lrow, rd - 1, t);
           ct_round_w<LEB>(e, W, r, rinv);
         }
@@ -977,18 +994,17 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
       // fold after the fourth and after every further pair
 #pragma unroll
       for (int m = 0; m < E; ++m) {
-        uint32_t av = d < AREG ? am[d < AREG ? d : 0][m] : (&am_lds[d < AREG ? 0 : d - AREG][m][0])[am_base];
-        uint32_t bv = bm[d][m];
-        // 32-bit here: otherwise the compiler hoists their 64-bit extensions
-        // out of the batch loop, two registers per key value
-        asm volatile("" : "+v"(av), "+v"(bv));
-        s0[m] += mul_wide(e[m], bv);
-        s1[m] += mul_wide(e[m], av);
-        asm volatile("" : "+v"(s0[m]), "+v"(s1[m]));
+        const uint32_t av = d < AREG ? am[d < AREG ? d : 0][m] : (&am_lds[d < AREG ? 0 : d - AREG][m][0])[am_base];
+        if (d == 0) {
+          s0[m] = mul_wide_op(e[m], bm[d][m]);
+          s1[m] = mul_wide_op(e[m], av);
+        } else {
+          mac_wide_op(s0[m], e[m], bm[d][m]);
+          mac_wide_op(s1[m], e[m], av);
+        }
         if (d == 3 || (d > 3 && (d & 1))) {
           s0[m] = fold_hi(s0[m], r);
           s1[m] = fold_hi(s1[m], r);
-          asm volatile("" : "+v"(s0[m]), "+v"(s1[m]));
         }
       }
     }
