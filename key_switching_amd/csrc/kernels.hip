@@ -847,6 +847,13 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
   using Lay = FusedLay<LRB, LEB>;
   __shared__ uint32_t lds[Lay::words(CF)];
   __shared__ uint32_t am_lds[NS][E][THREADS];  // [digit - AREG][slot][consumer thread]
+  // 256-point blocks of 16 words per thread (N = 2^16): the tile's twiddles
+  // sit on chip for the whole batch (TWW words per block in twl, the rest in
+  // registers), so the loop reads them with short LDS latency and its only
+  // global loads are the inputs that are prefetched a step ahead
+  constexpr bool TWL = LRB == 8 && LEB == 4;
+  constexpr int TWW = 16 + 64 + 128;
+  __shared__ __align__(16) uint32_t twl[TWL ? CF * TWW : 4];
   const int tid = (int)threadIdx.x;
   const int lk = A.level + A.K;
   int quad, j, g;
@@ -864,6 +871,30 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
   const int kj = j < A.level ? j : A.key_level + (j - A.level);
   const size_t kdig = (size_t)(A.key_level + A.K) * A.N;  // words per digit of the key
 
+  // twl, block kb of the tile (natural block bitrev(c0 + kb)): words 0..14 are
+  // round 0's entries 1..15 (one run shared by the block's 16 threads, word 15
+  // a pad), words 16 + 4t .. 19 + 4t stage 2 of round 1 (entries 64 + 4t ..),
+  // and words 80 + 64u + 4t .. 83 + 64u + 4t stage 3 of round 1 (entries
+  // 128 + 8t + 4u ..), so that 8 consecutive threads' 16-byte reads cover 32
+  // banks. Stages 0 and 1 of round 1 (3 entries per thread) stay in registers.
+  if constexpr (TWL) {
+    const uint32_t* twp = A.T.tw_fblk + pj * A.N;
+    for (int w = tid; w < CF * TWW; w += THREADS) {
+      const int kb = w / TWW, o = w % TWW;
+      const uint32_t Bk = bitrev((uint32_t)(c0 + kb), LRC);
+      int ent;
+      if (o < 16)
+        ent = o < 15 ? 1 + o : 1;
+      else if (o < 80)
+        ent = 64 + (o - 16);
+      else {
+        const int q = o - 80;
+        ent = 128 + 8 * ((q % 64) / 4) + 4 * (q / 64) + (q % 4);
+      }
+      twl[w] = twp[(Bk << LRB) + (uint32_t)ent];
+    }
+  }
+
   uint32_t am[AREG > 0 ? AREG : 1][E];
   if constexpr (STORED) {
 #pragma unroll
@@ -876,6 +907,7 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
         else
           am_lds[d < AREG ? 0 : d - AREG][m][tid] = v;  // read back by this thread only
       }
+    if constexpr (TWL) __syncthreads();  // twl is filled by every thread
   } else {
     // row x of the tile (natural row bitrev(x)) is one ChaCha block per digit;
     // thread i expands rows i + THREADS s and files value k under consumer
@@ -929,6 +961,36 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
   // registers per round
   const uint32_t* const tw = A.T.tw_fblk + pj * A.N;
   auto twb = [B](int st) { return (B << LRB) + (1 << st); };  // block-major table
+  uint32_t w10 = 0, w11a = 0, w11b = 0;  // round 1, stages 0 and 1 (twl layout)
+  if constexpr (TWL) {
+    w10 = tw[twb(4) + t];
+    w11a = tw[twb(5) + 2 * t];
+    w11b = tw[twb(5) + 2 * t + 1];
+  }
+  const uint32_t* const tblk = twl + (TWL ? k * TWW : 0);
+  auto lds_round_tw = [&](int rd, uint32_t (&W)[E - 1]) {
+    auto q4 = [](const uint32_t* p, uint32_t* w) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p);
+      w[0] = x.x;
+      w[1] = x.y;
+      w[2] = x.z;
+      w[3] = x.w;
+    };
+    if (rd == 0) {
+      uint32_t w[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q4(tblk + 4 * i, w + 4 * i);
+#pragma unroll
+      for (int i = 0; i < E - 1; ++i) W[i] = w[i];
+    } else {
+      W[0] = w10;
+      W[1] = w11a;
+      W[2] = w11b;
+      q4(tblk + 16 + 4 * t, W + 3);
+      q4(tblk + 80 + 4 * t, W + 7);
+      q4(tblk + 144 + 4 * t, W + 11);
+    }
+  };
   uint32_t* const lrow = lds + Lay::row(k);
   // the transposed tile: slot m of this thread at row(kk) + col(rest) + m col(TPB)
   // (col(x) adds x/16 or x/8, and TPB is a multiple of that divisor)
@@ -939,21 +1001,20 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
   constexpr bool folded_last = BETA == 4 || (BETA > 4 && !(BETA & 1));
   // the next digit's inputs are loaded one step ahead, into en: c1's limb j at
   // the consumer positions for the digit that owns j, else the column-pass
-  // output at the block pass's round-0 positions. A digit's loads are issued
-  // after the last twiddle loads of the step before, so that waiting for
-  // those twiddles (the counter of outstanding loads is in order) never waits
-  // for them; they land while that step finishes its butterflies, transpose
-  // and products.
+  // output at the block pass's round-0 positions. With the twiddles on chip
+  // they are issued at the top of the step before; otherwise after that
+  // step's last twiddle loads, so that waiting for those twiddles (the counter
+  // of outstanding loads is in order) never waits for them.
+  // Both patterns are one uniform base, one per-lane offset and a uniform step
+  // per slot, selected without a branch: straight-line loads keep the
+  // compiler's wait counts exact.
   auto issue = [&](int bn, int dn, uint32_t (&x)[E]) {
-    if (dn == own_d) {
-      const uint32_t* c1 = A.ct + bn * A.ct_stride + A.c1_off + (size_t)j * A.N;
+    const bool own = dn == own_d;
+    const uint32_t* base = own ? A.ct + bn * A.ct_stride + A.c1_off + (size_t)j * A.N
+                               : A.tmp + (((size_t)bn * BETA + dn) * lk + j) * A.N;
+    const uint32_t lane = own ? pos0 : blk0;
 #pragma unroll
-      for (int m = 0; m < E; ++m) x[m] = at32(c1 + slot_of(m), pos0);
-    } else {
-      const uint32_t* src = A.tmp + (((size_t)bn * BETA + dn) * lk + j) * A.N;
-#pragma unroll
-      for (int m = 0; m < E; ++m) x[m] = at32(src, blk0 + (uint32_t)(TPB * m));
-    }
+    for (int m = 0; m < E; ++m) x[m] = at32(base, lane + (own ? (uint32_t)slot_of(m) : (uint32_t)(TPB * m)));
   };
   uint32_t en[E];
   issue(0, 0, en);
@@ -970,16 +1031,22 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
       uint32_t e[E];
 #pragma unroll
       for (int m = 0; m < E; ++m) e[m] = en[m];
-      if (d == own_d) {
+      if (d == own_d || TWL) {
         if (bn < A.batch) issue(bn, dn, en);
-      } else {
+        // keeps the compiler from sinking the loads towards their use
+        asm volatile("" ::: "memory");
+      }
+      if (d != own_d) {
         int zero = 0;
         asm volatile("" : "+s"(zero));  // keeps the twiddle loads in the loop
 #pragma unroll
         for (int rd = 0; rd < RB; ++rd) {
           uint32_t W[E - 1];
-          load_round_tw<LRB, LEB, false>(rd, t, tw + zero, twb, W);
-          if (rd == RB - 1 && bn < A.batch) issue(bn, dn, en);
+          if constexpr (TWL)
+            lds_round_tw(rd, W);
+          else
+            load_round_tw<LRB, LEB, false>(rd, t, tw + zero, twb, W);
+          if (!TWL && rd == RB - 1 && bn < A.batch) issue(bn, dn, en);
           if (rd > 0) exchange<LRB, LEB, false, Lay, block_in_wave<LRB, LEB>()>(e, lrow, rd - 1, t);
           ct_round_w<LEB>(e, W, r, rinv);
         }
