@@ -877,11 +877,17 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
   // and words 80 + 64u + 4t .. 83 + 64u + 4t stage 3 of round 1 (entries
   // 128 + 8t + 4u ..), so that 8 consecutive threads' 16-byte reads cover 32
   // banks. Stages 0 and 1 of round 1 (3 entries per thread) stay in registers.
+  // Thread tid fetches words tid + THREADS i; they are stored after the a half
+  // is expanded, so that the fetches run under the expansion.
+  constexpr int TWN = TWL ? (CF * TWW + THREADS - 1) / THREADS : 1;
+  uint32_t twv[TWN];
   if constexpr (TWL) {
     const uint32_t* twp = A.T.tw_fblk + pj * A.N;
-    for (int w = tid; w < CF * TWW; w += THREADS) {
+#pragma unroll
+    for (int i = 0; i < TWN; ++i) {
+      const int w = tid + THREADS * i;
       const int kb = w / TWW, o = w % TWW;
-      const uint32_t Bk = bitrev((uint32_t)(c0 + kb), LRC);
+      const uint32_t Bk = bitrev((uint32_t)(c0 + (w < CF * TWW ? kb : 0)), LRC);
       int ent;
       if (o < 16)
         ent = o < 15 ? 1 + o : 1;
@@ -891,74 +897,30 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
         const int q = o - 80;
         ent = 128 + 8 * ((q % 64) / 4) + 4 * (q / 64) + (q % 4);
       }
-      twl[w] = twp[(Bk << LRB) + (uint32_t)ent];
+      twv[i] = twp[(Bk << LRB) + (uint32_t)ent];
     }
   }
 
-  uint32_t am[AREG > 0 ? AREG : 1][E];
-  if constexpr (STORED) {
+  // b's raw words (reduced once the a half is on chip) and the first step's
+  // inputs: fetched before the a half is expanded where the registers allow
+  // (EARLY), so that they arrive under the expansion; otherwise after it
+  constexpr bool EARLY = TWL && !STORED;
+  uint32_t bm[BETA][E];
+  auto fetch_b = [&]() {
 #pragma unroll
     for (int d = 0; d < BETA; ++d)
 #pragma unroll
-      for (int m = 0; m < E; ++m) {
-        const uint32_t v = redc(at32(A.evk_a + d * kdig + (size_t)kj * A.N + slot_of(m), pos0), r, rinv);
-        if (d < AREG)
-          am[d < AREG ? d : 0][m] = v;
-        else
-          am_lds[d < AREG ? 0 : d - AREG][m][tid] = v;  // read back by this thread only
-      }
-    if constexpr (TWL) __syncthreads();  // twl is filled by every thread
-  } else {
-    // row x of the tile (natural row bitrev(x)) is one ChaCha block per digit;
-    // thread i expands rows i + THREADS s and files value k under consumer
-    // thread (x mod TPB) CF + k, slot x / TPB
-    auto fill = [&](int d, int slot) {
-#pragma unroll
-      for (int s = 0; s < ((1 << LRB) + THREADS - 1) / THREADS; ++s) {
-        const int x = tid + THREADS * s;
-        if (x >= (1 << LRB)) break;
-        const int p = (int)(bitrev((uint32_t)x, LRB) << LRC) + c0;
-        uint32_t w[16];
-        chacha_block<ROUNDS>(A.seed, (uint32_t)(p >> 3), 0u, (uint32_t)d, (uint32_t)kj, w);
-        uint32_t v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = word_pair_to_mont(w[2 * k], w[2 * k + 1], r, rinv);
-        uint4* dst = reinterpret_cast<uint4*>(&am_lds[slot][x / TPB][(x % TPB) * CF]);
-        dst[0] = make_uint4(v[0], v[1], v[2], v[3]);
-        dst[1] = make_uint4(v[4], v[5], v[6], v[7]);
-        // one block at a time: interleaved ChaCha states would take every register
-        asm volatile("" ::: "memory");
-      }
-    };
-#pragma unroll
-    for (int d = 0; d < AREG; ++d) {
-      fill(d, 0);
-      __syncthreads();
-#pragma unroll
-      for (int m = 0; m < E; ++m) am[d][m] = am_lds[0][m][tid];
-      __syncthreads();
-    }
-#pragma unroll
-    for (int d = AREG; d < BETA; ++d) fill(d, d - AREG);
-    __syncthreads();
-  }
-  // b after the a half, so that its loads are not held in registers across the
-  // ChaCha expansion
-  asm volatile("" ::: "memory");
-  uint32_t bm[BETA][E];
-#pragma unroll
-  for (int d = 0; d < BETA; ++d)
-#pragma unroll
-    for (int m = 0; m < E; ++m) bm[d][m] = redc(at32(A.evk_b + d * kdig + (size_t)kj * A.N + slot_of(m), pos0), r, rinv);
+      for (int m = 0; m < E; ++m) bm[d][m] = at32(A.evk_b + d * kdig + (size_t)kj * A.N + slot_of(m), pos0);
+  };
 
   // block-pass layout: block k of the tile, thread t within it; the round-0
   // input of slot m is word blk0 + TPB m of the limb
   const int t = tid % TPB, k = tid / TPB;
   const int B = (int)bitrev((uint32_t)(c0 + k), LRC);
   const uint32_t blk0 = ((uint32_t)B << LRB) + (uint32_t)t;
-  // the block's twiddles (the same for every digit and item) are re-read per
-  // round from L1: held across the batch loop they would take 2^LEB - 1
-  // registers per round
+  // the block's twiddles are the same for every digit and item; shapes other
+  // than TWL re-read them per round from L1 (held across the batch loop they
+  // would take 2^LEB - 1 registers per round)
   const uint32_t* const tw = A.T.tw_fblk + pj * A.N;
   auto twb = [B](int st) { return (B << LRB) + (1 << st); };  // block-major table
   uint32_t w10 = 0, w11a = 0, w11b = 0;  // round 1, stages 0 and 1 (twl layout)
@@ -1005,19 +967,100 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
   // they are issued at the top of the step before; otherwise after that
   // step's last twiddle loads, so that waiting for those twiddles (the counter
   // of outstanding loads is in order) never waits for them.
-  // Both patterns are one uniform base, one per-lane offset and a uniform step
-  // per slot, selected without a branch: straight-line loads keep the
-  // compiler's wait counts exact.
+  // With TWL both patterns are one uniform base, one per-lane offset and a
+  // uniform step per slot, selected without a branch: straight-line loads keep
+  // the compiler's wait counts exact, so that they stay in flight. The other
+  // shapes branch, which takes fewer registers.
   auto issue = [&](int bn, int dn, uint32_t (&x)[E]) {
     const bool own = dn == own_d;
-    const uint32_t* base = own ? A.ct + bn * A.ct_stride + A.c1_off + (size_t)j * A.N
-                               : A.tmp + (((size_t)bn * BETA + dn) * lk + j) * A.N;
-    const uint32_t lane = own ? pos0 : blk0;
+    if constexpr (TWL) {
+      const uint32_t* base = own ? A.ct + bn * A.ct_stride + A.c1_off + (size_t)j * A.N
+                                 : A.tmp + (((size_t)bn * BETA + dn) * lk + j) * A.N;
+      const uint32_t lane = own ? pos0 : blk0;
 #pragma unroll
-    for (int m = 0; m < E; ++m) x[m] = at32(base, lane + (own ? (uint32_t)slot_of(m) : (uint32_t)(TPB * m)));
+      for (int m = 0; m < E; ++m) x[m] = at32(base, lane + (own ? (uint32_t)slot_of(m) : (uint32_t)(TPB * m)));
+    } else if (own) {
+      const uint32_t* c1 = A.ct + bn * A.ct_stride + A.c1_off + (size_t)j * A.N;
+#pragma unroll
+      for (int m = 0; m < E; ++m) x[m] = at32(c1 + slot_of(m), pos0);
+    } else {
+      const uint32_t* src = A.tmp + (((size_t)bn * BETA + dn) * lk + j) * A.N;
+#pragma unroll
+      for (int m = 0; m < E; ++m) x[m] = at32(src, blk0 + (uint32_t)(TPB * m));
+    }
   };
   uint32_t en[E];
-  issue(0, 0, en);
+  if constexpr (EARLY) {
+    fetch_b();
+    issue(0, 0, en);
+    // keeps the compiler from sinking these fetches below the expansion
+    asm volatile("" ::: "memory");
+  }
+
+  uint32_t am[AREG > 0 ? AREG : 1][E];
+  if constexpr (STORED) {
+#pragma unroll
+    for (int d = 0; d < BETA; ++d)
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        const uint32_t v = redc(at32(A.evk_a + d * kdig + (size_t)kj * A.N + slot_of(m), pos0), r, rinv);
+        if (d < AREG)
+          am[d < AREG ? d : 0][m] = v;
+        else
+          am_lds[d < AREG ? 0 : d - AREG][m][tid] = v;  // read back by this thread only
+      }
+  } else {
+    // row x of the tile (natural row bitrev(x)) is one ChaCha block per digit;
+    // thread i expands rows i + THREADS s and files value k under consumer
+    // thread (x mod TPB) CF + k, slot x / TPB
+    auto fill = [&](int d, int slot) {
+#pragma unroll
+      for (int s = 0; s < ((1 << LRB) + THREADS - 1) / THREADS; ++s) {
+        const int x = tid + THREADS * s;
+        if (x >= (1 << LRB)) break;
+        const int p = (int)(bitrev((uint32_t)x, LRB) << LRC) + c0;
+        uint32_t w[16];
+        chacha_block<ROUNDS>(A.seed, (uint32_t)(p >> 3), 0u, (uint32_t)d, (uint32_t)kj, w);
+        uint32_t v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = word_pair_to_mont(w[2 * k], w[2 * k + 1], r, rinv);
+        uint4* dst = reinterpret_cast<uint4*>(&am_lds[slot][x / TPB][(x % TPB) * CF]);
+        dst[0] = make_uint4(v[0], v[1], v[2], v[3]);
+        dst[1] = make_uint4(v[4], v[5], v[6], v[7]);
+        // one block at a time: interleaved ChaCha states would take every register
+        asm volatile("" ::: "memory");
+      }
+    };
+#pragma unroll
+    for (int d = 0; d < AREG; ++d) {
+      fill(d, 0);
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < E; ++m) am[d][m] = am_lds[0][m][tid];
+      __syncthreads();
+    }
+#pragma unroll
+    for (int d = AREG; d < BETA; ++d) fill(d, d - AREG);
+    __syncthreads();
+  }
+  // the a half is on chip: store the twiddle words and reduce b
+  if constexpr (!EARLY) {
+    asm volatile("" ::: "memory");
+    fetch_b();
+    issue(0, 0, en);
+  }
+  if constexpr (TWL) {
+#pragma unroll
+    for (int i = 0; i < TWN; ++i) {
+      const int w = tid + THREADS * i;
+      if (w < CF * TWW) twl[w] = twv[i];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int d = 0; d < BETA; ++d)
+#pragma unroll
+    for (int m = 0; m < E; ++m) bm[d][m] = redc(bm[d][m], r, rinv);
 #pragma unroll 1
   for (int b = 0; b < A.batch; ++b) {
     // the a values in LDS are re-read for every item (an opaque base keeps the
