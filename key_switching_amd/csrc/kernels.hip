@@ -793,20 +793,27 @@ struct ModUpIPArgs {
   int N, level, K, L, alpha, batch, key_level;
 };
 
-// Columns per fused tile: one ChaCha block (8 consecutive positions) per row.
-constexpr int kFusedCols = 8;
+// Columns per fused tile: whole ChaCha blocks (8 consecutive positions) per
+// row. 256-point blocks of 16 words per thread (N = 2^16) take 16 columns, so
+// that the key's, c1's and the outputs' runs are 64 bytes long (measured: 8
+// columns 150 us per batch-8 launch, and with 16-byte runs 227 us); other
+// shapes take 8.
+template <int LOGN>
+constexpr int fused_cols() {
+  return (Cfg<LOGN>::LRB == 8 && Cfg<LOGN>::LEB == 4) ? 16 : 8;
+}
 // Key values a thread keeps per half (beta digits x its E positions): larger
 // shapes take the separate block pass and inner product.
 constexpr int kFusedKeyValues = 64;
 
 template <int LOGN>
 constexpr int fused_threads() {
-  return kFusedCols << (Cfg<LOGN>::LRB - Cfg<LOGN>::LEB);
+  return fused_cols<LOGN>() << (Cfg<LOGN>::LRB - Cfg<LOGN>::LEB);
 }
 // a-half digits kept in registers (the rest sit in LDS), and the waves per
-// SIMD the register budget is cut for: at N = 2^16 a 4-digit tile in 128
-// threads then takes 33 KB of LDS and at most 256 registers, so that four
-// workgroups share a CU and the 960 tiles of 30 limbs run in one wave of
+// SIMD the register budget is cut for: at N = 2^16 a 4-digit tile in 256
+// threads then takes 78 KB of LDS and at most 256 registers, so that two
+// workgroups share a CU and the 480 tiles of 30 limbs run in one wave of
 // workgroups
 template <int LOGN, int BETA>
 constexpr int fused_areg() {
@@ -817,34 +824,37 @@ constexpr int fused_waves() {
   return 2;
 }
 
-// LDS layout of a fused tile (8 blocks): the block pass's padded rows, col(x) =
-// x + x/16 at N = 2^16, with row(k) = 272 k + 4 (k >> 1). The exchange's two
-// patterns put the blocks k, k + 1 of a half-wave 16 banks apart, as in the
-// pass's own layout, and the transposed read of x = rest + 16 m across the 8
-// blocks (4 rests per half-wave) starts the blocks on the 8 distinct multiples
-// of 4, so every access covers 32 distinct banks (the pass's own skew, k/2, is
-// made for 32 blocks and conflicts up to 4 ways here). Other shapes keep the
-// pass's layout.
-template <int LRB, int LEB>
+// LDS layout of a fused tile of C blocks (8 or 16): the block pass's padded
+// rows, col(x) = x + x/16 at N = 2^16, with row(k) = 272 k + (32/C)(k >> 1).
+// The exchange's two patterns put the blocks k, k + 1 of a half-wave 16 banks
+// apart, as in the pass's own layout, and the transposed read of x = rest +
+// 16 m across the C blocks (32/C rests per half-wave) starts the blocks on the
+// C distinct multiples of 32/C, so every access covers 32 distinct banks (the
+// pass's own skew, k/2, is made for 32 blocks). Other shapes keep the pass's
+// layout.
+template <int LRB, int LEB, int C>
 struct FusedLay : BlkLds<LRB, LEB> {
   using Base = BlkLds<LRB, LEB>;
-  static constexpr bool K8 = Base::SWZ;
-  __device__ __forceinline__ static int row(int k) { return K8 ? k * Base::S + 4 * (k >> 1) : Base::row(k); }
-  static constexpr int words(int c) { return K8 ? c * Base::S + 4 * ((c - 1) >> 1) : Base::words(c); }
+  static constexpr bool SK = Base::SWZ;
+  static constexpr int SKEW = 32 / C;
+  static_assert(!SK || C == 8 || C == 16, "skew made for 8 or 16 blocks");
+  __device__ __forceinline__ static int row(int k) { return SK ? k * Base::S + SKEW * (k >> 1) : Base::row(k); }
+  static constexpr int words(int c) { return SK ? c * Base::S + SKEW * ((c - 1) >> 1) : Base::words(c); }
 };
 
-// Tile quads: the four tiles that share each row's 128-byte line run on one
-// XCD in consecutive slots (xcd_unit with 4 groups), so the 32-byte runs of
-// their loads and stores meet in that XCD's L2.
+// Tile groups: the 128 / (4 CF) tiles that share each row's 128-byte line run
+// on one XCD in consecutive slots (xcd_unit with that many groups), so the
+// runs of their loads and stores meet in that XCD's L2.
 template <int LOGN, int BETA, int ROUNDS, bool STORED>
 __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_modup_ip(ModUpIPArgs A) {
   using C = Cfg<LOGN>;
-  constexpr int LRC = C::LRC, LRB = C::LRB, LEB = C::LEB, CF = kFusedCols;
+  constexpr int LRC = C::LRC, LRB = C::LRB, LEB = C::LEB, CF = fused_cols<LOGN>();
+  constexpr int G = 32 / CF, CB = CF / 8;  // tiles per 128-byte line, ChaCha blocks per tile row
   constexpr int E = 1 << LEB, TPB = 1 << (LRB - LEB), THREADS = CF * TPB, RB = LRB / LEB;
   constexpr int AREG = fused_areg<LOGN, BETA>(), NS = BETA - AREG > 0 ? BETA - AREG : 1;
-  static_assert(CF == 8, "a tile row is one ChaCha block");
-  static_assert(((1 << LRC) / CF) % 4 == 0, "tiles group into quads");
-  using Lay = FusedLay<LRB, LEB>;
+  static_assert(CF % 8 == 0 && 32 % CF == 0, "a tile row is whole ChaCha blocks within a 128-byte line");
+  static_assert(((1 << LRC) / CF) % G == 0, "tiles group by line");
+  using Lay = FusedLay<LRB, LEB, CF>;
   __shared__ uint32_t lds[Lay::words(CF)];
   __shared__ uint32_t am_lds[NS][E][THREADS];  // [digit - AREG][slot][consumer thread]
   // 256-point blocks of 16 words per thread (N = 2^16): the tile's twiddles
@@ -856,9 +866,9 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
   __shared__ __align__(16) uint32_t twl[TWL ? CF * TWW : 4];
   const int tid = (int)threadIdx.x;
   const int lk = A.level + A.K;
-  int quad, j, g;
-  if (!xcd_unit((1 << LRC) / CF / 4, lk, 4, quad, j, g)) return;
-  const int c0 = (quad * 4 + g) * CF;
+  int line, j, g;
+  if (!xcd_unit((1 << LRC) / CF / G, lk, G, line, j, g)) return;
+  const int c0 = (line * G + g) * CF;
   // consumer layout (after the block pass's transpose): column c0 + kk, rows
   // bitrev(rest + TPB m). rest fills the low LRB - LEB bits and TPB m the top
   // LEB, so position m = pos0 + (bitrev(m, LEB) << LRC): one per-lane offset,
@@ -1010,21 +1020,23 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
           am_lds[d < AREG ? 0 : d - AREG][m][tid] = v;  // read back by this thread only
       }
   } else {
-    // row x of the tile (natural row bitrev(x)) is one ChaCha block per digit;
-    // thread i expands rows i + THREADS s and files value k under consumer
-    // thread (x mod TPB) CF + k, slot x / TPB
+    // row x of the tile (natural row bitrev(x)) is CB ChaCha blocks per digit;
+    // thread i expands units u = i + THREADS s (row u / CB, block h = u mod CB)
+    // and files value k under consumer thread (x mod TPB) CF + 8 h + k, slot
+    // x / TPB
     auto fill = [&](int d, int slot) {
 #pragma unroll
-      for (int s = 0; s < ((1 << LRB) + THREADS - 1) / THREADS; ++s) {
-        const int x = tid + THREADS * s;
-        if (x >= (1 << LRB)) break;
-        const int p = (int)(bitrev((uint32_t)x, LRB) << LRC) + c0;
+      for (int s = 0; s < ((1 << LRB) * CB + THREADS - 1) / THREADS; ++s) {
+        const int u = tid + THREADS * s;
+        if (u >= (1 << LRB) * CB) break;
+        const int x = u / CB, h = u % CB;
+        const int p = (int)(bitrev((uint32_t)x, LRB) << LRC) + c0 + 8 * h;
         uint32_t w[16];
         chacha_block<ROUNDS>(A.seed, (uint32_t)(p >> 3), 0u, (uint32_t)d, (uint32_t)kj, w);
         uint32_t v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = word_pair_to_mont(w[2 * k], w[2 * k + 1], r, rinv);
-        uint4* dst = reinterpret_cast<uint4*>(&am_lds[slot][x / TPB][(x % TPB) * CF]);
+        uint4* dst = reinterpret_cast<uint4*>(&am_lds[slot][x / TPB][(x % TPB) * CF + 8 * h]);
         dst[0] = make_uint4(v[0], v[1], v[2], v[3]);
         dst[1] = make_uint4(v[4], v[5], v[6], v[7]);
         // one block at a time: interleaved ChaCha states would take every register
@@ -2076,7 +2088,8 @@ hipError_t launch_modup_ip(const pc_params* p, const uint32_t* ct, uint64_t ct_s
   const int lk = (int)(level + p->K);
   LaunchTimer tm(p, KID_MODUP_IP, s);
   PC_DISPATCH_LOGN(p->log2n, {
-    const dim3 grid(xcd_grid((1 << Cfg<LN>::LRC) / kFusedCols / 4, lk, 4));
+    constexpr int CF = fused_cols<LN>(), G = 32 / CF;
+    const dim3 grid(xcd_grid((1 << Cfg<LN>::LRC) / CF / G, lk, G));
     switch (beta) {
       case 1: launch_modup_ip_kernel<LN, 1>(p, A, grid, s); break;
       case 2: launch_modup_ip_kernel<LN, 2>(p, A, grid, s); break;
