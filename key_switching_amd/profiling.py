@@ -85,6 +85,32 @@ FAMILIES_N17 = {
 }
 FAMILY_SETS = {"n16": FAMILIES, "n17": FAMILIES_N17}
 
+# Kernels whose grid does not grow with the batch (the fused tile loops over
+# the items): a dispatch is the family's batch-8 launch when the dispatch just
+# before it on its queue is the batch-8 launch (largest grid) of the kernel
+# named here, the one that precedes it in every key switch.
+FOLLOWS = {"k_modup_ip<16, 4, 12, false>": "k_modup_bconv<16, 6, 3>"}
+
+
+def _batch8_ids(disp, prefix):
+    """Dispatch ids of the batch-8 launch of `prefix` and its grid. disp maps a
+    dispatch id (int) to (queue, short kernel name, grid)."""
+    mine = [d for d, (_, k, _) in disp.items() if k == prefix]
+    if not mine:
+        return [], 0
+    g = max(disp[d][2] for d in mine)
+    if prefix not in FOLLOWS:
+        return sorted(d for d in mine if disp[d][2] == g), g
+    pred = FOLLOWS[prefix]
+    pg = max((gg for (_, k, gg) in disp.values() if k == pred), default=-1)
+    prev, out = {}, []
+    for d in sorted(disp):
+        q, k, gg = disp[d]
+        if k == prefix and q in prev and prev[q] == (pred, pg):
+            out.append(d)
+        prev[q] = (k, gg)
+    return out, g
+
 
 def device_source_hash() -> str:
     h = hashlib.sha256()
@@ -106,11 +132,10 @@ def _grid(row: dict) -> int:
 
 
 def _family_rows(rows, prefix):
-    mine = [r for r in rows if _short(r["Kernel_Name"]) == prefix]
-    if not mine:
-        return [], 0
-    g = max(_grid(r) for r in mine)
-    return [r for r in mine if _grid(r) == g], g
+    disp = {int(r["Dispatch_Id"]): (r.get("Queue_Id", ""), _short(r["Kernel_Name"]), _grid(r)) for r in rows}
+    ids, g = _batch8_ids(disp, prefix)
+    keep = set(ids)
+    return [r for r in rows if int(r["Dispatch_Id"]) in keep], g
 
 
 def cmd_stats(a) -> str:
@@ -120,7 +145,9 @@ def cmd_stats(a) -> str:
            f"device_sources_hash: {device_source_hash()}", ""]
     if a.note:
         out += [a.note, ""]
-    out += ["Per kernel family, dispatches of its batch-8 launch (largest grid of that kernel in the run):", "",
+    out += ["Per kernel family, dispatches of its batch-8 launch (largest grid of that kernel in the run; for "
+            "the fused tile, whose grid does not grow with the batch, the dispatches that follow a batch-8 "
+            "base conversion):", "",
            "| family | dispatch | grid | launches | avg us | median us | min us | max us |",
            "|---|---|---|---|---|---|---|---|"]
     for fam, prefix in FAMILIES.items():
@@ -141,18 +168,21 @@ def cmd_stats(a) -> str:
 
 
 def _counter_per_dispatch(path: str, counter: str):
-    per = {}
+    """Counter value per dispatch, keyed (dispatch id, short name, grid), and the
+    dispatch table (id -> queue, short name, grid) of the file."""
+    per, disp = {}, {}
     for r in csv.DictReader(open(path)):
+        disp[int(r["Dispatch_Id"])] = (r.get("Queue_Id", ""), _short(r["Kernel_Name"]), _grid(r))
         if r["Counter_Name"] != counter:
             continue
         key = (r["Dispatch_Id"], _short(r["Kernel_Name"]), _grid(r))
         per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
-    return per
+    return per, disp
 
 
 def cmd_traffic(a) -> str:
-    f = _counter_per_dispatch(a.fetch, "FETCH_SIZE")
-    w = _counter_per_dispatch(a.write, "WRITE_SIZE")
+    f, fdisp = _counter_per_dispatch(a.fetch, "FETCH_SIZE")
+    w, wdisp = _counter_per_dispatch(a.write, "WRITE_SIZE")
     cf = [v for (d, k, g), v in f.items() if COPY_KERNEL_HINT in k.lower()]
     cw = [v for (d, k, g), v in w.items() if COPY_KERNEL_HINT in k.lower()]
     if not cf or not cw:
@@ -176,13 +206,14 @@ def cmd_traffic(a) -> str:
             continue
         g = max(gg for (_, gg) in fk)
 
-        def pick(m):
-            ds = sorted((d for (d, gg) in m if gg == g), key=int)
+        def pick(m, disp):
+            ids, _ = _batch8_ids(disp, prefix)
+            ds = [str(d) for d in ids if (str(d), g) in m]
             if parity is not None:
                 ds = ds[parity::2]
             return [m[(d, g)] for d in ds]
 
-        kf, kw = pick(fk), pick(wk)
+        kf, kw = pick(fk, fdisp), pick(wk, wdisp)
         fb = statistics.median(kf) * 1024.0 * rf
         wb = statistics.median(kw) * 1024.0 * rw
         out.append(f"| {fam} | `{prefix}` | {g} | {len(kf)} | {statistics.median(kf):.0f} | "
@@ -253,11 +284,12 @@ VALU_COUNTERS = ("SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_WAVES", "SQ_BUSY_CY
 def _per_dispatch(path: str):
     rows, meta = {}, {}
     for r in csv.DictReader(open(path)):
-        d = r["Dispatch_Id"]
+        d = int(r["Dispatch_Id"])
         rows.setdefault(d, {})[r["Counter_Name"]] = rows.get(d, {}).get(r["Counter_Name"], 0.0) + float(
             r["Counter_Value"])
         meta[d] = (_short(r["Kernel_Name"]), _grid(r), int(r.get("VGPR_Count", 0) or 0),
-                   (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3, r["Kernel_Name"])
+                   (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3, r["Kernel_Name"],
+                   r.get("Queue_Id", ""))
     return rows, meta
 
 
@@ -284,11 +316,9 @@ def cmd_valu(a) -> str:
     for fam, prefix in FAMILIES.items():
         if fam not in bench.KERNELS and fam != "modup_ip":
             continue
-        ds = [d for d, m in meta.items() if m[0] == prefix]
+        ds, g = _batch8_ids({d: (m[5], m[0], m[1]) for d, m in meta.items()}, prefix)
         if not ds:
             continue
-        g = max(meta[d][1] for d in ds)
-        ds = [d for d in ds if meta[d][1] == g]
 
         def med(c):
             return statistics.median(rows[d].get(c, 0.0) for d in ds)
