@@ -817,7 +817,7 @@ constexpr int fused_threads() {
 // workgroups
 template <int LOGN, int BETA>
 constexpr int fused_areg() {
-  return LOGN == 16 ? 1 : LOGN == 17 ? (BETA < 3 ? BETA : 3) : 0;
+  return LOGN == 16 ? (BETA < 2 ? BETA : 2) : LOGN == 17 ? (BETA < 3 ? BETA : 3) : 0;
 }
 template <int LOGN>
 constexpr int fused_waves() {
@@ -855,7 +855,13 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
   static_assert(CF % 8 == 0 && 32 % CF == 0, "a tile row is whole ChaCha blocks within a 128-byte line");
   static_assert(((1 << LRC) / CF) % G == 0, "tiles group by line");
   using Lay = FusedLay<LRB, LEB, CF>;
-  __shared__ uint32_t lds[Lay::words(CF)];
+  // with TWL the exchange/transpose tile is double-buffered (NB = 2): steps
+  // that run the block pass alternate between the buffers, so a step needs one
+  // barrier, between its transposed write and read (a wave that reaches the
+  // next step's barrier has finished this step's reads)
+  constexpr int NB = LRB == 8 && LEB == 4 ? 2 : 1;
+  constexpr int TW = Lay::words(CF);
+  __shared__ uint32_t lds[NB * TW];
   __shared__ uint32_t am_lds[NS][E][THREADS];  // [digit - AREG][slot][consumer thread]
   // 256-point blocks of 16 words per thread (N = 2^16): the tile's twiddles
   // sit on chip for the whole batch (TWW words per block in twl, the rest in
@@ -963,10 +969,11 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
       q4(tblk + 144 + 4 * t, W + 11);
     }
   };
-  uint32_t* const lrow = lds + Lay::row(k);
+  uint32_t* const lrow0 = lds + Lay::row(k);
   // the transposed tile: slot m of this thread at row(kk) + col(rest) + m col(TPB)
   // (col(x) adds x/16 or x/8, and TPB is a multiple of that divisor)
-  const uint32_t* const tcol = lds + Lay::row(kk) + Lay::col(rest);
+  const uint32_t* const tcol0 = lds + Lay::row(kk) + Lay::col(rest);
+  int buf = 0;  // the buffer of the next step that runs the block pass
   constexpr int TSTEP = (1 << LRB) / E == TPB ? TPB + (Lay::SWZ ? TPB / 16 : Lay::SWZ9 ? TPB / 8 : 0) : 0;
   static_assert(TSTEP > 0, "transposed slot stride");
   const int own_d = j < A.level ? j / A.alpha : -1;  // the digit whose own limb is j
@@ -1092,6 +1099,8 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
         asm volatile("" ::: "memory");
       }
       if (d != own_d) {
+        uint32_t* const lrow = lrow0 + (NB == 2 ? buf * TW : 0);
+        const uint32_t* const tcol = tcol0 + (NB == 2 ? buf * TW : 0);
         int zero = 0;
         asm volatile("" : "+s"(zero));  // keeps the twiddle loads in the loop
 #pragma unroll
@@ -1110,7 +1119,8 @@ __global__ void __launch_bounds__(fused_threads<LOGN>(), fused_waves<LOGN>()) k_
         __syncthreads();
 #pragma unroll
         for (int m = 0; m < E; ++m) e[m] = tcol[TSTEP * m];
-        __syncthreads();
+        if constexpr (NB == 1) __syncthreads();
+        buf ^= 1;
       }
       // the sums of dot_redc, one digit at a time: products below r 2^31, a
       // fold after the fourth and after every further pair
