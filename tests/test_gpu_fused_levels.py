@@ -67,3 +67,28 @@ def test_fused_tile_every_digit_count(prm, level):
             diff = np.flatnonzero(got[i].astype(np.uint64).reshape(-1) != want[b].reshape(-1))
             assert diff.size == 0, (f"level {level} ({LEVELS[level]} digits), {label}, item {b}: "
                                     f"{diff.size} words differ from the oracle, first at {diff[0]}")
+
+
+@pytest.mark.parametrize("level", [24, 9])
+def test_fused_tile_chacha20(level):
+    """The same tile with the a half expanded by ChaCha20 (the 20-round build of
+    the expander), against the oracle with the same round count."""
+    assert torch.cuda.is_available(), "these tests need the GPU"
+    torch.cuda.set_device(0)
+    oprm = ks.Params(16, 24, 4, 6, chacha_rounds=20)
+    p = ksa.Params(16, 24, 4, 6, device=0, chacha_rounds=20, max_batch=3)
+    try:
+        assert tuple(p.primes) == oprm.primes
+        widx = ki.WORKLOADS["n16"].index * 1000 + 500 + level
+        cts = ki.ciphertexts(widx, oprm.q[:level], oprm.N, 3)
+        key = cases.uniform_keys(oprm, widx, level, [1])[0]
+        out = ksa.keyswitch_ex(p, ksa.to_device(cts, 0), [ksa.to_device(key.b, 0)], [1], level, seeds=[key.seed])
+        torch.cuda.synchronize()
+        got = ksa.to_host(out)[0]
+        for b in range(3):
+            want = ks.keyswitch(oprm, cts[b], key, level)
+            diff = np.flatnonzero(got[b].astype(np.uint64).reshape(-1) != want.reshape(-1))
+            assert diff.size == 0, f"level {level}, ChaCha20, item {b}: {diff.size} words differ, first at {diff[0]}"
+    finally:
+        torch.cuda.synchronize()
+        p.close()
