@@ -7,7 +7,9 @@ only with four digits (level 24), so this test runs one relinearisation key at
 levels whose digit counts are 1 to 4, with full and ragged last digits, at
 batch 3 and batch 1, with the a half regenerated and stored, and compares
 every output item word for word with a live run of the oracle (the uniform key
-halves of the full-size recipe; inputs from ks_inputs).
+halves of the full-size recipe; inputs from ks_inputs). At N = 2^17 the tile
+has 8 columns and loads its twiddles per round; it is checked at three levels
+below the top one against the C++ oracle tier.
 """
 
 import os
@@ -92,3 +94,38 @@ def test_fused_tile_chacha20(level):
     finally:
         torch.cuda.synchronize()
         p.close()
+
+
+# N = 2^17, L = 40, dnum = 5, K = 8 (the 8-column tile with per-round twiddle
+# loads): 7+7+7+7+5, 2+2+2+2 and 1+1+1 primes per digit
+N17_LEVELS = {33: 5, 8: 4, 3: 3}
+
+
+@pytest.mark.parametrize("level", sorted(N17_LEVELS))
+def test_fused_tile_n17_levels(level):
+    """One relinearisation key at N = 2^17 below the top level, batch 2, against the
+    C++ oracle tier (equal to the numpy oracle word for word, pinned by the CPU
+    tests; used here for its speed at this ring size)."""
+    from oracle import o2
+    assert torch.cuda.is_available(), "these tests need the GPU"
+    torch.cuda.set_device(0)
+    oprm = cases.n17_params()
+    assert len(oprm.digits(level)) == N17_LEVELS[level]
+    O = o2.O2(oprm.log2n, oprm.L, oprm.dnum, oprm.K)
+    p = ksa.Params(oprm.log2n, oprm.L, oprm.dnum, oprm.K, device=0, max_batch=2)
+    try:
+        assert tuple(p.primes) == oprm.primes and tuple(O.primes) == oprm.primes
+        widx = ki.WORKLOADS["n17"].index * 1000 + level
+        cts = ki.ciphertexts(widx, oprm.q[:level], oprm.N, 2)
+        key = cases.uniform_keys(oprm, widx, level, [1])[0]
+        out = ksa.keyswitch_ex(p, ksa.to_device(cts, 0), [ksa.to_device(key.b, 0)], [1], level, seeds=[key.seed])
+        torch.cuda.synchronize()
+        got = ksa.to_host(out)[0]
+        for b in range(2):
+            want = O.keyswitch(cts[b], level, 1, key.b, seed=key.seed)
+            diff = np.flatnonzero(got[b].reshape(-1) != want.reshape(-1))
+            assert diff.size == 0, f"N=2^17 level {level}, item {b}: {diff.size} words differ, first at {diff[0]}"
+    finally:
+        torch.cuda.synchronize()
+        p.close()
+        O.close()
