@@ -795,9 +795,10 @@ struct ModUpIPArgs {
 
 // Columns per fused tile: whole ChaCha blocks (8 consecutive positions) per
 // row. 256-point blocks of 16 words per thread (N = 2^16) take 16 columns, so
-// that the key's, c1's and the outputs' runs are 64 bytes long (measured: 8
-// columns 150 us per batch-8 launch, and with 16-byte runs 227 us); other
-// shapes take 8.
+// that the key's, c1's and the outputs' runs are 64 bytes long (measured per
+// batch-8 launch: 8 columns 150 us, 16 columns 139 us, 32 columns 154 us with
+// 16 CUs idle, and with the block pass's own order, 16-byte runs, 227 us);
+// other shapes take 8.
 template <int LOGN>
 constexpr int fused_cols() {
   return (Cfg<LOGN>::LRB == 8 && Cfg<LOGN>::LEB == 4) ? 16 : 8;
@@ -812,9 +813,9 @@ constexpr int fused_threads() {
 }
 // a-half digits kept in registers (the rest sit in LDS), and the waves per
 // SIMD the register budget is cut for: at N = 2^16 a 4-digit tile in 256
-// threads then takes 78 KB of LDS and at most 256 registers, so that two
-// workgroups share a CU and the 480 tiles of 30 limbs run in one wave of
-// workgroups
+// threads then takes 81 KB of LDS (two a digits, the double-buffered exchange
+// tile and the twiddles) and at most 256 registers, so that two workgroups
+// share a CU and the 480 tiles of 30 limbs run in one wave of workgroups
 template <int LOGN, int BETA>
 constexpr int fused_areg() {
   return LOGN == 16 ? (BETA < 2 ? BETA : 2) : LOGN == 17 ? (BETA < 3 ? BETA : 3) : 0;
