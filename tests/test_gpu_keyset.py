@@ -78,6 +78,9 @@ def test_generated_bundle_small_ring(full):
                 assert e is not None and np.abs(e).max() <= ks.error_bound(oprm, level, emax, 32)
         sub = host(ksa.keyswitch_keyset(prm, bundle, dev(cts), [2, 0], level))
         assert np.array_equal(sub[0], out[2]) and np.array_equal(sub[1], out[0])
+        # the relinearisation key alone takes the fused ModUp/inner-product tile
+        one = host(ksa.keyswitch_keyset(prm, bundle, dev(cts), [2], level))
+        assert np.array_equal(one[0], out[2]), full
         with pytest.raises(ksa.PcError):
             ksa.keyswitch_keyset(prm, bundle, dev(cts), [3], level)
     prm.close()
@@ -102,4 +105,23 @@ def test_hoisted16_from_bundle_every_key(full):
         sub = host(ksa.keyswitch_keyset(prm, bundle, dev(c.cts), pick, c.level))
         for n, r in enumerate(pick):
             assert cases.digest(sub[n, 0]) == want[r], f"selected key {r}"
+    prm.close()
+
+
+@pytest.mark.parametrize("full", [False, True])
+def test_relinearisation_key_from_bundle_every_item(full):
+    """The headline's relinearisation key (N = 2^16, L = 24) in a bundle, drawn alone
+    for the batch of 8 (the fused tile with the bundle's b half and seed, or with its
+    stored a half); every item against the oracle's digests."""
+    c = cases.case_n16_relin_k8()
+    doc = cases.load_digests()
+    assert doc["sources_hash"] == cases.sources_hash()
+    want = doc["cases"][c.name]["digests"]
+    prm = ksa.Params(c.prm.log2n, c.prm.L, c.prm.dnum, c.prm.K, device=0, max_batch=8)
+    key = c.keys[0]
+    with ksa.KeySet(prm, c.level, [key.galois], full=full) as bundle:
+        bundle.set(0, dev(key.b), key.seed)
+        out = host(ksa.keyswitch_keyset(prm, bundle, dev(c.cts), [0], c.level))
+        for b in range(c.batch):
+            assert cases.digest(out[0, b]) == want[b], f"item {b} (full={full})"
     prm.close()
