@@ -2,8 +2,9 @@
 
 Two calls in a row through the C ABI, the second with a smaller input (a lower
 level, so less of the shared scratch is written and the first call's contents
-stay in the rest of it); every output word must equal pc_keyswitch_ex's on the
-same inputs. Shapes whose workspace exceeds the scratch are refused.
+stay in the rest of it), then a third with one relinearisation key (the fused
+ModUp/inner-product tile); every output word must equal pc_keyswitch_ex's on
+the same inputs. Shapes whose workspace exceeds the scratch are refused.
 """
 
 import numpy as np
@@ -28,7 +29,8 @@ def test_static_matches_ex_on_two_calls_the_second_smaller():
     w = ki.WORKLOADS["n16"]
     prm = ksa.Params(w.log2n, w.L, w.dnum, w.K, max_batch=8, max_hoist=2, device=0)
     q = prm.primes[: w.L]
-    calls = [(w.L, [1, 5]), (12, [2 * w.N - 1])]  # two keys at level 24, then one key at level 12
+    # two keys at level 24, then one key at level 12, then the relinearisation key at level 20
+    calls = [(w.L, [1, 5]), (12, [2 * w.N - 1]), (20, [1])]
     for n, (level, galois) in enumerate(calls):
         basis, beta = prm.basis(level), prm.beta(level)
         keys = [ksa.to_device(ki.uniform_key_b(90 + n, k, beta, basis, w.N), 0) for k in range(len(galois))]
